@@ -1,0 +1,229 @@
+/*
+ * moe.h -- C ABI of the routed MoE expert layer for MI355X (gfx950).
+ *
+ * The layer is the expert block of a sparse mixture-of-experts decoder: every
+ * token is sent to k routed experts out of E, each expert is a SwiGLU
+ * feed-forward block with block-scaled FP4 weights, and the k expert outputs
+ * are mixed by the router's weights. The FreeToken pages describe this
+ * sparsity as what makes edge serving of very large models possible
+ * (winzheng.com page, "Why Now of All Times": six routed experts per token in
+ * each of 43 decoder layers, an FP4 expert pool of about 140 GB that can live
+ * in host memory and be loaded on demand) and list MXFP4, NVFP4, FP8 and BF16
+ * weights (aimodeling.com/en page, "Reported Numbers and Ecosystem Position").
+ * The expert cache calls follow the pages' global LRU expert cache and
+ * full-layer double-buffered prefill streaming (winzheng.com page,
+ * "FreeToken's Three-Layer Mechanism"; aimodeling.com/en page, "Three
+ * Engineering Cores").
+ *
+ * Conventions for every call below
+ *   - Pointers are device pointers unless marked (host).
+ *   - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL is the
+ *     null stream); the call returns once the work is enqueued.
+ *   - Return value: MOE_OK (0) or a negative moe_err. Argument errors are
+ *     detected before anything is enqueued and leave every output untouched.
+ *     A HIP launch/copy failure returns MOE_EHIP; moe_last_hip_error() gives
+ *     the HIP code. Faults inside kernels surface at the caller's next
+ *     synchronisation, as for any HIP kernel.
+ *   - The caller owns and allocates all buffers (activations, logits, ids,
+ *     offsets, outputs, workspaces, the expert-cache pool). The layer calls
+ *     allocate nothing; only expert_cache_reserve allocates (its small device
+ *     table and host metadata).
+ *   - bf16 values are passed as uint16_t bit patterns.
+ *   - Token-pair numbering: pair p = t*k + j is the j-th expert (in routing
+ *     order) of token t.
+ *
+ * Expert weight layout (one contiguous blob per expert, described by
+ * moe_expert_w): W13 has 2I rows of length H (rows 0..I-1 are the gate
+ * projection W1, rows I..2I-1 the up projection W3); W2 has H rows of length I.
+ *   MOE_W_MXFP4: rows of E2M1 codes, two per byte, the even element in the low
+ *                nibble; one E8M0 scale byte per 32 consecutive elements of a
+ *                row (scales [rows][K/32], row-major).
+ *   MOE_W_BF16 : rows of bf16; scale pointers are ignored.
+ * All weight row starts must be 16-byte aligned.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MOE_OK = 0,
+    MOE_EINVAL = -1,        /* bad argument (size, null pointer, small workspace) */
+    MOE_ENOMEM = -2,        /* not enough cache slots / host memory */
+    MOE_EHIP = -3,          /* a HIP call failed; see moe_last_hip_error() */
+    MOE_EUNSUPPORTED = -4,  /* valid request this build does not handle */
+    MOE_EBUSY = -5          /* resource in use */
+} moe_err;
+
+typedef enum { MOE_W_BF16 = 0, MOE_W_MXFP4 = 1 } moe_wfmt;
+
+/* One expert's weights. w13/w2 point to codes (MXFP4) or bf16 values; s13/s2
+ * to E8M0 scales (MXFP4 only). */
+typedef struct {
+    const void *w13;
+    const uint8_t *s13;
+    const void *w2;
+    const uint8_t *s2;
+} moe_expert_w;
+
+/* Human-readable text for a moe_err. Never NULL. */
+const char *moe_strerror(int err);
+/* HIP error code of the last MOE_EHIP returned on this host thread. */
+int moe_last_hip_error(void);
+
+/*
+ * moe_route -- router: top-k expert choice and mixing weights per token.
+ *
+ * Logits come either from logits_in [T][E] fp32, or (when logits_in is NULL)
+ * from the router gate: logit[t][e] = sum_h x[t][h] * wg[e][h] over bf16 x
+ * [T][H] and wg [E][H], formed in fp32 in a fixed order (lane l of 64 sums,
+ * in ascending h, the products of the 8-element chunks c with c mod 64 == l;
+ * the 64 partial sums are then combined by a butterfly with partner distances
+ * 32,16,8,4,2,1), so that the choice of experts is reproducible bit for bit.
+ * logits_out [T][E] (optional) receives the logits used.
+ *
+ * Selection: the k largest logits per token, in descending order; equal
+ * logits are taken lower expert index first. topk_ids [T][k] int32.
+ * Weights topk_w [T][k] fp32:
+ *   renormalize != 0: w_j = exp(l_j - l_0) / sum_{i<k} exp(l_i - l_0)
+ *                     (softmax over all E, renormalised over the k chosen)
+ *   renormalize == 0: w_j = exp(l_j - l_max) / sum_{e<E} exp(l_e - l_max)
+ * Requires 1 <= k <= min(E, 64), E <= 1024, T >= 0, H % 8 == 0 for the gate.
+ * Logits must be finite (non-finite logits give unspecified routing).
+ */
+int moe_route(const uint16_t *x_bf16, const uint16_t *wg_bf16, const float *logits_in,
+              float *logits_out, int T, int H, int E, int k, int renormalize,
+              int32_t *topk_ids, float *topk_w, void *stream);
+
+/*
+ * moe_permute -- group the T*k token pairs by expert (stable counting sort).
+ *
+ * offsets [E+1]: offsets[e] = number of pairs routed to experts < e,
+ *                offsets[E] = T*k (pairs of expert e are rows
+ *                offsets[e] .. offsets[e+1]-1 of sorted order);
+ * sorted_pair [T*k]: sorted_pair[offsets[e] + r] = the r-th pair, in
+ *                ascending p, routed to expert e;
+ * pair_row [T*k]: inverse, pair_row[sorted_pair[r]] = r.
+ * ws: device workspace of at least the permute size from moe_workspace_size.
+ * Requires E <= 512. Ids outside [0, E) are skipped (not counted; their
+ * pair_row entry is left unwritten), so offsets[E] < T*k flags them.
+ * T = 0 writes offsets only.
+ */
+int moe_permute(const int32_t *topk_ids, int T, int k, int E, int32_t *offsets,
+                int32_t *sorted_pair, int32_t *pair_row, void *ws, size_t ws_bytes,
+                void *stream);
+
+/*
+ * moe_expert_ffn -- grouped SwiGLU expert FFN over the permuted pairs.
+ *
+ * For every row r of sorted order, with e its expert (offsets[e] <= r <
+ * offsets[e+1]) and t = sorted_pair[r] / k its token:
+ *   g = W1_e x_t, u = W3_e x_t, a = silu(g) * u (silu(g) = g / (1 + e^-g)),
+ *   y[sorted_pair[r]] = W2_e a.
+ * y [T*k][H] is written in pair order (row p = t*k + j), bf16 (y_is_fp32 = 0)
+ * or fp32. Accumulation is fp32; the activation a is rounded to bf16 between
+ * the two contractions.
+ * experts: device array [E] of moe_expert_w; entries of experts that receive
+ * no pair are never read. x_bf16 [T][H]. H and I must be multiples of 32.
+ * ws: device workspace of at least the ffn size from moe_workspace_size.
+ * The shared (always-on) expert is this call with E = 1, k = 1,
+ * sorted_pair = 0..T-1 and offsets = {0, T}.
+ */
+int moe_expert_ffn(const uint16_t *x_bf16, const int32_t *sorted_pair, const int32_t *offsets,
+                   const moe_expert_w *experts, int fmt, int T, int k, int H, int I, int E,
+                   void *y, int y_is_fp32, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * moe_combine -- weighted sum of each token's k expert outputs.
+ *   out[t][n] = bf16_rne( sum_{j<k} topk_w[t][j] * y[t*k+j][n] + y_shared[t][n] )
+ * summed in fp32 with j ascending; y_shared [T][H] (same dtype as y) is
+ * optional (NULL = no shared expert) and added with weight 1.
+ * out_bf16 [T][H]. Requires H % 8 == 0.
+ */
+int moe_combine(const void *y, int y_is_fp32, const float *topk_w, const void *y_shared, int T,
+                int k, int H, uint16_t *out_bf16, void *stream);
+
+/* Device workspace bytes needed by moe_permute and moe_expert_ffn for these
+ * sizes (host call, no device work). Either output pointer may be NULL. */
+int moe_workspace_size(int T, int k, int H, int I, int E, size_t *permute_bytes,
+                       size_t *ffn_bytes);
+
+/* Tuning and test knobs (process-wide).
+ *   MOE_OPT_FFN_PATH: 0 = choose by size (default), 1 = force the decode
+ *                     (weight-streaming) kernels, 2 = force the prefill
+ *                     (tiled matrix-core) kernels. */
+enum { MOE_OPT_FFN_PATH = 1 };
+int moe_set_option(int option, int value);
+int moe_get_option(int option);
+
+/* ---------------------------------------------------------------------------
+ * Expert cache: a pool of device slots holding expert blobs copied from pinned
+ * host memory, with a per-layer device table of moe_expert_w that points into
+ * the slots. The host keeps the least-recently-used order over (layer,
+ * expert) keys and evicts the least recently used unpinned slot on a miss.
+ * Copies are hipMemcpyAsync from pinned host memory on the copy stream given
+ * at reserve time, so they overlap with compute on other streams.
+ */
+typedef struct moe_cache moe_cache;
+
+/*
+ * expert_cache_reserve -- create a cache over a caller-owned device pool.
+ * pool: device buffer of pool_bytes (owned by the caller; must outlive the
+ *       cache); it is cut into floor(pool_bytes / slot_bytes) slots, where
+ *       slot_bytes is expert_bytes rounded up to 256.
+ * host_src: (host) array [n_layers * n_experts] of pointers to each expert's
+ *       blob in pinned host memory (entry layer*n_experts + e); the array is
+ *       copied, the blobs must outlive the cache.
+ * lay_*: byte offsets of w13/s13/w2/s2 inside a blob (the table entries are
+ *       slot + offset).
+ * copy_stream: stream for the host-to-device copies.
+ * Returns MOE_ENOMEM if the pool holds fewer slots than n_experts.
+ */
+int expert_cache_reserve(moe_cache **cache, void *pool, size_t pool_bytes, size_t expert_bytes,
+                         int n_layers, int n_experts, const void *const *host_src,
+                         size_t lay_w13, size_t lay_s13, size_t lay_w2, size_t lay_s2,
+                         void *copy_stream);
+
+/*
+ * expert_cache_prefetch -- make experts of one layer resident.
+ * ids: (host) expert indices of `layer` to make resident (duplicates
+ *      allowed); NULL means every expert of the layer.
+ * Hits refresh the LRU order; each miss takes the least recently used slot
+ * that no call since the previous prefetch has handed out, waits (on the copy
+ * stream) for the compute work that last used it, and copies the blob into it.
+ * On return, compute_stream has been made to wait for this layer's copies and
+ * table update, and *table_out (if not NULL) is the layer's device table
+ * [n_experts] for moe_expert_ffn. Entries of experts not requested may be
+ * stale and must not be read (moe_expert_ffn only reads experts with pairs).
+ * Returns MOE_ENOMEM (cache unchanged) if more distinct misses are requested
+ * than slots can be freed.
+ */
+int expert_cache_prefetch(moe_cache *cache, int layer, const int32_t *ids, int n,
+                          void *compute_stream, const moe_expert_w **table_out);
+
+/* expert_cache_evict -- drop experts of `layer` from the cache (NULL ids =
+ * the whole layer). Their slots become free for later misses. */
+int expert_cache_evict(moe_cache *cache, int layer, const int32_t *ids, int n);
+
+/* Counters since reserve: hits, misses, bytes copied host-to-device. */
+int expert_cache_stats(const moe_cache *cache, long long *hits, long long *misses,
+                       long long *h2d_bytes);
+
+/* Number of slots and the slot (or -1) holding (layer, expert). */
+int expert_cache_slots(const moe_cache *cache);
+int expert_cache_slot_of(const moe_cache *cache, int layer, int expert);
+
+/* Release the cache's metadata (host and its device table). Synchronises the
+ * copy stream first. The pool stays the caller's. */
+int expert_cache_destroy(moe_cache *cache);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_MI355X_H */

@@ -1,0 +1,202 @@
+"""ctypes binding of ``libmoe.so`` (the C ABI in include/moe.h).
+
+Argument marshalling only: tensors become raw device pointers, streams become
+hipStream_t handles, and every return code is turned into an exception. All of
+the layer's work runs in the HIP kernels of the library. There is no fallback:
+if the library is missing or fails to load, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmoe.so")
+
+MOE_OK, MOE_EINVAL, MOE_ENOMEM, MOE_EHIP, MOE_EUNSUPPORTED, MOE_EBUSY = 0, -1, -2, -3, -4, -5
+MOE_W_BF16, MOE_W_MXFP4 = 0, 1
+MOE_OPT_FFN_PATH = 1
+
+# every symbol include/moe.h declares
+EXPORTS = [
+    "moe_strerror", "moe_last_hip_error", "moe_route", "moe_permute", "moe_expert_ffn",
+    "moe_combine", "moe_workspace_size", "moe_set_option", "moe_get_option",
+    "expert_cache_reserve", "expert_cache_prefetch", "expert_cache_evict", "expert_cache_stats",
+    "expert_cache_slots", "expert_cache_slot_of", "expert_cache_destroy",
+]
+
+
+class MoeError(RuntimeError):
+    def __init__(self, fn: str, code: int, text: str, hip: int):
+        super().__init__(f"{fn} failed: {text} ({code})" + (f", hip error {hip}" if code == MOE_EHIP else ""))
+        self.code = code
+        self.hip = hip
+
+
+class ExpertW(C.Structure):
+    """moe_expert_w"""
+    _fields_ = [("w13", C.c_void_p), ("s13", C.c_void_p), ("w2", C.c_void_p), ("s2", C.c_void_p)]
+
+
+_lib = None
+
+
+def load(path: str | None = None):
+    """Load the library (raises if it is not built)."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise RuntimeError(f"{p} is not built; run __graft_entry__.build() or "
+                           "python -m mixture_experts_gate_amd.build")
+    L = C.CDLL(p)
+    P, I, Z = C.c_void_p, C.c_int, C.c_size_t
+    sig = {
+        "moe_strerror": (C.c_char_p, [I]),
+        "moe_last_hip_error": (I, []),
+        "moe_route": (I, [P, P, P, P, I, I, I, I, I, P, P, P]),
+        "moe_permute": (I, [P, I, I, I, P, P, P, P, Z, P]),
+        "moe_expert_ffn": (I, [P, P, P, P, I, I, I, I, I, I, P, I, P, Z, P]),
+        "moe_combine": (I, [P, I, P, P, I, I, I, P, P]),
+        "moe_workspace_size": (I, [I, I, I, I, I, C.POINTER(Z), C.POINTER(Z)]),
+        "moe_set_option": (I, [I, I]),
+        "moe_get_option": (I, [I]),
+        "expert_cache_reserve": (I, [C.POINTER(P), P, Z, Z, I, I, P, Z, Z, Z, Z, P]),
+        "expert_cache_prefetch": (I, [P, I, P, I, P, C.POINTER(P)]),
+        "expert_cache_evict": (I, [P, I, P, I]),
+        "expert_cache_stats": (I, [P, C.POINTER(C.c_longlong), C.POINTER(C.c_longlong),
+                                   C.POINTER(C.c_longlong)]),
+        "expert_cache_slots": (I, [P]),
+        "expert_cache_slot_of": (I, [P, I, I]),
+        "expert_cache_destroy": (I, [P]),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(L, name)
+        f.restype = res
+        f.argtypes = args
+    if path is None:
+        _lib = L
+    return L
+
+
+def _check(fn: str, rc: int) -> int:
+    if rc < 0:
+        L = load()
+        raise MoeError(fn, rc, L.moe_strerror(rc).decode(), L.moe_last_hip_error())
+    return rc
+
+
+def _ptr(t):
+    """Device (or host) address of a tensor, or None."""
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+# ------------------------------------------------------------- layer calls --
+
+def moe_route(x_bf16, wg_bf16, logits_in, logits_out, T, H, E, k, renormalize, topk_ids, topk_w,
+              stream=None):
+    return _check("moe_route", load().moe_route(
+        _ptr(x_bf16), _ptr(wg_bf16), _ptr(logits_in), _ptr(logits_out), T, H, E, k,
+        int(bool(renormalize)), _ptr(topk_ids), _ptr(topk_w), _stream(stream)))
+
+
+def moe_permute(topk_ids, T, k, E, offsets, sorted_pair, pair_row, ws, ws_bytes, stream=None):
+    return _check("moe_permute", load().moe_permute(
+        _ptr(topk_ids), T, k, E, _ptr(offsets), _ptr(sorted_pair), _ptr(pair_row), _ptr(ws),
+        ws_bytes, _stream(stream)))
+
+
+def moe_expert_ffn(x_bf16, sorted_pair, offsets, experts, fmt, T, k, H, I, E, y, y_is_fp32, ws,
+                   ws_bytes, stream=None):
+    return _check("moe_expert_ffn", load().moe_expert_ffn(
+        _ptr(x_bf16), _ptr(sorted_pair), _ptr(offsets), _ptr(experts), fmt, T, k, H, I, E, _ptr(y),
+        int(bool(y_is_fp32)), _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def moe_combine(y, y_is_fp32, topk_w, y_shared, T, k, H, out_bf16, stream=None):
+    return _check("moe_combine", load().moe_combine(
+        _ptr(y), int(bool(y_is_fp32)), _ptr(topk_w), _ptr(y_shared), T, k, H, _ptr(out_bf16),
+        _stream(stream)))
+
+
+def moe_workspace_size(T, k, H, I, E):
+    a, b = C.c_size_t(0), C.c_size_t(0)
+    _check("moe_workspace_size", load().moe_workspace_size(T, k, H, I, E, C.byref(a), C.byref(b)))
+    return a.value, b.value
+
+
+def moe_set_option(option, value):
+    return _check("moe_set_option", load().moe_set_option(option, value))
+
+
+def moe_get_option(option):
+    return _check("moe_get_option", load().moe_get_option(option))
+
+
+# ------------------------------------------------------------ expert cache --
+
+def expert_cache_reserve(pool, pool_bytes, expert_bytes, n_layers, n_experts, host_src, layout,
+                         copy_stream):
+    """host_src: sequence of host addresses (ints) of pinned blobs, [L*E]."""
+    h = C.c_void_p(0)
+    arr = (C.c_void_p * len(host_src))(*host_src)
+    _check("expert_cache_reserve", load().expert_cache_reserve(
+        C.byref(h), _ptr(pool), pool_bytes, expert_bytes, n_layers, n_experts, arr,
+        layout.w13, layout.s13, layout.w2, layout.s2, _stream(copy_stream)))
+    return h.value
+
+
+def expert_cache_prefetch(cache, layer, ids, compute_stream=None):
+    """ids: host int32 numpy array or None (whole layer). Returns the device table address."""
+    tab = C.c_void_p(0)
+    if ids is None:
+        p, n = None, 0
+    else:
+        import numpy as np
+        ids = np.ascontiguousarray(ids, dtype=np.int32)
+        p, n = ids.ctypes.data_as(C.c_void_p), int(ids.size)
+    _check("expert_cache_prefetch", load().expert_cache_prefetch(
+        cache, layer, p, n, _stream(compute_stream), C.byref(tab)))
+    return tab.value
+
+
+def expert_cache_evict(cache, layer, ids=None):
+    if ids is None:
+        p, n = None, 0
+    else:
+        import numpy as np
+        ids = np.ascontiguousarray(ids, dtype=np.int32)
+        p, n = ids.ctypes.data_as(C.c_void_p), int(ids.size)
+    return _check("expert_cache_evict", load().expert_cache_evict(cache, layer, p, n))
+
+
+def expert_cache_stats(cache):
+    h, m, b = C.c_longlong(0), C.c_longlong(0), C.c_longlong(0)
+    _check("expert_cache_stats", load().expert_cache_stats(cache, C.byref(h), C.byref(m), C.byref(b)))
+    return h.value, m.value, b.value
+
+
+def expert_cache_slots(cache):
+    return _check("expert_cache_slots", load().expert_cache_slots(cache))
+
+
+def expert_cache_slot_of(cache, layer, expert):
+    return load().expert_cache_slot_of(cache, layer, expert)
+
+
+def expert_cache_destroy(cache):
+    return _check("expert_cache_destroy", load().expert_cache_destroy(cache))

@@ -1,0 +1,96 @@
+// C-ABI glue: error text, options, workspace sizing and the expert-FFN
+// dispatcher (decode-shaped weight streaming vs prefill-shaped tiled GEMM).
+#include <atomic>
+
+#include "common.hpp"
+
+namespace moe {
+
+static thread_local int g_last_hip_error = 0;
+static std::atomic<int> g_ffn_path{0};
+
+void set_last_hip_error(hipError_t e) { g_last_hip_error = (int)e; }
+int ffn_path_option() { return g_ffn_path.load(); }
+
+size_t permute_ws_bytes(long n, int E);
+int ffn_decode(const uint16_t *x, const int32_t *sorted_pair, const int32_t *offsets,
+               const moe_expert_w *experts, int fmt, int T, int k, int H, int I, int E, void *y,
+               int y_is_fp32, uint16_t *act, hipStream_t s);
+int ffn_prefill(const uint16_t *x, const int32_t *sorted_pair, const int32_t *offsets,
+                const moe_expert_w *experts, int fmt, int T, int k, int H, int I, int E, void *y,
+                int y_is_fp32, uint16_t *act, hipStream_t s);
+bool ffn_prefill_supported(int fmt, int H, int I);
+
+static size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
+
+size_t ffn_ws_bytes(long n_pairs, int I) { return align256((size_t)n_pairs * I * 2) + 256; }
+
+// Decode kernels stream each touched expert once; prefill kernels tile the
+// contraction for the matrix cores. Tokens per touched expert decide.
+static bool use_prefill(long n_pairs, int E, int fmt, int H, int I) {
+    const int opt = g_ffn_path.load();
+    if (opt == 1) return false;
+    if (opt == 2) return ffn_prefill_supported(fmt, H, I);
+    return ffn_prefill_supported(fmt, H, I) && n_pairs >= 48L * E;
+}
+
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" const char *moe_strerror(int err) {
+    switch (err) {
+        case MOE_OK: return "ok";
+        case MOE_EINVAL: return "invalid argument";
+        case MOE_ENOMEM: return "not enough memory or cache slots";
+        case MOE_EHIP: return "HIP runtime error";
+        case MOE_EUNSUPPORTED: return "unsupported request";
+        case MOE_EBUSY: return "resource busy";
+        default: return "unknown error";
+    }
+}
+
+extern "C" int moe_last_hip_error(void) { return g_last_hip_error; }
+
+extern "C" int moe_set_option(int option, int value) {
+    if (option == MOE_OPT_FFN_PATH) {
+        if (value < 0 || value > 2) return MOE_EINVAL;
+        g_ffn_path.store(value);
+        return MOE_OK;
+    }
+    return MOE_EINVAL;
+}
+
+extern "C" int moe_get_option(int option) {
+    if (option == MOE_OPT_FFN_PATH) return g_ffn_path.load();
+    return MOE_EINVAL;
+}
+
+extern "C" int moe_workspace_size(int T, int k, int H, int I, int E, size_t *permute_bytes,
+                                  size_t *ffn_bytes) {
+    if (T < 0 || k < 1 || E < 1 || H < 32 || I < 32) return MOE_EINVAL;
+    const long n = (long)T * k;
+    if (permute_bytes) *permute_bytes = permute_ws_bytes(n, E);
+    if (ffn_bytes) *ffn_bytes = ffn_ws_bytes(n, I);
+    return MOE_OK;
+}
+
+extern "C" int moe_expert_ffn(const uint16_t *x_bf16, const int32_t *sorted_pair,
+                              const int32_t *offsets, const moe_expert_w *experts, int fmt, int T,
+                              int k, int H, int I, int E, void *y, int y_is_fp32, void *ws,
+                              size_t ws_bytes, void *stream) {
+    if (T < 0 || k < 1 || E < 1 || H < 32 || I < 32 || H % 32 || I % 32) return MOE_EINVAL;
+    if (fmt != MOE_W_MXFP4 && fmt != MOE_W_BF16) return MOE_EINVAL;
+    if (T == 0) return MOE_OK;
+    if (!x_bf16 || !sorted_pair || !offsets || !experts || !y || !ws) return MOE_EINVAL;
+    const long n = (long)T * k;
+    if (n > 0x7FFFFFFFL) return MOE_EINVAL;
+    if (ws_bytes < ffn_ws_bytes(n, I)) return MOE_EINVAL;
+    uint16_t *act = reinterpret_cast<uint16_t *>(ws);
+    hipStream_t s = (hipStream_t)stream;
+    if (use_prefill(n, E, fmt, H, I))
+        return ffn_prefill(x_bf16, sorted_pair, offsets, experts, fmt, T, k, H, I, E, y, y_is_fp32,
+                           act, s);
+    return ffn_decode(x_bf16, sorted_pair, offsets, experts, fmt, T, k, H, I, E, y, y_is_fp32, act,
+                      s);
+}

@@ -1,0 +1,320 @@
+// Expert cache: device slots fed from pinned host memory by hipMemcpyAsync on
+// a copy stream, a least-recently-used order over (layer, expert) keys, and a
+// per-layer device table of moe_expert_w that the expert FFN reads.
+//
+// The pages' design keeps most experts in host memory and loads them on
+// demand (winzheng.com page, "Why Now of All Times"), reuses frequently used
+// experts through a global LRU expert cache and overlaps weight movement with
+// computation by double-buffered full-layer streaming in prefill (winzheng.com
+// page, "FreeToken's Three-Layer Mechanism"; aimodeling.com/en page, "Three
+// Engineering Cores").
+//
+// Release protocol (what makes the overlap safe): every prefetch call is a
+// generation g and records an event ev[g] on the compute stream at entry, so
+// ev[g] covers all compute enqueued before call g. A slot last handed out by
+// call g is read only by compute enqueued after call g and before call g+1,
+// hence is free once ev[g+1] has completed. A miss reuses the least recently
+// used slot not handed out by the current call; the copy stream waits on
+// ev[last_gen + 1] of that slot before overwriting it. With room for two
+// layers of experts, prefetching layer l+1 evicts layer l-1 and overlaps the
+// compute of layer l.
+#include <algorithm>
+#include <deque>
+#include <new>
+#include <vector>
+
+#include "common.hpp"
+
+namespace moe {
+
+constexpr int kTableBatch = 240;
+
+struct TableUpdate {
+    int n;
+    int key[kTableBatch];
+    int slot[kTableBatch];
+};
+
+__global__ void cache_table_kernel(moe_expert_w *table, const char *pool, size_t slot_bytes,
+                                   size_t o_w13, size_t o_s13, size_t o_w2, size_t o_s2,
+                                   TableUpdate up) {
+    for (int i = threadIdx.x; i < up.n; i += blockDim.x) {
+        const char *b = pool + (size_t)up.slot[i] * slot_bytes;
+        moe_expert_w w;
+        w.w13 = b + o_w13;
+        w.s13 = reinterpret_cast<const uint8_t *>(b + o_s13);
+        w.w2 = b + o_w2;
+        w.s2 = reinterpret_cast<const uint8_t *>(b + o_s2);
+        table[up.key[i]] = w;
+    }
+}
+
+}  // namespace moe
+
+using namespace moe;
+
+struct moe_cache {
+    char *pool = nullptr;
+    size_t slot_bytes = 0, expert_bytes = 0;
+    int L = 0, E = 0, nslots = 0;
+    size_t lay[4] = {0, 0, 0, 0};
+    std::vector<const void *> src;      // [L*E] pinned host blobs
+    hipStream_t copy_stream = nullptr;
+    moe_expert_w *d_table = nullptr;    // [L*E]
+    hipEvent_t ready = nullptr;
+
+    std::vector<int> slot_of;           // key -> slot or -1
+    std::vector<int> key_of;            // slot -> key or -1
+    std::vector<int> prev, next;        // LRU list over slots; head = most recent
+    int head = -1, tail = -1;
+    std::vector<long long> last_gen;    // slot -> generation that last handed it out (0 = never)
+    long long gen = 0;
+    std::deque<hipEvent_t> entry_ev;    // entry_ev[i] belongs to generation ev_front_gen + i
+    long long ev_front_gen = 1;
+    long long done_gen = 0;             // every generation <= done_gen has its entry event complete
+    std::vector<hipEvent_t> spare_ev;
+
+    long long hits = 0, misses = 0, h2d_bytes = 0;
+
+    void unlink(int s) {
+        if (prev[s] >= 0) next[prev[s]] = next[s]; else head = next[s];
+        if (next[s] >= 0) prev[next[s]] = prev[s]; else tail = prev[s];
+        prev[s] = next[s] = -1;
+    }
+    void push_front(int s) {
+        prev[s] = -1;
+        next[s] = head;
+        if (head >= 0) prev[head] = s;
+        head = s;
+        if (tail < 0) tail = s;
+    }
+    void push_back(int s) {
+        next[s] = -1;
+        prev[s] = tail;
+        if (tail >= 0) next[tail] = s;
+        tail = s;
+        if (head < 0) head = s;
+    }
+    hipEvent_t get_event() {
+        if (!spare_ev.empty()) {
+            hipEvent_t e = spare_ev.back();
+            spare_ev.pop_back();
+            return e;
+        }
+        hipEvent_t e = nullptr;
+        if (hipEventCreateWithFlags(&e, hipEventDisableTiming) != hipSuccess) return nullptr;
+        return e;
+    }
+    // Drop entry events that have completed, advancing done_gen.
+    void retire_events() {
+        while (!entry_ev.empty() && hipEventQuery(entry_ev.front()) == hipSuccess) {
+            spare_ev.push_back(entry_ev.front());
+            entry_ev.pop_front();
+            done_gen = ev_front_gen;
+            ++ev_front_gen;
+        }
+    }
+};
+
+extern "C" int expert_cache_reserve(moe_cache **cache, void *pool, size_t pool_bytes,
+                                    size_t expert_bytes, int n_layers, int n_experts,
+                                    const void *const *host_src, size_t lay_w13, size_t lay_s13,
+                                    size_t lay_w2, size_t lay_s2, void *copy_stream) {
+    if (!cache || !pool || !host_src || expert_bytes == 0 || n_layers < 1 || n_experts < 1)
+        return MOE_EINVAL;
+    if (lay_w13 >= expert_bytes || lay_w2 >= expert_bytes || lay_s13 > expert_bytes ||
+        lay_s2 > expert_bytes)
+        return MOE_EINVAL;
+    const size_t slot_bytes = (expert_bytes + 255) & ~(size_t)255;
+    const size_t nslots = pool_bytes / slot_bytes;
+    if (nslots < (size_t)n_experts) return MOE_ENOMEM;
+    if (nslots > 0x7FFFFFFF || (long long)n_layers * n_experts > 0x7FFFFFFF) return MOE_EINVAL;
+    const long nkeys = (long)n_layers * n_experts;
+    for (long i = 0; i < nkeys; ++i)
+        if (!host_src[i]) return MOE_EINVAL;
+
+    moe_cache *c = new (std::nothrow) moe_cache();
+    if (!c) return MOE_ENOMEM;
+    c->pool = reinterpret_cast<char *>(pool);
+    c->slot_bytes = slot_bytes;
+    c->expert_bytes = expert_bytes;
+    c->L = n_layers;
+    c->E = n_experts;
+    c->nslots = (int)nslots;
+    c->lay[0] = lay_w13;
+    c->lay[1] = lay_s13;
+    c->lay[2] = lay_w2;
+    c->lay[3] = lay_s2;
+    c->copy_stream = (hipStream_t)copy_stream;
+    try {
+        c->src.assign(host_src, host_src + nkeys);
+        c->slot_of.assign(nkeys, -1);
+        c->key_of.assign(nslots, -1);
+        c->prev.assign(nslots, -1);
+        c->next.assign(nslots, -1);
+        c->last_gen.assign(nslots, 0);
+    } catch (...) {
+        delete c;
+        return MOE_ENOMEM;
+    }
+    for (int s = 0; s < c->nslots; ++s) c->push_back(s);
+    int rc = check_hip(hipMalloc(&c->d_table, sizeof(moe_expert_w) * (size_t)nkeys));
+    if (!rc) rc = check_hip(hipMemset(c->d_table, 0, sizeof(moe_expert_w) * (size_t)nkeys));
+    if (!rc) rc = check_hip(hipEventCreateWithFlags(&c->ready, hipEventDisableTiming));
+    if (rc) {
+        if (c->d_table) (void)hipFree(c->d_table);
+        delete c;
+        return rc;
+    }
+    *cache = c;
+    return MOE_OK;
+}
+
+extern "C" int expert_cache_prefetch(moe_cache *c, int layer, const int32_t *ids, int n,
+                                     void *compute_stream, const moe_expert_w **table_out) {
+    if (!c || layer < 0 || layer >= c->L || (ids && n < 0)) return MOE_EINVAL;
+    const int E = c->E;
+    std::vector<int> want;
+    if (ids) {
+        want.reserve(n);
+        for (int i = 0; i < n; ++i) {
+            if (ids[i] < 0 || ids[i] >= E) return MOE_EINVAL;
+            want.push_back(ids[i]);
+        }
+        std::sort(want.begin(), want.end());
+        want.erase(std::unique(want.begin(), want.end()), want.end());
+    } else {
+        want.resize(E);
+        for (int e = 0; e < E; ++e) want[e] = e;
+    }
+    if ((int)want.size() > c->nslots) return MOE_ENOMEM;
+    hipStream_t cs = (hipStream_t)compute_stream;
+
+    // new generation: mark everything enqueued on the compute stream so far
+    c->retire_events();
+    hipEvent_t ev = c->get_event();
+    if (!ev) return MOE_EHIP;
+    int rc = check_hip(hipEventRecord(ev, cs));
+    if (rc) {
+        c->spare_ev.push_back(ev);
+        return rc;
+    }
+    const long long g = ++c->gen;
+    c->entry_ev.push_back(ev);      // generation g == ev_front_gen + index
+
+    const long base_key = (long)layer * E;
+    // hits first: they are handed out by this call and must not become victims
+    std::vector<int> miss;
+    for (int e : want) {
+        const int s = c->slot_of[base_key + e];
+        if (s >= 0) {
+            ++c->hits;
+            c->unlink(s);
+            c->push_front(s);
+            c->last_gen[s] = g;
+        } else {
+            miss.push_back(e);
+        }
+    }
+    TableUpdate up;
+    up.n = 0;
+    auto flush = [&]() -> int {
+        if (up.n == 0) return MOE_OK;
+        hipLaunchKernelGGL(cache_table_kernel, dim3(1), dim3(256), 0, c->copy_stream, c->d_table,
+                           (const char *)c->pool, c->slot_bytes, c->lay[0], c->lay[1], c->lay[2],
+                           c->lay[3], up);
+        up.n = 0;
+        return check_launch();
+    };
+    for (int e : miss) {
+        // least recently used slot not handed out by this call (tail side)
+        int s = c->tail;
+        while (s >= 0 && c->last_gen[s] == g) s = c->prev[s];
+        if (s < 0) return MOE_ENOMEM;    // cannot happen: want.size() <= nslots
+        const long long lg = c->last_gen[s];
+        if (lg > 0 && lg + 1 > c->done_gen) {
+            // its readers are covered by the entry event of generation lg + 1
+            const long long idx = lg + 1 - c->ev_front_gen;
+            if (idx >= 0 && idx < (long long)c->entry_ev.size()) {
+                rc = check_hip(hipStreamWaitEvent(c->copy_stream, c->entry_ev[(size_t)idx], 0));
+                if (rc) return rc;
+            }
+        }
+        const int old = c->key_of[s];
+        if (old >= 0) c->slot_of[old] = -1;
+        c->key_of[s] = -1;
+        rc = check_hip(hipMemcpyAsync(c->pool + (size_t)s * c->slot_bytes, c->src[base_key + e],
+                                      c->expert_bytes, hipMemcpyHostToDevice, c->copy_stream));
+        if (rc) {
+            c->unlink(s);
+            c->push_back(s);
+            return rc;
+        }
+        c->key_of[s] = (int)(base_key + e);
+        c->slot_of[base_key + e] = s;
+        c->unlink(s);
+        c->push_front(s);
+        c->last_gen[s] = g;
+        ++c->misses;
+        c->h2d_bytes += (long long)c->expert_bytes;
+        up.key[up.n] = (int)(base_key + e);
+        up.slot[up.n] = s;
+        if (++up.n == kTableBatch && (rc = flush())) return rc;
+    }
+    if ((rc = flush())) return rc;
+    rc = check_hip(hipEventRecord(c->ready, c->copy_stream));
+    if (!rc) rc = check_hip(hipStreamWaitEvent(cs, c->ready, 0));
+    if (rc) return rc;
+    if (table_out) *table_out = c->d_table + base_key;
+    return MOE_OK;
+}
+
+extern "C" int expert_cache_evict(moe_cache *c, int layer, const int32_t *ids, int n) {
+    if (!c || layer < 0 || layer >= c->L || (ids && n < 0)) return MOE_EINVAL;
+    const long base_key = (long)layer * c->E;
+    const int cnt = ids ? n : c->E;
+    for (int i = 0; i < cnt; ++i) {
+        const int e = ids ? ids[i] : i;
+        if (e < 0 || e >= c->E) return MOE_EINVAL;
+    }
+    for (int i = 0; i < cnt; ++i) {
+        const int e = ids ? ids[i] : i;
+        const int s = c->slot_of[base_key + e];
+        if (s < 0) continue;
+        c->slot_of[base_key + e] = -1;
+        c->key_of[s] = -1;
+        c->unlink(s);
+        c->push_back(s);     // first in line for reuse; last_gen keeps its readers safe
+    }
+    return MOE_OK;
+}
+
+extern "C" int expert_cache_stats(const moe_cache *c, long long *hits, long long *misses,
+                                  long long *h2d_bytes) {
+    if (!c) return MOE_EINVAL;
+    if (hits) *hits = c->hits;
+    if (misses) *misses = c->misses;
+    if (h2d_bytes) *h2d_bytes = c->h2d_bytes;
+    return MOE_OK;
+}
+
+extern "C" int expert_cache_slots(const moe_cache *c) { return c ? c->nslots : MOE_EINVAL; }
+
+extern "C" int expert_cache_slot_of(const moe_cache *c, int layer, int expert) {
+    if (!c || layer < 0 || layer >= c->L || expert < 0 || expert >= c->E) return MOE_EINVAL;
+    return c->slot_of[(long)layer * c->E + expert];
+}
+
+extern "C" int expert_cache_destroy(moe_cache *c) {
+    if (!c) return MOE_EINVAL;
+    int rc = check_hip(hipStreamSynchronize(c->copy_stream));
+    for (hipEvent_t e : c->entry_ev) (void)hipEventSynchronize(e), (void)hipEventDestroy(e);
+    for (hipEvent_t e : c->spare_ev) (void)hipEventDestroy(e);
+    if (c->ready) (void)hipEventDestroy(c->ready);
+    if (c->d_table) {
+        const int rc2 = check_hip(hipFree(c->d_table));
+        if (!rc) rc = rc2;
+    }
+    delete c;
+    return rc;
+}

@@ -1,0 +1,77 @@
+// Weighted combine of each token's k expert outputs (plus the always-on
+// shared expert when given). Memory-bound: each thread owns 8 consecutive
+// hidden elements of one token and sums its k rows in fp32, j ascending.
+#include "common.hpp"
+
+namespace moe {
+
+template <bool YF32>
+__device__ __forceinline__ void load8(const void *base, size_t off, float v[8]) {
+    if (YF32) {
+        const f32x4 a = *reinterpret_cast<const f32x4 *>(reinterpret_cast<const float *>(base) + off);
+        const f32x4 b =
+            *reinterpret_cast<const f32x4 *>(reinterpret_cast<const float *>(base) + off + 4);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            v[i] = a[i];
+            v[4 + i] = b[i];
+        }
+    } else {
+        const u32x4 q = load16(reinterpret_cast<const uint16_t *>(base) + off);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            v[2 * i] = bf16_bits_to_f32(q[i] & 0xFFFFu);
+            v[2 * i + 1] = bf16_bits_to_f32(q[i] >> 16);
+        }
+    }
+}
+
+template <bool YF32>
+__global__ __launch_bounds__(256) void combine_kernel(const void *__restrict__ y,
+                                                      const float *__restrict__ w,
+                                                      const void *__restrict__ ysh, int T, int k,
+                                                      int H, uint16_t *__restrict__ out) {
+    const int per_tok = H / 8;
+    const long gid = (long)blockIdx.x * blockDim.x + threadIdx.x;
+    if (gid >= (long)T * per_tok) return;
+    const int t = (int)(gid / per_tok), h8 = (int)(gid - (long)t * per_tok) * 8;
+    float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    for (int j = 0; j < k; ++j) {
+        const float wj = w[(size_t)t * k + j];
+        float v[8];
+        load8<YF32>(y, ((size_t)t * k + j) * H + h8, v);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] += wj * v[i];
+    }
+    if (ysh) {
+        float v[8];
+        load8<YF32>(ysh, (size_t)t * H + h8, v);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] += v[i];
+    }
+    u32x4 o;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o[i] = pack_bf16x2(acc[2 * i], acc[2 * i + 1]);
+    *reinterpret_cast<u32x4 *>(out + (size_t)t * H + h8) = o;
+}
+
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" int moe_combine(const void *y, int y_is_fp32, const float *topk_w, const void *y_shared,
+                           int T, int k, int H, uint16_t *out_bf16, void *stream) {
+    if (T < 0 || k < 1 || H < 8 || H % 8) return MOE_EINVAL;
+    if (T == 0) return MOE_OK;
+    if (!y || !topk_w || !out_bf16) return MOE_EINVAL;
+    const long n = (long)T * (H / 8);
+    dim3 grid((unsigned)((n + 255) / 256)), block(256);
+    hipStream_t s = (hipStream_t)stream;
+    if (y_is_fp32)
+        hipLaunchKernelGGL(combine_kernel<true>, grid, block, 0, s, y, topk_w, y_shared, T, k, H,
+                           out_bf16);
+    else
+        hipLaunchKernelGGL(combine_kernel<false>, grid, block, 0, s, y, topk_w, y_shared, T, k, H,
+                           out_bf16);
+    return check_launch();
+}

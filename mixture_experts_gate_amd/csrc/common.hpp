@@ -1,0 +1,120 @@
+// Internal helpers shared by the gfx950 kernels of the MoE layer library.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "moe.h"
+
+namespace moe {
+
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------- errors --
+
+void set_last_hip_error(hipError_t e);
+
+// Returns MOE_EHIP (and records the code) if a launch failed.
+inline int check_launch() {
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) {
+        set_last_hip_error(e);
+        return MOE_EHIP;
+    }
+    return MOE_OK;
+}
+
+inline int check_hip(hipError_t e) {
+    if (e != hipSuccess) {
+        set_last_hip_error(e);
+        return MOE_EHIP;
+    }
+    return MOE_OK;
+}
+
+int ffn_path_option();
+
+// ------------------------------------------------------------ bf16 bits --
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) {
+    return __uint_as_float(b << 16);
+}
+
+// fp32 -> bf16, round to nearest even (NaN kept quiet).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x7FFFFFu)) return (u >> 16) | 0x40u;
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+}
+
+// E8M0 scale byte -> fp32 multiplier 2^(s-127) (s = 0 gives the subnormal 2^-127).
+__device__ __forceinline__ float e8m0_to_f32(uint32_t s) {
+    return s ? __uint_as_float(s << 23) : __uint_as_float(0x00400000u);
+}
+
+// ------------------------------------------------------------- loads -----
+
+__device__ __forceinline__ u32x4 load_nt16(const void *p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+}
+
+__device__ __forceinline__ u32x4 load16(const void *p) {
+    return *reinterpret_cast<const u32x4 *>(p);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) {
+    return __builtin_bit_cast(bf16x8, v);
+}
+
+// 8 MXFP4 codes (one dword, element 0 in the low nibble) -> 8 bf16 scaled by sc.
+__device__ __forceinline__ bf16x8 dequant8_fp4(uint32_t w, float sc) {
+    bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 0);
+    bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 1);
+    bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 2);
+    bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 3);
+    bf16x8 r = {a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+    return r;
+}
+
+// ---------------------------------------------------------- wave utils ---
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
+
+__device__ __forceinline__ uint64_t lanemask_lt() {
+    const int l = lane_id();
+    return l ? (~0ull >> (64 - l)) : 0ull;
+}
+
+// Index of the a-th (0-based) expert that received at least one pair, or -1.
+// Called by a whole wavefront (all lanes get the same answer).
+__device__ __forceinline__ int find_active_expert(const int32_t *__restrict__ offsets, int E, int a) {
+    const int lane = lane_id();
+    int seen = 0;
+    for (int base = 0; base < E; base += kWave) {
+        const int e = base + lane;
+        const bool act = e < E && offsets[e + 1] > offsets[e];
+        const uint64_t m = __ballot(act);
+        const int c = __popcll(m);
+        if (a < seen + c) {
+            const int r = a - seen;
+            const bool hit = act && __popcll(m & lanemask_lt()) == r;
+            const uint64_t hm = __ballot(hit);
+            return base + __ffsll((long long)hm) - 1;
+        }
+        seen += c;
+    }
+    return -1;
+}
+
+}  // namespace moe

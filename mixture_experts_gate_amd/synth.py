@@ -17,6 +17,7 @@ that any tensor can be regenerated independently of generation order.
 from __future__ import annotations
 
 import dataclasses
+import os
 
 import numpy as np
 
@@ -39,14 +40,20 @@ class LayerConfig:
     weights: str      # weight recipe: "gauss_bf16" | "gauss_mxfp4" | "marginal_mxfp4"
     layers: int = 1
     seed: int = 0
+    weight_seed: int | None = None   # draw expert weights from another workload's seed
+
+    @property
+    def wseed(self) -> int:
+        return self.seed if self.weight_seed is None else self.weight_seed
 
 
 CONFIGS = {
     1: LayerConfig("tiny", 256, 8, 2, 512, "bf16", 0, "gate", (16,), "gauss_bf16", seed=1),
     2: LayerConfig("decode", 2048, 128, 8, 768, "mxfp4", 0, "uniform", (1, 8, 32, 64),
                    "gauss_mxfp4", seed=2),
+    # the prefill workload runs the decode workload's layer (same weights) at T=8192
     3: LayerConfig("prefill", 2048, 128, 8, 768, "mxfp4", 0, "gumbel_bias", (8192,),
-                   "gauss_mxfp4", seed=3),
+                   "gauss_mxfp4", seed=3, weight_seed=2),
     4: LayerConfig("large_sparse", 4096, 256, 6, 2048, "mxfp4", 1, "zipf", (1, 64, 4096),
                    "marginal_mxfp4", seed=4),
     5: LayerConfig("stack43", 4096, 256, 6, 2048, "mxfp4", 1, "zipf", (1, 2, 4, 8, 16),
@@ -243,7 +250,7 @@ def expert_blob(cfg: LayerConfig, layer: int, expert: int, shared: bool = False,
     """One expert's blob (uint8 [nbytes]) in the storage layout of ``blob_layout``."""
     H = cfg.H if H is None else H
     I = cfg.I if I is None else I
-    rng = _rng(cfg.seed, _S_SHARED if shared else _S_W, layer, expert)
+    rng = _rng(cfg.wseed, _S_SHARED if shared else _S_W, layer, expert)
     if cfg.weights == "gauss_mxfp4":
         return _gauss_mxfp4_blob(rng, H, I, WEIGHT_SIGMA)
     if cfg.weights == "marginal_mxfp4":
@@ -261,8 +268,17 @@ def expert_pool(cfg: LayerConfig, layer: int = 0, E: int | None = None, H: int |
     I = cfg.I if I is None else I
     lay = blob_layout(H, I, cfg.fmt)
     pool = np.empty((E, lay.nbytes), dtype=np.uint8)
-    for e in range(E):
+
+    def fill(e):
         pool[e] = expert_blob(cfg, layer, e, H=H, I=I)
+
+    if E * lay.nbytes < (64 << 20):
+        for e in range(E):
+            fill(e)
+    else:
+        from concurrent.futures import ThreadPoolExecutor
+        with ThreadPoolExecutor(max_workers=min(8, os.cpu_count() or 1)) as ex:
+            list(ex.map(fill, range(E)))
     return pool
 
 

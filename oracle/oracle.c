@@ -91,11 +91,15 @@ double orc_e8m0(int s) {
 /* Decode rows [R][K] of MXFP4 (codes [R][K/2], even element in the low
  * nibble; one E8M0 scale per 32 consecutive elements of a row). */
 void orc_mxfp4_decode(const uint8_t *codes, const uint8_t *scales, long R, long K, double *out) {
+    /* the 16 element values and 256 scale values, tabulated once per call */
+    double elem[16], scale[256];
+    for (int i = 0; i < 16; ++i) elem[i] = orc_e2m1(i);
+    for (int i = 0; i < 256; ++i) scale[i] = orc_e8m0(i);
     for (long r = 0; r < R; ++r)
         for (long c = 0; c < K; ++c) {
             uint8_t byte = codes[r * (K / 2) + c / 2];
             int code = (c % 2 == 0) ? (byte & 15) : (byte >> 4);
-            out[r * K + c] = orc_e2m1(code) * orc_e8m0(scales[r * (K / 32) + c / 32]);
+            out[r * K + c] = elem[code] * scale[scales[r * (K / 32) + c / 32]];
         }
 }
 

@@ -1,0 +1,50 @@
+"""Shared helpers for the GPU parity tests: device upload of seeded inputs and
+the error measures the tolerances are stated in."""
+from __future__ import annotations
+
+import numpy as np
+
+# Tolerance for floating-point outputs: the layer's output (bf16, fp32
+# accumulation) must satisfy max|got - ref| / max|ref| <= 2e-2 against the
+# oracle's exact (fp64) result.
+MAX_REL = 2e-2
+# Tighter bound derived from the arithmetic: bf16 rounding of the SwiGLU
+# activation, of each expert output and of the final sum each contribute at
+# most 2^-9 relative error per element, so the L2-relative error of a correct
+# kernel stays well under 1e-2 (a dropped K block or expert term does not).
+L2_REL = 1e-2
+# Routing weights: fp32 exp on the GPU vs double in the oracle.
+W_ATOL = 1e-6
+
+
+def max_rel(got, ref) -> float:
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    return float(np.abs(got - ref).max() / max(np.abs(ref).max(), 1e-30))
+
+
+def l2_rel(got, ref) -> float:
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    return float(np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-30))
+
+
+def assert_close(got, ref, what: str):
+    mr, lr = max_rel(got, ref), l2_rel(got, ref)
+    print(f"  {what}: max-rel {mr:.3e}  l2-rel {lr:.3e}", flush=True)
+    assert mr <= MAX_REL, f"{what}: max-rel {mr:.3e} > {MAX_REL}"
+    assert lr <= L2_REL, f"{what}: l2-rel {lr:.3e} > {L2_REL}"
+
+
+def to_dev_bf16(bits: np.ndarray, dev="cuda"):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
+
+
+def to_dev(a: np.ndarray, dev="cuda"):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+
+def bf16_dev_to_f64(t) -> np.ndarray:
+    return t.float().cpu().numpy().astype(np.float64)

@@ -1,0 +1,356 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle on the
+same seeded inputs.
+
+Routing ids, permutation offsets / order / inverse are compared bit for bit;
+routing weights within 1e-6; floating-point outputs by max-relative error
+(<= 2e-2, the stated tolerance) and L2-relative error (<= 1e-2, from the bf16
+roundings). Large workloads are checked in full for routing and permutation
+and on sampled tokens for the FFN and combine (the layer is token-independent
+once routing is fixed, which the oracle tests pin).
+"""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+from mixture_experts_gate_amd import synth  # noqa: E402
+
+from parity import W_ATOL, assert_close, bf16_dev_to_f64, to_dev, to_dev_bf16  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def _announce(msg):
+    print(f"[gpu-parity] {msg}", flush=True)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from mixture_experts_gate_amd import _lib
+    _lib.load()
+    _lib.moe_set_option(_lib.MOE_OPT_FFN_PATH, 0)
+    return _lib
+
+
+@pytest.fixture(scope="module")
+def orc():
+    import oracle
+    oracle.build(force=False)
+    return oracle
+
+
+class Workload:
+    """Weights of one layer, generated once and resident on the device."""
+
+    def __init__(self, cfg, E=None):
+        from mixture_experts_gate_amd.layer import DeviceExperts
+        self.cfg = cfg
+        self.E = cfg.E if E is None else E
+        self.lay = synth.blob_layout(cfg.H, cfg.I, cfg.fmt)
+        self.pool = synth.expert_pool(cfg, E=self.E)
+        self.dev = DeviceExperts(self.pool, self.lay, device=DEV)
+        self.shared = synth.shared_expert(cfg) if cfg.n_shared else None
+        self.dev_shared = DeviceExperts(self.shared, self.lay, device=DEV) if cfg.n_shared else None
+
+
+_WL = {}
+
+
+def workload(c, E=None):
+    key = (c, E)
+    if key not in _WL:
+        _announce(f"generating weights for config {c} (E={E})")
+        _WL[key] = Workload(synth.CONFIGS[c], E)
+    return _WL[key]
+
+
+def run_layer(w: Workload, T, x, logits=None, wg=None, y_fp32=False, renormalize=True):
+    from mixture_experts_gate_amd.layer import MoeLayer
+    cfg = w.cfg
+    L = MoeLayer(cfg.H, w.E, cfg.k, cfg.I, cfg.fmt, T, shared=bool(cfg.n_shared), y_fp32=y_fp32,
+                 device=DEV)
+    xd = to_dev_bf16(x)
+    out = L.forward(T, xd, w.dev.table,
+                    logits=None if logits is None else to_dev(logits),
+                    wg=None if wg is None else to_dev_bf16(wg),
+                    shared_table=w.dev_shared.table if w.dev_shared else None,
+                    renormalize=renormalize, write_logits=True)
+    torch.cuda.synchronize()
+    return L, out
+
+
+def oracle_tokens(orc, w: Workload, x, ids, wts, toks):
+    """Oracle FFN + combine for the listed tokens (its own routing ids / weights)."""
+    k = w.cfg.k
+    toks = np.asarray(toks, dtype=np.int32)
+    rt = np.repeat(toks, k)
+    re_ = ids[toks].reshape(-1)
+    y = orc.ffn_rows(x, w.pool, w.lay, rt, re_)
+    ysh = None
+    if w.shared is not None:
+        ysh = orc.ffn_rows(x, w.shared[None], w.lay, toks, np.zeros(len(toks), np.int32))
+    out, _ = orc.combine(y, wts[toks], ysh)
+    return y, out
+
+
+def check_routing(L, T, ref_ids, ref_w, logits_ref=None):
+    ids = L.topk_ids[:T].cpu().numpy()
+    assert np.array_equal(ids, ref_ids), "routing ids differ"
+    w = L.topk_w[:T].cpu().numpy()
+    assert np.abs(w.astype(np.float64) - ref_w).max() <= W_ATOL
+    if logits_ref is not None:
+        assert np.array_equal(L.logits[:T].cpu().numpy(), logits_ref), "logits differ"
+
+
+def check_permutation(L, T, E, ref_off, ref_sp, ref_pr):
+    n = T * L.k
+    assert np.array_equal(L.offsets.cpu().numpy(), ref_off), "offsets differ"
+    assert np.array_equal(L.sorted_pair[:n].cpu().numpy(), ref_sp), "sorted_pair differs"
+    assert np.array_equal(L.pair_row[:n].cpu().numpy(), ref_pr), "pair_row differs"
+
+
+# ------------------------------------------------------------------ router --
+
+def test_route_gate_tiny_bitwise(lib, orc):
+    _announce("route: tiny config, bf16 gate on GPU")
+    w = workload(1)
+    cfg = w.cfg
+    x = synth.activations(cfg, 16)
+    wg = synth.gate_weights(cfg)
+    L, _ = run_layer(w, 16, x, wg=wg)
+    lg = orc.gate_logits_f32(x, wg)
+    ids, wts, _ = orc.topk(lg, cfg.k)
+    check_routing(L, 16, ids, wts, logits_ref=lg)
+
+
+@pytest.mark.parametrize("T,H,E", [(3, 2048, 128), (37, 4096, 256), (5, 64, 1000)])
+def test_route_gate_shapes_bitwise(lib, orc, T, H, E):
+    _announce(f"route: gate GEMV T={T} H={H} E={E}")
+    rng = np.random.default_rng(T)
+    x = synth.f32_to_bf16_bits(rng.standard_normal((T, H)).astype(np.float32))
+    wg = synth.f32_to_bf16_bits((rng.standard_normal((E, H)) * 0.02).astype(np.float32))
+    k = 6
+    ids_d = torch.empty((T, k), dtype=torch.int32, device=DEV)
+    w_d = torch.empty((T, k), dtype=torch.float32, device=DEV)
+    lg_d = torch.empty((T, E), dtype=torch.float32, device=DEV)
+    lib.moe_route(to_dev_bf16(x), to_dev_bf16(wg), None, lg_d, T, H, E, k, True, ids_d, w_d)
+    torch.cuda.synchronize()
+    lg = orc.gate_logits_f32(x, wg)
+    assert np.array_equal(lg_d.cpu().numpy(), lg)
+    ids, wts, _ = orc.topk(lg, k)
+    assert np.array_equal(ids_d.cpu().numpy(), ids)
+    assert np.abs(w_d.cpu().numpy().astype(np.float64) - wts).max() <= W_ATOL
+
+
+ROUTE_CASES = [
+    ("cfg2-T64", lambda: synth.router_logits(synth.CONFIGS[2], 64), 8, True),
+    ("cfg3-T8192", lambda: synth.router_logits(synth.CONFIGS[3], 8192), 8, True),
+    ("cfg4-T4096", lambda: synth.router_logits(synth.CONFIGS[4], 4096), 6, True),
+    ("ties", lambda: synth.tie_logits(500, 16), 5, True),
+    ("ties-k-boundary", lambda: synth.tie_logits(300, 64), 8, True),
+    ("no-renorm", lambda: synth.router_logits(synth.CONFIGS[4], 100), 6, False),
+    ("k=E", lambda: synth.router_logits(synth.CONFIGS[2], 20, E=8), 8, True),
+    ("k=1", lambda: synth.router_logits(synth.CONFIGS[2], 50), 1, True),
+    ("E=1000", lambda: np.random.default_rng(4).random((33, 1000), dtype=np.float32), 7, True),
+    ("signed-zero", lambda: np.tile(np.array([[-0.0, 0.0, -1.0, 0.0, 0.5]], np.float32), (4, 1)), 3,
+     True),
+]
+
+
+@pytest.mark.parametrize("name,make,k,renorm", ROUTE_CASES, ids=[c[0] for c in ROUTE_CASES])
+def test_route_logits_bitwise(lib, orc, name, make, k, renorm):
+    _announce(f"route: {name}")
+    lg = make()
+    T, E = lg.shape
+    ids_d = torch.empty((T, k), dtype=torch.int32, device=DEV)
+    w_d = torch.empty((T, k), dtype=torch.float32, device=DEV)
+    lib.moe_route(None, None, to_dev(lg), None, T, 0, E, k, renorm, ids_d, w_d)
+    torch.cuda.synchronize()
+    ids, wts, _ = orc.topk(lg, k, renormalize=renorm)
+    assert np.array_equal(ids_d.cpu().numpy(), ids)
+    assert np.abs(w_d.cpu().numpy().astype(np.float64) - wts).max() <= W_ATOL
+
+
+# ------------------------------------------------------------- permutation --
+
+def _perm_case(T, E, k, kind, seed=0):
+    rng = np.random.default_rng(seed + T)
+    if kind == "uniform":
+        lg = rng.random((T, E), dtype=np.float32)
+    elif kind == "skew":   # one expert takes every token's first slot, many experts empty
+        lg = rng.random((T, E), dtype=np.float32)
+        lg[:, 3] += 10.0
+        lg[:, E // 2:] -= 10.0
+    else:
+        raise ValueError(kind)
+    return lg
+
+
+PERM_CASES = [(1, 128, 8, "uniform"), (8, 128, 8, "uniform"), (64, 128, 8, "uniform"),
+              (16, 8, 2, "uniform"), (500, 256, 6, "skew"), (513, 512, 4, "uniform"),
+              (4096, 256, 6, "uniform"), (8192, 128, 8, "uniform"), (6000, 64, 3, "skew"),
+              (1, 1, 1, "uniform"), (3, 7, 7, "uniform")]
+
+
+@pytest.mark.parametrize("T,E,k,kind", PERM_CASES)
+def test_permute_bitwise(lib, orc, T, E, k, kind):
+    _announce(f"permute: T={T} E={E} k={k} {kind}")
+    lg = _perm_case(T, E, k, kind)
+    ids, _, _ = orc.topk(lg, k)
+    off, sp, pr = orc.permute(ids, E)
+    pb, _ = lib.moe_workspace_size(T, k, 64, 64, E)
+    ws = torch.empty(max(pb, 256), dtype=torch.uint8, device=DEV)
+    off_d = torch.full((E + 1,), -7, dtype=torch.int32, device=DEV)
+    sp_d = torch.full((T * k,), -7, dtype=torch.int32, device=DEV)
+    pr_d = torch.full((T * k,), -7, dtype=torch.int32, device=DEV)
+    lib.moe_permute(to_dev(ids), T, k, E, off_d, sp_d, pr_d, ws, max(pb, 256))
+    torch.cuda.synchronize()
+    assert np.array_equal(off_d.cpu().numpy(), off)
+    assert np.array_equal(sp_d.cpu().numpy(), sp)
+    assert np.array_equal(pr_d.cpu().numpy(), pr)
+
+
+def test_permute_empty_batch(lib):
+    off_d = torch.full((9,), -7, dtype=torch.int32, device=DEV)
+    lib.moe_permute(None, 0, 2, 8, off_d, None, None, None, 0)
+    torch.cuda.synchronize()
+    assert (off_d.cpu().numpy() == 0).all()
+
+
+# ------------------------------------------------------------- whole layer --
+
+def _check_layer_full(orc, w, T, x, L, out, logits=None, wg=None):
+    cfg = w.cfg
+    ref = orc.moe_layer(x, w.lay, w.pool, cfg.k, logits=logits, wg=wg,
+                        shared_blob=w.shared)
+    check_routing(L, T, ref["ids"], ref["w"], logits_ref=ref["logits"])
+    check_permutation(L, T, w.E, ref["offsets"], ref["sorted_pair"], ref["pair_row"])
+    yg = L.y[:T * cfg.k].float().cpu().numpy()
+    assert_close(yg, ref["y"], f"expert outputs y (T={T})")
+    assert_close(bf16_dev_to_f64(out), ref["out_f64"], f"layer output (T={T})")
+    return ref
+
+
+def test_layer_tiny_bf16(lib, orc):
+    _announce("layer: tiny bf16 config, T=16")
+    w = workload(1)
+    x = synth.activations(w.cfg, 16)
+    wg = synth.gate_weights(w.cfg)
+    L, out = run_layer(w, 16, x, wg=wg)
+    _check_layer_full(orc, w, 16, x, L, out, wg=wg)
+
+
+@pytest.mark.parametrize("T", [1, 8, 32, 64])
+def test_layer_decode_cfg2(lib, orc, T):
+    _announce(f"layer: decode config 2, T={T}")
+    w = workload(2)
+    x = synth.activations(w.cfg, T)
+    lg = synth.router_logits(w.cfg, T)
+    L, out = run_layer(w, T, x, logits=lg)
+    _check_layer_full(orc, w, T, x, L, out, logits=lg)
+
+
+def test_layer_decode_cfg2_fp32_y(lib, orc):
+    _announce("layer: decode config 2, T=32, fp32 expert outputs")
+    w = workload(2)
+    x = synth.activations(w.cfg, 32, step=1)
+    lg = synth.router_logits(w.cfg, 32, step=1)
+    L, out = run_layer(w, 32, x, logits=lg, y_fp32=True)
+    _check_layer_full(orc, w, 32, x, L, out, logits=lg)
+
+
+def _check_layer_sampled(orc, w, T, x, lg, L, out, n_sample=24, seed=0):
+    cfg = w.cfg
+    ids, wts, _ = orc.topk(lg, cfg.k)
+    off, sp, pr = orc.permute(ids, w.E)
+    check_routing(L, T, ids, wts)
+    check_permutation(L, T, w.E, off, sp, pr)
+    rng = np.random.default_rng(seed)
+    toks = np.sort(rng.choice(T, size=min(n_sample, T), replace=False))
+    toks[-1] = T - 1    # always include the ragged tail's last token
+    y_ref, out_ref = oracle_tokens(orc, w, x, ids, wts, toks)
+    yg = L.y[:T * cfg.k].float().cpu().numpy().reshape(T, cfg.k, cfg.H)[toks].reshape(-1, cfg.H)
+    assert_close(yg, y_ref, f"expert outputs y, {len(toks)} sampled tokens (T={T})")
+    assert_close(bf16_dev_to_f64(out)[toks], out_ref, f"layer output, sampled (T={T})")
+
+
+def test_layer_prefill_cfg3(lib, orc):
+    _announce("layer: prefill config 3, T=8192")
+    w = workload(3)
+    T = 8192
+    x = synth.activations(w.cfg, T)
+    lg = synth.router_logits(w.cfg, T)
+    L, out = run_layer(w, T, x, logits=lg)
+    _check_layer_sampled(orc, w, T, x, lg, L, out)
+
+
+@pytest.mark.parametrize("T", [1, 64])
+def test_layer_large_sparse_cfg4(lib, orc, T):
+    _announce(f"layer: config 4 (shared expert, Zipf), T={T}")
+    w = workload(4)
+    x = synth.activations(w.cfg, T)
+    lg = synth.router_logits(w.cfg, T)
+    L, out = run_layer(w, T, x, logits=lg)
+    _check_layer_sampled(orc, w, T, x, lg, L, out, n_sample=8)
+
+
+def test_layer_large_sparse_cfg4_T4096(lib, orc):
+    _announce("layer: config 4, T=4096")
+    w = workload(4)
+    T = 4096
+    x = synth.activations(w.cfg, T)
+    lg = synth.router_logits(w.cfg, T)
+    L, out = run_layer(w, T, x, logits=lg)
+    _check_layer_sampled(orc, w, T, x, lg, L, out, n_sample=8)
+
+
+@pytest.mark.parametrize("path", [1, 2])
+def test_ffn_paths_agree_with_oracle(lib, orc, path):
+    """Both FFN implementations on one ragged workload: an expert with more
+    than 64 tokens (several weight passes in the decode kernels), empty
+    experts, a partial last tile."""
+    _announce(f"ffn: forced path {path}, skewed T=300 on 16 experts")
+    w = workload(2, E=16)
+    T = 300
+    x = synth.activations(w.cfg, T, step=5)
+    lg = _perm_case(T, 16, 8, "skew")
+    lib.moe_set_option(lib.MOE_OPT_FFN_PATH, path)
+    try:
+        L, out = run_layer(w, T, x, logits=lg)
+    except lib.MoeError as e:
+        if e.code == lib.MOE_EUNSUPPORTED:
+            pytest.skip("this FFN path is not available for the shape")
+        raise
+    finally:
+        lib.moe_set_option(lib.MOE_OPT_FFN_PATH, 0)
+    _check_layer_sampled(orc, w, T, x, lg, L, out, n_sample=20)
+
+
+def test_shared_expert_call_is_plain_swiglu(lib, orc):
+    _announce("ffn: E=1, k=1 identity call (shared-expert form)")
+    w = workload(4)
+    T = 40
+    x = synth.activations(w.cfg, T, step=2)
+    from mixture_experts_gate_amd.layer import MoeLayer
+    M = MoeLayer(w.cfg.H, w.cfg.E, w.cfg.k, w.cfg.I, w.cfg.fmt, T, shared=True, device=DEV)
+    M.prepare_shared(T)
+    M.shared_ffn(T, to_dev_bf16(x), w.dev_shared.table)
+    torch.cuda.synchronize()
+    ref = orc.ffn_rows(x, w.shared[None], w.lay, np.arange(T, dtype=np.int32),
+                       np.zeros(T, np.int32))
+    assert_close(M.y_sh[:T].float().cpu().numpy(), ref, "shared expert y")
+
+
+def test_layer_deterministic(lib):
+    _announce("determinism: config 2 T=64 twice")
+    w = workload(2)
+    x = synth.activations(w.cfg, 64, step=3)
+    lg = synth.router_logits(w.cfg, 64, step=3)
+    L1, o1 = run_layer(w, 64, x, logits=lg)
+    a = (o1.clone(), L1.y.clone(), L1.sorted_pair.clone())
+    L2, o2 = run_layer(w, 64, x, logits=lg)
+    assert torch.equal(a[0], o2) and torch.equal(a[1], L2.y) and torch.equal(a[2], L2.sorted_pair)

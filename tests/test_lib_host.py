@@ -1,0 +1,98 @@
+"""Host-side checks of the HIP library (no GPU needed): it loads, exports every
+symbol the header declares, and rejects bad arguments before touching the
+device."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from mixture_experts_gate_amd import _lib
+    if not os.path.exists(_lib.LIB_PATH):
+        from mixture_experts_gate_amd import build
+        build.build()
+    return _lib
+
+
+def _declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"\b(moe_\w+|expert_cache_\w+)\s*\(", src)
+    return sorted(set(names))
+
+
+def test_header_declares_binding_exports(lib):
+    assert _declared_functions() == sorted(lib.EXPORTS)
+
+
+def test_library_exports_every_symbol(lib):
+    L = C.CDLL(lib.LIB_PATH)
+    for name in _declared_functions():
+        assert hasattr(L, name), name
+
+
+def test_strerror_and_options(lib):
+    L = lib.load()
+    assert L.moe_strerror(0) == b"ok"
+    assert L.moe_strerror(lib.MOE_EINVAL) == b"invalid argument"
+    assert L.moe_strerror(-99) == b"unknown error"
+    assert L.moe_get_option(lib.MOE_OPT_FFN_PATH) == 0
+    assert L.moe_set_option(lib.MOE_OPT_FFN_PATH, 3) == lib.MOE_EINVAL
+    assert L.moe_set_option(99, 0) == lib.MOE_EINVAL
+
+
+def test_workspace_sizes(lib):
+    pb, fb = lib.moe_workspace_size(64, 8, 2048, 768, 128)
+    assert pb == 0                      # one-workgroup permutation needs no workspace
+    assert fb >= 64 * 8 * 768 * 2
+    pb, fb = lib.moe_workspace_size(8192, 8, 2048, 768, 128)
+    assert pb >= (64 * 128 + 65536) * 4
+    assert fb >= 65536 * 768 * 2
+    with pytest.raises(lib.MoeError):
+        lib.moe_workspace_size(-1, 8, 2048, 768, 128)
+
+
+def test_argument_errors_before_any_device_work(lib):
+    L = lib.load()
+    dummy = 0x1000  # never dereferenced: validation fails first
+    # k > E
+    assert L.moe_route(None, None, dummy, None, 4, 64, 8, 9, 1, dummy, dummy, None) == lib.MOE_EINVAL
+    # gate needs H % 8 == 0
+    assert L.moe_route(dummy, dummy, None, None, 4, 12, 8, 2, 1, dummy, dummy, None) == lib.MOE_EINVAL
+    # E above the permutation's limit
+    assert L.moe_permute(dummy, 4, 2, 513, dummy, dummy, dummy, None, 0, None) == lib.MOE_EINVAL
+    # H not a multiple of 32
+    assert L.moe_expert_ffn(dummy, dummy, dummy, dummy, 1, 4, 2, 48, 64, 8, dummy, 0, dummy,
+                            1 << 20, None) == lib.MOE_EINVAL
+    # workspace too small
+    assert L.moe_expert_ffn(dummy, dummy, dummy, dummy, 1, 4, 2, 64, 64, 8, dummy, 0, dummy,
+                            16, None) == lib.MOE_EINVAL
+    # bad weight format
+    assert L.moe_expert_ffn(dummy, dummy, dummy, dummy, 7, 4, 2, 64, 64, 8, dummy, 0, dummy,
+                            1 << 20, None) == lib.MOE_EINVAL
+    # combine: H % 8
+    assert L.moe_combine(dummy, 0, dummy, None, 4, 2, 12, dummy, None) == lib.MOE_EINVAL
+    # T == 0 is a no-op that succeeds
+    assert L.moe_combine(None, 0, None, None, 0, 2, 64, None, None) == lib.MOE_OK
+    assert L.moe_route(None, None, None, None, 0, 64, 8, 2, 1, None, None, None) == lib.MOE_OK
+
+
+def test_cache_reserve_argument_errors(lib):
+    L = lib.load()
+    h = C.c_void_p(0)
+    src = (C.c_void_p * 2)(0x1000, 0x2000)
+    # pool too small for one layer of experts
+    assert L.expert_cache_reserve(C.byref(h), 0x1000, 1024, 1024, 1, 2, src, 0, 0, 0, 0,
+                                  None) == lib.MOE_ENOMEM
+    # null host source
+    src0 = (C.c_void_p * 2)(0x1000, None)
+    assert L.expert_cache_reserve(C.byref(h), 0x1000, 1 << 20, 1024, 1, 2, src0, 0, 0, 0, 0,
+                                  None) == lib.MOE_EINVAL
+    assert L.expert_cache_destroy(None) == lib.MOE_EINVAL
+    assert L.expert_cache_slots(None) == lib.MOE_EINVAL
