@@ -153,13 +153,23 @@ int moe_combine(const void *y, int y_is_fp32, const float *topk_w, const void *y
 int moe_workspace_size(int T, int k, int H, int I, int E, size_t *permute_bytes,
                        size_t *ffn_bytes);
 
-/* Tuning and test knobs (process-wide).
+/* Tuning and diagnostic knobs (process-wide).
  *   MOE_OPT_FFN_PATH: 0 = choose by size (default), 1 = force the decode
  *                     (weight-streaming) kernels, 2 = force the prefill
- *                     (tiled matrix-core) kernels. */
-enum { MOE_OPT_FFN_PATH = 1 };
+ *                     (tiled matrix-core) kernels.
+ *   MOE_OPT_TIMING:   1 = bracket every kernel launch of the library with two
+ *                     events on the launch's stream (adds two event records
+ *                     per launch; do not use under graph capture); 0 = off.
+ *                     Setting it clears the accumulated timings. */
+enum { MOE_OPT_FFN_PATH = 1, MOE_OPT_TIMING = 2 };
 int moe_set_option(int option, int value);
 int moe_get_option(int option);
+
+/* Kernel ids 0 .. (number of kernels - 1); NULL past the last. */
+const char *moe_kernel_name(int kernel_id);
+/* Launches of kernel_id timed since MOE_OPT_TIMING was last set, and their
+ * summed durations in milliseconds (waits for the recorded events). */
+int moe_timing_query(int kernel_id, long long *launches, double *total_ms);
 
 /* ---------------------------------------------------------------------------
  * Expert cache: a pool of device slots holding expert blobs copied from pinned

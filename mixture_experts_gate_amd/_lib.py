@@ -16,11 +16,13 @@ LIB_PATH = os.path.join(_PKG, "libmoe.so")
 MOE_OK, MOE_EINVAL, MOE_ENOMEM, MOE_EHIP, MOE_EUNSUPPORTED, MOE_EBUSY = 0, -1, -2, -3, -4, -5
 MOE_W_BF16, MOE_W_MXFP4 = 0, 1
 MOE_OPT_FFN_PATH = 1
+MOE_OPT_TIMING = 2
 
 # every symbol include/moe.h declares
 EXPORTS = [
     "moe_strerror", "moe_last_hip_error", "moe_route", "moe_permute", "moe_expert_ffn",
-    "moe_combine", "moe_workspace_size", "moe_set_option", "moe_get_option",
+    "moe_combine", "moe_workspace_size", "moe_set_option", "moe_get_option", "moe_kernel_name",
+    "moe_timing_query",
     "expert_cache_reserve", "expert_cache_prefetch", "expert_cache_evict", "expert_cache_stats",
     "expert_cache_slots", "expert_cache_slot_of", "expert_cache_destroy",
 ]
@@ -62,6 +64,8 @@ def load(path: str | None = None):
         "moe_workspace_size": (I, [I, I, I, I, I, C.POINTER(Z), C.POINTER(Z)]),
         "moe_set_option": (I, [I, I]),
         "moe_get_option": (I, [I]),
+        "moe_kernel_name": (C.c_char_p, [I]),
+        "moe_timing_query": (I, [I, C.POINTER(C.c_longlong), C.POINTER(C.c_double)]),
         "expert_cache_reserve": (I, [C.POINTER(P), P, Z, Z, I, I, P, Z, Z, Z, Z, P]),
         "expert_cache_prefetch": (I, [P, I, P, I, P, C.POINTER(P)]),
         "expert_cache_evict": (I, [P, I, P, I]),
@@ -145,6 +149,35 @@ def moe_set_option(option, value):
 
 def moe_get_option(option):
     return _check("moe_get_option", load().moe_get_option(option))
+
+
+def kernel_names():
+    L = load()
+    out = []
+    i = 0
+    while True:
+        n = L.moe_kernel_name(i)
+        if n is None:
+            return out
+        out.append(n.decode())
+        i += 1
+
+
+def moe_timing_query(kernel_id):
+    """(launches, total_ms) of one kernel since timing was last switched."""
+    n, ms = C.c_longlong(0), C.c_double(0.0)
+    _check("moe_timing_query", load().moe_timing_query(kernel_id, C.byref(n), C.byref(ms)))
+    return n.value, ms.value
+
+
+def timing_report():
+    """{kernel name: (launches, total_ms)} for kernels launched while timing was on."""
+    rep = {}
+    for i, name in enumerate(kernel_names()):
+        n, ms = moe_timing_query(i)
+        if n:
+            rep[name] = (n, ms)
+    return rep
 
 
 # ------------------------------------------------------------ expert cache --

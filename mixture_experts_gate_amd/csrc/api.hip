@@ -1,6 +1,8 @@
 // C-ABI glue: error text, options, workspace sizing and the expert-FFN
 // dispatcher (decode-shaped weight streaming vs prefill-shaped tiled GEMM).
 #include <atomic>
+#include <mutex>
+#include <vector>
 
 #include "common.hpp"
 
@@ -11,6 +13,71 @@ static std::atomic<int> g_ffn_path{0};
 
 void set_last_hip_error(hipError_t e) { g_last_hip_error = (int)e; }
 int ffn_path_option() { return g_ffn_path.load(); }
+
+// ---------------------------------------------------------------- timing --
+// Optional per-kernel launch timing: each launch is bracketed by two events
+// recorded on its own stream; moe_timing_query sums the elapsed times.
+static std::atomic<bool> g_timing{false};
+static std::mutex g_tmu;
+struct TimingRec {
+    int kid;
+    hipEvent_t a, b;
+};
+static std::vector<TimingRec> g_recs;        // completed brackets awaiting a query
+static std::vector<TimingRec> g_open;        // started, not yet closed (per kernel id)
+static std::vector<hipEvent_t> g_evpool;
+static long long g_launches[K_COUNT];
+static double g_ms[K_COUNT];
+
+static const char *const g_kernel_names[K_COUNT] = {
+    "route", "permute_small", "permute_rank", "permute_scan", "permute_scatter", "permute_empty",
+    "ffn_decode_gate_up", "ffn_decode_down", "ffn_prefill_gate_up", "ffn_prefill_down",
+    "combine", "cache_table"};
+
+static hipEvent_t pool_event() {
+    if (!g_evpool.empty()) {
+        hipEvent_t e = g_evpool.back();
+        g_evpool.pop_back();
+        return e;
+    }
+    hipEvent_t e = nullptr;
+    (void)hipEventCreate(&e);
+    return e;
+}
+
+bool timing_enabled() { return g_timing.load(std::memory_order_relaxed); }
+
+void timing_mark(hipStream_t s, int kid, bool start) {
+    std::lock_guard<std::mutex> lk(g_tmu);
+    if (start) {
+        TimingRec r{kid, pool_event(), nullptr};
+        (void)hipEventRecord(r.a, s);
+        g_open.push_back(r);
+    } else {
+        for (size_t i = g_open.size(); i-- > 0;) {
+            if (g_open[i].kid != kid) continue;
+            TimingRec r = g_open[i];
+            g_open.erase(g_open.begin() + (long)i);
+            r.b = pool_event();
+            (void)hipEventRecord(r.b, s);
+            g_recs.push_back(r);
+            break;
+        }
+    }
+}
+
+static void timing_drain() {
+    for (TimingRec &r : g_recs) {
+        float ms = 0.0f;
+        if (hipEventSynchronize(r.b) == hipSuccess && hipEventElapsedTime(&ms, r.a, r.b) == hipSuccess) {
+            g_ms[r.kid] += ms;
+            g_launches[r.kid] += 1;
+        }
+        g_evpool.push_back(r.a);
+        g_evpool.push_back(r.b);
+    }
+    g_recs.clear();
+}
 
 size_t permute_ws_bytes(long n, int E);
 int ffn_decode(const uint16_t *x, const int32_t *sorted_pair, const int32_t *offsets,
@@ -58,12 +125,38 @@ extern "C" int moe_set_option(int option, int value) {
         g_ffn_path.store(value);
         return MOE_OK;
     }
+    if (option == MOE_OPT_TIMING) {
+        if (value < 0 || value > 1) return MOE_EINVAL;
+        std::lock_guard<std::mutex> lk(g_tmu);
+        timing_drain();
+        for (int i = 0; i < K_COUNT; ++i) {
+            g_launches[i] = 0;
+            g_ms[i] = 0.0;
+        }
+        g_timing.store(value == 1);
+        return MOE_OK;
+    }
     return MOE_EINVAL;
 }
 
 extern "C" int moe_get_option(int option) {
     if (option == MOE_OPT_FFN_PATH) return g_ffn_path.load();
+    if (option == MOE_OPT_TIMING) return g_timing.load() ? 1 : 0;
     return MOE_EINVAL;
+}
+
+extern "C" const char *moe_kernel_name(int kernel_id) {
+    if (kernel_id < 0 || kernel_id >= K_COUNT) return nullptr;
+    return g_kernel_names[kernel_id];
+}
+
+extern "C" int moe_timing_query(int kernel_id, long long *launches, double *total_ms) {
+    if (kernel_id < 0 || kernel_id >= K_COUNT) return MOE_EINVAL;
+    std::lock_guard<std::mutex> lk(g_tmu);
+    timing_drain();
+    if (launches) *launches = g_launches[kernel_id];
+    if (total_ms) *total_ms = g_ms[kernel_id];
+    return MOE_OK;
 }
 
 extern "C" int moe_workspace_size(int T, int k, int H, int I, int E, size_t *permute_bytes,

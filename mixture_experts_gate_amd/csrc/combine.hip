@@ -68,10 +68,12 @@ extern "C" int moe_combine(const void *y, int y_is_fp32, const float *topk_w, co
     dim3 grid((unsigned)((n + 255) / 256)), block(256);
     hipStream_t s = (hipStream_t)stream;
     if (y_is_fp32)
-        hipLaunchKernelGGL(combine_kernel<true>, grid, block, 0, s, y, topk_w, y_shared, T, k, H,
-                           out_bf16);
+        MOE_TIMED(s, K_COMBINE,
+                  hipLaunchKernelGGL(combine_kernel<true>, grid, block, 0, s, y, topk_w, y_shared,
+                                     T, k, H, out_bf16));
     else
-        hipLaunchKernelGGL(combine_kernel<false>, grid, block, 0, s, y, topk_w, y_shared, T, k, H,
-                           out_bf16);
+        MOE_TIMED(s, K_COMBINE,
+                  hipLaunchKernelGGL(combine_kernel<false>, grid, block, 0, s, y, topk_w, y_shared,
+                                     T, k, H, out_bf16));
     return check_launch();
 }

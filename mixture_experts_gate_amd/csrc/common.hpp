@@ -40,6 +40,35 @@ inline int check_hip(hipError_t e) {
 
 int ffn_path_option();
 
+// Kernel ids for the optional launch timing (moe_timing_query).
+enum KernelId {
+    K_ROUTE = 0, K_PERM_SMALL, K_PERM_RANK, K_PERM_SCAN, K_PERM_SCATTER, K_PERM_EMPTY,
+    K_DEC_GATE_UP, K_DEC_DOWN, K_PRE_GATE_UP, K_PRE_DOWN, K_COMBINE, K_CACHE_TABLE, K_COUNT
+};
+
+bool timing_enabled();
+void timing_mark(hipStream_t s, int kid, bool start);
+
+// Brackets one launch with events on its stream when timing is enabled.
+struct TimedLaunch {
+    hipStream_t s;
+    int kid;
+    bool on;
+    TimedLaunch(hipStream_t s_, int kid_) : s(s_), kid(kid_), on(timing_enabled()) {
+        if (on) timing_mark(s, kid, true);
+    }
+    ~TimedLaunch() {
+        if (on) timing_mark(s, kid, false);
+    }
+};
+
+// Launch statement `launch` bracketed for timing as kernel `kid` on `stream`.
+#define MOE_TIMED(stream, kid, launch)                 \
+    do {                                               \
+        ::moe::TimedLaunch moe_timed_((stream), (kid)); \
+        launch;                                        \
+    } while (0)
+
 // ------------------------------------------------------------ bf16 bits --
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) {

@@ -261,9 +261,10 @@ template <int FMT>
 static int launch_gate_up(int spw, dim3 grid, hipStream_t s, const uint16_t *x, const int32_t *sp,
                           const int32_t *off, const moe_expert_w *ex, int k, int H, int I, int E,
                           uint16_t *act) {
-#define MOE_GU(N)                                                                               \
-    hipLaunchKernelGGL((ffn_dec_gate_up<FMT, N>), grid, dim3(256), 0, s, x, sp, off, ex, k, H, I, \
-                       E, act)
+#define MOE_GU(N)                                                                          \
+    MOE_TIMED(s, K_DEC_GATE_UP,                                                            \
+              hipLaunchKernelGGL((ffn_dec_gate_up<FMT, N>), grid, dim3(256), 0, s, x, sp, off, \
+                                 ex, k, H, I, E, act))
     switch (spw) {
         case 1: MOE_GU(1); break;
         case 2: MOE_GU(2); break;
@@ -278,9 +279,10 @@ static int launch_gate_up(int spw, dim3 grid, hipStream_t s, const uint16_t *x, 
 template <int FMT, bool YF32>
 static int launch_down(int spk, dim3 grid, hipStream_t s, const uint16_t *act, const int32_t *sp,
                        const int32_t *off, const moe_expert_w *ex, int H, int I, int E, void *y) {
-#define MOE_DN(N)                                                                                \
-    hipLaunchKernelGGL((ffn_dec_down<FMT, N, YF32>), grid, dim3(256), 0, s, act, sp, off, ex, H, \
-                       I, E, y)
+#define MOE_DN(N)                                                                             \
+    MOE_TIMED(s, K_DEC_DOWN,                                                                  \
+              hipLaunchKernelGGL((ffn_dec_down<FMT, N, YF32>), grid, dim3(256), 0, s, act, sp, \
+                                 off, ex, H, I, E, y))
     switch (spk) {
         case 2: MOE_DN(2); break;
         case 4: MOE_DN(4); break;

@@ -205,14 +205,16 @@ extern "C" int moe_permute(const int32_t *topk_ids, int T, int k, int E, int32_t
     if (n > 0x7FFFFFFFL) return MOE_EINVAL;
     hipStream_t s = (hipStream_t)stream;
     if (n == 0) {
-        hipLaunchKernelGGL(permute_empty_kernel, dim3(1), dim3(256), 0, s, E, offsets);
+        MOE_TIMED(s, K_PERM_EMPTY,
+                  hipLaunchKernelGGL(permute_empty_kernel, dim3(1), dim3(256), 0, s, E, offsets));
         return check_launch();
     }
     if (!topk_ids || !sorted_pair || !pair_row) return MOE_EINVAL;
     if (n <= kSmallMax) {
         const size_t lds = (size_t)(E + (E + 1) + E + 32 + kWavesPerChunk * E) * sizeof(int);
-        hipLaunchKernelGGL(permute_small_kernel, dim3(1), dim3(kChunk), lds, s, topk_ids, (int)n,
-                           E, offsets, sorted_pair, pair_row);
+        MOE_TIMED(s, K_PERM_SMALL,
+                  hipLaunchKernelGGL(permute_small_kernel, dim3(1), dim3(kChunk), lds, s, topk_ids,
+                                     (int)n, E, offsets, sorted_pair, pair_row));
         return check_launch();
     }
     if (ws_bytes < permute_ws_bytes(n, E) || !ws) return MOE_EINVAL;
@@ -220,14 +222,18 @@ extern "C" int moe_permute(const int32_t *topk_ids, int T, int k, int E, int32_t
     int32_t *hist = (int32_t *)ws;
     int32_t *lrank = hist + (size_t)nb * E;
     const size_t lds1 = (size_t)(E + kWavesPerChunk * E) * sizeof(int);
-    hipLaunchKernelGGL(permute_rank_kernel, dim3(nb), dim3(kChunk), lds1, s, topk_ids, (int)n, E,
-                       hist, lrank);
+    MOE_TIMED(s, K_PERM_RANK,
+              hipLaunchKernelGGL(permute_rank_kernel, dim3(nb), dim3(kChunk), lds1, s, topk_ids,
+                                 (int)n, E, hist, lrank));
     int rc = check_launch();
     if (rc) return rc;
-    hipLaunchKernelGGL(permute_scan_kernel, dim3(1), dim3(kChunk), 0, s, nb, E, hist, offsets);
+    MOE_TIMED(s, K_PERM_SCAN,
+              hipLaunchKernelGGL(permute_scan_kernel, dim3(1), dim3(kChunk), 0, s, nb, E, hist,
+                                 offsets));
     rc = check_launch();
     if (rc) return rc;
-    hipLaunchKernelGGL(permute_scatter_kernel, dim3(nb), dim3(kChunk), 0, s, topk_ids, (int)n, E,
-                       hist, lrank, sorted_pair, pair_row);
+    MOE_TIMED(s, K_PERM_SCATTER,
+              hipLaunchKernelGGL(permute_scatter_kernel, dim3(nb), dim3(kChunk), 0, s, topk_ids,
+                                 (int)n, E, hist, lrank, sorted_pair, pair_row));
     return check_launch();
 }
