@@ -32,14 +32,25 @@
  *   - Token-pair numbering: pair p = t*k + j is the j-th expert (in routing
  *     order) of token t.
  *
- * Expert weight layout (one contiguous blob per expert, described by
- * moe_expert_w): W13 has 2I rows of length H (rows 0..I-1 are the gate
- * projection W1, rows I..2I-1 the up projection W3); W2 has H rows of length I.
- *   MOE_W_MXFP4: rows of E2M1 codes, two per byte, the even element in the low
- *                nibble; one E8M0 scale byte per 32 consecutive elements of a
- *                row (scales [rows][K/32], row-major).
- *   MOE_W_BF16 : rows of bf16; scale pointers are ignored.
- * All weight row starts must be 16-byte aligned.
+ * Expert weights (one contiguous blob per expert, described by moe_expert_w):
+ * W13 has 2I rows of length H (rows 0..I-1 are the gate projection W1, rows
+ * I..2I-1 the up projection W3); W2 has H rows of length I.
+ *   Interchange MXFP4 layout (row-major; what moe_pack_mxfp4 reads): rows of
+ *     E2M1 codes, two per byte, the even element in the low nibble; one E8M0
+ *     scale byte per 32 consecutive elements of a row (scales [rows][K/32]).
+ *   Kernel MXFP4 layout (MOE_W_MXFP4; what moe_expert_ffn reads): the same
+ *     codes and scales regrouped into 16-row x 128-column blocks. Block
+ *     (rb, s) of a matrix with K columns (nslab = K/128) holds rows
+ *     16rb..16rb+15, columns 128s..128s+127:
+ *       codes : 1024 bytes at (rb*nslab + s)*1024; bytes 16l..16l+15 are the
+ *               32 codes of row 16rb + l%16, columns 128s + 32(l/16) + 0..31
+ *               (even element in the low nibble);
+ *       scales: 64 bytes at (rb*nslab + s)*64; byte l is the scale of row
+ *               16rb + l%16, columns 128s + 32(l/16) + 0..31.
+ *     Sizes equal the interchange layout's. Requires H and I to be multiples
+ *     of 128.
+ *   MOE_W_BF16: rows of bf16, row-major; scale pointers are ignored.
+ * All weight matrix starts must be 16-byte aligned.
  */
 #ifndef MOE_MI355X_H
 #define MOE_MI355X_H
@@ -119,6 +130,17 @@ int moe_permute(const int32_t *topk_ids, int T, int k, int E, int32_t *offsets,
                 void *stream);
 
 /*
+ * moe_route_permute -- moe_route followed by moe_permute, with the same
+ * arguments and results as the two calls. For T <= 16 (and E <= 512) both run
+ * in one single-workgroup kernel that keeps the chosen ids on chip; larger
+ * batches make the two calls. ws / ws_bytes as for moe_permute.
+ */
+int moe_route_permute(const uint16_t *x_bf16, const uint16_t *wg_bf16, const float *logits_in,
+                      float *logits_out, int T, int H, int E, int k, int renormalize,
+                      int32_t *topk_ids, float *topk_w, int32_t *offsets, int32_t *sorted_pair,
+                      int32_t *pair_row, void *ws, size_t ws_bytes, void *stream);
+
+/*
  * moe_expert_ffn -- grouped SwiGLU expert FFN over the permuted pairs.
  *
  * For every row r of sorted order, with e its expert (offsets[e] <= r <
@@ -129,7 +151,8 @@ int moe_permute(const int32_t *topk_ids, int T, int k, int E, int32_t *offsets,
  * or fp32. Accumulation is fp32; the activation a is rounded to bf16 between
  * the two contractions.
  * experts: device array [E] of moe_expert_w; entries of experts that receive
- * no pair are never read. x_bf16 [T][H]. H and I must be multiples of 32.
+ * no pair are never read. x_bf16 [T][H]. fmt: MOE_W_MXFP4 (kernel layout,
+ * H and I multiples of 128) or MOE_W_BF16 (H and I multiples of 32).
  * ws: device workspace of at least the ffn size from moe_workspace_size.
  * The shared (always-on) expert is this call with E = 1, k = 1,
  * sorted_pair = 0..T-1 and offsets = {0, T}.
@@ -147,6 +170,18 @@ int moe_expert_ffn(const uint16_t *x_bf16, const int32_t *sorted_pair, const int
  */
 int moe_combine(const void *y, int y_is_fp32, const float *topk_w, const void *y_shared, int T,
                 int k, int H, uint16_t *out_bf16, void *stream);
+
+/*
+ * moe_pack_mxfp4 -- convert n expert blobs from the interchange MXFP4 layout
+ * to the kernel layout (see the top of this file). src and dst are device
+ * buffers of n blobs spaced src_stride / dst_stride bytes apart; within a blob
+ * the four sections sit at the byte offsets lay_w13, lay_s13, lay_w2, lay_s2
+ * in both. Sizes are unchanged. src and dst must not overlap. H and I must
+ * be multiples of 128.
+ */
+int moe_pack_mxfp4(const void *src, void *dst, int n, size_t src_stride, size_t dst_stride,
+                   int H, int I, size_t lay_w13, size_t lay_s13, size_t lay_w2, size_t lay_s2,
+                   void *stream);
 
 /* Device workspace bytes needed by moe_permute and moe_expert_ffn for these
  * sizes (host call, no device work). Either output pointer may be NULL. */

@@ -22,7 +22,7 @@ MOE_OPT_TIMING = 2
 EXPORTS = [
     "moe_strerror", "moe_last_hip_error", "moe_route", "moe_permute", "moe_expert_ffn",
     "moe_combine", "moe_workspace_size", "moe_set_option", "moe_get_option", "moe_kernel_name",
-    "moe_timing_query",
+    "moe_timing_query", "moe_pack_mxfp4", "moe_route_permute",
     "expert_cache_reserve", "expert_cache_prefetch", "expert_cache_evict", "expert_cache_stats",
     "expert_cache_slots", "expert_cache_slot_of", "expert_cache_destroy",
 ]
@@ -59,6 +59,7 @@ def load(path: str | None = None):
         "moe_last_hip_error": (I, []),
         "moe_route": (I, [P, P, P, P, I, I, I, I, I, P, P, P]),
         "moe_permute": (I, [P, I, I, I, P, P, P, P, Z, P]),
+        "moe_route_permute": (I, [P, P, P, P, I, I, I, I, I, P, P, P, P, P, P, Z, P]),
         "moe_expert_ffn": (I, [P, P, P, P, I, I, I, I, I, I, P, I, P, Z, P]),
         "moe_combine": (I, [P, I, P, P, I, I, I, P, P]),
         "moe_workspace_size": (I, [I, I, I, I, I, C.POINTER(Z), C.POINTER(Z)]),
@@ -66,6 +67,7 @@ def load(path: str | None = None):
         "moe_get_option": (I, [I]),
         "moe_kernel_name": (C.c_char_p, [I]),
         "moe_timing_query": (I, [I, C.POINTER(C.c_longlong), C.POINTER(C.c_double)]),
+        "moe_pack_mxfp4": (I, [P, P, I, Z, Z, I, I, Z, Z, Z, Z, P]),
         "expert_cache_reserve": (I, [C.POINTER(P), P, Z, Z, I, I, P, Z, Z, Z, Z, P]),
         "expert_cache_prefetch": (I, [P, I, P, I, P, C.POINTER(P)]),
         "expert_cache_evict": (I, [P, I, P, I]),
@@ -124,6 +126,14 @@ def moe_permute(topk_ids, T, k, E, offsets, sorted_pair, pair_row, ws, ws_bytes,
         ws_bytes, _stream(stream)))
 
 
+def moe_route_permute(x_bf16, wg_bf16, logits_in, logits_out, T, H, E, k, renormalize, topk_ids,
+                      topk_w, offsets, sorted_pair, pair_row, ws, ws_bytes, stream=None):
+    return _check("moe_route_permute", load().moe_route_permute(
+        _ptr(x_bf16), _ptr(wg_bf16), _ptr(logits_in), _ptr(logits_out), T, H, E, k,
+        int(bool(renormalize)), _ptr(topk_ids), _ptr(topk_w), _ptr(offsets), _ptr(sorted_pair),
+        _ptr(pair_row), _ptr(ws), ws_bytes, _stream(stream)))
+
+
 def moe_expert_ffn(x_bf16, sorted_pair, offsets, experts, fmt, T, k, H, I, E, y, y_is_fp32, ws,
                    ws_bytes, stream=None):
     return _check("moe_expert_ffn", load().moe_expert_ffn(
@@ -135,6 +145,12 @@ def moe_combine(y, y_is_fp32, topk_w, y_shared, T, k, H, out_bf16, stream=None):
     return _check("moe_combine", load().moe_combine(
         _ptr(y), int(bool(y_is_fp32)), _ptr(topk_w), _ptr(y_shared), T, k, H, _ptr(out_bf16),
         _stream(stream)))
+
+
+def moe_pack_mxfp4(src, dst, n, src_stride, dst_stride, H, I, layout, stream=None):
+    return _check("moe_pack_mxfp4", load().moe_pack_mxfp4(
+        _ptr(src), _ptr(dst), n, src_stride, dst_stride, H, I, layout.w13, layout.s13, layout.w2,
+        layout.s2, _stream(stream)))
 
 
 def moe_workspace_size(T, k, H, I, E):

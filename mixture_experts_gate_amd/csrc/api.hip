@@ -32,7 +32,7 @@ static double g_ms[K_COUNT];
 static const char *const g_kernel_names[K_COUNT] = {
     "route", "permute_small", "permute_rank", "permute_scan", "permute_scatter", "permute_empty",
     "ffn_decode_gate_up", "ffn_decode_down", "ffn_prefill_gate_up", "ffn_prefill_down",
-    "combine", "cache_table"};
+    "combine", "cache_table", "pack_mxfp4", "route_permute"};
 
 static hipEvent_t pool_event() {
     if (!g_evpool.empty()) {
@@ -174,6 +174,7 @@ extern "C" int moe_expert_ffn(const uint16_t *x_bf16, const int32_t *sorted_pair
                               size_t ws_bytes, void *stream) {
     if (T < 0 || k < 1 || E < 1 || H < 32 || I < 32 || H % 32 || I % 32) return MOE_EINVAL;
     if (fmt != MOE_W_MXFP4 && fmt != MOE_W_BF16) return MOE_EINVAL;
+    if (fmt == MOE_W_MXFP4 && (H % 128 || I % 128)) return MOE_EINVAL;
     if (T == 0) return MOE_OK;
     if (!x_bf16 || !sorted_pair || !offsets || !experts || !y || !ws) return MOE_EINVAL;
     const long n = (long)T * k;

@@ -26,22 +26,38 @@ __device__ __forceinline__ void load8(const void *base, size_t off, float v[8]) 
     }
 }
 
-template <bool YF32>
-__global__ __launch_bounds__(256) void combine_kernel(const void *__restrict__ y,
-                                                      const float *__restrict__ w,
-                                                      const void *__restrict__ ysh, int T, int k,
-                                                      int H, uint16_t *__restrict__ out) {
+// KMAX > 0: k == KMAX known at compile time (all k row loads issued at once).
+template <bool YF32, int KMAX>
+__global__ __launch_bounds__(64) void combine_kernel(const void *__restrict__ y,
+                                                     const float *__restrict__ w,
+                                                     const void *__restrict__ ysh, int T, int k,
+                                                     int H, uint16_t *__restrict__ out) {
     const int per_tok = H / 8;
     const long gid = (long)blockIdx.x * blockDim.x + threadIdx.x;
     if (gid >= (long)T * per_tok) return;
     const int t = (int)(gid / per_tok), h8 = (int)(gid - (long)t * per_tok) * 8;
+    const int kk = KMAX > 0 ? KMAX : k;
     float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    for (int j = 0; j < k; ++j) {
-        const float wj = w[(size_t)t * k + j];
-        float v[8];
-        load8<YF32>(y, ((size_t)t * k + j) * H + h8, v);
+    if (KMAX > 0) {
+        float v[KMAX > 0 ? KMAX : 1][8];
+        float wj[KMAX > 0 ? KMAX : 1];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) acc[i] += wj * v[i];
+        for (int j = 0; j < KMAX; ++j) {
+            wj[j] = w[(size_t)t * KMAX + j];
+            load8<YF32>(y, ((size_t)t * KMAX + j) * H + h8, v[j]);
+        }
+#pragma unroll
+        for (int j = 0; j < KMAX; ++j)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) acc[i] += wj[j] * v[j][i];
+    } else {
+        for (int j = 0; j < kk; ++j) {
+            const float wj = w[(size_t)t * kk + j];
+            float v[8];
+            load8<YF32>(y, ((size_t)t * kk + j) * H + h8, v);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) acc[i] += wj * v[i];
+        }
     }
     if (ysh) {
         float v[8];
@@ -55,6 +71,24 @@ __global__ __launch_bounds__(256) void combine_kernel(const void *__restrict__ y
     *reinterpret_cast<u32x4 *>(out + (size_t)t * H + h8) = o;
 }
 
+template <bool YF32>
+static void launch_combine(dim3 grid, hipStream_t s, const void *y, const float *w, const void *ysh,
+                           int T, int k, int H, uint16_t *out) {
+#define MOE_CB(KM)                                                                            \
+    MOE_TIMED(s, K_COMBINE,                                                                   \
+              hipLaunchKernelGGL((combine_kernel<YF32, KM>), grid, dim3(64), 0, s, y, w, ysh, T, \
+                                 k, H, out))
+    switch (k) {
+        case 1: MOE_CB(1); break;
+        case 2: MOE_CB(2); break;
+        case 4: MOE_CB(4); break;
+        case 6: MOE_CB(6); break;
+        case 8: MOE_CB(8); break;
+        default: MOE_CB(0); break;
+    }
+#undef MOE_CB
+}
+
 }  // namespace moe
 
 using namespace moe;
@@ -65,15 +99,9 @@ extern "C" int moe_combine(const void *y, int y_is_fp32, const float *topk_w, co
     if (T == 0) return MOE_OK;
     if (!y || !topk_w || !out_bf16) return MOE_EINVAL;
     const long n = (long)T * (H / 8);
-    dim3 grid((unsigned)((n + 255) / 256)), block(256);
+    dim3 grid((unsigned)((n + 63) / 64));
     hipStream_t s = (hipStream_t)stream;
-    if (y_is_fp32)
-        MOE_TIMED(s, K_COMBINE,
-                  hipLaunchKernelGGL(combine_kernel<true>, grid, block, 0, s, y, topk_w, y_shared,
-                                     T, k, H, out_bf16));
-    else
-        MOE_TIMED(s, K_COMBINE,
-                  hipLaunchKernelGGL(combine_kernel<false>, grid, block, 0, s, y, topk_w, y_shared,
-                                     T, k, H, out_bf16));
+    if (y_is_fp32) launch_combine<true>(grid, s, y, topk_w, y_shared, T, k, H, out_bf16);
+    else launch_combine<false>(grid, s, y, topk_w, y_shared, T, k, H, out_bf16);
     return check_launch();
 }

@@ -43,7 +43,7 @@ int ffn_path_option();
 // Kernel ids for the optional launch timing (moe_timing_query).
 enum KernelId {
     K_ROUTE = 0, K_PERM_SMALL, K_PERM_RANK, K_PERM_SCAN, K_PERM_SCATTER, K_PERM_EMPTY,
-    K_DEC_GATE_UP, K_DEC_DOWN, K_PRE_GATE_UP, K_PRE_DOWN, K_COMBINE, K_CACHE_TABLE, K_COUNT
+    K_DEC_GATE_UP, K_DEC_DOWN, K_PRE_GATE_UP, K_PRE_DOWN, K_COMBINE, K_CACHE_TABLE, K_PACK, K_ROUTE_PERMUTE, K_COUNT
 };
 
 bool timing_enabled();
@@ -94,12 +94,21 @@ __device__ __forceinline__ float e8m0_to_f32(uint32_t s) {
 
 // ------------------------------------------------------------- loads -----
 
+// Loads through the global address space: pointers read from device tables
+// are generic, and generic (FLAT) loads also count against the LDS/scalar
+// wait counter, which would make every LDS wait also wait for them.
+#define MOE_GLOBAL __attribute__((address_space(1)))
+
 __device__ __forceinline__ u32x4 load_nt16(const void *p) {
-    return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+    return __builtin_nontemporal_load((const MOE_GLOBAL u32x4 *)(p));
 }
 
 __device__ __forceinline__ u32x4 load16(const void *p) {
-    return *reinterpret_cast<const u32x4 *>(p);
+    return *(const MOE_GLOBAL u32x4 *)(p);
+}
+
+__device__ __forceinline__ uint32_t load_u8(const void *p) {
+    return *(const MOE_GLOBAL uint8_t *)(p);
 }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) {

@@ -3,10 +3,10 @@
 //
 // The pages place the cost of decoding a sparse MoE in expert-weight movement
 // (winzheng.com page, "Why Now of All Times": only the routed experts'
-// parameters take part per token). Here every touched expert's weights are
-// read exactly once, coalesced and non-temporal, decoded in registers
-// (E2M1 x E8M0 -> bf16 with the gfx950 scaled convert) and fed to bf16
-// matrix-core instructions whose other operand is the expert's tokens.
+// parameters take part per token). Every touched expert's weights are read
+// exactly once, coalesced and non-temporal, decoded in registers (E2M1 x E8M0
+// -> bf16 with the gfx950 scaled convert) and fed to bf16 matrix-core
+// instructions whose other operand is the expert's tokens.
 //
 // Operand layout of v_mfma_f32_16x16x32_bf16 as used here: lane l supplies row
 // (l % 16) and K-chunk (l / 16) of A (8 consecutive K), column (l % 16) and
@@ -15,27 +15,31 @@
 // feed 4 MFMAs, and the token operand is loaded with the same K mapping, so
 // the K order inside an MFMA is a consistent permutation on both sides.
 //
-// Kernel 1 (gate/up + SwiGLU): one workgroup = 16 gate rows + the matching 16
-// up rows of one touched expert; its 4 wavefronts split K and meet in LDS.
-// Kernel 2 (down): one workgroup = 64 output rows (16 per wavefront) of one
-// touched expert, full K per wavefront.
-// Both grids are fixed by (min(E, T*k) touched-expert slots) x (row groups);
-// each workgroup finds its expert from the device offsets, so nothing depends
-// on a host round trip.
+// Work decomposition (both stages): a tile is two 16-row blocks of one
+// touched expert over the full contraction length K; the KS wavefronts of a
+// workgroup split K, and their partial sums meet in LDS (fixed order). Each
+// workgroup owns a contiguous range of the U * tiles_per_expert tiles (U =
+// experts with pairs, counted on the device), so the grid is fixed and no
+// host round trip is needed. While a tile is being multiplied, the next
+// tile's weights are already in flight; the token operand stays in registers
+// while consecutive tiles belong to the same expert.
+//   stage 1: blocks = 16 gate rows and the matching 16 up rows of W13 (K = H);
+//            epilogue a = silu(g) * u -> act[sorted row][I] (bf16).
+//   stage 2: blocks = 32 consecutive rows of W2 (K = I);
+//            epilogue -> y[pair][H] (bf16 or fp32).
 #include <math.h>
 
 #include "common.hpp"
 
 namespace moe {
 
-constexpr int kTokPerPass = 64;     // tokens (4 groups of 16) per weight pass
-constexpr int kGroups = kTokPerPass / 16;
+constexpr int kPass = 16;     // tokens per MFMA pass (one 16-column block)
 
 __device__ __forceinline__ float silu_mul(float g, float u) {
     return g / (1.0f + __expf(-g)) * u;
 }
 
-// Weight fragment of one lane for one 32-element K block: 4 x bf16x8.
+// One lane's weights for one 32-element K block of one row.
 template <int FMT>
 struct WFrag;
 
@@ -43,11 +47,16 @@ template <>
 struct WFrag<MOE_W_MXFP4> {
     u32x4 q;
     uint32_t s;
-    __device__ __forceinline__ void load(const uint8_t *codes_row, const uint8_t *scales_row,
-                                         int kb, bool ok) {
+    // Opaque to the optimiser: keeps the decode next to its use instead of
+    // hoisting every decoded fragment out of the token-pass loop.
+    __device__ __forceinline__ void pin() { asm volatile("" : "+v"(q), "+v"(s)); }
+    // kernel layout: block `chunk` = (row block, 128-column slab); lane l's
+    // 16 code bytes and scale byte sit at lane-contiguous positions
+    __device__ __forceinline__ void load_block(const uint8_t *codes, const uint8_t *scales,
+                                               size_t chunk, int lane, bool ok) {
         if (ok) {
-            q = load_nt16(codes_row + (size_t)kb * 16);
-            s = scales_row[kb];
+            q = load_nt16(codes + chunk * 1024 + lane * 16);
+            s = load_u8(scales + chunk * 64 + lane);
         } else {
             q = u32x4{0, 0, 0, 0};
             s = 127;
@@ -59,6 +68,7 @@ struct WFrag<MOE_W_MXFP4> {
 template <>
 struct WFrag<MOE_W_BF16> {
     u32x4 q[4];
+    __device__ __forceinline__ void pin() { asm volatile("" : "+v"(q[0]), "+v"(q[1]), "+v"(q[2]), "+v"(q[3])); }
     __device__ __forceinline__ void load(const uint8_t *row, const uint8_t *, int kb, bool ok) {
 #pragma unroll
         for (int j = 0; j < 4; ++j)
@@ -77,257 +87,358 @@ __device__ __forceinline__ const uint8_t *srow(const uint8_t *base, long r, int 
     return base ? base + r * (K / 32) : nullptr;
 }
 
-// -------------------------------------------------------------- kernel 1 --
-// SPW: 128-wide K slabs per wavefront (4 wavefronts cover ceil(H/128) slabs).
-template <int FMT, int SPW>
-__global__ __launch_bounds__(256) void ffn_dec_gate_up(
-    const uint16_t *__restrict__ x, const int32_t *__restrict__ sorted_pair,
-    const int32_t *__restrict__ offsets, const moe_expert_w *__restrict__ experts, int k, int H,
-    int I, int E, uint16_t *__restrict__ act) {
-    __shared__ float red[3][kGroups][2][4][kWave];
-    const int lane = lane_id(), wv = threadIdx.x / kWave;
-    const int nrg = I / 16;
-    const int a = blockIdx.x / nrg, rg = blockIdx.x - a * nrg;
-    const int e = find_active_expert(offsets, E, a);
-    if (e < 0) return;
-    const int row0 = offsets[e], n_e = offsets[e + 1] - row0;
-    const moe_expert_w W = experts[e];
-    const int m = lane & 15, c = lane >> 4;
-    const int nblk = H / 32;
-
-    const uint8_t *rg_codes = wrow<FMT>(W.w13, rg * 16 + m, H);
-    const uint8_t *ru_codes = wrow<FMT>(W.w13, I + rg * 16 + m, H);
-    const uint8_t *rg_sc = srow(W.s13, rg * 16 + m, H);
-    const uint8_t *ru_sc = srow(W.s13, I + rg * 16 + m, H);
-
-    WFrag<FMT> fg[SPW], fu[SPW];
+// Experts that received at least one pair, as a bitmask (E <= 512), computed
+// by the whole wavefront; lookups afterwards are scalar.
+struct ActiveSet {
+    uint64_t w[8];
+    int count;
+    __device__ __forceinline__ void init(const int32_t *__restrict__ offsets, int E) {
+        count = 0;
 #pragma unroll
-    for (int i = 0; i < SPW; ++i) {
-        const int kb = (wv * SPW + i) * 4 + c;
-        fg[i].load(rg_codes, rg_sc, kb, kb < nblk);
-        fu[i].load(ru_codes, ru_sc, kb, kb < nblk);
+        for (int i = 0; i < 8; ++i) {
+            const int e = i * kWave + lane_id();
+            w[i] = __ballot(e < E && offsets[e + 1] > offsets[e]);
+            count += __popcll(w[i]);
+        }
     }
+    // index of the a-th (0-based) active expert; a < count
+    __device__ __forceinline__ int nth(int a) const {
+        int base = 0;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int c = __popcll(w[i]);
+            if (a < c) {
+                uint64_t m = w[i];
+                for (int r = 0; r < a; ++r) m &= m - 1;
+                return i * kWave + __ffsll((long long)m) - 1;
+            }
+            a -= c;
+            base += c;
+        }
+        return -1;
+    }
+};
 
-    for (int g0 = 0; g0 < n_e; g0 += kTokPerPass) {
-        f32x4 accg[kGroups], accu[kGroups];
-        const uint16_t *xrow[kGroups];
-        bool has[kGroups];
+struct DecArgs {
+    const uint16_t *src;            // B-operand rows: x [T][H] (stage 1) or act [T*k][I] (stage 2)
+    const int32_t *sorted_pair;
+    const int32_t *offsets;
+    const moe_expert_w *experts;
+    void *out;                      // act (stage 1) or y (stage 2)
+    int k, K, H, I, E, nrt;         // nrt: tiles per expert
+};
+
+// Expert-level state of the tile being processed.
+struct ExpertState {
+    int a, e, row0, n_e;
+    const uint8_t *w, *s;           // matrix base (W13 or W2) and its scales
+};
+
+template <int STAGE>
+__device__ __forceinline__ void expert_state(const DecArgs &A, const ActiveSet &act, int a,
+                                             ExpertState &st) {
+    st.a = a;
+    st.e = act.nth(a);
+    st.row0 = A.offsets[st.e];
+    st.n_e = A.offsets[st.e + 1] - st.row0;
+    const moe_expert_w W = A.experts[st.e];
+    st.w = reinterpret_cast<const uint8_t *>(STAGE == 1 ? W.w13 : W.w2);
+    st.s = STAGE == 1 ? W.s13 : W.s2;
+}
+
+// 16-row block index (within the stage's matrix) of block b of tile rt.
+// Stage 1: the first NB/2 blocks are gate rows, the last NB/2 the matching up rows.
+template <int STAGE, int NB>
+__device__ __forceinline__ long tile_block(const DecArgs &A, int rt, int b) {
+    if (STAGE == 1) {
+        constexpr int H2 = NB / 2;
+        return b < H2 ? (long)rt * H2 + b : (long)A.I / 16 + (long)rt * H2 + (b - H2);
+    }
+    return (long)rt * NB + b;
+}
+
+// FULL: the KS wavefronts x SPW slabs cover the K slabs exactly (no bounds checks).
+template <int FMT, int STAGE, int SPW, int NB, bool FULL>
+__device__ __forceinline__ void load_tile(const DecArgs &A, const ExpertState &st, int rt, int wv,
+                                          int lane, WFrag<FMT> (&f)[SPW][NB]) {
+    if constexpr (FMT == MOE_W_MXFP4) {
+        const int nslab = A.K / 128;
 #pragma unroll
-        for (int gi = 0; gi < kGroups; ++gi) {
-            accg[gi] = f32x4{0, 0, 0, 0};
-            accu[gi] = f32x4{0, 0, 0, 0};
-            const int r = g0 + gi * 16 + m;
-            has[gi] = r < n_e;
-            xrow[gi] = x + (size_t)(has[gi] ? sorted_pair[row0 + r] / k : 0) * H;
-        }
+        for (int b = 0; b < NB; ++b) {
+            const long rb = tile_block<STAGE, NB>(A, rt, b);
 #pragma unroll
-        for (int i = 0; i < SPW; ++i) {
-            const int kb = (wv * SPW + i) * 4 + c;
-            bf16x8 ag[4], au[4];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                ag[j] = fg[i].get(j);
-                au[j] = fu[i].get(j);
-            }
-#pragma unroll
-            for (int gi = 0; gi < kGroups; ++gi) {
-                if (g0 + gi * 16 >= n_e) break;      // wavefront-uniform
-                const bool ld = has[gi] && kb < nblk;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const bf16x8 b =
-                        ld ? as_bf16x8(load16(xrow[gi] + kb * 32 + j * 8)) : bf16x8{};
-                    accg[gi] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ag[j], b, accg[gi], 0, 0, 0);
-                    accu[gi] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(au[j], b, accu[gi], 0, 0, 0);
-                }
-            }
-        }
-        // K-split partial sums meet in LDS; wavefront 0 adds them in order 0,1,2,3
-        if (wv > 0) {
-#pragma unroll
-            for (int gi = 0; gi < kGroups; ++gi) {
-                if (g0 + gi * 16 >= n_e) break;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    red[wv - 1][gi][0][i][lane] = accg[gi][i];
-                    red[wv - 1][gi][1][i][lane] = accu[gi][i];
-                }
-            }
-        }
-        __syncthreads();
-        if (wv == 0) {
-#pragma unroll
-            for (int gi = 0; gi < kGroups; ++gi) {
-                if (g0 + gi * 16 >= n_e) break;
-                const int r = g0 + gi * 16 + m;
-                float o[4];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    float gs = accg[gi][i], us = accu[gi][i];
-#pragma unroll
-                    for (int w = 0; w < 3; ++w) {
-                        gs += red[w][gi][0][i][lane];
-                        us += red[w][gi][1][i][lane];
-                    }
-                    o[i] = silu_mul(gs, us);
-                }
-                if (r < n_e) {
-                    uint2 pk;
-                    pk.x = pack_bf16x2(o[0], o[1]);
-                    pk.y = pack_bf16x2(o[2], o[3]);
-                    *reinterpret_cast<uint2 *>(act + (size_t)(row0 + r) * I + rg * 16 + 4 * c) = pk;
-                }
+            for (int s = 0; s < SPW; ++s) {
+                const int slab = wv * SPW + s;
+                f[s][b].load_block(st.w, st.s, (size_t)rb * nslab + slab, lane,
+                                   FULL || slab < nslab);
             }
         }
-        __syncthreads();
+    } else {
+        const int nblk = A.K / 32, m = lane & 15, c = lane >> 4;
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            const long r = tile_block<STAGE, NB>(A, rt, b) * 16 + m;
+            const uint8_t *cr = wrow<FMT>(st.w, r, A.K);
+#pragma unroll
+            for (int s = 0; s < SPW; ++s) {
+                const int kb = (wv * SPW + s) * 4 + c;
+                f[s][b].load(cr, nullptr, kb, kb < nblk);
+            }
+        }
     }
 }
 
-// -------------------------------------------------------------- kernel 2 --
-// SPK: 128-wide K slabs (K = I) per wavefront, covering all of I.
-template <int FMT, int SPK, bool YF32>
-__global__ __launch_bounds__(256) void ffn_dec_down(
-    const uint16_t *__restrict__ act, const int32_t *__restrict__ sorted_pair,
-    const int32_t *__restrict__ offsets, const moe_expert_w *__restrict__ experts, int H, int I,
-    int E, void *__restrict__ y) {
-    const int lane = lane_id(), wv = threadIdx.x / kWave;
-    const int ncg = (H + 63) / 64;
-    const int a = blockIdx.x / ncg, cg = blockIdx.x - a * ncg;
-    const int e = find_active_expert(offsets, E, a);
-    if (e < 0) return;
-    const int nbase = cg * 64 + wv * 16;
-    if (nbase >= H) return;
-    const int row0 = offsets[e], n_e = offsets[e + 1] - row0;
-    const moe_expert_w W = experts[e];
-    const int m = lane & 15, c = lane >> 4;
-    const int nblk = I / 32;
-
-    const uint8_t *codes = wrow<FMT>(W.w2, nbase + m, I);
-    const uint8_t *sc = srow(W.s2, nbase + m, I);
-    WFrag<FMT> f[SPK];
-#pragma unroll
-    for (int i = 0; i < SPK; ++i) {
-        const int kb = i * 4 + c;
-        f[i].load(codes, sc, kb, kb < nblk);
+// Token operand of pass p (rows p*16 .. p*16+15 of the expert), K slabs of
+// this wavefront; for stage 2 also the pair index each row's output goes to.
+template <int STAGE, int SPW>
+__device__ __forceinline__ void load_tokens(const DecArgs &A, const ExpertState &st, int p, int wv,
+                                            int m, int c, u32x4 (&xr)[SPW][4], int &pidx) {
+    const int nblk = A.K / 32;
+    const int r = p * kPass + m;
+    const bool has = r < st.n_e;
+    const uint16_t *row;
+    if (STAGE == 1) {
+        row = A.src + (size_t)(has ? A.sorted_pair[st.row0 + r] / A.k : 0) * A.K;
+    } else {
+        row = A.src + (size_t)(st.row0 + (has ? r : 0)) * A.K;
+        pidx = has ? A.sorted_pair[st.row0 + r] : 0;
     }
+#pragma unroll
+    for (int s = 0; s < SPW; ++s) {
+        const int kb = (wv * SPW + s) * 4 + c;
+        const bool ld = has && kb < nblk;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            xr[s][j] = ld ? load16(row + kb * 32 + j * 8) : u32x4{0, 0, 0, 0};
+    }
+}
 
-    for (int g0 = 0; g0 < n_e; g0 += kTokPerPass) {
-        f32x4 acc[kGroups];
-        bool has[kGroups];
-#pragma unroll
-        for (int gi = 0; gi < kGroups; ++gi) {
-            acc[gi] = f32x4{0, 0, 0, 0};
-            has[gi] = g0 + gi * 16 + m < n_e;
+// One tile: token operand if the expert changed, prefetch of the next tile's
+// weights into `wn`, multiply from `wc`, K-split reduction, epilogue.
+template <int FMT, int STAGE, int SPW, int KS, int NB, bool YF32, bool FULL>
+__device__ __forceinline__ void dec_step(const DecArgs &A, const ActiveSet &act,
+                                         float (&red)[2][KS > 1 ? KS - 1 : 1][NB][4][kWave],
+                                         WFrag<FMT> (&wc)[SPW][NB], WFrag<FMT> (&wn)[SPW][NB],
+                                         u32x4 (&xr)[SPW][4], ExpertState &cur, ExpertState &nxt,
+                                         int &pidx, int &x_key, int &buf, long t, long t1,
+                                         int lane, int wv, int m, int c) {
+
+        const int rt = (int)(t % A.nrt);
+        // token operand for the first pass of this tile (loaded before the next
+        // prefetch, so that waiting for it does not wait for the prefetched weights)
+        if (x_key != cur.a * 4096) {
+            load_tokens<STAGE, SPW>(A, cur, 0, wv, m, c, xr, pidx);
+            x_key = cur.a * 4096;
         }
+        const bool more = t + 1 < t1;
+        if (more) {
+            const int an = (int)((t + 1) / A.nrt);
+            if (an != cur.a) expert_state<STAGE>(A, act, an, nxt);
+            else nxt = cur;
+            load_tile<FMT, STAGE, SPW, NB, FULL>(A, nxt, (int)((t + 1) % A.nrt), wv, lane, wn);
+        }
+        for (int p = 0; p * kPass < cur.n_e; ++p) {
+            if (p > 0) {   // more than 16 tokens: next 16 of this expert
+                load_tokens<STAGE, SPW>(A, cur, p, wv, m, c, xr, pidx);
+                x_key = cur.a * 4096 + p;
+            }
+            f32x4 acc[NB];
 #pragma unroll
-        for (int i = 0; i < SPK; ++i) {
-            const int kb = i * 4 + c;
-            bf16x8 w[4];
+            for (int b = 0; b < NB; ++b) acc[b] = f32x4{0, 0, 0, 0};
 #pragma unroll
-            for (int j = 0; j < 4; ++j) w[j] = f[i].get(j);
+            for (int s = 0; s < SPW; ++s)
 #pragma unroll
-            for (int gi = 0; gi < kGroups; ++gi) {
-                if (g0 + gi * 16 >= n_e) break;
-                const bool ld = has[gi] && kb < nblk;
-                const uint16_t *arow = act + (size_t)(row0 + g0 + gi * 16 + m) * I + kb * 32;
+                for (int b = 0; b < NB; ++b) wc[s][b].pin();
+#pragma unroll
+            for (int s = 0; s < SPW; ++s)
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    const bf16x8 b = ld ? as_bf16x8(load16(arow + j * 8)) : bf16x8{};
-                    acc[gi] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w[j], b, acc[gi], 0, 0, 0);
+                    const bf16x8 bx = as_bf16x8(xr[s][j]);
+#pragma unroll
+                    for (int b = 0; b < NB; ++b)
+                        acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wc[s][b].get(j), bx,
+                                                                        acc[b], 0, 0, 0);
+                }
+            // partial sums of the K split meet in LDS (double-buffered: one barrier per pass)
+            if (KS > 1) {
+                if (wv > 0) {
+#pragma unroll
+                    for (int b = 0; b < NB; ++b)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) red[buf][wv - 1][b][i][lane] = acc[b][i];
+                }
+                __syncthreads();
+            }
+            if (wv == 0) {
+#pragma unroll
+                for (int b = 0; b < NB; ++b)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+#pragma unroll
+                        for (int w = 0; w < KS - 1; ++w) acc[b][i] += red[buf][w][b][i][lane];
+                const int r = p * kPass + m;
+                if (r < cur.n_e) {
+                    if (STAGE == 1) {
+                        constexpr int H2 = NB / 2;
+                        uint16_t *actp = reinterpret_cast<uint16_t *>(A.out) + (size_t)(cur.row0 + r) * A.I;
+#pragma unroll
+                        for (int b = 0; b < H2; ++b) {
+                            uint2 pk;
+                            pk.x = pack_bf16x2(silu_mul(acc[b][0], acc[b + H2][0]),
+                                               silu_mul(acc[b][1], acc[b + H2][1]));
+                            pk.y = pack_bf16x2(silu_mul(acc[b][2], acc[b + H2][2]),
+                                               silu_mul(acc[b][3], acc[b + H2][3]));
+                            *reinterpret_cast<uint2 *>(actp + (rt * H2 + b) * 16 + 4 * c) = pk;
+                        }
+                    } else {
+                        const size_t prow = (size_t)pidx * A.H;
+#pragma unroll
+                        for (int b = 0; b < NB; ++b) {
+                            const size_t off = prow + (size_t)(rt * NB + b) * 16 + 4 * c;
+                            if (YF32) {
+                                *reinterpret_cast<f32x4 *>(reinterpret_cast<float *>(A.out) + off) = acc[b];
+                            } else {
+                                uint2 pk;
+                                pk.x = pack_bf16x2(acc[b][0], acc[b][1]);
+                                pk.y = pack_bf16x2(acc[b][2], acc[b][3]);
+                                *reinterpret_cast<uint2 *>(reinterpret_cast<uint16_t *>(A.out) + off) = pk;
+                            }
+                        }
+                    }
                 }
             }
+            buf ^= 1;
         }
-#pragma unroll
-        for (int gi = 0; gi < kGroups; ++gi) {
-            if (g0 + gi * 16 >= n_e) break;
-            if (!has[gi]) continue;
-            const int p = sorted_pair[row0 + g0 + gi * 16 + m];
-            const size_t off = (size_t)p * H + nbase + 4 * c;
-            if (YF32) {
-                *reinterpret_cast<f32x4 *>(reinterpret_cast<float *>(y) + off) = acc[gi];
-            } else {
-                uint2 pk;
-                pk.x = pack_bf16x2(acc[gi][0], acc[gi][1]);
-                pk.y = pack_bf16x2(acc[gi][2], acc[gi][3]);
-                *reinterpret_cast<uint2 *>(reinterpret_cast<uint16_t *>(y) + off) = pk;
-            }
-        }
+        if (more) cur = nxt;
+    
+}
+
+template <int FMT, int STAGE, int SPW, int KS, int NB, bool YF32, bool FULL>
+__global__ __launch_bounds__(kWave *KS) void ffn_dec_kernel(DecArgs A) {
+    __shared__ float red[2][KS > 1 ? KS - 1 : 1][NB][4][kWave];
+    const int lane = lane_id();
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);   // wavefront-uniform
+    const int m = lane & 15, c = lane >> 4;
+
+    ActiveSet act;
+    act.init(A.offsets, A.E);
+    const long total = (long)act.count * A.nrt;
+    const long t0 = (long)blockIdx.x * total / gridDim.x;
+    const long t1 = ((long)blockIdx.x + 1) * total / gridDim.x;
+    if (t0 >= t1) return;
+
+    ExpertState cur, nxt;
+    expert_state<STAGE>(A, act, (int)(t0 / A.nrt), cur);
+    // two register buffers used in turn: tile t computes from one while tile
+    // t+1's weights land in the other (no copy between them, so nothing waits
+    // for the prefetch before it is needed)
+    WFrag<FMT> wa[SPW][NB], wb[SPW][NB];
+    load_tile<FMT, STAGE, SPW, NB, FULL>(A, cur, (int)(t0 % A.nrt), wv, lane, wa);
+
+    u32x4 xr[SPW][4];
+    int pidx = 0;
+    int x_key = -1;
+    int buf = 0;
+
+    for (long t = t0; t < t1; t += 2) {
+        dec_step<FMT, STAGE, SPW, KS, NB, YF32, FULL>(A, act, red, wa, wb, xr, cur, nxt, pidx,
+                                                      x_key, buf, t, t1, lane, wv, m, c);
+        if (t + 1 < t1)
+            dec_step<FMT, STAGE, SPW, KS, NB, YF32, FULL>(A, act, red, wb, wa, xr, cur, nxt, pidx,
+                                                          x_key, buf, t + 1, t1, lane, wv, m, c);
     }
 }
 
 // ------------------------------------------------------------- launchers --
 
+// Persistent grid: as many workgroups as can be resident at once.
+static int num_cus() {
+    static int n = 0;
+    if (!n) {
+        int dev = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            n <= 0)
+            n = 256;
+    }
+    return n;
+}
+
+template <typename K>
+static unsigned resident_grid(K kernel, int threads) {
+    int per_cu = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) != hipSuccess ||
+        per_cu <= 0)
+        per_cu = 1;
+    return (unsigned)(per_cu * num_cus());
+}
+
+template <int FMT, int STAGE, int SPW, int KS, int NB, bool YF32, bool FULL>
+static int launch_dec(hipStream_t s, DecArgs A, long slots) {
+    static unsigned full = 0;
+    if (!full)
+        full = resident_grid(ffn_dec_kernel<FMT, STAGE, SPW, KS, NB, YF32, FULL>, kWave * KS);
+    // tiles per expert
+    A.nrt = STAGE == 1 ? A.I / (8 * NB) : A.H / (16 * NB);
+    const long max_tiles = slots * A.nrt;
+    const unsigned grid = (unsigned)(max_tiles < (long)full ? max_tiles : (long)full);
+    if (grid == 0) return MOE_OK;
+    MOE_TIMED(s, STAGE == 1 ? K_DEC_GATE_UP : K_DEC_DOWN,
+              hipLaunchKernelGGL((ffn_dec_kernel<FMT, STAGE, SPW, KS, NB, YF32, FULL>), dim3(grid),
+                                 dim3(kWave * KS), 0, s, A));
+    return check_launch();
+}
+
+// K split: KS wavefronts x SPW 128-column slabs each. Exact splits for the
+// slab counts of the supported shapes; otherwise a bounds-checked split.
+// Tiles: stage 1 = 16 gate + 16 up rows (NB = 2); stage 2 = NB2 x 16 rows.
+template <int FMT, int STAGE, bool YF32>
+static int launch_stage(int slabs, hipStream_t s, const DecArgs &A, long slots) {
+    const bool nb4 = STAGE == 2 && A.H % 64 == 0;
+#define MOE_ST(SPW_, KS_, FULL_)                                                              \
+    return nb4 ? launch_dec<FMT, STAGE, SPW_, KS_, (STAGE == 2 ? 4 : 2), YF32, FULL_>(s, A, slots) \
+               : launch_dec<FMT, STAGE, SPW_, KS_, 2, YF32, FULL_>(s, A, slots)
+    switch (slabs) {
+        case 1: MOE_ST(1, 1, true);
+        case 2: MOE_ST(1, 2, true);
+        case 3: MOE_ST(1, 3, true);
+        case 4: MOE_ST(1, 4, true);
+        case 6: MOE_ST(2, 3, true);
+        case 8: MOE_ST(2, 4, true);
+        case 12: MOE_ST(3, 4, true);
+        case 16: MOE_ST(4, 4, true);
+        case 24: MOE_ST(3, 8, true);
+        case 32: MOE_ST(4, 8, true);
+        default: break;
+    }
+    if (slabs <= 16) MOE_ST(4, 4, false);
+    if (slabs <= 32) MOE_ST(4, 8, false);
+#undef MOE_ST
+    return MOE_EUNSUPPORTED;
+}
+
 template <int FMT>
-static int launch_gate_up(int spw, dim3 grid, hipStream_t s, const uint16_t *x, const int32_t *sp,
-                          const int32_t *off, const moe_expert_w *ex, int k, int H, int I, int E,
-                          uint16_t *act) {
-#define MOE_GU(N)                                                                          \
-    MOE_TIMED(s, K_DEC_GATE_UP,                                                            \
-              hipLaunchKernelGGL((ffn_dec_gate_up<FMT, N>), grid, dim3(256), 0, s, x, sp, off, \
-                                 ex, k, H, I, E, act))
-    switch (spw) {
-        case 1: MOE_GU(1); break;
-        case 2: MOE_GU(2); break;
-        case 4: MOE_GU(4); break;
-        case 8: MOE_GU(8); break;
-        default: return MOE_EUNSUPPORTED;
-    }
-#undef MOE_GU
-    return check_launch();
-}
-
-template <int FMT, bool YF32>
-static int launch_down(int spk, dim3 grid, hipStream_t s, const uint16_t *act, const int32_t *sp,
-                       const int32_t *off, const moe_expert_w *ex, int H, int I, int E, void *y) {
-#define MOE_DN(N)                                                                             \
-    MOE_TIMED(s, K_DEC_DOWN,                                                                  \
-              hipLaunchKernelGGL((ffn_dec_down<FMT, N, YF32>), grid, dim3(256), 0, s, act, sp, \
-                                 off, ex, H, I, E, y))
-    switch (spk) {
-        case 2: MOE_DN(2); break;
-        case 4: MOE_DN(4); break;
-        case 6: MOE_DN(6); break;
-        case 8: MOE_DN(8); break;
-        case 16: MOE_DN(16); break;
-        default: return MOE_EUNSUPPORTED;
-    }
-#undef MOE_DN
-    return check_launch();
-}
-
-static int round_slabs(int slabs, const int *choices, int n) {
-    for (int i = 0; i < n; ++i)
-        if (slabs <= choices[i]) return choices[i];
-    return -1;
+static int ffn_decode_fmt(const uint16_t *x, const int32_t *sorted_pair, const int32_t *offsets,
+                          const moe_expert_w *experts, int T, int k, int H, int I, int E, void *y,
+                          int y_is_fp32, uint16_t *act, hipStream_t s) {
+    const long n_pairs = (long)T * k;
+    const long slots = n_pairs < E ? n_pairs : E;
+    DecArgs a1{x, sorted_pair, offsets, experts, act, k, H, H, I, E, 0};
+    int rc = launch_stage<FMT, 1, false>((H + 127) / 128, s, a1, slots);
+    if (rc) return rc;
+    DecArgs a2{act, sorted_pair, offsets, experts, y, k, I, H, I, E, 0};
+    if (y_is_fp32) return launch_stage<FMT, 2, true>((I + 127) / 128, s, a2, slots);
+    return launch_stage<FMT, 2, false>((I + 127) / 128, s, a2, slots);
 }
 
 int ffn_decode(const uint16_t *x, const int32_t *sorted_pair, const int32_t *offsets,
                const moe_expert_w *experts, int fmt, int T, int k, int H, int I, int E, void *y,
                int y_is_fp32, uint16_t *act, hipStream_t s) {
-    const int slabs_h = (H + 127) / 128, slabs_i = (I + 127) / 128;
-    static const int spw_choices[] = {1, 2, 4, 8};
-    static const int spk_choices[] = {2, 4, 6, 8, 16};
-    const int spw = round_slabs((slabs_h + 3) / 4, spw_choices, 4);
-    const int spk = round_slabs(slabs_i, spk_choices, 5);
-    if (spw < 0 || spk < 0) return MOE_EUNSUPPORTED;
-    const long n_pairs = (long)T * k;
-    const int slots = (int)(n_pairs < E ? n_pairs : E);
-    dim3 g1((unsigned)slots * (I / 16)), g2((unsigned)slots * ((H + 63) / 64));
-    int rc = fmt == MOE_W_MXFP4
-                 ? launch_gate_up<MOE_W_MXFP4>(spw, g1, s, x, sorted_pair, offsets, experts, k, H,
-                                               I, E, act)
-                 : launch_gate_up<MOE_W_BF16>(spw, g1, s, x, sorted_pair, offsets, experts, k, H, I,
-                                              E, act);
-    if (rc) return rc;
     if (fmt == MOE_W_MXFP4)
-        return y_is_fp32 ? launch_down<MOE_W_MXFP4, true>(spk, g2, s, act, sorted_pair, offsets,
-                                                          experts, H, I, E, y)
-                         : launch_down<MOE_W_MXFP4, false>(spk, g2, s, act, sorted_pair, offsets,
-                                                           experts, H, I, E, y);
-    return y_is_fp32 ? launch_down<MOE_W_BF16, true>(spk, g2, s, act, sorted_pair, offsets, experts,
-                                                     H, I, E, y)
-                     : launch_down<MOE_W_BF16, false>(spk, g2, s, act, sorted_pair, offsets,
-                                                      experts, H, I, E, y);
+        return ffn_decode_fmt<MOE_W_MXFP4>(x, sorted_pair, offsets, experts, T, k, H, I, E, y,
+                                           y_is_fp32, act, s);
+    return ffn_decode_fmt<MOE_W_BF16>(x, sorted_pair, offsets, experts, T, k, H, I, E, y,
+                                      y_is_fp32, act, s);
 }
 
 }  // namespace moe

@@ -6,7 +6,7 @@
 // of a chunk are ordered by a per-expert prefix over their counts in LDS.
 //   small path (T*k <= kSmallMax): one workgroup does histogram, scan and scatter;
 //   large path: per-chunk ranks + histograms, one column scan, one scatter.
-#include "common.hpp"
+#include "route_dev.hpp"
 
 namespace moe {
 
@@ -14,6 +14,7 @@ constexpr int kChunk = 1024;            // pairs per chunk (one per thread)
 constexpr int kWavesPerChunk = kChunk / kWave;
 constexpr int kMaxE = 512;
 constexpr int kSmallMax = 4 * kChunk;   // pairs handled by the one-workgroup kernel
+constexpr int kFusedMaxT = 16;          // tokens routed by the fused kernel (one per wavefront)
 
 // Multisplit rank of this lane's expert e within its wavefront. Returns the
 // number of lower lanes with the same e; *count = lanes with the same e.
@@ -86,10 +87,11 @@ __device__ void block_exclusive_scan(const int *in, int *out, int E, int *scratc
     __syncthreads();
 }
 
-__global__ __launch_bounds__(kChunk) void permute_small_kernel(
-    const int32_t *__restrict__ ids, int n, int E, int32_t *__restrict__ offsets,
-    int32_t *__restrict__ sorted_pair, int32_t *__restrict__ pair_row) {
-    extern __shared__ int lds[];
+// Whole permutation of n <= kSmallMax pairs by one 1024-thread workgroup.
+// `ids` may point to global memory or LDS; `lds` holds (19E + 33) ints.
+__device__ void permute_block(const int32_t *ids, int n, int E, int32_t *__restrict__ offsets,
+                              int32_t *__restrict__ sorted_pair, int32_t *__restrict__ pair_row,
+                              int *lds) {
     int *cnt = lds;                       // [E]
     int *base = cnt + E;                  // [E+1]
     int *tot = base + E + 1;              // [E]
@@ -124,6 +126,38 @@ __global__ __launch_bounds__(kChunk) void permute_small_kernel(
         for (int x = tid; x < kWavesPerChunk * E; x += kChunk) wcnt[x] = 0;
         __syncthreads();
     }
+}
+
+__device__ __host__ constexpr size_t permute_block_lds_ints(int E) { return (size_t)19 * E + 33; }
+
+__global__ __launch_bounds__(kChunk) void permute_small_kernel(
+    const int32_t *__restrict__ ids, int n, int E, int32_t *__restrict__ offsets,
+    int32_t *__restrict__ sorted_pair, int32_t *__restrict__ pair_row) {
+    extern __shared__ int lds[];
+    permute_block(ids, n, E, offsets, sorted_pair, pair_row, lds);
+}
+
+// Router + permutation in one workgroup (T <= kFusedMaxT): wavefront w routes
+// token w; the chosen ids stay in LDS for the permutation. (With more tokens a
+// single workgroup routes them serially and the two separate kernels win.)
+template <int VPL>
+__global__ __launch_bounds__(kChunk) void route_permute_kernel(
+    const uint16_t *__restrict__ x, const uint16_t *__restrict__ wg,
+    const float *__restrict__ logits_in, float *__restrict__ logits_out, int T, int H, int E,
+    int k, int renormalize, int32_t *__restrict__ topk_ids, float *__restrict__ topk_w,
+    int32_t *__restrict__ offsets, int32_t *__restrict__ sorted_pair,
+    int32_t *__restrict__ pair_row) {
+    extern __shared__ int lds[];
+    int *ids_lds = lds;                   // [T*k]
+    int *plds = lds + T * k;
+    const int w = threadIdx.x / kWave, lane = lane_id();
+    for (int t = w; t < T; t += kWavesPerChunk) {
+        const int id = route_token<VPL>(t, x, wg, logits_in, logits_out, H, E, k, renormalize,
+                                        topk_ids, topk_w);
+        if (lane < k) ids_lds[t * k + lane] = id;
+    }
+    __syncthreads();
+    permute_block(ids_lds, T * k, E, offsets, sorted_pair, pair_row, plds);
 }
 
 // Large path, pass 1: per-chunk ranks and histograms.
@@ -211,7 +245,7 @@ extern "C" int moe_permute(const int32_t *topk_ids, int T, int k, int E, int32_t
     }
     if (!topk_ids || !sorted_pair || !pair_row) return MOE_EINVAL;
     if (n <= kSmallMax) {
-        const size_t lds = (size_t)(E + (E + 1) + E + 32 + kWavesPerChunk * E) * sizeof(int);
+        const size_t lds = permute_block_lds_ints(E) * sizeof(int);
         MOE_TIMED(s, K_PERM_SMALL,
                   hipLaunchKernelGGL(permute_small_kernel, dim3(1), dim3(kChunk), lds, s, topk_ids,
                                      (int)n, E, offsets, sorted_pair, pair_row));
@@ -235,5 +269,36 @@ extern "C" int moe_permute(const int32_t *topk_ids, int T, int k, int E, int32_t
     MOE_TIMED(s, K_PERM_SCATTER,
               hipLaunchKernelGGL(permute_scatter_kernel, dim3(nb), dim3(kChunk), 0, s, topk_ids,
                                  (int)n, E, hist, lrank, sorted_pair, pair_row));
+    return check_launch();
+}
+
+extern "C" int moe_route_permute(const uint16_t *x_bf16, const uint16_t *wg_bf16,
+                                 const float *logits_in, float *logits_out, int T, int H, int E,
+                                 int k, int renormalize, int32_t *topk_ids, float *topk_w,
+                                 int32_t *offsets, int32_t *sorted_pair, int32_t *pair_row,
+                                 void *ws, size_t ws_bytes, void *stream) {
+    if (T < 0 || E < 1 || E > kMaxE || k < 1 || k > E || k > kWave || !offsets) return MOE_EINVAL;
+    if (!logits_in && T > 0 && (!x_bf16 || !wg_bf16 || H < 8 || H % 8)) return MOE_EINVAL;
+    const long n = (long)T * k;
+    if (T == 0 || T > kFusedMaxT || n > kSmallMax) {
+        int rc = moe_route(x_bf16, wg_bf16, logits_in, logits_out, T, H, E, k, renormalize,
+                           topk_ids, topk_w, stream);
+        if (rc) return rc;
+        return moe_permute(topk_ids, T, k, E, offsets, sorted_pair, pair_row, ws, ws_bytes,
+                           stream);
+    }
+    if (!topk_ids || !topk_w || !sorted_pair || !pair_row) return MOE_EINVAL;
+    hipStream_t s = (hipStream_t)stream;
+    const size_t lds = ((size_t)n + permute_block_lds_ints(E)) * sizeof(int);
+#define MOE_RP(VPL)                                                                            \
+    MOE_TIMED(s, K_ROUTE_PERMUTE,                                                              \
+              hipLaunchKernelGGL(route_permute_kernel<VPL>, dim3(1), dim3(kChunk), lds, s, x_bf16, \
+                                 wg_bf16, logits_in, logits_out, T, H, E, k, renormalize,        \
+                                 topk_ids, topk_w, offsets, sorted_pair, pair_row))
+    if (E <= 64) MOE_RP(1);
+    else if (E <= 128) MOE_RP(2);
+    else if (E <= 256) MOE_RP(4);
+    else MOE_RP(8);
+#undef MOE_RP
     return check_launch();
 }

@@ -28,25 +28,37 @@ def expert_table(base_ptr: int, n: int, layout, stride: int | None = None, devic
     return torch.from_numpy(np.ascontiguousarray(tab)).to(device)
 
 
+def pack_to_device(pool: np.ndarray, layout, device="cuda"):
+    """Upload expert blobs [n][nbytes] in the interchange layout and return a
+    device tensor of the same shape in the kernel layout (MXFP4 blocks packed
+    by the library; bf16 blobs are used as they are)."""
+    host = torch.from_numpy(np.ascontiguousarray(pool, dtype=np.uint8))
+    if host.dim() == 1:
+        host = host[None, :]
+    src = host.to(device)
+    if layout.fmt != "mxfp4":
+        return src
+    dst = torch.empty_like(src)
+    n, nb = src.shape
+    _lib.moe_pack_mxfp4(src, dst, n, nb, nb, layout.H, layout.I, layout)
+    torch.cuda.synchronize()
+    del src
+    return dst
+
+
 class DeviceExperts:
-    """Expert blobs resident in HBM (``copies`` identical replicas, so that a
-    benchmark can rotate between them and read every byte from HBM), plus one
-    moe_expert_w table per replica."""
+    """Expert blobs resident in HBM in the kernel layout (``copies`` identical
+    replicas, so that a benchmark can rotate between them and read every byte
+    from HBM), plus one moe_expert_w table per replica."""
 
     def __init__(self, pool: np.ndarray, layout, copies: int = 1, device="cuda"):
-        pool = np.ascontiguousarray(pool, dtype=np.uint8)
-        if pool.ndim == 1:
-            pool = pool[None, :]
         self.layout = layout
-        self.E = pool.shape[0]
-        host = torch.from_numpy(pool)
-        self.bufs = []
-        self.tables = []
-        for _ in range(copies):
-            b = torch.empty(pool.shape, dtype=torch.uint8, device=device)
-            b.copy_(host)
-            self.bufs.append(b)
-            self.tables.append(expert_table(b.data_ptr(), self.E, layout, device=device))
+        first = pack_to_device(pool, layout, device)
+        self.E = first.shape[0]
+        self.bufs = [first]
+        for _ in range(copies - 1):
+            self.bufs.append(first.clone())
+        self.tables = [expert_table(b.data_ptr(), self.E, layout, device=device) for b in self.bufs]
 
     @property
     def table(self):
@@ -93,6 +105,13 @@ class MoeLayer:
         _lib.moe_route(x, wg, logits, self.logits if write_logits else None, T, self.H, self.E,
                        self.k, renormalize, self.topk_ids, self.topk_w, stream)
 
+    def route_permute(self, T, x=None, wg=None, logits=None, renormalize=True, stream=None,
+                      write_logits=True):
+        _lib.moe_route_permute(x, wg, logits, self.logits if write_logits else None, T, self.H,
+                               self.E, self.k, renormalize, self.topk_ids, self.topk_w,
+                               self.offsets, self.sorted_pair, self.pair_row, self.ws_perm,
+                               self.ws_perm_bytes, stream)
+
     def permute(self, T, stream=None):
         _lib.moe_permute(self.topk_ids, T, self.k, self.E, self.offsets, self.sorted_pair,
                          self.pair_row, self.ws_perm, self.ws_perm_bytes, stream)
@@ -108,13 +127,20 @@ class MoeLayer:
 
     # whole layer -----------------------------------------------------------
     def forward(self, T, x, table, logits=None, wg=None, shared_table=None, renormalize=True,
-                stream=None, write_logits=False):
-        """route -> permute -> expert FFN (+ shared expert) -> combine; returns out[:T]."""
+                stream=None, write_logits=False, fused_routing=True):
+        """route -> permute -> expert FFN (+ shared expert) -> combine; returns out[:T].
+        fused_routing: route and permute with the one-call entry (one kernel for
+        small batches) instead of the two separate calls."""
         if T > self.T_max:
             raise ValueError("T exceeds the buffers' T_max")
-        self.route(T, x=x, wg=wg, logits=logits, renormalize=renormalize, stream=stream,
-                   write_logits=write_logits or logits is None)
-        self.permute(T, stream)
+        wl = write_logits or logits is None
+        if fused_routing:
+            self.route_permute(T, x=x, wg=wg, logits=logits, renormalize=renormalize,
+                               stream=stream, write_logits=wl)
+        else:
+            self.route(T, x=x, wg=wg, logits=logits, renormalize=renormalize, stream=stream,
+                       write_logits=wl)
+            self.permute(T, stream)
         self.ffn(T, x, table, stream)
         if shared_table is not None:
             if self._sh_T != T:

@@ -68,7 +68,8 @@ def workload(c, E=None):
     return _WL[key]
 
 
-def run_layer(w: Workload, T, x, logits=None, wg=None, y_fp32=False, renormalize=True):
+def run_layer(w: Workload, T, x, logits=None, wg=None, y_fp32=False, renormalize=True,
+              fused=True):
     from mixture_experts_gate_amd.layer import MoeLayer
     cfg = w.cfg
     L = MoeLayer(cfg.H, w.E, cfg.k, cfg.I, cfg.fmt, T, shared=bool(cfg.n_shared), y_fp32=y_fp32,
@@ -78,7 +79,7 @@ def run_layer(w: Workload, T, x, logits=None, wg=None, y_fp32=False, renormalize
                     logits=None if logits is None else to_dev(logits),
                     wg=None if wg is None else to_dev_bf16(wg),
                     shared_table=w.dev_shared.table if w.dev_shared else None,
-                    renormalize=renormalize, write_logits=True)
+                    renormalize=renormalize, write_logits=True, fused_routing=fused)
     torch.cuda.synchronize()
     return L, out
 
@@ -115,13 +116,14 @@ def check_permutation(L, T, E, ref_off, ref_sp, ref_pr):
 
 # ------------------------------------------------------------------ router --
 
-def test_route_gate_tiny_bitwise(lib, orc):
-    _announce("route: tiny config, bf16 gate on GPU")
+@pytest.mark.parametrize("fused", [True, False])
+def test_route_gate_tiny_bitwise(lib, orc, fused):
+    _announce(f"route: tiny config, bf16 gate on GPU (fused={fused})")
     w = workload(1)
     cfg = w.cfg
     x = synth.activations(cfg, 16)
     wg = synth.gate_weights(cfg)
-    L, _ = run_layer(w, 16, x, wg=wg)
+    L, _ = run_layer(w, 16, x, wg=wg, fused=fused)
     lg = orc.gate_logits_f32(x, wg)
     ids, wts, _ = orc.topk(lg, cfg.k)
     check_routing(L, 16, ids, wts, logits_ref=lg)
@@ -214,6 +216,28 @@ def test_permute_bitwise(lib, orc, T, E, k, kind):
     assert np.array_equal(pr_d.cpu().numpy(), pr)
 
 
+@pytest.mark.parametrize("T,E,k,kind", [c for c in PERM_CASES if c[0] * c[2] <= 4096])
+def test_route_permute_fused_bitwise(lib, orc, T, E, k, kind):
+    _announce(f"route+permute fused: T={T} E={E} k={k} {kind}")
+    lg = _perm_case(T, E, k, kind)
+    ids, wts, _ = orc.topk(lg, k)
+    off, sp, pr = orc.permute(ids, E)
+    ids_d = torch.full((T, k), -7, dtype=torch.int32, device=DEV)
+    w_d = torch.empty((T, k), dtype=torch.float32, device=DEV)
+    off_d = torch.full((E + 1,), -7, dtype=torch.int32, device=DEV)
+    sp_d = torch.full((T * k,), -7, dtype=torch.int32, device=DEV)
+    pr_d = torch.full((T * k,), -7, dtype=torch.int32, device=DEV)
+    ws = torch.empty(256, dtype=torch.uint8, device=DEV)
+    lib.moe_route_permute(None, None, to_dev(lg), None, T, 0, E, k, True, ids_d, w_d, off_d, sp_d,
+                          pr_d, ws, 256)
+    torch.cuda.synchronize()
+    assert np.array_equal(ids_d.cpu().numpy(), ids)
+    assert np.abs(w_d.cpu().numpy().astype(np.float64) - wts).max() <= W_ATOL
+    assert np.array_equal(off_d.cpu().numpy(), off)
+    assert np.array_equal(sp_d.cpu().numpy(), sp)
+    assert np.array_equal(pr_d.cpu().numpy(), pr)
+
+
 def test_permute_empty_batch(lib):
     off_d = torch.full((9,), -7, dtype=torch.int32, device=DEV)
     lib.moe_permute(None, 0, 2, 8, off_d, None, None, None, 0)
@@ -244,13 +268,13 @@ def test_layer_tiny_bf16(lib, orc):
     _check_layer_full(orc, w, 16, x, L, out, wg=wg)
 
 
-@pytest.mark.parametrize("T", [1, 8, 32, 64])
-def test_layer_decode_cfg2(lib, orc, T):
-    _announce(f"layer: decode config 2, T={T}")
+@pytest.mark.parametrize("T,fused", [(1, True), (8, True), (32, True), (64, True), (64, False)])
+def test_layer_decode_cfg2(lib, orc, T, fused):
+    _announce(f"layer: decode config 2, T={T} (fused routing={fused})")
     w = workload(2)
     x = synth.activations(w.cfg, T)
     lg = synth.router_logits(w.cfg, T)
-    L, out = run_layer(w, T, x, logits=lg)
+    L, out = run_layer(w, T, x, logits=lg, fused=fused)
     _check_layer_full(orc, w, T, x, L, out, logits=lg)
 
 
@@ -354,3 +378,33 @@ def test_layer_deterministic(lib):
     a = (o1.clone(), L1.y.clone(), L1.sorted_pair.clone())
     L2, o2 = run_layer(w, 64, x, logits=lg)
     assert torch.equal(a[0], o2) and torch.equal(a[1], L2.y) and torch.equal(a[2], L2.sorted_pair)
+
+
+def test_pack_mxfp4_layout(lib):
+    """The kernel layout as the header states it, built independently in numpy
+    from random interchange bytes."""
+    _announce("pack: interchange -> kernel MXFP4 layout")
+    H, I, n = 256, 384, 3
+    lay = synth.blob_layout(H, I, "mxfp4")
+    rng = np.random.default_rng(21)
+    src = rng.integers(0, 256, size=(n, lay.nbytes), dtype=np.uint8)
+
+    def tiled(codes, scales, R, K):
+        nslab = K // 128
+        c = codes.reshape(R // 16, 16, nslab, 4, 16)          # rb, row, s, cb, byte
+        oc = c.transpose(0, 2, 3, 1, 4).reshape(-1)              # rb, s, lane=(cb,row), byte
+        sc = scales.reshape(R // 16, 16, nslab, 4).transpose(0, 2, 3, 1).reshape(-1)
+        return oc, sc
+
+    want = np.empty_like(src)
+    for e in range(n):
+        b = src[e]
+        c13, s13 = tiled(b[lay.w13:lay.s13], b[lay.s13:lay.w2], 2 * I, H)
+        c2, s2 = tiled(b[lay.w2:lay.s2], b[lay.s2:lay.nbytes], H, I)
+        want[e, lay.w13:lay.s13], want[e, lay.s13:lay.w2] = c13, s13
+        want[e, lay.w2:lay.s2], want[e, lay.s2:lay.nbytes] = c2, s2
+    d_src = to_dev(src)
+    d_dst = torch.zeros_like(d_src)
+    lib.moe_pack_mxfp4(d_src, d_dst, n, lay.nbytes, lay.nbytes, H, I, lay)
+    torch.cuda.synchronize()
+    assert np.array_equal(d_dst.cpu().numpy(), want)
