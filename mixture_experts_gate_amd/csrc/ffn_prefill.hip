@@ -3,23 +3,34 @@
 //
 // In prefill almost every expert receives tokens (winzheng.com page, "Why Now
 // of All Times": large prefill batches route to nearly all experts in every
-// layer). Each expert's block is a grouped matrix product; this kernel tiles
-// it for bf16 32x32x16 MFMA, decoding the MXFP4 weights in registers.
+// layer). Each expert's block is a grouped matrix product, tiled here for the
+// block-scaled MFMA of gfx950 (v_mfma_scale_f32_16x16x128_f8f6f4), which
+// multiplies the MXFP4 weights as they are stored: E2M1 codes with one E8M0
+// scale per 32 elements, no decode in registers.
 //
-// Tile (one 512-thread workgroup: 8 wavefronts, two per SIMD, each 64 weight
-// rows x 64 token rows): 256 weight rows x 128 token rows of one expert over
-// the full contraction K, in 128-column slabs
-// that stream straight from global memory into a 3-stage LDS ring (two slabs
-// in flight while one is multiplied; one barrier per slab):
-//   - weights (MFMA operand A, kernel MXFP4 layout): the tile's 16 row blocks
-//     (16 rows x 128 columns = one 1 KB block each) are copied as they are;
-//     each wavefront decodes its 4 blocks in registers right before use;
-//   - tokens (operand B): the tile's 128 rows (gathered x rows in stage 1,
-//     activation rows in stage 2) with the 16-byte column chunks XOR-swizzled
-//     by row so the fragment reads hit distinct banks.
-// (On gfx950 the 32x32x16 bf16 MFMA issues at twice the 16x16x32 rate.)
-// Stage 1 tile rows: 128 gate rows and the matching 128 up rows (32 + 32 per
-// wavefront), so SwiGLU happens in registers. Stage 2 tile rows: 256 W2 rows.
+// The token operand is carried as two FP8 (E4M3) terms with one E8M0 scale
+// per 32 elements: hi = fp8(x / 2^e), lo = fp8(32 (x / 2^e - hi)) with scale
+// 2^(e-5), e = floor(log2 max|x|) - 7 over the 32-element block. hi holds x to
+// 2^-4 relative, lo the remainder to another 2^-4, so hi + lo is within
+// 2^-8 |x| of x (bf16 keeps 2^-9); both terms run through the FP8 x FP4 matrix
+// pipe, whose rate is twice bf16's, so the pair costs what one bf16 product
+// would, and the weights need no conversion at all. x is split once per token
+// by a row pass; the activation a = silu(g) * u is split by the gate/up
+// kernel's epilogue as it is produced.
+//
+// Tile (one 512-thread workgroup: 8 wavefronts, two per SIMD, each 32 tokens x
+// 128 weight rows): 128 tokens x 256 weight rows of one expert over the full
+// contraction K, in 128-column slabs copied straight from global memory into a
+// 3-stage LDS ring (two slabs in flight while one is multiplied; one barrier
+// per slab). Every operand lands in LDS in the order the matrix core reads it,
+// so each fragment read is one contiguous 16-byte-per-lane LDS read:
+//   - weights (operand A, kernel MXFP4 layout): 16 row blocks of 16 rows x 128
+//     columns (1 KB codes + 64 B scales each), copied as they are;
+//   - tokens (operand B): per 16-token block, term and 64-column half, lane l
+//     holds token l%16, columns 64 half + 16(l/16) .. +15;
+//   - token scales: lane l of a token block holds token l%16's four scales.
+// Stage 1 rows: 128 gate rows and the matching 128 up rows (64 + 64 per
+// wavefront), so SwiGLU happens in registers. Stage 2 rows: 256 W2 rows.
 // Tiles are numbered per expert (token tile major, weight tile minor) and the
 // numbering is split into 8 contiguous ranges, one per XCD (workgroup b runs
 // on XCD b % 8), so an expert's tiles share one XCD's L2.
@@ -29,22 +40,110 @@
 
 namespace moe {
 
-constexpr int kPreTok = 128;      // token rows per tile
+constexpr int kPreTok = 128;      // tokens per tile
 constexpr int kPreThreads = 512;
-constexpr int kSlabBytes = 256;   // one token row's slab: 128 bf16
+constexpr int kLoShift = 5;       // lo term scale = hi scale / 2^5
+
+typedef __attribute__((ext_vector_type(8))) int i32x8;
+typedef __attribute__((ext_vector_type(4))) int i32x4;
 
 __device__ __forceinline__ float silu_mul_p(float g, float u) {
     return g / (1.0f + __expf(-g)) * u;
 }
 
+// ---------------------------------------------------------- two-term FP8 --
+
+// Block exponent e (as the hi scale's E8M0 byte, e + 127) for a block whose
+// largest magnitude is amax: e = floor(log2 amax) - 7 puts the block maximum
+// in [128, 256), inside E4M3's range (448). Clamped to [5, 254] so the lo
+// scale byte (hi - 5) stays a valid E8M0 value; blocks below 2^-115 lose
+// relative precision, which no bf16 activation of interest reaches.
+__device__ __forceinline__ int split_scale_byte(float amax) {
+    const int eb = (int)((__float_as_uint(amax) >> 23) & 0xFFu);   // biased exponent
+    int b = eb - 7;                                                 // (eb - 127 - 7) + 127
+    b = b < kLoShift ? kLoShift : b;
+    return b > 254 ? 254 : b;
+}
+
+// 1 / 2^e for hi scale byte b (2^(127 - b), exact).
+__device__ __forceinline__ float split_inv_scale(int b) {
+    return __uint_as_float((uint32_t)(254 - b) << 23);
+}
+
+// Two values (already divided by the hi scale) -> two hi and two lo E4M3
+// bytes, packed in the low 16 bits of hi / lo.
+__device__ __forceinline__ void split_pair(float v0, float v1, uint32_t &hi, uint32_t &lo) {
+    const int h = __builtin_amdgcn_cvt_pk_fp8_f32(v0, v1, 0, false);
+    const float r0 = v0 - __builtin_amdgcn_cvt_f32_fp8(h, 0);     // exact (Sterbenz)
+    const float r1 = v1 - __builtin_amdgcn_cvt_f32_fp8(h, 1);
+    const int l = __builtin_amdgcn_cvt_pk_fp8_f32(r0 * 32.0f, r1 * 32.0f, 0, false);
+    hi = (uint32_t)h & 0xFFFFu;
+    lo = (uint32_t)l & 0xFFFFu;
+}
+
+// Four values -> four hi and four lo bytes.
+__device__ __forceinline__ void split_quad(const float (&v)[4], float inv, uint32_t &hi,
+                                           uint32_t &lo) {
+    uint32_t h0, l0, h1, l1;
+    split_pair(v[0] * inv, v[1] * inv, h0, l0);
+    split_pair(v[2] * inv, v[3] * inv, h1, l1);
+    hi = h0 | (h1 << 16);
+    lo = l0 | (l1 << 16);
+}
+
+// Row split of bf16 rows [rows][K] into hi [rows][K], lo [rows][K] and hi
+// scale bytes [rows][K/32]. One thread per 32-element block.
+__global__ __launch_bounds__(256) void split_rows_kernel(const uint16_t *__restrict__ src,
+                                                         long nblk, uint8_t *__restrict__ hi,
+                                                         uint8_t *__restrict__ lo,
+                                                         uint8_t *__restrict__ sc) {
+    const long b = (long)blockIdx.x * 256 + threadIdx.x;
+    if (b >= nblk) return;
+    u32x4 q[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) q[j] = load_nt16(src + b * 32 + 8 * j);
+    float amax = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+            amax = fmaxf(amax, fmaxf(fabsf(bf16_bits_to_f32(q[j][c] & 0xFFFFu)),
+                                     fabsf(bf16_bits_to_f32(q[j][c] >> 16))));
+    const int sb = split_scale_byte(amax);
+    const float inv = split_inv_scale(sb);
+    u32x4 oh[2], ol[2];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int c = 0; c < 4; c += 2) {
+            const float v[4] = {bf16_bits_to_f32(q[j][c] & 0xFFFFu), bf16_bits_to_f32(q[j][c] >> 16),
+                                bf16_bits_to_f32(q[j][c + 1] & 0xFFFFu),
+                                bf16_bits_to_f32(q[j][c + 1] >> 16)};
+            uint32_t h, l;
+            split_quad(v, inv, h, l);
+            oh[j >> 1][2 * (j & 1) + (c >> 1)] = h;
+            ol[j >> 1][2 * (j & 1) + (c >> 1)] = l;
+        }
+    u32x4 *ph = reinterpret_cast<u32x4 *>(hi + b * 32);
+    u32x4 *pl = reinterpret_cast<u32x4 *>(lo + b * 32);
+    ph[0] = oh[0];
+    ph[1] = oh[1];
+    pl[0] = ol[0];
+    pl[1] = ol[1];
+    sc[b] = (uint8_t)sb;
+}
+
+// ------------------------------------------------------------ GEMM tiles --
+
 struct PreArgs {
-    const uint16_t *src;          // token operand rows: x [T][H] or act [T*k][I]
+    const uint8_t *bhi, *blo, *bsc;   // token operand: hi/lo rows [.][K], scales [.][K/32]
     const int32_t *sorted_pair;
     const int32_t *offsets;
     const moe_expert_w *experts;
-    void *out;                    // act (stage 1) or y (stage 2)
+    void *out;                        // stage 2: y
+    uint8_t *ohi, *olo, *osc;         // stage 1: activation hi/lo rows [n][I], scales [n][I/32]
     int k, K, H, I, E;
-    int ntiles_w;                 // weight tiles per expert
+    int ntiles_w;                     // weight tiles per expert
 };
 
 // Expert, token-tile and weight-tile of tile q (all lanes get the same) and
@@ -82,21 +181,31 @@ __device__ __forceinline__ bool pre_find_tile(const PreArgs &A, long q, int &e, 
     return e >= 0;
 }
 
-// LDS of one slab stage: the tile's 128 token rows (swizzled 16-byte chunks)
-// and its 16 weight blocks (1 KB codes + 64 B scales each).
+// LDS of one slab stage (50176 bytes).
+//   tok   : [term hi/lo][16-token block] 16 rows x 128 bytes; the 16-byte chunk c
+//           of row r sits at position c ^ ((r / 2) % 8), so the 16 lanes that
+//           read one chunk of 16 rows hit 16 different 16-byte bank groups;
+//   tsc   : the 128 tokens' 4 scale bytes of this slab;
+//   wcode / wscale: the tile's 16 weight blocks, kernel layout.
 struct PreStage {
-    uint8_t tok[kPreTok * kSlabBytes];
+    uint8_t tok[2][8][2048];
     uint8_t wcode[16][1024];
+    uint8_t tsc[kPreTok][4];
     uint8_t wscale[16][64];
 };
-constexpr int kPreStages = 3;                  // computing s, landing s+1 and s+2
+constexpr int kPreStages = 3;     // computing s, landing s+1 and s+2
+
+__device__ __forceinline__ int tok_swz(int r) { return (r >> 1) & 7; }
 
 #define MOE_LDS __attribute__((address_space(3)))
 
-// Direct global -> LDS copies: lane l's 16 bytes land at dst + 16 l (dst is
-// wavefront-uniform).
+// Direct global -> LDS copies: lane l's 16 (4) bytes land at dst + 16 l (4 l);
+// dst is wavefront-uniform.
 __device__ __forceinline__ void lds_dma16(const void *src, void *dst) {
     __builtin_amdgcn_global_load_lds((const MOE_GLOBAL void *)src, (MOE_LDS void *)dst, 16, 0, 0);
+}
+__device__ __forceinline__ void lds_dma4(const void *src, void *dst) {
+    __builtin_amdgcn_global_load_lds((const MOE_GLOBAL void *)src, (MOE_LDS void *)dst, 4, 0, 0);
 }
 
 // Waits until at most n of this wavefront's vector-memory operations are
@@ -107,98 +216,176 @@ __device__ __forceinline__ void wait_vm() {
     __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
-// This wavefront's copies of slab s into stage st (8 wavefronts):
-//  tokens: copy u (u < 4) covers tile rows 16w + 4u .. +3 (lane l: row + l/16,
-//          LDS slot l%16, which holds global 16-byte chunk slot ^ (row & 15));
-//  codes : tile-local blocks 2w, 2w+1 (1 KB each, copied as they are);
-//  scales: wavefront 7 copies all 16 blocks' 64-byte scale rows (lane l:
-//          bytes 16(l%4) .. +15 of block l/4).
-// Returns the number of copies issued (6, or 7 on wavefront 7).
-__device__ __forceinline__ void pre_issue(PreStage &st, int s, int w, int lane,
-                                          const uint16_t *const (&trow)[4], const uint8_t *wcodes,
-                                          const uint8_t *wscales, const long (&rbw)[2],
-                                          long rbs, int nslab) {
-    const int r_lane = lane >> 4, slot = lane & 15;
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-        const int r = 16 * w + 4 * u + r_lane;
-        const int c16 = slot ^ (r & 15);
-        lds_dma16(trow[u] + s * 128 + c16 * 8, &st.tok[(16 * w + 4 * u) * kSlabBytes]);
-    }
-#pragma unroll
-    for (int u = 0; u < 2; ++u)
-        lds_dma16(wcodes + ((size_t)rbw[u] * nslab + s) * 1024 + lane * 16,
-                  &st.wcode[2 * w + u][0]);
-    if (w == 7)
-        lds_dma16(wscales + ((size_t)rbs * nslab + s) * 64 + (lane & 3) * 16, &st.wscale[0][0]);
-}
-
-// Fragments of half a slab (4 MFMA steps of 16 columns) for this
-// wavefront's 64 weight rows (two 32-row groups = tile-local blocks 4wn ..
-// 4wn+3) and 64 tokens (two 32-token groups). Step k reads columns 16k ..
-// 16k+15; lane l supplies 8 of them (8(l/32) ..): for the weights, row l%32 of
-// the group sits in block l/16 as lane-chunk (l%16) + 16(k/2), bytes
-// 8(k%2) + 4(l/32) .. +3; for the tokens, row l%32 of the token group, 16-byte
-// chunk 2k + l/32 (swizzled).
-struct PreFrag {
-    u32x4 tb[4][2];
-    uint32_t wq[4][2];
-    uint32_t sb[2];         // scale bytes of the half's two 32-column blocks, per weight group
+// Per-lane copy sources of one tile (slab 0; slab s adds s * 128 bytes to a
+// token row, s * 4 to a scale row, s * 1024 / s * 64 to a weight block).
+struct PreSrc {
+    const uint8_t *thi[2], *tlo[2];   // token block w, rows 8u + lane/8: the lane's 16-byte chunk
+    const uint8_t *tsc;               // wavefronts 5, 6: scale row of token 64(w-5) + lane
+    const uint8_t *wc[2];             // blocks 2w, 2w+1: codes + 16 lane
+    const uint8_t *ws;                // wavefront 7: scales of block lane/4 + 16 (lane%4)
 };
 
-__device__ __forceinline__ void pre_read(const PreStage &st, PreFrag &f, int half, int wm, int wn,
-                                         int lane) {
-    const int r32 = lane & 31, h = lane >> 5;
+// Copies per slab issued by wavefront w (what its vmcnt waits count).
+__device__ __forceinline__ int pre_copies(int w) { return w >= 5 ? 7 : 6; }
+
+// This wavefront's copies of slab s into stage st (8 wavefronts): its token
+// block's two terms (8 rows x 128 bytes per copy), weight blocks 2w and 2w+1,
+// on wavefronts 5 and 6 half of the token scales, on wavefront 7 the 16 weight
+// blocks' scale rows.
+__device__ __forceinline__ void pre_issue(PreStage &st, int s, int w, const PreSrc &p) {
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-        const int k = 4 * half + kk;
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-            const int r = wm * 64 + t * 32 + r32;
-            const int slot = (2 * k + h) ^ (r & 15);
-            f.tb[kk][t] = *reinterpret_cast<const u32x4 *>(&st.tok[r * kSlabBytes + slot * 16]);
-        }
-#pragma unroll
-        for (int gq = 0; gq < 2; ++gq) {
-            const int wb = 4 * wn + 2 * gq + (r32 >> 4);
-            f.wq[kk][gq] = *reinterpret_cast<const uint32_t *>(
-                &st.wcode[wb][((r32 & 15) + 16 * (k >> 1)) * 16 + 8 * (k & 1) + 4 * h]);
-        }
+    for (int u = 0; u < 2; ++u) {
+        lds_dma16(p.thi[u] + s * 128, &st.tok[0][w][u * 1024]);
+        lds_dma16(p.tlo[u] + s * 128, &st.tok[1][w][u * 1024]);
     }
 #pragma unroll
-    for (int gq = 0; gq < 2; ++gq) {
-        const int wb = 4 * wn + 2 * gq + (r32 >> 4);
-        // this half's 32-column blocks are 2 half and 2 half + 1
-        f.sb[gq] = (uint32_t)st.wscale[wb][(r32 & 15) + 32 * half] |
-                   ((uint32_t)st.wscale[wb][(r32 & 15) + 32 * half + 16] << 8);
-    }
+    for (int u = 0; u < 2; ++u) lds_dma16(p.wc[u] + (size_t)s * 1024, &st.wcode[2 * w + u][0]);
+    if (w == 5 || w == 6) lds_dma4(p.tsc + s * 4, &st.tsc[64 * (w - 5)][0]);
+    if (w == 7) lds_dma16(p.ws + (size_t)s * 64, &st.wscale[0][0]);
 }
 
-__device__ __forceinline__ void pre_math(const PreFrag &f, f32x16 (&acc)[2][2]) {
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-#pragma unroll
-        for (int gq = 0; gq < 2; ++gq) {
-            const float sc = e8m0_to_f32((f.sb[gq] >> (8 * (kk >> 1))) & 0xFFu);
-            const bf16x8 aw = dequant8_fp4(f.wq[kk][gq], sc);
-#pragma unroll
-            for (int t = 0; t < 2; ++t)
-                acc[gq][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aw, as_bf16x8(f.tb[kk][t]),
-                                                                    acc[gq][t], 0, 0, 0);
-        }
-    }
-}
+// One slab's operands for one wavefront: its 8 weight blocks and its two
+// 16-token blocks (both terms, both halves), with the lane's scale bytes.
+struct PreFrag {
+    u32x4 w[8];
+    uint32_t ws[8];
+    i32x8 t[2][2];                // [token block][term]; elements 0-3 / 4-7 = column half 0 / 1
+    uint32_t ts[2];
+};
 
-// 16-row weight block (within the stage's matrix) of tile-local block wb of
-// weight tile nt (wb = 4q + b, q = the wavefront's weight quarter): stage 1 ->
-// q's two gate blocks for b < 2 and the matching up blocks for b >= 2 (act
-// columns nt*128 + 32q .. +31); stage 2 -> 16 consecutive W2 blocks.
+// LDS block (of the stage's 16) holding this wavefront's weight block b:
+// stage 1 -> gate blocks 4wn .. 4wn+3 then the matching up blocks 8 + 4wn ..;
+// stage 2 -> blocks 8wn .. 8wn+7.
 template <int STAGE>
-__device__ __forceinline__ long pre_block(const PreArgs &A, int nt, int wb) {
-    const int qq = wb >> 2, b = wb & 3;
-    if (STAGE == 1)
-        return b < 2 ? (long)nt * 8 + qq * 2 + b : (long)A.I / 16 + nt * 8 + qq * 2 + (b - 2);
-    return (long)nt * 16 + wb;
+__device__ __forceinline__ int lds_block(int wn, int b) {
+    if (STAGE == 1) return b < 4 ? 4 * wn + b : 8 + 4 * wn + (b - 4);
+    return 8 * wn + b;
+}
+
+// Token fragment positions of this lane (row lane%16 of a block, chunks
+// lane/16 and lane/16 + 4 of the row: columns 16(lane/16) and 64 + 16(lane/16)).
+struct TokPos {
+    int a0, a1;
+    __device__ __forceinline__ explicit TokPos(int lane) {
+        const int r = lane & 15, c0 = lane >> 4;
+        a0 = 128 * r + 16 * (c0 ^ tok_swz(r));
+        a1 = 128 * r + 16 * ((c0 + 4) ^ tok_swz(r));
+    }
+};
+
+template <int STAGE>
+__device__ __forceinline__ void pre_read(const PreStage &st, PreFrag &f, int wm, int wn, int lane,
+                                         const TokPos &tp) {
+#pragma unroll
+    for (int b = 0; b < 8; ++b) {
+        const int lb = lds_block<STAGE>(wn, b);
+        f.w[b] = *reinterpret_cast<const u32x4 *>(&st.wcode[lb][16 * lane]);
+        f.ws[b] = st.wscale[lb][lane];
+    }
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb) {
+#pragma unroll
+        for (int term = 0; term < 2; ++term) {
+            const uint8_t *blk = st.tok[term][2 * wm + tb];
+            f.t[tb][term].lo = *reinterpret_cast<const i32x4 *>(blk + tp.a0);
+            f.t[tb][term].hi = *reinterpret_cast<const i32x4 *>(blk + tp.a1);
+        }
+        f.ts[tb] = st.tsc[16 * (2 * wm + tb) + (lane & 15)][lane >> 4];
+    }
+}
+
+__device__ __forceinline__ void pre_math(const PreFrag &f, f32x4 (&acc)[8][2]) {
+#pragma unroll
+    for (int term = 0; term < 2; ++term)
+#pragma unroll
+        for (int b = 0; b < 8; ++b) {
+            // E2M1 operand: only the low four dwords are read
+            const i32x4 w4 = __builtin_bit_cast(i32x4, f.w[b]);
+            const i32x8 a = __builtin_shufflevector(w4, w4, 0, 1, 2, 3, -1, -1, -1, -1);
+#pragma unroll
+            for (int tb = 0; tb < 2; ++tb) {
+                const int tsc = (int)f.ts[tb] - (term ? kLoShift : 0);
+                // A: E2M1 (format 4), B: E4M3 (format 0)
+                acc[b][tb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                    a, f.t[tb][term], acc[b][tb], 4, 0, 0, (int)f.ws[b], 0, tsc);
+            }
+        }
+}
+
+// 16-row weight block (within the stage's matrix) copied into LDS block lb of
+// weight tile nt: stage 1 -> gate blocks nt*8 + lb (lb < 8), up blocks I/16 +
+// nt*8 + lb - 8; stage 2 -> W2 blocks nt*16 + lb.
+template <int STAGE>
+__device__ __forceinline__ long pre_block(const PreArgs &A, int nt, int lb) {
+    if (STAGE == 1) return lb < 8 ? (long)nt * 8 + lb : (long)A.I / 16 + nt * 8 + (lb - 8);
+    return (long)nt * 16 + lb;
+}
+
+// Barrier without a memory fence (a fenced __syncthreads would also wait for
+// the copies still in flight); the empty asm statements keep the compiler from
+// moving LDS accesses across it.
+__device__ __forceinline__ void bare_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// Ping-pong schedule. The two wavefronts of a SIMD belong to different
+// groups (waves 0-3 and 4-7) that run half a period apart: while one issues
+// a slab's 32 MFMAs (C), the other issues its copies and LDS reads (M), so
+// the matrix core always has work. With half-periods h = 0, 1, ..:
+//   group 0: M(j) at h = 2j, C(j) at h = 2j + 1
+//   group 1: M(j) at h = 2j + 1, C(j) at h = 2j + 2
+// M(j) reads slab j into registers and, for j >= 1, issues this wavefront's
+// copies of slab j + 2 into the stage slab j - 1 came from (both groups have
+// read slab j - 1 by then). A barrier ends every half-period up to 2n - 2;
+// before the one ending h = 2j + 1 every wavefront has seen its copies of
+// slab j + 1 land (group 0 reads it next) and group 1 has its reads of slab j
+// back (the stage is refilled after it).
+template <int STAGE, int GRP>
+__device__ __forceinline__ void pre_mainloop(PreStage (&lds)[kPreStages], f32x4 (&acc)[8][2],
+                                             int n, int wv, int wm, int wn, int lane,
+                                             const PreSrc &src) {
+    PreFrag F;
+    const TokPos tp(lane);
+    auto wait_next = [&](int j) {            // end of h = 2j + 1: slab j + 1 landed
+        if (j + 2 < n) {
+            if (pre_copies(wv) == 7) wait_vm<7>();
+            else wait_vm<6>();
+        } else {
+            wait_vm<0>();
+        }
+    };
+    if (GRP == 0) pre_read<STAGE>(lds[0], F, wm, wn, lane, tp);    // M(0)
+    bare_barrier();                                                  // end of h = 0
+    int st = 0;                               // stage of slab j
+    for (int j = 0; j < n; ++j) {
+        const int st1 = st == kPreStages - 1 ? 0 : st + 1;
+        const int st2 = st1 == kPreStages - 1 ? 0 : st1 + 1;       // stage of slab j + 2
+        if (GRP == 0) {
+            pre_math(F, acc);                                        // C(j), h = 2j + 1
+            if (j + 1 < n) {
+                wait_next(j);
+                bare_barrier();
+                // M(j + 1), h = 2j + 2: slab j + 3 goes where slab j was
+                if (j + 3 < n) pre_issue(lds[st], j + 3, wv, src);
+                pre_read<STAGE>(lds[st1], F, wm, wn, lane, tp);
+                bare_barrier();
+            }
+        } else {
+            // M(j), h = 2j + 1
+            if (j >= 1 && j + 2 < n) pre_issue(lds[st2], j + 2, wv, src);
+            pre_read<STAGE>(lds[st], F, wm, wn, lane, tp);
+            __builtin_amdgcn_s_waitcnt(0xC07F);                      // lgkmcnt(0)
+            if (j + 1 < n) {
+                wait_next(j);
+                bare_barrier();
+            }
+            pre_math(F, acc);                                        // C(j), h = 2j + 2
+            if (j + 1 < n) bare_barrier();
+        }
+        st = st1;
+    }
 }
 
 template <int STAGE, bool YF32>
@@ -206,7 +393,7 @@ __global__ __launch_bounds__(kPreThreads) void ffn_pre_kernel(PreArgs A) {
     __shared__ __attribute__((aligned(16))) PreStage lds[kPreStages];
     const int tid = threadIdx.x, lane = lane_id();
     const int wv = __builtin_amdgcn_readfirstlane(tid / kWave);
-    const int wm = wv >> 2, wn = wv & 3;     // token half, weight quarter
+    const int wm = wv & 3, wn = wv >> 2;     // token quarter (32 tokens), weight half
 
     // total tiles, then this workgroup's tile (XCD-aware numbering)
     int e, mt, nt;
@@ -225,107 +412,112 @@ __global__ __launch_bounds__(kPreThreads) void ffn_pre_kernel(PreArgs A) {
     const uint8_t *wscales = STAGE == 1 ? W.s13 : W.s2;
     const int nslab = A.K / 128;
 
-    // blocks whose codes this wavefront copies (tile-local 2wv, 2wv+1) and the
-    // block whose scales this lane copies on wavefront 7 (tile-local lane/4)
-    long rbw[2];
+    PreSrc src;
+    {
+        auto token_row = [&](int r) -> long {   // operand row of tile row r
+            r = r < n_e ? r : n_e - 1;             // rows past the expert's end repeat its last row
+            return STAGE == 1 ? (long)(A.sorted_pair[row0 + r] / A.k) : (long)(row0 + r);
+        };
 #pragma unroll
-    for (int u = 0; u < 2; ++u) rbw[u] = pre_block<STAGE>(A, nt, 2 * wv + u);
-    const long rbs = pre_block<STAGE>(A, nt, lane >> 2);
-    // token rows this lane copies: 16 wv + 4u + lane/16 (u < 4)
-    const uint16_t *trow[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-        int r = tok0 + 16 * wv + 4 * u + (lane >> 4);
-        r = r < n_e ? r : n_e - 1;              // rows past the expert's end repeat its last row
-        if (STAGE == 1) trow[u] = A.src + (size_t)(A.sorted_pair[row0 + r] / A.k) * A.K;
-        else trow[u] = A.src + (size_t)(row0 + r) * A.K;
-    }
-
-    f32x16 acc[2][2];
-#pragma unroll
-    for (int gq = 0; gq < 2; ++gq)
-#pragma unroll
-        for (int t = 0; t < 2; ++t)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) acc[gq][t][i] = 0.0f;
-
-    // Software pipeline over half slabs: fragments of the next half are read
-    // from LDS while the current half is multiplied from registers. One
-    // barrier per slab, between its two halves: before it every wavefront has
-    // slab s in registers and has seen slab s + 1 land; after it slab s + 1 is
-    // visible to all and slab s's stage takes the copy of slab s + 3. (A bare
-    // barrier: a fenced __syncthreads would also wait for the copies still in
-    // flight.)
-    const int nw = wv == 7 ? 7 : 6;          // copies per slab issued by this wavefront
-    auto wait_copies = [&](int later) {       // wait until only `later` slabs' copies remain
-        const int n = later * nw;
-        if (n == 0) wait_vm<0>();
-        else if (n == 6) wait_vm<6>();
-        else if (n == 7) wait_vm<7>();
-        else if (n == 12) wait_vm<12>();
-        else wait_vm<14>();
-    };
-    for (int i = 0; i < kPreStages && i < nslab; ++i)
-        pre_issue(lds[i], i, wv, lane, trow, wcodes, wscales, rbw, rbs, nslab);
-    wait_copies(nslab - 1 < kPreStages - 1 ? nslab - 1 : kPreStages - 1);
-    __builtin_amdgcn_s_barrier();
-    PreFrag fa, fb;
-    pre_read(lds[0], fa, 0, wm, wn, lane);
-    for (int s = 0; s < nslab; ++s) {
-        pre_read(lds[s % kPreStages], fb, 1, wm, wn, lane);
-        pre_math(fa, acc);
-        if (s + 1 < nslab) {
-            __builtin_amdgcn_s_waitcnt(0xC07F);      // lgkmcnt(0): slab s fully in registers
-            wait_copies(s + 2 < nslab ? 1 : 0);      // slab s + 1 landed
-            __builtin_amdgcn_s_barrier();
-            if (s + 3 < nslab)
-                pre_issue(lds[s % kPreStages], s + 3, wv, lane, trow, wcodes, wscales, rbw, rbs,
-                          nslab);
-            pre_read(lds[(s + 1) % kPreStages], fa, 0, wm, wn, lane);
+        for (int u = 0; u < 2; ++u) {
+            // token block wv, row 8u + lane/8; lane position lane%8 holds chunk pos ^ swizzle
+            const int rb = 8 * u + (lane >> 3);
+            const long row = token_row(tok0 + 16 * wv + rb);
+            const int chunk = (lane & 7) ^ tok_swz(rb);
+            src.thi[u] = A.bhi + row * A.K + 16 * chunk;
+            src.tlo[u] = A.blo + row * A.K + 16 * chunk;
         }
-        pre_math(fb, acc);
+        src.tsc = A.bsc + token_row(tok0 + 64 * (wv == 6 ? 1 : 0) + lane) * (A.K / 32);
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+            src.wc[u] = wcodes + (size_t)pre_block<STAGE>(A, nt, 2 * wv + u) * nslab * 1024 +
+                        16 * lane;
+        src.ws = wscales + (size_t)pre_block<STAGE>(A, nt, lane >> 2) * nslab * 64 +
+                 16 * (lane & 3);
     }
 
-    // epilogue: for token group t the lane holds token 64wm + 32t + lane%32 and,
-    // in weight group gq, rows 8(i/4) + 4(lane/32) + i%4 (i < 16) of the group
-    const int r32 = lane & 31, h = lane >> 5;
+    f32x4 acc[8][2];
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-        const int r = tok0 + wm * 64 + t * 32 + r32;
-        if (r >= n_e) continue;
-        if (STAGE == 1) {
-            // group 0 = 32 gate rows, group 1 = the matching 32 up rows
-            uint16_t *act = reinterpret_cast<uint16_t *>(A.out) + (size_t)(row0 + r) * A.I +
-                            nt * 128 + wn * 32 + 4 * h;
+    for (int b = 0; b < 8; ++b)
 #pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) {
-                const int i0 = 4 * q4;
-                uint2 pk;
-                pk.x = pack_bf16x2(silu_mul_p(acc[0][t][i0], acc[1][t][i0]),
-                                   silu_mul_p(acc[0][t][i0 + 1], acc[1][t][i0 + 1]));
-                pk.y = pack_bf16x2(silu_mul_p(acc[0][t][i0 + 2], acc[1][t][i0 + 2]),
-                                   silu_mul_p(acc[0][t][i0 + 3], acc[1][t][i0 + 3]));
-                *reinterpret_cast<uint2 *>(act + 8 * q4) = pk;
-            }
-        } else {
-            const size_t prow = (size_t)A.sorted_pair[row0 + r] * A.H + nt * 256 + wn * 64 + 4 * h;
+        for (int tb = 0; tb < 2; ++tb) acc[b][tb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+    for (int i = 0; i < kPreStages && i < nslab; ++i) pre_issue(lds[i], i, wv, src);
+    // slab 0 landed: the later prologue slabs' copies may remain
+    const int later = nslab - 1 < kPreStages - 1 ? nslab - 1 : kPreStages - 1;
+    const int n_later = later * pre_copies(wv);
+    if (n_later == 0) wait_vm<0>();
+    else if (n_later == 6) wait_vm<6>();
+    else if (n_later == 7) wait_vm<7>();
+    else if (n_later == 12) wait_vm<12>();
+    else wait_vm<14>();
+    bare_barrier();
+
+    if (wv < 4) pre_mainloop<STAGE, 0>(lds, acc, nslab, wv, wm, wn, lane, src);
+    else pre_mainloop<STAGE, 1>(lds, acc, nslab, wv, wm, wn, lane, src);
+
+    // epilogue: for token block tb the lane holds token 32wm + 16tb + lane%16 and,
+    // in weight block b, rows 4(lane/16) + i (i < 4) of the block
+    const int g4 = lane >> 4;
+    if (STAGE == 1) {
+        // blocks b < 4: gate rows, b + 4: the matching up rows -> activation
+        // columns nt*128 + 64wn + 16b + 4g4 + i; 32-column scale blocks j = b/2
+        const int I = A.I;
 #pragma unroll
-            for (int gq = 0; gq < 2; ++gq)
+        for (int tb = 0; tb < 2; ++tb) {
+            const int r = tok0 + 32 * wm + 16 * tb + (lane & 15);
+            const bool ok = r < n_e;
+            const size_t orow = (size_t)(row0 + (ok ? r : 0));
 #pragma unroll
-                for (int q4 = 0; q4 < 4; ++q4) {
-                    const int i0 = 4 * q4;
-                    const size_t off = prow + gq * 32 + 8 * q4;
-                    if (YF32) {
-                        f32x4 v = {acc[gq][t][i0], acc[gq][t][i0 + 1], acc[gq][t][i0 + 2],
-                                   acc[gq][t][i0 + 3]};
-                        *reinterpret_cast<f32x4 *>(reinterpret_cast<float *>(A.out) + off) = v;
-                    } else {
-                        uint2 pk;
-                        pk.x = pack_bf16x2(acc[gq][t][i0], acc[gq][t][i0 + 1]);
-                        pk.y = pack_bf16x2(acc[gq][t][i0 + 2], acc[gq][t][i0 + 3]);
-                        *reinterpret_cast<uint2 *>(reinterpret_cast<uint16_t *>(A.out) + off) = pk;
+            for (int j = 0; j < 2; ++j) {
+                float a[2][4];
+                float amax = 0.0f;
+#pragma unroll
+                for (int bb = 0; bb < 2; ++bb)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int b = 2 * j + bb;
+                        a[bb][i] = silu_mul_p(acc[b][tb][i], acc[b + 4][tb][i]);
+                        amax = fmaxf(amax, fabsf(a[bb][i]));
+                    }
+                // the block's other 24 values sit in lanes lane ^ 16, ^ 32, ^ 48
+                amax = fmaxf(amax, __shfl_xor(amax, 16));
+                amax = fmaxf(amax, __shfl_xor(amax, 32));
+                const int sb = split_scale_byte(amax);
+                const float inv = split_inv_scale(sb);
+                const int col0 = nt * 128 + 64 * wn + 32 * j;
+#pragma unroll
+                for (int bb = 0; bb < 2; ++bb) {
+                    uint32_t h, l;
+                    split_quad(a[bb], inv, h, l);
+                    const size_t off = orow * I + col0 + 16 * bb + 4 * g4;
+                    if (ok) {
+                        *reinterpret_cast<uint32_t *>(A.ohi + off) = h;
+                        *reinterpret_cast<uint32_t *>(A.olo + off) = l;
                     }
                 }
+                if (ok && g4 == 0) A.osc[orow * (I / 32) + col0 / 32] = (uint8_t)sb;
+            }
+        }
+    } else {
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb) {
+            const int r = tok0 + 32 * wm + 16 * tb + (lane & 15);
+            if (r >= n_e) continue;
+            const size_t prow =
+                (size_t)A.sorted_pair[row0 + r] * A.H + nt * 256 + 128 * wn + 4 * g4;
+#pragma unroll
+            for (int b = 0; b < 8; ++b) {
+                const size_t off = prow + 16 * b;
+                if (YF32) {
+                    *reinterpret_cast<f32x4 *>(reinterpret_cast<float *>(A.out) + off) = acc[b][tb];
+                } else {
+                    uint2 pk;
+                    pk.x = pack_bf16x2(acc[b][tb][0], acc[b][tb][1]);
+                    pk.y = pack_bf16x2(acc[b][tb][2], acc[b][tb][3]);
+                    *reinterpret_cast<uint2 *>(reinterpret_cast<uint16_t *>(A.out) + off) = pk;
+                }
+            }
         }
     }
 }
@@ -334,6 +526,15 @@ __global__ __launch_bounds__(kPreThreads) void ffn_pre_kernel(PreArgs A) {
 // 256-row tiles in stage 2 (H % 256), and whole 128-column slabs.
 bool ffn_prefill_supported(int fmt, int H, int I) {
     return fmt == MOE_W_MXFP4 && I % 128 == 0 && H % 256 == 0;
+}
+
+static size_t al256(size_t b) { return (b + 255) & ~(size_t)255; }
+
+// Workspace of the tiled path: the activation's two terms and scales
+// [n_pairs][I] and the token rows' [T][H].
+size_t prefill_ws_bytes(long n_pairs, long T, int H, int I) {
+    return 2 * al256((size_t)n_pairs * I) + al256((size_t)n_pairs * I / 32) +
+           2 * al256((size_t)T * H) + al256((size_t)T * H / 32);
 }
 
 template <int STAGE, bool YF32>
@@ -351,13 +552,32 @@ static int launch_pre(hipStream_t s, PreArgs A, long n_pairs) {
 
 int ffn_prefill(const uint16_t *x, const int32_t *sorted_pair, const int32_t *offsets,
                 const moe_expert_w *experts, int fmt, int T, int k, int H, int I, int E, void *y,
-                int y_is_fp32, uint16_t *act, hipStream_t s) {
+                int y_is_fp32, void *ws, hipStream_t s) {
     if (!ffn_prefill_supported(fmt, H, I)) return MOE_EUNSUPPORTED;
     const long n = (long)T * k;
-    PreArgs a1{x, sorted_pair, offsets, experts, act, k, H, H, I, E, I / 128};
-    int rc = launch_pre<1, false>(s, a1, n);
+    uint8_t *p = reinterpret_cast<uint8_t *>(ws);
+    uint8_t *ahi = p;
+    uint8_t *alo = ahi + al256((size_t)n * I);
+    uint8_t *asc = alo + al256((size_t)n * I);
+    uint8_t *xhi = asc + al256((size_t)n * I / 32);
+    uint8_t *xlo = xhi + al256((size_t)T * H);
+    uint8_t *xsc = xlo + al256((size_t)T * H);
+
+    const long nblk = (long)T * H / 32;
+    const long grid = (nblk + 255) / 256;
+    if (grid > 0x7FFFFFFFL) return MOE_EUNSUPPORTED;
+    MOE_TIMED(s, K_PRE_SPLIT,
+              hipLaunchKernelGGL(split_rows_kernel, dim3((unsigned)grid), dim3(256), 0, s, x, nblk,
+                                 xhi, xlo, xsc));
+    int rc = check_launch();
     if (rc) return rc;
-    PreArgs a2{act, sorted_pair, offsets, experts, y, k, I, H, I, E, H / 256};
+
+    PreArgs a1{xhi, xlo, xsc, sorted_pair, offsets, experts, nullptr, ahi, alo, asc,
+               k, H, H, I, E, I / 128};
+    rc = launch_pre<1, false>(s, a1, n);
+    if (rc) return rc;
+    PreArgs a2{ahi, alo, asc, sorted_pair, offsets, experts, y, nullptr, nullptr, nullptr,
+               k, I, H, I, E, H / 256};
     return y_is_fp32 ? launch_pre<2, true>(s, a2, n) : launch_pre<2, false>(s, a2, n);
 }
 

@@ -54,6 +54,8 @@ def test_workspace_sizes(lib):
     pb, fb = lib.moe_workspace_size(8192, 8, 2048, 768, 128)
     assert pb >= (64 * 128 + 65536) * 4
     assert fb >= 65536 * 768 * 2
+    # tiled path: two FP8 terms + block scales of the activation and of x
+    assert fb >= 2 * 65536 * 768 + 65536 * 768 // 32 + 2 * 8192 * 2048 + 8192 * 2048 // 32
     with pytest.raises(lib.MoeError):
         lib.moe_workspace_size(-1, 8, 2048, 768, 128)
 
