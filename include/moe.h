@@ -148,8 +148,11 @@ int moe_route_permute(const uint16_t *x_bf16, const uint16_t *wg_bf16, const flo
  *   g = W1_e x_t, u = W3_e x_t, a = silu(g) * u (silu(g) = g / (1 + e^-g)),
  *   y[sorted_pair[r]] = W2_e a.
  * y [T*k][H] is written in pair order (row p = t*k + j), bf16 (y_is_fp32 = 0)
- * or fp32. Accumulation is fp32; the activation a is rounded to bf16 between
- * the two contractions.
+ * or fp32. Accumulation is fp32. Between the two contractions the activation
+ * a is rounded to bf16 (weight-streaming kernels), or, in the tiled kernels
+ * (MXFP4, chosen when experts see many rows), x and a enter the block-scaled
+ * FP8 x FP4 matrix cores as two E4M3 terms hi + lo with one E8M0 scale per
+ * 32 elements: |hi + lo - v| <= 2^-8 |v| + 2^-22 max|block| for every v.
  * experts: device array [E] of moe_expert_w; entries of experts that receive
  * no pair are never read. x_bf16 [T][H]. fmt: MOE_W_MXFP4 (kernel layout,
  * H and I multiples of 128) or MOE_W_BF16 (H and I multiples of 32).

@@ -12,7 +12,9 @@
 // per 32 elements: hi = fp8(x / 2^e), lo = fp8(32 (x / 2^e - hi)) with scale
 // 2^(e-5), e = floor(log2 max|x|) - 7 over the 32-element block. hi holds x to
 // 2^-4 relative, lo the remainder to another 2^-4, so hi + lo is within
-// 2^-8 |x| of x (bf16 keeps 2^-9); both terms run through the FP8 x FP4 matrix
+// 2^-8 |x| + 2^-22 max|block| of x (bf16 keeps 2^-9; the second term covers
+// elements so small that a term falls in E4M3's subnormal range); both terms
+// run through the FP8 x FP4 matrix
 // pipe, whose rate is twice bf16's, so the pair costs what one bf16 product
 // would, and the weights need no conversion at all. x is split once per token
 // by a row pass; the activation a = silu(g) * u is split by the gate/up
