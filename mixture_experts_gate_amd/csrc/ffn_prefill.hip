@@ -14,9 +14,8 @@
 // 2^-4 relative, lo the remainder to another 2^-4, so hi + lo is within
 // 2^-8 |x| + 2^-22 max|block| of x (bf16 keeps 2^-9; the second term covers
 // elements so small that a term falls in E4M3's subnormal range); both terms
-// run through the FP8 x FP4 matrix
-// pipe, whose rate is twice bf16's, so the pair costs what one bf16 product
-// would, and the weights need no conversion at all. x is split once per token
+// run through the FP8 x FP4 matrix pipe, whose rate is twice bf16's, so the
+// pair costs what one bf16 product would, and the weights need no conversion. x is split once per token
 // by a row pass; the activation a = silu(g) * u is split by the gate/up
 // kernel's epilogue as it is produced.
 //
