@@ -163,3 +163,90 @@ class MoeLayer:
 
 def layout_for(cfg):
     return blob_layout(cfg.H, cfg.I, cfg.fmt)
+
+
+class HostExperts:
+    """Expert blobs of several layers in pinned host memory, in the kernel
+    layout (packed on the device by the library, then copied back), as the
+    source store of an expert cache. ``blobs[l]`` is [E][nbytes] in the
+    interchange layout. Keys (layer, expert) may share storage through
+    ``alias``: key (l, e) reads stored blob alias(l, e) (a benchmark can then
+    stream a stack larger than it stores; the copies move the same bytes)."""
+
+    def __init__(self, blobs, layout, alias=None, device="cuda"):
+        self.layout = layout
+        self.n_stored = sum(int(b.shape[0]) for b in blobs)
+        self.E = int(blobs[0].shape[0])
+        nb = layout.nbytes
+        self.host = torch.empty((self.n_stored, nb), dtype=torch.uint8, pin_memory=True)
+        row = 0
+        for b in blobs:
+            packed = pack_to_device(b, layout, device)
+            self.host[row:row + packed.shape[0]].copy_(packed)
+            row += packed.shape[0]
+            del packed
+        torch.cuda.synchronize()
+        self.alias = alias
+
+    def address(self, stored: int) -> int:
+        return self.host.data_ptr() + stored * self.layout.nbytes
+
+    def sources(self, n_layers: int, n_experts: int):
+        """Host address of each key's blob, [n_layers * n_experts]."""
+        out = []
+        for l in range(n_layers):
+            for e in range(n_experts):
+                s = l * n_experts + e if self.alias is None else self.alias(l, e)
+                out.append(self.address(s))
+        return out
+
+
+class ExpertCache:
+    """Owner of a device slot pool and a ``moe_cache`` over it.
+
+    Use: ``tab = cache.prefetch(l, ids)`` and enqueue the compute that reads
+    ``tab`` before the next ``prefetch`` call (that call may refill slots handed
+    out by the call before this one once their compute is done); the copies of
+    a prefetch overlap whatever the compute stream is still running."""
+
+    def __init__(self, store: HostExperts, n_layers: int, n_experts: int, pool_bytes: int,
+                 device="cuda", copy_stream=None):
+        lay = store.layout
+        slot = (lay.nbytes + 255) // 256 * 256
+        self.pool = torch.empty(pool_bytes // slot * slot, dtype=torch.uint8, device=device)
+        self.slot_bytes = slot
+        self.copy_stream = copy_stream if copy_stream is not None else torch.cuda.Stream(device)
+        self.store = store
+        self.srcs = store.sources(n_layers, n_experts)
+        self.handle = _lib.expert_cache_reserve(self.pool, self.pool.numel(), lay.nbytes, n_layers,
+                                                n_experts, self.srcs, lay,
+                                                self.copy_stream.cuda_stream)
+
+    def prefetch(self, layer, ids=None, compute_stream=None):
+        return _lib.expert_cache_prefetch(self.handle, layer, ids, compute_stream)
+
+    def evict(self, layer, ids=None):
+        return _lib.expert_cache_evict(self.handle, layer, ids)
+
+    def stats(self):
+        return _lib.expert_cache_stats(self.handle)
+
+    def slots(self):
+        return _lib.expert_cache_slots(self.handle)
+
+    def slot_of(self, layer, expert):
+        return _lib.expert_cache_slot_of(self.handle, layer, expert)
+
+    def slot_bytes_view(self, slot: int, nbytes: int):
+        return self.pool[slot * self.slot_bytes: slot * self.slot_bytes + nbytes]
+
+    def close(self):
+        if self.handle:
+            _lib.expert_cache_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

@@ -1,0 +1,249 @@
+"""GPU tests of the expert cache (LRU slots over pinned host blobs, device
+table read by the expert FFN): slot bytes equal the host blob, the hit / miss
+/ victim trace equals a brute-force LRU list, and outputs computed through the
+cache equal the resident outputs bit for bit, also while the next layer's
+experts stream in on the copy stream during the current layer's compute.
+
+The pages' design keeps experts in host memory, loads them on demand and keeps
+the frequently used ones in a global LRU cache, overlapping weight movement
+with compute (winzheng.com page, "FreeToken's Three-Layer Mechanism")."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+from mixture_experts_gate_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+# a small MXFP4 layer (kernel layout needs H, I multiples of 128)
+H, I, E, K = 256, 256, 16, 4
+
+
+def _blobs(n_layers, seed=11):
+    cfg = synth.LayerConfig("cache_test", H, E, K, I, "mxfp4", 0, "uniform", (16,),
+                            "gauss_mxfp4", layers=n_layers, seed=seed)
+    return [synth.expert_pool(cfg, layer=l) for l in range(n_layers)]
+
+
+@pytest.fixture(scope="module")
+def env():
+    import torch
+    from mixture_experts_gate_amd import _lib
+    from mixture_experts_gate_amd.layer import HostExperts, pack_to_device
+    _lib.load()
+    lay = synth.blob_layout(H, I, "mxfp4")
+    L = 4
+    blobs = _blobs(L)
+    store = HostExperts(blobs, lay)
+    resident = [pack_to_device(b, lay) for b in blobs]
+    return dict(torch=torch, lib=_lib, lay=lay, L=L, blobs=blobs, store=store, resident=resident)
+
+
+class LruModel:
+    """Brute-force model of the cache policy: a list of slots from most to least
+    recently used; a call hands out its hits first (ascending expert), then
+    fills its misses (ascending expert) from the least recently used slot not
+    handed out by the same call."""
+
+    def __init__(self, nslots, E):
+        self.order = list(range(nslots))
+        self.key_of = [-1] * nslots
+        self.slot_of = {}
+        self.last = [0] * nslots
+        self.gen = 0
+        self.E = E
+        self.hits = self.misses = 0
+
+    def _front(self, s):
+        self.order.remove(s)
+        self.order.insert(0, s)
+
+    def prefetch(self, layer, ids):
+        want = sorted(set(int(i) for i in ids)) if ids is not None else list(range(self.E))
+        self.gen += 1
+        g = self.gen
+        miss = []
+        for e in want:
+            s = self.slot_of.get(layer * self.E + e, -1)
+            if s >= 0:
+                self.hits += 1
+                self._front(s)
+                self.last[s] = g
+            else:
+                miss.append(e)
+        for e in miss:
+            s = next(s for s in reversed(self.order) if self.last[s] != g)
+            if self.key_of[s] >= 0:
+                del self.slot_of[self.key_of[s]]
+            key = layer * self.E + e
+            self.key_of[s] = key
+            self.slot_of[key] = s
+            self._front(s)
+            self.last[s] = g
+            self.misses += 1
+
+    def evict(self, layer, ids):
+        for e in (ids if ids is not None else range(self.E)):
+            s = self.slot_of.pop(layer * self.E + int(e), None)
+            if s is not None:
+                self.key_of[s] = -1
+                self.order.remove(s)
+                self.order.append(s)
+
+
+def _cache(env, nslots):
+    from mixture_experts_gate_amd.layer import ExpertCache
+    slot = (env["lay"].nbytes + 255) // 256 * 256
+    return ExpertCache(env["store"], env["L"], E, nslots * slot)
+
+
+def test_prefetched_slots_hold_the_host_bytes(env):
+    torch = env["torch"]
+    c = _cache(env, 24)
+    try:
+        c.prefetch(1, np.array([3, 5, 7, 3]))
+        c.prefetch(2, None)
+        torch.cuda.synchronize()
+        nb = env["lay"].nbytes
+        checked = 0
+        for l in range(env["L"]):
+            for e in range(E):
+                s = c.slot_of(l, e)
+                if s < 0:
+                    continue
+                got = c.slot_bytes_view(s, nb).cpu()
+                want = env["store"].host[l * E + e]
+                assert torch.equal(got, want), (l, e, s)
+                checked += 1
+        assert checked == 3 + E           # 24 slots hold both requests
+        h, m, b = c.stats()
+        assert b == m * nb
+    finally:
+        c.close()
+
+
+def test_lru_trace_matches_brute_force(env):
+    torch = env["torch"]
+    nslots = 20
+    c = _cache(env, nslots)
+    model = LruModel(nslots, E)
+    rng = np.random.default_rng(5)
+    try:
+        for step in range(80):
+            layer = int(rng.integers(env["L"]))
+            if step % 17 == 16:
+                ids = rng.choice(E, size=int(rng.integers(1, 5)), replace=False)
+                c.evict(layer, ids)
+                model.evict(layer, ids)
+                continue
+            if step % 23 == 0:
+                ids = None
+            else:
+                ids = rng.integers(0, E, size=int(rng.integers(1, 12)))
+            c.prefetch(layer, ids)
+            model.prefetch(layer, ids)
+            for l in range(env["L"]):
+                for e in range(E):
+                    assert c.slot_of(l, e) == model.slot_of.get(l * E + e, -1), (step, l, e)
+            h, m, _ = c.stats()
+            assert (h, m) == (model.hits, model.misses), step
+        torch.cuda.synchronize()
+    finally:
+        c.close()
+
+
+def test_bad_request_changes_nothing(env):
+    lib = env["lib"]
+    c = _cache(env, E)          # exactly one layer fits
+    try:
+        c.prefetch(0, None)
+        before = [c.slot_of(0, e) for e in range(E)]
+        stats = c.stats()
+        for bad in (np.array([1, 2, E]), np.array([-1])):
+            with pytest.raises(lib.MoeError):
+                c.prefetch(1, bad)
+        with pytest.raises(lib.MoeError):
+            c.prefetch(env["L"], None)
+        assert [c.slot_of(0, e) for e in range(E)] == before
+        assert c.stats() == stats
+        # with room for one layer only, the next layer takes every slot over
+        c.prefetch(1, None)
+        assert sorted(c.slot_of(1, e) for e in range(E)) == sorted(before)
+        assert all(c.slot_of(0, e) == -1 for e in range(E))
+    finally:
+        c.close()
+
+
+def _layer_outputs(env, tables, T, seed):
+    """Run the FFN of every layer with its table; returns y per layer (host)."""
+    import torch
+    from mixture_experts_gate_amd.layer import MoeLayer
+    out = []
+    rng = np.random.default_rng(seed)
+    L = MoeLayer(H, E, K, I, "mxfp4", T)
+    x = torch.from_numpy(
+        synth.f32_to_bf16_bits(rng.standard_normal((T, H)).astype(np.float32)).view(np.int16)
+    ).cuda()
+    logits = torch.from_numpy(rng.random((T, E), dtype=np.float32)).cuda()
+    L.route_permute(T, logits=logits, write_logits=False)
+    for tab in tables:
+        L.ffn(T, x, tab)
+        out.append(L.y[:T * K].clone())
+    torch.cuda.synchronize()
+    return [o.cpu() for o in out]
+
+
+@pytest.mark.parametrize("T", [8, 512])
+def test_cached_output_equals_resident_bitwise(env, T):
+    torch = env["torch"]
+    from mixture_experts_gate_amd.layer import expert_table
+    lay = env["lay"]
+    res_tabs = [expert_table(r.data_ptr(), E, lay) for r in env["resident"]]
+    want = _layer_outputs(env, res_tabs, T, seed=T)
+    c = _cache(env, 2 * E)
+    try:
+        tabs = []
+        for l in range(env["L"]):
+            tabs.append(c.prefetch(l, None))
+            torch.cuda.synchronize()      # each table used before the next call refills slots
+            got = _layer_outputs(env, [tabs[-1]], T, seed=T)[0]
+            assert torch.equal(got, want[l]), l
+    finally:
+        c.close()
+
+
+def test_streaming_next_layer_during_compute_is_bitwise(env):
+    """Double-buffered stack: prefetch(l + 1) is called right after layer l's
+    compute is enqueued, so its copies run while layer l computes and reuse the
+    slots of layer l - 1. Outputs of three passes over the 4-layer stack equal
+    the resident outputs bit for bit."""
+    torch = env["torch"]
+    from mixture_experts_gate_amd.layer import MoeLayer, expert_table
+    lay = env["lay"]
+    T = 512
+    res_tabs = [expert_table(r.data_ptr(), E, lay) for r in env["resident"]]
+    want = _layer_outputs(env, res_tabs, T, seed=77)
+    rng = np.random.default_rng(77)
+    Lyr = MoeLayer(H, E, K, I, "mxfp4", T)
+    x = torch.from_numpy(
+        synth.f32_to_bf16_bits(rng.standard_normal((T, H)).astype(np.float32)).view(np.int16)
+    ).cuda()
+    logits = torch.from_numpy(rng.random((T, E), dtype=np.float32)).cuda()
+    Lyr.route_permute(T, logits=logits, write_logits=False)
+    c = _cache(env, 2 * E)
+    outs = []
+    try:
+        tab = c.prefetch(0, None)
+        for step in range(3 * env["L"]):
+            l = step % env["L"]
+            Lyr.ffn(T, x, tab)
+            outs.append((l, Lyr.y[:T * K].clone()))
+            tab = c.prefetch((l + 1) % env["L"], None)
+        torch.cuda.synchronize()
+        for l, y in outs:
+            assert torch.equal(y.cpu(), want[l]), l
+        h, m, b = c.stats()
+        assert m >= 3 * env["L"] * E - E     # every layer change misses (two layers fit)
+    finally:
+        c.close()
