@@ -5,8 +5,13 @@ One step = one pass of the routed MoE expert layer (route -> permute ->
 grouped SwiGLU expert FFN -> combine) over one batch of synthetic tokens, all
 inputs resident in HBM. The headline workload is the decode-shaped layer
 (H=2048, 128 experts, top-8, I=768, MXFP4 weights, bf16 activations, uniform
-router logits) at T=64 tokens; the JSON line also carries T=1, 8, 32 and the
-prefill-shaped T=8192 batch of the same layer.
+router logits) at T=64 tokens. The JSON line's sweep also carries T=1, 8, 32
+and the prefill-shaped T=8192 batch of the same layer; the large sparse layer
+(H=4096, 256 experts + 1 shared, top-6, I=2048, Zipf popularity) at T=1, 64,
+4096; and the 43-layer stack of that layer decoding T=1 and 16 tokens, once
+with every layer resident in HBM and once through a 32 GB LRU expert cache
+fed from pinned host memory (hit rate, H2D bytes and GB/s against the
+measured pinned copy rate).
 
 Timing: W eager warm-up steps, then K steps replayed from HIP graphs (one
 graph holds 16 consecutive steps), bracketed by device synchronisation.
@@ -47,6 +52,9 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--profile", action="store_true",
                     help="short run for profilers: headline workload, no sweep, no CPU leg")
+    ap.add_argument("--no-stack", action="store_true", help="skip the 43-layer stack runs")
+    ap.add_argument("--only", default="",
+                    help="comma list of sweep parts to run: decode,prefill,cfg4,stack")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run one plain 512 MiB device copy (HBM counter calibration)")
     return ap.parse_args()
@@ -91,35 +99,48 @@ def measured_traffic(kernel, T):
 
 
 class Workload:
-    def __init__(self, torch, T, dev, replicas=REPLICAS, pool=None, dexp=None):
+    """One routed MoE layer of config ``cfg`` at T tokens, inputs resident in
+    HBM: ``replicas`` copies of the expert weights and as many input batches,
+    rotated step by step (plus the shared expert when the config has one)."""
+
+    def __init__(self, torch, cfg, T, dev, replicas=REPLICAS, pool=None, dexp=None,
+                 shared=None):
         from mixture_experts_gate_amd import synth
         from mixture_experts_gate_amd.layer import DeviceExperts, MoeLayer
-        self.cfg = synth.CONFIGS[2] if T <= 64 else synth.CONFIGS[3]
-        c = self.cfg
+        self.cfg = c = cfg
         self.T = T
         self.lay = synth.blob_layout(c.H, c.I, c.fmt)
         self.pool = synth.expert_pool(c) if pool is None else pool
         self.dexp = DeviceExperts(self.pool, self.lay, copies=replicas, device=dev) if dexp is None else dexp
         self.R = len(self.dexp.tables)
+        self.has_shared = c.n_shared > 0
+        self.sh = None
+        if self.has_shared:
+            self.sh = shared if shared is not None else DeviceExperts(
+                synth.shared_expert(c)[None, :], self.lay, copies=self.R, device=dev)
         to16 = lambda a: torch.from_numpy(a.view("int16")).to(dev)
         self.x_host = [synth.activations(c, T, step=r) for r in range(self.R)]
         self.lg_host = [synth.router_logits(c, T, step=r) for r in range(self.R)]
         self.x = [to16(a) for a in self.x_host]
         self.lg = [torch.from_numpy(a).to(dev) for a in self.lg_host]
-        self.layer = MoeLayer(c.H, c.E, c.k, c.I, c.fmt, T, device=dev)
+        self.layer = MoeLayer(c.H, c.E, c.k, c.I, c.fmt, T, shared=self.has_shared, device=dev)
+        if self.has_shared:
+            self.layer.prepare_shared(T)
 
     def step(self, i):
         r = i % self.R
-        self.layer.forward(self.T, self.x[r], self.dexp.tables[r], logits=self.lg[r])
+        self.layer.forward(self.T, self.x[r], self.dexp.tables[r], logits=self.lg[r],
+                           shared_table=self.sh.tables[r] if self.has_shared else None)
 
-    def unique_experts(self):
-        """Distinct experts touched per step (average over the input batches)."""
+    def unique_experts(self, torch):
+        """Distinct experts the GPU router picks per step (average over the input
+        batches), read back from its top-k ids."""
         import numpy as np
-        import oracle  # only for the host-side count of routed experts
         us = []
-        for lg in self.lg_host:
-            ids, _, _ = oracle.topk(lg, self.cfg.k)
-            us.append(len(np.unique(ids)))
+        for r in range(self.R):
+            self.layer.route(self.T, logits=self.lg[r], write_logits=False)
+            torch.cuda.synchronize()
+            us.append(len(np.unique(self.layer.topk_ids[:self.T].cpu().numpy())))
         return float(np.mean(us)), us
 
 
@@ -175,12 +196,15 @@ def kernel_timing(torch, wl, steps):
 
 def algorithmic_bytes(wl, U):
     """Bytes each kernel must move at minimum (weights of touched experts read
-    once, activations read once, outputs written once)."""
+    once, activations read once, outputs written once). With a shared expert
+    the layer adds its weights and its output; the per-kernel figures are those
+    of the routed launches."""
     c, T, lay = wl.cfg, wl.T, wl.lay
     H, I, E, k = c.H, c.I, c.E, c.k
     w13 = lay.w2 - lay.w13           # W13 codes + scales of one expert
     w2 = lay.nbytes - lay.w2         # W2 codes + scales
     n = T * k
+    sh = (lay.nbytes + T * H * 2) if c.n_shared else 0
     return {
         "route": T * E * 4 + n * 8,
         "permute_small": n * 4 + n * 8 + (E + 1) * 4,
@@ -189,20 +213,22 @@ def algorithmic_bytes(wl, U):
         "ffn_prefill_gate_up": U * w13 + T * H * 2 + n * I * 2,
         "ffn_prefill_down": U * w2 + n * I * 2 + n * H * 2,
         "combine": n * H * 2 + n * 4 + T * H * 2,
-        "layer": U * lay.nbytes + 2 * T * H * 2 + T * E * 4 + n * 8,
+        "layer": U * lay.nbytes + 2 * T * H * 2 + T * E * 4 + n * 8 + sh,
     }
 
 
-def run_workload(torch, T, steps, warmup, dev, pool=None, dexp=None, kernel_steps=None):
-    wl = Workload(torch, T, dev, pool=pool, dexp=dexp)
-    U, _ = wl.unique_experts()
+def run_workload(torch, cfg, T, steps, warmup, dev, pool=None, dexp=None, shared=None,
+                 kernel_steps=None, replicas=REPLICAS):
+    wl = Workload(torch, cfg, T, dev, replicas=replicas, pool=pool, dexp=dexp, shared=shared)
+    U, _ = wl.unique_experts(torch)
     ms, wall = time_graphs(torch, wl, steps, warmup)
     kt = kernel_timing(torch, wl, kernel_steps or min(steps, 64))
     ab = algorithmic_bytes(wl, U)
     ms_step = ms / steps
     c = wl.cfg
-    flops = 6.0 * c.H * c.I * T * c.k
+    flops = 6.0 * c.H * c.I * T * (c.k + c.n_shared)
     res = {
+        "config": c.name,
         "T": T,
         "tokens_per_s": T * steps / (ms / 1000.0),
         "ms_per_step": ms_step,
@@ -237,6 +263,170 @@ def roofline(res, T):
                  "algorithmic_bytes_per_launch": k.get("algorithmic_bytes"),
                  "avg_us": k["avg_us"], "launches": k["launches"],
                  "timing": "library events around each launch, K eager steps"}
+
+
+class Stack:
+    """The 43-layer stack of config-4-shaped layers (config 5): layer l's bf16
+    output is layer l+1's input; each layer has its own router logits (Zipf
+    popularity re-permuted every 256 steps) and its shared expert.
+
+    Weights: ``distinct`` layers are generated (the remaining layers repeat
+    them with that period); in the resident run every one of the 43 layers
+    has its own full copy in HBM, so a step reads the same bytes it would with
+    43 distinct layers."""
+
+    def __init__(self, torch, cfg, dev, distinct=2):
+        from mixture_experts_gate_amd import synth
+        self.cfg = c = cfg
+        self.L = c.layers
+        self.D = distinct
+        self.lay = synth.blob_layout(c.H, c.I, c.fmt)
+        self.blobs = [synth.expert_pool(c, layer=d) for d in range(distinct)]
+        self.shared_blobs = [synth.shared_expert(c, layer=d) for d in range(distinct)]
+        self.dev = dev
+
+    def logits(self, torch, T, steps):
+        """Router logits of every layer for each of the given steps (fresh Gumbel
+        noise per step and layer; the Zipf popularity permutation changes every
+        256 steps), device tensor [len(steps)][L][T][E]."""
+        import numpy as np
+        from mixture_experts_gate_amd import synth
+        a = np.stack([np.stack([synth.router_logits(self.cfg, T, step=s, layer=l)
+                                for l in range(self.L)]) for s in steps])
+        return torch.from_numpy(a).to(self.dev)
+
+
+def run_stack_resident(torch, st, Ts, steps, warmup):
+    """All 43 layers resident in HBM; a step is 43 layers, replayed from a graph."""
+    from mixture_experts_gate_amd import synth
+    from mixture_experts_gate_amd.layer import MoeLayer, expert_table, pack_to_device
+    c, lay, dev = st.cfg, st.lay, st.dev
+    packed = [pack_to_device(b, lay, dev) for b in st.blobs]
+    spacked = [pack_to_device(b[None, :], lay, dev) for b in st.shared_blobs]
+    bufs = [packed[l % st.D].clone() for l in range(st.L)]
+    sbufs = [spacked[l % st.D].clone() for l in range(st.L)]
+    del packed, spacked
+    tabs = [expert_table(b.data_ptr(), c.E, lay, device=dev) for b in bufs]
+    stabs = [expert_table(b.data_ptr(), 1, lay, device=dev) for b in sbufs]
+    out = {}
+    for T in Ts:
+        # four input steps replayed in turn: two of the first popularity phase,
+        # two of the second
+        lg = st.logits(torch, T, (0, 1, 256, 257))
+        x0 = torch.from_numpy(synth.activations(c, T).view("int16")).to(dev)
+        layers = [MoeLayer(c.H, c.E, c.k, c.I, c.fmt, T, shared=True, device=dev) for _ in (0, 1)]
+        for ly in layers:
+            ly.prepare_shared(T)
+
+        class W:
+            def step(self_, i):
+                x = x0
+                for l in range(st.L):
+                    x = layers[l % 2].forward(T, x, tabs[l], logits=lg[i % 4][l],
+                                              shared_table=stabs[l])
+
+        ms, wall = time_graphs(torch, W(), steps, warmup)
+        ms_step = ms / steps
+        # bytes: the distinct experts each layer's router picks, read once
+        import numpy as np
+        nbytes = 0
+        for l in range(st.L):
+            layers[0].route(T, logits=lg[0][l], write_logits=False)
+            torch.cuda.synchronize()
+            u = len(np.unique(layers[0].topk_ids[:T].cpu().numpy()))
+            nbytes += (u + 1) * lay.nbytes + 2 * T * c.H * 2
+        out[f"T{T}"] = {"T": T, "tokens_per_s": T / (ms_step / 1000.0), "ms_per_step": ms_step,
+                        "host_wall_ms_per_step": 1000.0 * wall / steps,
+                        "step_algorithmic_bytes": nbytes,
+                        "hbm_GBs": nbytes / (ms_step / 1000.0) / 1e9,
+                        "hbm_frac": nbytes / (ms_step / 1000.0) / 1e9 / HBM_PEAK_GBS}
+        log(f"stack resident T={T}: {out[f'T{T}']['tokens_per_s']:.0f} tok/s, "
+            f"{ms_step:.3f} ms/step, HBM {out[f'T{T}']['hbm_frac']*100:.1f}%")
+    del bufs, sbufs, tabs, stabs
+    torch.cuda.empty_cache()
+    return out
+
+
+def h2d_peak(torch, dev, nbytes=1 << 30):
+    """Pinned host -> device copy rate on a side stream (the link reference)."""
+    src = torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
+    dst = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    s = torch.cuda.Stream(dev)
+    dst.copy_(src, non_blocking=True)
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(s):
+        a.record(s)
+        for _ in range(3):
+            dst.copy_(src, non_blocking=True)
+        b.record(s)
+    torch.cuda.synchronize()
+    gbs = 3 * nbytes / (a.elapsed_time(b) / 1000.0) / 1e9
+    del src, dst
+    return gbs
+
+
+def run_stack_cached(torch, st, runs, pool_bytes):
+    """The stack through a pool_bytes LRU expert cache fed from pinned host
+    memory: per layer, route on the GPU, read the ids back, prefetch the misses
+    (hipMemcpyAsync on the copy stream), then the expert FFN, shared expert and
+    combine. Shared experts stay resident. runs: [(T, warmup, steps)]."""
+    import numpy as np
+    from mixture_experts_gate_amd import synth
+    from mixture_experts_gate_amd.layer import (ExpertCache, HostExperts, MoeLayer, expert_table,
+                                                pack_to_device)
+    c, lay, dev = st.cfg, st.lay, st.dev
+    store = HostExperts(st.blobs, lay, alias=lambda l, e: (l % st.D) * c.E + e, device=dev)
+    spacked = [pack_to_device(b[None, :], lay, dev) for b in st.shared_blobs]
+    stabs = [expert_table(spacked[l % st.D].data_ptr(), 1, lay, device=dev) for l in range(st.L)]
+    link = h2d_peak(torch, dev)
+    log(f"pinned H2D copy rate: {link:.1f} GB/s")
+    out = {"h2d_link_GBs": link, "pool_bytes": pool_bytes}
+    for T, warmup, steps in runs:
+        cache = ExpertCache(store, st.L, c.E, pool_bytes, device=dev)
+        lg = st.logits(torch, T, range(warmup + steps))
+        x0 = torch.from_numpy(synth.activations(c, T).view("int16")).to(dev)
+        layers = [MoeLayer(c.H, c.E, c.k, c.I, c.fmt, T, shared=True, device=dev) for _ in (0, 1)]
+        for ly in layers:
+            ly.prepare_shared(T)
+
+        def step(i):
+            x = x0
+            for l in range(st.L):
+                ly = layers[l % 2]
+                ly.route_permute(T, logits=lg[i][l], write_logits=False)
+                ids = ly.topk_ids[:T].cpu().numpy().ravel()
+                tab = cache.prefetch(l, ids)
+                ly.ffn(T, x, tab)
+                ly.shared_ffn(T, x, stabs[l])
+                ly.combine(T, with_shared=True)
+                x = ly.out[:T]
+
+        for i in range(warmup):
+            step(i)
+        torch.cuda.synchronize()
+        h0, m0, b0 = cache.stats()
+        t0 = time.perf_counter()
+        for i in range(warmup, warmup + steps):
+            step(i)
+        torch.cuda.synchronize()
+        el = time.perf_counter() - t0
+        h1, m1, b1 = cache.stats()
+        hits, misses, nb = h1 - h0, m1 - m0, b1 - b0
+        r = {"T": T, "steps": steps, "warmup": warmup, "slots": cache.slots(),
+             "tokens_per_s": T * steps / el, "ms_per_step": 1000.0 * el / steps,
+             "hit_rate": hits / max(hits + misses, 1), "misses_per_step": misses / steps,
+             "h2d_bytes_per_step": nb / steps, "h2d_GBs": nb / el / 1e9,
+             "h2d_frac_of_link": nb / el / 1e9 / link,
+             "steps_cross_popularity_change": (warmup + steps) > 256}
+        out[f"T{T}"] = r
+        log(f"stack cached T={T}: {r['tokens_per_s']:.1f} tok/s, hit {r['hit_rate']:.3f}, "
+            f"H2D {r['h2d_GBs']:.1f} GB/s ({r['h2d_frac_of_link']*100:.0f}% of the copy rate)")
+        cache.close()
+        del cache
+    del store
+    return out
 
 
 def cpu_baseline(wl, budget_s=12.0):
@@ -287,7 +477,7 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
-    from mixture_experts_gate_amd import _lib
+    from mixture_experts_gate_amd import _lib, synth
     _lib.load()
     dev = "cuda:0"
     torch.cuda.set_device(0)
@@ -296,25 +486,57 @@ def main():
         args.no_cpu = True
     if args.calib_copy:
         calib_copy(torch, dev)
+    only = set(args.only.split(",")) if args.only else None
+    want = lambda name: only is None or name in only
 
+    c2 = synth.CONFIGS[2]
+    sweep = {}
     log(f"headline: decode layer T={args.T}, {args.steps} steps, {args.warmup} warm-up")
-    wl, head = run_workload(torch, args.T, args.steps, args.warmup, dev)
+    wl, head = run_workload(torch, c2, args.T, args.steps, args.warmup, dev)
     dom, roof = roofline(head, args.T)
     log(f"T={args.T}: {head['tokens_per_s']:.0f} tok/s, {head['ms_per_step']*1000:.1f} us/step, "
         f"layer HBM {head['layer_hbm_frac']*100:.1f}%")
-    sweep = {}
-    if not args.no_sweep:
+    if not args.no_sweep and want("decode"):
         for T in (1, 8, 32):
             if T == args.T:
                 continue
-            _, r = run_workload(torch, T, max(args.steps // 2, 32), args.warmup, dev,
+            _, r = run_workload(torch, c2, T, max(args.steps // 2, 32), args.warmup, dev,
                                 pool=wl.pool, dexp=wl.dexp)
             sweep[f"decode_T{T}"] = r
             log(f"T={T}: {r['tokens_per_s']:.0f} tok/s, {r['ms_per_step']*1000:.1f} us/step")
-        _, r = run_workload(torch, 8192, 16, 3, dev, pool=wl.pool, dexp=wl.dexp, kernel_steps=8)
+    if not args.no_sweep and want("prefill"):
+        # the prefill workload runs the same layer (same weights) at T=8192
+        _, r = run_workload(torch, synth.CONFIGS[3], 8192, 16, 3, dev, pool=wl.pool,
+                            dexp=wl.dexp, kernel_steps=8)
         r["mfma_frac_bf16_peak"] = r["layer_tflops"] / BF16_PEAK_TFLOPS
         sweep["prefill_T8192"] = r
         log(f"T=8192: {r['tokens_per_s']:.0f} tok/s, {r['layer_tflops']:.1f} TFLOP/s")
+    if not args.no_sweep and want("cfg4"):
+        c4 = synth.CONFIGS[4]
+        log("config 4: generating 256 experts + shared ...")
+        w4 = None
+        for T, steps in ((1, 100), (64, 100), (4096, 8)):
+            w, r = run_workload(torch, c4, T, steps, 3, dev, replicas=2,
+                                pool=None if w4 is None else w4.pool,
+                                dexp=None if w4 is None else w4.dexp,
+                                shared=None if w4 is None else w4.sh,
+                                kernel_steps=min(steps, 16))
+            w4 = w4 or w
+            if T == 4096:
+                r["mfma_frac_bf16_peak"] = r["layer_tflops"] / BF16_PEAK_TFLOPS
+            sweep[f"cfg4_T{T}"] = r
+            log(f"config 4 T={T}: {r['tokens_per_s']:.0f} tok/s, {r['ms_per_step']*1000:.1f} us/step, "
+                f"layer HBM {r['layer_hbm_frac']*100:.1f}%, {r['layer_tflops']:.1f} TFLOP/s")
+        del w4
+        torch.cuda.empty_cache()
+    if not args.no_sweep and not args.no_stack and want("stack"):
+        c5 = synth.CONFIGS[5]
+        log("config 5: generating 2 distinct layers ...")
+        st = Stack(torch, c5, dev, distinct=2)
+        sweep["stack43_resident"] = run_stack_resident(torch, st, (1, 16), 40, 3)
+        sweep["stack43_cache32GB"] = run_stack_cached(torch, st, [(1, 32, 288), (16, 4, 8)],
+                                                      32 * 10**9)
+        del st
     cpu = None
     if not args.no_cpu:
         log("CPU oracle baseline ...")

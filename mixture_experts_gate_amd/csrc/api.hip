@@ -100,12 +100,15 @@ size_t ffn_ws_bytes(long n_pairs, long T, int H, int I) {
 }
 
 // Decode kernels stream each touched expert once; prefill kernels tile the
-// contraction for the matrix cores. Tokens per touched expert decide.
+// contraction for the matrix cores. The tiled path needs many rows per expert
+// (48 on average) and enough 128-row x 128-column tiles to give every compute
+// unit at least one (a single shared expert over a few dozen tokens has 16).
 static bool use_prefill(long n_pairs, int E, int fmt, int H, int I) {
     const int opt = g_ffn_path.load();
     if (opt == 1) return false;
     if (opt == 2) return ffn_prefill_supported(fmt, H, I);
-    return ffn_prefill_supported(fmt, H, I) && n_pairs >= 48L * E;
+    return ffn_prefill_supported(fmt, H, I) && n_pairs >= 48L * E &&
+           (n_pairs / 128) * (I / 128) >= 256;
 }
 
 }  // namespace moe
