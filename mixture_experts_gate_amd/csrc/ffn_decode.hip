@@ -88,18 +88,28 @@ __device__ __forceinline__ const uint8_t *srow(const uint8_t *base, long r, int 
 }
 
 // Experts that received at least one pair, as a bitmask (E <= 512), computed
-// by the whole wavefront; lookups afterwards are scalar.
+// by the whole wavefront from one round of loads; lookups afterwards are
+// scalar.
 struct ActiveSet {
     uint64_t w[8];
     int count;
+    bool multi_pass;         // some expert has more rows than one token pass
     __device__ __forceinline__ void init(const int32_t *__restrict__ offsets, int E) {
         count = 0;
+        int cnt[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const int e = i * kWave + lane_id();
-            w[i] = __ballot(e < E && offsets[e + 1] > offsets[e]);
+            cnt[i] = e < E ? offsets[e + 1] - offsets[e] : 0;
+        }
+        uint64_t many = 0;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            w[i] = __ballot(cnt[i] > 0);
+            many |= __ballot(cnt[i] > kPass);
             count += __popcll(w[i]);
         }
+        multi_pass = many != 0;
     }
     // index of the a-th (0-based) active expert; a < count
     __device__ __forceinline__ int nth(int a) const {
@@ -220,8 +230,8 @@ __device__ __forceinline__ void dec_step(const DecArgs &A, const ActiveSet &act,
                                          float (&red)[2][KS > 1 ? KS - 1 : 1][NB][4][kWave],
                                          WFrag<FMT> (&wc)[SPW][NB], WFrag<FMT> (&wn)[SPW][NB],
                                          u32x4 (&xr)[SPW][4], ExpertState &cur, ExpertState &nxt,
-                                         int &pidx, int &x_key, int &buf, long t, long t1,
-                                         int lane, int wv, int m, int c) {
+                                         int &pidx, int &x_key, int &buf, long t, long ts,
+                                         long t1, int lane, int wv, int m, int c) {
 
         const int rt = (int)(t % A.nrt);
         // token operand for the first pass of this tile (loaded before the next
@@ -230,12 +240,12 @@ __device__ __forceinline__ void dec_step(const DecArgs &A, const ActiveSet &act,
             load_tokens<STAGE, SPW>(A, cur, 0, wv, m, c, xr, pidx);
             x_key = cur.a * 4096;
         }
-        const bool more = t + 1 < t1;
+        const bool more = t + ts < t1;
         if (more) {
-            const int an = (int)((t + 1) / A.nrt);
+            const int an = (int)((t + ts) / A.nrt);
             if (an != cur.a) expert_state<STAGE>(A, act, an, nxt);
             else nxt = cur;
-            load_tile<FMT, STAGE, SPW, NB, FULL>(A, nxt, (int)((t + 1) % A.nrt), wv, lane, wn);
+            load_tile<FMT, STAGE, SPW, NB, FULL>(A, nxt, (int)((t + ts) % A.nrt), wv, lane, wn);
         }
         for (int p = 0; p * kPass < cur.n_e; ++p) {
             if (p > 0) {   // more than 16 tokens: next 16 of this expert
@@ -322,9 +332,23 @@ __global__ __launch_bounds__(kWave *KS) void ffn_dec_kernel(DecArgs A) {
 
     ActiveSet act;
     act.init(A.offsets, A.E);
+    // Tiles are active-expert-major. Workgroups take contiguous ranges, which
+    // keep an expert's token operand in registers across its tiles, unless some
+    // expert has more rows than one token pass: then workgroup b takes tiles b,
+    // b + g, b + 2g, .. (g workgroups), so the tiles of the few experts with
+    // many rows (skewed popularity) spread over many workgroups instead of
+    // stretching the ones that hold them.
     const long total = (long)act.count * A.nrt;
-    const long t0 = (long)blockIdx.x * total / gridDim.x;
-    const long t1 = ((long)blockIdx.x + 1) * total / gridDim.x;
+    long t0, t1, ts;
+    if (act.multi_pass) {
+        t0 = blockIdx.x;
+        t1 = total;
+        ts = gridDim.x;
+    } else {
+        t0 = (long)blockIdx.x * total / gridDim.x;
+        t1 = ((long)blockIdx.x + 1) * total / gridDim.x;
+        ts = 1;
+    }
     if (t0 >= t1) return;
 
     ExpertState cur, nxt;
@@ -340,12 +364,13 @@ __global__ __launch_bounds__(kWave *KS) void ffn_dec_kernel(DecArgs A) {
     int x_key = -1;
     int buf = 0;
 
-    for (long t = t0; t < t1; t += 2) {
+    for (long t = t0; t < t1; t += 2 * ts) {
         dec_step<FMT, STAGE, SPW, KS, NB, YF32, FULL>(A, act, red, wa, wb, xr, cur, nxt, pidx,
-                                                      x_key, buf, t, t1, lane, wv, m, c);
-        if (t + 1 < t1)
+                                                      x_key, buf, t, ts, t1, lane, wv, m, c);
+        if (t + ts < t1)
             dec_step<FMT, STAGE, SPW, KS, NB, YF32, FULL>(A, act, red, wb, wa, xr, cur, nxt, pidx,
-                                                          x_key, buf, t + 1, t1, lane, wv, m, c);
+                                                          x_key, buf, t + ts, ts, t1, lane, wv, m,
+                                                          c);
     }
 }
 
