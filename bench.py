@@ -19,8 +19,10 @@ Steps rotate over 8 replicas of the expert weights (8 x 321 MB, well above the
 256 MB last-level cache) and 8 input batches, so weight bytes come from HBM.
 
 roofline: the dominant kernel's algorithmic bytes per launch divided by its
-average launch time, from events the library records around each of its
-launches on the launch stream (a second pass of K eager steps).
+average launch time, from the start/end events hipExtLaunchKernel attaches to
+each of its dispatches on the launch stream (library timing mode, a second
+pass of K eager steps); traffic: HBM bytes per launch from the committed
+counter summary (profiles/traffic.json) when it matches the kernel's source.
 cpu_baseline: the CPU oracle (single-threaded C, fp64) on the same layer.
 """
 from __future__ import annotations
@@ -262,7 +264,7 @@ def roofline(res, T):
                  "traffic": measured_traffic(dom, T),
                  "algorithmic_bytes_per_launch": k.get("algorithmic_bytes"),
                  "avg_us": k["avg_us"], "launches": k["launches"],
-                 "timing": "library events around each launch, K eager steps"}
+                 "timing": "hipExtLaunchKernel start/end events of each launch, K eager steps"}
 
 
 class Stack:

@@ -195,9 +195,10 @@ int moe_workspace_size(int T, int k, int H, int I, int E, size_t *permute_bytes,
  *   MOE_OPT_FFN_PATH: 0 = choose by size (default), 1 = force the decode
  *                     (weight-streaming) kernels, 2 = force the prefill
  *                     (tiled matrix-core) kernels.
- *   MOE_OPT_TIMING:   1 = bracket every kernel launch of the library with two
- *                     events on the launch's stream (adds two event records
- *                     per launch; do not use under graph capture); 0 = off.
+ *   MOE_OPT_TIMING:   1 = launch every kernel of the library through
+ *                     hipExtLaunchKernel with two events that take the
+ *                     dispatch's own start and end times on the launch's
+ *                     stream (do not use under graph capture); 0 = off.
  *                     Setting it clears the accumulated timings. */
 enum { MOE_OPT_FFN_PATH = 1, MOE_OPT_TIMING = 2 };
 int moe_set_option(int option, int value);

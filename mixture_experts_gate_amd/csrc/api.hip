@@ -15,16 +15,16 @@ void set_last_hip_error(hipError_t e) { g_last_hip_error = (int)e; }
 int ffn_path_option() { return g_ffn_path.load(); }
 
 // ---------------------------------------------------------------- timing --
-// Optional per-kernel launch timing: each launch is bracketed by two events
-// recorded on its own stream; moe_timing_query sums the elapsed times.
+// Optional per-kernel launch timing: each launch is made with
+// hipExtLaunchKernel and two events that take the dispatch's own start and end
+// times on its stream; moe_timing_query sums the elapsed times.
 static std::atomic<bool> g_timing{false};
 static std::mutex g_tmu;
 struct TimingRec {
     int kid;
     hipEvent_t a, b;
 };
-static std::vector<TimingRec> g_recs;        // completed brackets awaiting a query
-static std::vector<TimingRec> g_open;        // started, not yet closed (per kernel id)
+static std::vector<TimingRec> g_recs;        // launches awaiting a query
 static std::vector<hipEvent_t> g_evpool;
 static long long g_launches[K_COUNT];
 static double g_ms[K_COUNT];
@@ -47,23 +47,18 @@ static hipEvent_t pool_event() {
 
 bool timing_enabled() { return g_timing.load(std::memory_order_relaxed); }
 
-void timing_mark(hipStream_t s, int kid, bool start) {
+bool timing_begin(int kid, hipEvent_t *start, hipEvent_t *stop) {
     std::lock_guard<std::mutex> lk(g_tmu);
-    if (start) {
-        TimingRec r{kid, pool_event(), nullptr};
-        (void)hipEventRecord(r.a, s);
-        g_open.push_back(r);
-    } else {
-        for (size_t i = g_open.size(); i-- > 0;) {
-            if (g_open[i].kid != kid) continue;
-            TimingRec r = g_open[i];
-            g_open.erase(g_open.begin() + (long)i);
-            r.b = pool_event();
-            (void)hipEventRecord(r.b, s);
-            g_recs.push_back(r);
-            break;
-        }
+    TimingRec r{kid, pool_event(), pool_event()};
+    if (!r.a || !r.b) {
+        if (r.a) g_evpool.push_back(r.a);
+        if (r.b) g_evpool.push_back(r.b);
+        return false;
     }
+    g_recs.push_back(r);
+    *start = r.a;
+    *stop = r.b;
+    return true;
 }
 
 static void timing_drain() {

@@ -220,10 +220,9 @@ extern "C" int expert_cache_prefetch(moe_cache *c, int layer, const int32_t *ids
     up.n = 0;
     auto flush = [&]() -> int {
         if (up.n == 0) return MOE_OK;
-        MOE_TIMED(c->copy_stream, K_CACHE_TABLE,
-                  hipLaunchKernelGGL(cache_table_kernel, dim3(1), dim3(256), 0, c->copy_stream,
+        MOE_LAUNCH(K_CACHE_TABLE, cache_table_kernel, dim3(1), dim3(256), 0, c->copy_stream,
                                      c->d_table, (const char *)c->pool, c->slot_bytes, c->lay[0],
-                                     c->lay[1], c->lay[2], c->lay[3], up));
+                                     c->lay[1], c->lay[2], c->lay[3], up);
         up.n = 0;
         return check_launch();
     };

@@ -75,9 +75,8 @@ template <bool YF32>
 static void launch_combine(dim3 grid, hipStream_t s, const void *y, const float *w, const void *ysh,
                            int T, int k, int H, uint16_t *out) {
 #define MOE_CB(KM)                                                                            \
-    MOE_TIMED(s, K_COMBINE,                                                                   \
-              hipLaunchKernelGGL((combine_kernel<YF32, KM>), grid, dim3(64), 0, s, y, w, ysh, T, \
-                                 k, H, out))
+    MOE_LAUNCH(K_COMBINE, (combine_kernel<YF32, KM>), grid, dim3(64), 0, s, y, w, ysh, T, \
+                                 k, H, out)
     switch (k) {
         case 1: MOE_CB(1); break;
         case 2: MOE_CB(2); break;

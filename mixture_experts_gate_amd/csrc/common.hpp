@@ -2,6 +2,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
 #include <stdint.h>
 
 #include "moe.h"
@@ -47,26 +48,20 @@ enum KernelId {
 };
 
 bool timing_enabled();
-void timing_mark(hipStream_t s, int kid, bool start);
+// When timing is enabled, hands out the two events a launch of kernel `kid`
+// records its start and end in (they are read by moe_timing_query).
+bool timing_begin(int kid, hipEvent_t *start, hipEvent_t *stop);
 
-// Brackets one launch with events on its stream when timing is enabled.
-struct TimedLaunch {
-    hipStream_t s;
-    int kid;
-    bool on;
-    TimedLaunch(hipStream_t s_, int kid_) : s(s_), kid(kid_), on(timing_enabled()) {
-        if (on) timing_mark(s, kid, true);
-    }
-    ~TimedLaunch() {
-        if (on) timing_mark(s, kid, false);
-    }
-};
-
-// Launch statement `launch` bracketed for timing as kernel `kid` on `stream`.
-#define MOE_TIMED(stream, kid, launch)                 \
-    do {                                               \
-        ::moe::TimedLaunch moe_timed_((stream), (kid)); \
-        launch;                                        \
+// Launch of kernel `kid`; with timing enabled the start and end of the
+// dispatch itself land in two events on the launch stream (hipExtLaunchKernel).
+#define MOE_LAUNCH(kid, kernel, grid, block, shmem, stream, ...)                              \
+    do {                                                                                      \
+        hipEvent_t moe_ev0_ = nullptr, moe_ev1_ = nullptr;                                    \
+        if (::moe::timing_enabled() && ::moe::timing_begin((kid), &moe_ev0_, &moe_ev1_))      \
+            hipExtLaunchKernelGGL(kernel, grid, block, shmem, stream, moe_ev0_, moe_ev1_, 0,  \
+                                  __VA_ARGS__);                                               \
+        else                                                                                  \
+            hipLaunchKernelGGL(kernel, grid, block, shmem, stream, __VA_ARGS__);              \
     } while (0)
 
 // ------------------------------------------------------------ bf16 bits --

@@ -408,9 +408,8 @@ static int launch_dec(hipStream_t s, DecArgs A, long slots) {
     const long max_tiles = slots * A.nrt;
     const unsigned grid = (unsigned)(max_tiles < (long)full ? max_tiles : (long)full);
     if (grid == 0) return MOE_OK;
-    MOE_TIMED(s, STAGE == 1 ? K_DEC_GATE_UP : K_DEC_DOWN,
-              hipLaunchKernelGGL((ffn_dec_kernel<FMT, STAGE, SPW, KS, NB, YF32, FULL>), dim3(grid),
-                                 dim3(kWave * KS), 0, s, A));
+    MOE_LAUNCH(STAGE == 1 ? K_DEC_GATE_UP : K_DEC_DOWN, (ffn_dec_kernel<FMT, STAGE, SPW, KS, NB, YF32, FULL>), dim3(grid),
+                                 dim3(kWave * KS), 0, s, A);
     return check_launch();
 }
 

@@ -545,9 +545,8 @@ static int launch_pre(hipStream_t s, PreArgs A, long n_pairs) {
     const long tiles_max = mt_max * A.ntiles_w;
     const long grid = ((tiles_max + 7) / 8) * 8;
     if (grid > 0x7FFFFFFFL) return MOE_EUNSUPPORTED;
-    MOE_TIMED(s, STAGE == 1 ? K_PRE_GATE_UP : K_PRE_DOWN,
-              hipLaunchKernelGGL((ffn_pre_kernel<STAGE, YF32>), dim3((unsigned)grid),
-                                 dim3(kPreThreads), 0, s, A));
+    MOE_LAUNCH(STAGE == 1 ? K_PRE_GATE_UP : K_PRE_DOWN, (ffn_pre_kernel<STAGE, YF32>), dim3((unsigned)grid),
+                                 dim3(kPreThreads), 0, s, A);
     return check_launch();
 }
 
@@ -567,9 +566,8 @@ int ffn_prefill(const uint16_t *x, const int32_t *sorted_pair, const int32_t *of
     const long nblk = (long)T * H / 32;
     const long grid = (nblk + 255) / 256;
     if (grid > 0x7FFFFFFFL) return MOE_EUNSUPPORTED;
-    MOE_TIMED(s, K_PRE_SPLIT,
-              hipLaunchKernelGGL(split_rows_kernel, dim3((unsigned)grid), dim3(256), 0, s, x, nblk,
-                                 xhi, xlo, xsc));
+    MOE_LAUNCH(K_PRE_SPLIT, split_rows_kernel, dim3((unsigned)grid), dim3(256), 0, s, x, nblk,
+                                 xhi, xlo, xsc);
     int rc = check_launch();
     if (rc) return rc;
 

@@ -43,15 +43,13 @@ extern "C" int moe_pack_mxfp4(const void *src, void *dst, int n, size_t src_stri
     // W13: 2I rows x H columns; W2: H rows x I columns
     const long l13 = (long)(2 * I / 16) * (H / 128) * 64;
     const long l2 = (long)(H / 16) * (I / 128) * 64;
-    MOE_TIMED(s, K_PACK,
-              hipLaunchKernelGGL(pack_mxfp4_kernel, dim3((unsigned)((l13 + 255) / 256), n),
+    MOE_LAUNCH(K_PACK, pack_mxfp4_kernel, dim3((unsigned)((l13 + 255) / 256), n),
                                  dim3(256), 0, s, sp, dp, src_stride, dst_stride, lay_w13, lay_s13,
-                                 2 * I, H));
+                                 2 * I, H);
     int rc = check_launch();
     if (rc) return rc;
-    MOE_TIMED(s, K_PACK,
-              hipLaunchKernelGGL(pack_mxfp4_kernel, dim3((unsigned)((l2 + 255) / 256), n),
+    MOE_LAUNCH(K_PACK, pack_mxfp4_kernel, dim3((unsigned)((l2 + 255) / 256), n),
                                  dim3(256), 0, s, sp, dp, src_stride, dst_stride, lay_w2, lay_s2,
-                                 H, I));
+                                 H, I);
     return check_launch();
 }

@@ -239,16 +239,14 @@ extern "C" int moe_permute(const int32_t *topk_ids, int T, int k, int E, int32_t
     if (n > 0x7FFFFFFFL) return MOE_EINVAL;
     hipStream_t s = (hipStream_t)stream;
     if (n == 0) {
-        MOE_TIMED(s, K_PERM_EMPTY,
-                  hipLaunchKernelGGL(permute_empty_kernel, dim3(1), dim3(256), 0, s, E, offsets));
+        MOE_LAUNCH(K_PERM_EMPTY, permute_empty_kernel, dim3(1), dim3(256), 0, s, E, offsets);
         return check_launch();
     }
     if (!topk_ids || !sorted_pair || !pair_row) return MOE_EINVAL;
     if (n <= kSmallMax) {
         const size_t lds = permute_block_lds_ints(E) * sizeof(int);
-        MOE_TIMED(s, K_PERM_SMALL,
-                  hipLaunchKernelGGL(permute_small_kernel, dim3(1), dim3(kChunk), lds, s, topk_ids,
-                                     (int)n, E, offsets, sorted_pair, pair_row));
+        MOE_LAUNCH(K_PERM_SMALL, permute_small_kernel, dim3(1), dim3(kChunk), lds, s, topk_ids,
+                                     (int)n, E, offsets, sorted_pair, pair_row);
         return check_launch();
     }
     if (ws_bytes < permute_ws_bytes(n, E) || !ws) return MOE_EINVAL;
@@ -256,19 +254,16 @@ extern "C" int moe_permute(const int32_t *topk_ids, int T, int k, int E, int32_t
     int32_t *hist = (int32_t *)ws;
     int32_t *lrank = hist + (size_t)nb * E;
     const size_t lds1 = (size_t)(E + kWavesPerChunk * E) * sizeof(int);
-    MOE_TIMED(s, K_PERM_RANK,
-              hipLaunchKernelGGL(permute_rank_kernel, dim3(nb), dim3(kChunk), lds1, s, topk_ids,
-                                 (int)n, E, hist, lrank));
+    MOE_LAUNCH(K_PERM_RANK, permute_rank_kernel, dim3(nb), dim3(kChunk), lds1, s, topk_ids,
+                                 (int)n, E, hist, lrank);
     int rc = check_launch();
     if (rc) return rc;
-    MOE_TIMED(s, K_PERM_SCAN,
-              hipLaunchKernelGGL(permute_scan_kernel, dim3(1), dim3(kChunk), 0, s, nb, E, hist,
-                                 offsets));
+    MOE_LAUNCH(K_PERM_SCAN, permute_scan_kernel, dim3(1), dim3(kChunk), 0, s, nb, E, hist,
+                                 offsets);
     rc = check_launch();
     if (rc) return rc;
-    MOE_TIMED(s, K_PERM_SCATTER,
-              hipLaunchKernelGGL(permute_scatter_kernel, dim3(nb), dim3(kChunk), 0, s, topk_ids,
-                                 (int)n, E, hist, lrank, sorted_pair, pair_row));
+    MOE_LAUNCH(K_PERM_SCATTER, permute_scatter_kernel, dim3(nb), dim3(kChunk), 0, s, topk_ids,
+                                 (int)n, E, hist, lrank, sorted_pair, pair_row);
     return check_launch();
 }
 
@@ -291,10 +286,9 @@ extern "C" int moe_route_permute(const uint16_t *x_bf16, const uint16_t *wg_bf16
     hipStream_t s = (hipStream_t)stream;
     const size_t lds = ((size_t)n + permute_block_lds_ints(E)) * sizeof(int);
 #define MOE_RP(VPL)                                                                            \
-    MOE_TIMED(s, K_ROUTE_PERMUTE,                                                              \
-              hipLaunchKernelGGL(route_permute_kernel<VPL>, dim3(1), dim3(kChunk), lds, s, x_bf16, \
+    MOE_LAUNCH(K_ROUTE_PERMUTE, route_permute_kernel<VPL>, dim3(1), dim3(kChunk), lds, s, x_bf16, \
                                  wg_bf16, logits_in, logits_out, T, H, E, k, renormalize,        \
-                                 topk_ids, topk_w, offsets, sorted_pair, pair_row))
+                                 topk_ids, topk_w, offsets, sorted_pair, pair_row)
     if (E <= 64) MOE_RP(1);
     else if (E <= 128) MOE_RP(2);
     else if (E <= 256) MOE_RP(4);

@@ -31,10 +31,9 @@ extern "C" int moe_route(const uint16_t *x_bf16, const uint16_t *wg_bf16, const 
     const int waves_per_block = 4;
     dim3 grid((T + waves_per_block - 1) / waves_per_block), block(kWave * waves_per_block);
 #define MOE_ROUTE_LAUNCH(VPL)                                                                 \
-    MOE_TIMED(s, K_ROUTE,                                                                     \
-              hipLaunchKernelGGL(route_kernel<VPL>, grid, block, 0, s, x_bf16, wg_bf16,       \
+    MOE_LAUNCH(K_ROUTE, route_kernel<VPL>, grid, block, 0, s, x_bf16, wg_bf16,       \
                                  logits_in, logits_out, T, H, E, k, renormalize, topk_ids,    \
-                                 topk_w))
+                                 topk_w)
     if (E <= 64) MOE_ROUTE_LAUNCH(1);
     else if (E <= 128) MOE_ROUTE_LAUNCH(2);
     else if (E <= 256) MOE_ROUTE_LAUNCH(4);
