@@ -106,6 +106,36 @@ __device__ __forceinline__ uint32_t load_u8(const void *p) {
     return *(const MOE_GLOBAL uint8_t *)(p);
 }
 
+// Raw buffer loads through a resource with a byte range: an offset at or past
+// the range returns zeros without a memory access. A load that is issued on
+// every path and switched off by its offset keeps the count of loads in
+// flight the same on all paths, so the compiler's wait before a use can leave
+// later loads (a prefetch) in flight instead of draining all of them where
+// paths with and without the load merge.
+using buf_rsrc = __amdgpu_buffer_rsrc_t;
+constexpr uint32_t kBufOff = 0x80000000u;   // past every range made here (< 2 GiB)
+constexpr int kBufNt = 2;                    // non-temporal cache policy bit
+__device__ __forceinline__ buf_rsrc make_rsrc(const void *base, uint32_t bytes) {
+    // word 3 = 0x00020000: raw dword data format for the gfx9 family
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
+                                             0x00020000);
+}
+__device__ __forceinline__ u32x4 buf_load_nt16(buf_rsrc r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kBufNt);
+}
+__device__ __forceinline__ uint32_t buf_load_u8(buf_rsrc r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b8(r, off, 0, kBufNt);
+}
+
+// Reads through the constant address space become scalar loads when the
+// address is wavefront-uniform; they wait on the scalar counter and never on
+// the vector loads in flight. Only for data the kernel does not write.
+#define MOE_CONST __attribute__((address_space(4)))
+template <typename T>
+__device__ __forceinline__ const MOE_CONST T *as_scalar(const T *p) {
+    return (const MOE_CONST T *)(p);
+}
+
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) {
     return __builtin_bit_cast(bf16x8, v);
 }

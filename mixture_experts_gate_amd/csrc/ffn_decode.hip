@@ -34,9 +34,31 @@
 namespace moe {
 
 constexpr int kPass = 16;     // tokens per MFMA pass (one 16-column block)
+#ifndef MOE_DEC_DEPTH
+#define MOE_DEC_DEPTH 2
+#endif
+constexpr int kDepth = MOE_DEC_DEPTH;   // weight tiles held in registers (D - 1 in flight)
 
+// silu(g) * u with the hardware reciprocal (about 1 ulp) in place of a
+// correctly rounded division
 __device__ __forceinline__ float silu_mul(float g, float u) {
-    return g / (1.0f + __expf(-g)) * u;
+    return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
+}
+
+// Position of a tile: active expert a, tile rt within it; advanced by a
+// fixed stride of (sa, srt) tiles without divisions.
+struct TilePos {
+    int a, rt;
+};
+
+__device__ __forceinline__ TilePos advance(TilePos p, int sa, int srt, int nrt) {
+    p.a += sa;
+    p.rt += srt;
+    if (p.rt >= nrt) {
+        p.rt -= nrt;
+        p.a += 1;
+    }
+    return p;
 }
 
 // One lane's weights for one 32-element K block of one row.
@@ -51,16 +73,12 @@ struct WFrag<MOE_W_MXFP4> {
     // hoisting every decoded fragment out of the token-pass loop.
     __device__ __forceinline__ void pin() { asm volatile("" : "+v"(q), "+v"(s)); }
     // kernel layout: block `chunk` = (row block, 128-column slab); lane l's
-    // 16 code bytes and scale byte sit at lane-contiguous positions
-    __device__ __forceinline__ void load_block(const uint8_t *codes, const uint8_t *scales,
-                                               size_t chunk, int lane, bool ok) {
-        if (ok) {
-            q = load_nt16(codes + chunk * 1024 + lane * 16);
-            s = load_u8(scales + chunk * 64 + lane);
-        } else {
-            q = u32x4{0, 0, 0, 0};
-            s = 127;
-        }
+    // 16 code bytes and scale byte sit at lane-contiguous positions. Always
+    // issued; !ok loads zeros (codes 0 decode to 0 under any scale).
+    __device__ __forceinline__ void load_block(buf_rsrc codes, buf_rsrc scales, uint32_t chunk,
+                                               int lane, bool ok) {
+        q = buf_load_nt16(codes, ok ? chunk * 1024u + lane * 16 : kBufOff);
+        s = buf_load_u8(scales, ok ? chunk * 64u + lane : kBufOff);
     }
     __device__ __forceinline__ bf16x8 get(int j) const { return dequant8_fp4(q[j], e8m0_to_f32(s)); }
 };
@@ -138,10 +156,12 @@ struct DecArgs {
     int k, K, H, I, E, nrt;         // nrt: tiles per expert
 };
 
-// Expert-level state of the tile being processed.
+// Expert-level state of the tile being processed (wavefront-uniform: read
+// with scalar loads, so fetching it never waits for the weights in flight).
 struct ExpertState {
     int a, e, row0, n_e;
     const uint8_t *w, *s;           // matrix base (W13 or W2) and its scales
+    buf_rsrc wr, sr;                // the same as ranged buffer resources (MXFP4)
 };
 
 template <int STAGE>
@@ -149,11 +169,15 @@ __device__ __forceinline__ void expert_state(const DecArgs &A, const ActiveSet &
                                              ExpertState &st) {
     st.a = a;
     st.e = act.nth(a);
-    st.row0 = A.offsets[st.e];
-    st.n_e = A.offsets[st.e + 1] - st.row0;
-    const moe_expert_w W = A.experts[st.e];
-    st.w = reinterpret_cast<const uint8_t *>(STAGE == 1 ? W.w13 : W.w2);
-    st.s = STAGE == 1 ? W.s13 : W.s2;
+    const MOE_CONST int32_t *off = as_scalar(A.offsets);
+    st.row0 = off[st.e];
+    st.n_e = off[st.e + 1] - st.row0;
+    const MOE_CONST moe_expert_w *W = as_scalar(A.experts) + st.e;
+    st.w = reinterpret_cast<const uint8_t *>(STAGE == 1 ? W->w13 : W->w2);
+    st.s = reinterpret_cast<const uint8_t *>(STAGE == 1 ? W->s13 : W->s2);
+    const uint32_t elems = (uint32_t)(STAGE == 1 ? 2 * A.I : A.H) * (uint32_t)A.K;
+    st.wr = make_rsrc(st.w, elems / 2);
+    st.sr = make_rsrc(st.s, elems / 32);
 }
 
 // 16-row block index (within the stage's matrix) of block b of tile rt.
@@ -168,9 +192,10 @@ __device__ __forceinline__ long tile_block(const DecArgs &A, int rt, int b) {
 }
 
 // FULL: the KS wavefronts x SPW slabs cover the K slabs exactly (no bounds checks).
+// `on` = false issues the same loads switched off (MXFP4; see buf_rsrc).
 template <int FMT, int STAGE, int SPW, int NB, bool FULL>
 __device__ __forceinline__ void load_tile(const DecArgs &A, const ExpertState &st, int rt, int wv,
-                                          int lane, WFrag<FMT> (&f)[SPW][NB]) {
+                                          int lane, WFrag<FMT> (&f)[SPW][NB], bool on = true) {
     if constexpr (FMT == MOE_W_MXFP4) {
         const int nslab = A.K / 128;
 #pragma unroll
@@ -179,11 +204,12 @@ __device__ __forceinline__ void load_tile(const DecArgs &A, const ExpertState &s
 #pragma unroll
             for (int s = 0; s < SPW; ++s) {
                 const int slab = wv * SPW + s;
-                f[s][b].load_block(st.w, st.s, (size_t)rb * nslab + slab, lane,
-                                   FULL || slab < nslab);
+                f[s][b].load_block(st.wr, st.sr, (uint32_t)(rb * nslab + slab), lane,
+                                   on && (FULL || slab < nslab));
             }
         }
     } else {
+        if (!on) return;
         const int nblk = A.K / 32, m = lane & 15, c = lane >> 4;
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
@@ -208,7 +234,13 @@ __device__ __forceinline__ void load_tokens(const DecArgs &A, const ExpertState 
     const bool has = r < st.n_e;
     const uint16_t *row;
     if (STAGE == 1) {
-        row = A.src + (size_t)(has ? A.sorted_pair[st.row0 + r] / A.k : 0) * A.K;
+        // the pass's 16 pair indices by scalar loads; lane m takes the m-th
+        const MOE_CONST int32_t *sp = as_scalar(A.sorted_pair) + st.row0 + p * kPass;
+        int pair = 0;
+#pragma unroll
+        for (int i = 0; i < kPass; ++i)
+            if (p * kPass + i < st.n_e) pair = m == i ? sp[i] : pair;
+        row = A.src + (size_t)(pair / A.k) * A.K;
     } else {
         row = A.src + (size_t)(st.row0 + (has ? r : 0)) * A.K;
         pidx = has ? A.sorted_pair[st.row0 + r] : 0;
@@ -225,28 +257,28 @@ __device__ __forceinline__ void load_tokens(const DecArgs &A, const ExpertState 
 
 // One tile: token operand if the expert changed, prefetch of the next tile's
 // weights into `wn`, multiply from `wc`, K-split reduction, epilogue.
-template <int FMT, int STAGE, int SPW, int KS, int NB, bool YF32, bool FULL>
+template <int FMT, int STAGE, int SPW, int KS, int NB, bool YF32, bool FULL, int D>
 __device__ __forceinline__ void dec_step(const DecArgs &A, const ActiveSet &act,
                                          float (&red)[2][KS > 1 ? KS - 1 : 1][NB][4][kWave],
                                          WFrag<FMT> (&wc)[SPW][NB], WFrag<FMT> (&wn)[SPW][NB],
-                                         u32x4 (&xr)[SPW][4], ExpertState &cur, ExpertState &nxt,
-                                         int &pidx, int &x_key, int &buf, long t, long ts,
-                                         long t1, int lane, int wv, int m, int c) {
+                                         u32x4 (&xr)[SPW][4], const ExpertState &cur,
+                                         const ExpertState &prev, ExpertState &nxt,
+                                         int &pidx, int &x_key, int &buf, int rt, TilePos pn,
+                                         bool pf, int lane, int wv, int m, int c) {
 
-        const int rt = (int)(t % A.nrt);
         // token operand for the first pass of this tile (loaded before the next
         // prefetch, so that waiting for it does not wait for the prefetched weights)
         if (x_key != cur.a * 4096) {
             load_tokens<STAGE, SPW>(A, cur, 0, wv, m, c, xr, pidx);
             x_key = cur.a * 4096;
         }
-        const bool more = t + ts < t1;
-        if (more) {
-            const int an = (int)((t + ts) / A.nrt);
-            if (an != cur.a) expert_state<STAGE>(A, act, an, nxt);
-            else nxt = cur;
-            load_tile<FMT, STAGE, SPW, NB, FULL>(A, nxt, (int)((t + ts) % A.nrt), wv, lane, wn);
-        }
+        // prefetch the tile D - 1 steps ahead (position pn, present if pf);
+        // `prev` holds the state of the tile before it. Issued, switched off,
+        // also past the end (see buf_rsrc).
+        const int an = pf ? pn.a : prev.a;
+        if (an != prev.a) expert_state<STAGE>(A, act, an, nxt);
+        else nxt = prev;
+        load_tile<FMT, STAGE, SPW, NB, FULL>(A, nxt, pf ? pn.rt : 0, wv, lane, wn, pf);
         for (int p = 0; p * kPass < cur.n_e; ++p) {
             if (p > 0) {   // more than 16 tokens: next 16 of this expert
                 load_tokens<STAGE, SPW>(A, cur, p, wv, m, c, xr, pidx);
@@ -319,8 +351,6 @@ __device__ __forceinline__ void dec_step(const DecArgs &A, const ActiveSet &act,
             }
             buf ^= 1;
         }
-        if (more) cur = nxt;
-    
 }
 
 template <int FMT, int STAGE, int SPW, int KS, int NB, bool YF32, bool FULL>
@@ -338,39 +368,59 @@ __global__ __launch_bounds__(kWave *KS) void ffn_dec_kernel(DecArgs A) {
     // b + g, b + 2g, .. (g workgroups), so the tiles of the few experts with
     // many rows (skewed popularity) spread over many workgroups instead of
     // stretching the ones that hold them.
-    const long total = (long)act.count * A.nrt;
-    long t0, t1, ts;
+    const int total = act.count * A.nrt;
+    int t0, n, ts;
     if (act.multi_pass) {
         t0 = blockIdx.x;
-        t1 = total;
         ts = gridDim.x;
+        n = t0 < total ? (total - t0 + ts - 1) / ts : 0;
     } else {
-        t0 = (long)blockIdx.x * total / gridDim.x;
-        t1 = ((long)blockIdx.x + 1) * total / gridDim.x;
+        t0 = (int)((long)blockIdx.x * total / gridDim.x);
+        n = (int)(((long)blockIdx.x + 1) * total / gridDim.x) - t0;
         ts = 1;
     }
-    if (t0 >= t1) return;
+    if (n <= 0) return;
+    const int sa = ts / A.nrt, srt = ts % A.nrt;
 
-    ExpertState cur, nxt;
-    expert_state<STAGE>(A, act, (int)(t0 / A.nrt), cur);
-    // two register buffers used in turn: tile t computes from one while tile
-    // t+1's weights land in the other (no copy between them, so nothing waits
-    // for the prefetch before it is needed)
-    WFrag<FMT> wa[SPW][NB], wb[SPW][NB];
-    load_tile<FMT, STAGE, SPW, NB, FULL>(A, cur, (int)(t0 % A.nrt), wv, lane, wa);
-
+    // D register buffers used in turn: tile i computes from one while the
+    // weights of tiles i+1 .. i+D-1 are in flight into the others (no copies
+    // between them, so nothing waits for a prefetch before it is needed).
+    // Slots past the end repeat the last tile's position and load nothing.
+    constexpr int D = kDepth;
+    ExpertState es[D];
+    TilePos pos[D];
+    WFrag<FMT> wr[D][SPW][NB];
+    pos[0] = TilePos{t0 / A.nrt, t0 % A.nrt};
+    expert_state<STAGE>(A, act, pos[0].a, es[0]);
+#pragma unroll
+    for (int d = 1; d < D - 1; ++d) {
+        pos[d] = d < n ? advance(pos[d - 1], sa, srt, A.nrt) : pos[d - 1];
+        if (pos[d].a == es[d - 1].a) es[d] = es[d - 1];
+        else expert_state<STAGE>(A, act, pos[d].a, es[d]);
+    }
+    // the first tile's token operand is requested before any weights, so that
+    // resolving its row indices does not wait behind the weight prefetch
     u32x4 xr[SPW][4];
     int pidx = 0;
-    int x_key = -1;
+    load_tokens<STAGE, SPW>(A, es[0], 0, wv, m, c, xr, pidx);
+    int x_key = es[0].a * 4096;
     int buf = 0;
+#pragma unroll
+    for (int d = 0; d < D - 1; ++d)
+        load_tile<FMT, STAGE, SPW, NB, FULL>(A, es[d], pos[d].rt, wv, lane, wr[d], d < n);
 
-    for (long t = t0; t < t1; t += 2 * ts) {
-        dec_step<FMT, STAGE, SPW, KS, NB, YF32, FULL>(A, act, red, wa, wb, xr, cur, nxt, pidx,
-                                                      x_key, buf, t, ts, t1, lane, wv, m, c);
-        if (t + ts < t1)
-            dec_step<FMT, STAGE, SPW, KS, NB, YF32, FULL>(A, act, red, wb, wa, xr, cur, nxt, pidx,
-                                                          x_key, buf, t + ts, ts, t1, lane, wv, m,
-                                                          c);
+    for (int i = 0; i < n; i += D) {
+#pragma unroll
+        for (int d = 0; d < D; ++d) {
+            if (i + d < n) {
+                const int fd = (d + D - 1) % D, pd = (d + D - 2) % D;
+                const bool pf = i + d + D - 1 < n;
+                pos[fd] = pf ? advance(pos[pd], sa, srt, A.nrt) : pos[pd];
+                dec_step<FMT, STAGE, SPW, KS, NB, YF32, FULL, D>(
+                    A, act, red, wr[d], wr[fd], xr, es[d], es[pd], es[fd], pidx, x_key, buf,
+                    pos[d].rt, pos[fd], pf, lane, wv, m, c);
+            }
+        }
     }
 }
 
@@ -398,11 +448,15 @@ static unsigned resident_grid(K kernel, int threads) {
     return (unsigned)(per_cu * num_cus());
 }
 
+#ifndef MOE_DEC_WG_PER_CU
+#define MOE_DEC_WG_PER_CU 0
+#endif
 template <int FMT, int STAGE, int SPW, int KS, int NB, bool YF32, bool FULL>
 static int launch_dec(hipStream_t s, DecArgs A, long slots) {
     static unsigned full = 0;
     if (!full)
-        full = resident_grid(ffn_dec_kernel<FMT, STAGE, SPW, KS, NB, YF32, FULL>, kWave * KS);
+        full = MOE_DEC_WG_PER_CU ? MOE_DEC_WG_PER_CU * num_cus()
+                                 : resident_grid(ffn_dec_kernel<FMT, STAGE, SPW, KS, NB, YF32, FULL>, kWave * KS);
     // tiles per expert
     A.nrt = STAGE == 1 ? A.I / (8 * NB) : A.H / (16 * NB);
     const long max_tiles = slots * A.nrt;
