@@ -98,6 +98,7 @@ class MoeLayer:
             self.ws_sh = torch.empty(fbs, dtype=torch.uint8, device=dev)
             self.y_sh = torch.empty((T_max, H), dtype=ydt, device=dev)
         self._sh_T = -1
+        self._side = None       # stream of the shared expert (default priority)
 
     # individual stages ----------------------------------------------------
     def route(self, T, x=None, wg=None, logits=None, renormalize=True, stream=None,
@@ -133,6 +134,21 @@ class MoeLayer:
         small batches) instead of the two separate calls."""
         if T > self.T_max:
             raise ValueError("T exceeds the buffers' T_max")
+        if shared_table is not None:
+            # the shared expert needs only x: it runs on a side stream, forked
+            # before routing and joined before the combine, so that it overlaps
+            # routing and the routed experts
+            if self._sh_T != T:
+                self.prepare_shared(T)
+            main = stream if stream is not None else torch.cuda.current_stream()
+            if self._side is None:
+                self._side = torch.cuda.Stream(device=main.device)
+                self._fork = torch.cuda.Event()
+                self._join = torch.cuda.Event()
+            self._fork.record(main)
+            self._side.wait_event(self._fork)
+            self.shared_ffn(T, x, shared_table, self._side)
+            self._join.record(self._side)
         wl = write_logits or logits is None
         if fused_routing:
             self.route_permute(T, x=x, wg=wg, logits=logits, renormalize=renormalize,
@@ -143,9 +159,7 @@ class MoeLayer:
             self.permute(T, stream)
         self.ffn(T, x, table, stream)
         if shared_table is not None:
-            if self._sh_T != T:
-                self.prepare_shared(T)
-            self.shared_ffn(T, x, shared_table, stream)
+            main.wait_event(self._join)
         self.combine(T, with_shared=shared_table is not None, stream=stream)
         return self.out[:T]
 

@@ -195,7 +195,8 @@ def _perm_case(T, E, k, kind, seed=0):
 PERM_CASES = [(1, 128, 8, "uniform"), (8, 128, 8, "uniform"), (64, 128, 8, "uniform"),
               (16, 8, 2, "uniform"), (500, 256, 6, "skew"), (513, 512, 4, "uniform"),
               (4096, 256, 6, "uniform"), (8192, 128, 8, "uniform"), (6000, 64, 3, "skew"),
-              (1, 1, 1, "uniform"), (3, 7, 7, "uniform")]
+              (1, 1, 1, "uniform"), (3, 7, 7, "uniform"), (33, 128, 8, "uniform"),
+              (48, 64, 4, "skew"), (64, 512, 6, "skew")]
 
 
 @pytest.mark.parametrize("T,E,k,kind", PERM_CASES)
