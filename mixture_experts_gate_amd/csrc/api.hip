@@ -82,15 +82,15 @@ int ffn_prefill(const uint16_t *x, const int32_t *sorted_pair, const int32_t *of
                 const moe_expert_w *experts, int fmt, int T, int k, int H, int I, int E, void *y,
                 int y_is_fp32, void *ws, hipStream_t s);
 bool ffn_prefill_supported(int fmt, int H, int I);
-size_t prefill_ws_bytes(long n_pairs, long T, int H, int I);
+size_t prefill_ws_bytes(long n_pairs, long T, int H, int I, int E);
 
 static size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 
 // Decode kernels keep the bf16 activation [n_pairs][I]; the tiled kernels the
 // two-term FP8 activation and token rows. Either may run, so the larger.
-size_t ffn_ws_bytes(long n_pairs, long T, int H, int I) {
+size_t ffn_ws_bytes(long n_pairs, long T, int H, int I, int E) {
     const size_t dec = align256((size_t)n_pairs * I * 2);
-    const size_t pre = prefill_ws_bytes(n_pairs, T, H, I);
+    const size_t pre = prefill_ws_bytes(n_pairs, T, H, I, E);
     return (dec > pre ? dec : pre) + 256;
 }
 
@@ -169,7 +169,7 @@ extern "C" int moe_workspace_size(int T, int k, int H, int I, int E, size_t *per
     if (T < 0 || k < 1 || E < 1 || H < 32 || I < 32) return MOE_EINVAL;
     const long n = (long)T * k;
     if (permute_bytes) *permute_bytes = permute_ws_bytes(n, E);
-    if (ffn_bytes) *ffn_bytes = ffn_ws_bytes(n, T, H, I);
+    if (ffn_bytes) *ffn_bytes = ffn_ws_bytes(n, T, H, I, E);
     return MOE_OK;
 }
 
@@ -184,7 +184,7 @@ extern "C" int moe_expert_ffn(const uint16_t *x_bf16, const int32_t *sorted_pair
     if (!x_bf16 || !sorted_pair || !offsets || !experts || !y || !ws) return MOE_EINVAL;
     const long n = (long)T * k;
     if (n > 0x7FFFFFFFL) return MOE_EINVAL;
-    if (ws_bytes < ffn_ws_bytes(n, T, H, I)) return MOE_EINVAL;
+    if (ws_bytes < ffn_ws_bytes(n, T, H, I, E)) return MOE_EINVAL;
     uint16_t *act = reinterpret_cast<uint16_t *>(ws);
     hipStream_t s = (hipStream_t)stream;
     if (use_prefill(n, E, fmt, H, I))

@@ -70,16 +70,15 @@ __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) {
     return __uint_as_float(b << 16);
 }
 
-// fp32 -> bf16, round to nearest even (NaN kept quiet).
-__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x7FFFFFu)) return (u >> 16) | 0x40u;
-    u += 0x7FFFu + ((u >> 16) & 1u);
-    return u >> 16;
+// Two fp32 -> two bf16 (lo in the low half), rounded to nearest even by the
+// gfx950 packed convert (v_cvt_pk_bf16_f32; NaN stays a quiet NaN).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    const bf16x2 v = {(__bf16)lo, (__bf16)hi};
+    return __builtin_bit_cast(uint32_t, v);
 }
 
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+    return pack_bf16x2(f, 0.0f) & 0xFFFFu;
 }
 
 // E8M0 scale byte -> fp32 multiplier 2^(s-127) (s = 0 gives the subnormal 2^-127).

@@ -37,7 +37,11 @@ constexpr int kPass = 16;     // tokens per MFMA pass (one 16-column block)
 #ifndef MOE_DEC_DEPTH
 #define MOE_DEC_DEPTH 2
 #endif
+#ifndef MOE_DEC_DEPTH2
+#define MOE_DEC_DEPTH2 MOE_DEC_DEPTH
+#endif
 constexpr int kDepth = MOE_DEC_DEPTH;   // weight tiles held in registers (D - 1 in flight)
+constexpr int kDepth2 = MOE_DEC_DEPTH2; // the same for stage 2
 
 // silu(g) * u with the hardware reciprocal (about 1 ulp) in place of a
 // correctly rounded division
@@ -386,7 +390,7 @@ __global__ __launch_bounds__(kWave *KS) void ffn_dec_kernel(DecArgs A) {
     // weights of tiles i+1 .. i+D-1 are in flight into the others (no copies
     // between them, so nothing waits for a prefetch before it is needed).
     // Slots past the end repeat the last tile's position and load nothing.
-    constexpr int D = kDepth;
+    constexpr int D = STAGE == 2 ? kDepth2 : kDepth;
     ExpertState es[D];
     TilePos pos[D];
     WFrag<FMT> wr[D][SPW][NB];

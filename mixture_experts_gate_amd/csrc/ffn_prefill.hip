@@ -48,8 +48,9 @@ constexpr int kLoShift = 5;       // lo term scale = hi scale / 2^5
 typedef __attribute__((ext_vector_type(8))) int i32x8;
 typedef __attribute__((ext_vector_type(4))) int i32x4;
 
+// silu(g) * u with the hardware reciprocal (about 1 ulp)
 __device__ __forceinline__ float silu_mul_p(float g, float u) {
-    return g / (1.0f + __expf(-g)) * u;
+    return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
 }
 
 // ---------------------------------------------------------- two-term FP8 --
@@ -94,10 +95,50 @@ __device__ __forceinline__ void split_quad(const float (&v)[4], float inv, uint3
 
 // Row split of bf16 rows [rows][K] into hi [rows][K], lo [rows][K] and hi
 // scale bytes [rows][K/32]. One thread per 32-element block.
+// Token-tile map of the tiled kernels: map[0] = M, the number of 128-token
+// tiles over all experts; map[1 + m] = e | (mt << 16) for the m-th tile in
+// expert order (tile mt of expert e). One 256-thread workgroup.
+__device__ void build_tile_map(const int32_t *__restrict__ offsets, int E,
+                               int32_t *__restrict__ map) {
+    __shared__ int wsum[4];
+    const int t = threadIdx.x, lane = lane_id(), w = t / kWave;
+    int run = 0;   // tiles of the experts before this chunk
+    for (int e0 = 0; e0 < E; e0 += 256) {
+        const int e = e0 + t;
+        const int tiles = e < E ? (offsets[e + 1] - offsets[e] + kPreTok - 1) / kPreTok : 0;
+        int incl = tiles;
+#pragma unroll
+        for (int d = 1; d < kWave; d <<= 1) {
+            const int o = __shfl_up(incl, d);
+            if (lane >= d) incl += o;
+        }
+        if (lane == kWave - 1) wsum[w] = incl;
+        __syncthreads();
+        int wbase = 0, total = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            wbase += i < w ? wsum[i] : 0;
+            total += wsum[i];
+        }
+        const int base = run + wbase + incl - tiles;
+        for (int mt = 0; mt < tiles; ++mt) map[1 + base + mt] = e | (mt << 16);
+        run += total;
+        __syncthreads();
+    }
+    if (t == 0) map[0] = run;
+}
+
+// The last workgroup (one past the row blocks) builds the token-tile map.
 __global__ __launch_bounds__(256) void split_rows_kernel(const uint16_t *__restrict__ src,
                                                          long nblk, uint8_t *__restrict__ hi,
                                                          uint8_t *__restrict__ lo,
-                                                         uint8_t *__restrict__ sc) {
+                                                         uint8_t *__restrict__ sc,
+                                                         const int32_t *__restrict__ offsets,
+                                                         int E, int32_t *__restrict__ map) {
+    if (blockIdx.x == gridDim.x - 1) {
+        build_tile_map(offsets, E, map);
+        return;
+    }
     const long b = (long)blockIdx.x * 256 + threadIdx.x;
     if (b >= nblk) return;
     u32x4 q[4];
@@ -143,44 +184,10 @@ struct PreArgs {
     const moe_expert_w *experts;
     void *out;                        // stage 2: y
     uint8_t *ohi, *olo, *osc;         // stage 1: activation hi/lo rows [n][I], scales [n][I/32]
+    const int32_t *tile_map;          // token-tile map (build_tile_map)
     int k, K, H, I, E;
     int ntiles_w;                     // weight tiles per expert
 };
-
-// Expert, token-tile and weight-tile of tile q (all lanes get the same) and
-// the total number of tiles. Returns false if q is past the last tile.
-__device__ __forceinline__ bool pre_find_tile(const PreArgs &A, long q, int &e, int &mt, int &nt,
-                                              long &total) {
-    const int lane = lane_id();
-    long base = 0;
-    e = -1;
-    for (int e0 = 0; e0 < A.E; e0 += kWave) {
-        const int ee = e0 + lane;
-        long mtiles = 0;
-        if (ee < A.E) mtiles = (A.offsets[ee + 1] - A.offsets[ee] + kPreTok - 1) / kPreTok;
-        const long tiles = mtiles * A.ntiles_w;
-        // inclusive prefix over the wavefront
-        long incl = tiles;
-#pragma unroll
-        for (int d = 1; d < kWave; d <<= 1) {
-            const long o = __shfl_up(incl, d);
-            if (lane >= d) incl += o;
-        }
-        const long excl = base + incl - tiles;
-        const bool hit = e < 0 && tiles > 0 && q >= excl && q < excl + tiles;
-        const uint64_t hm = __ballot(hit);
-        if (hm) {
-            const int src = __ffsll((long long)hm) - 1;
-            e = e0 + src;
-            const long local = q - __shfl(excl, src);
-            mt = (int)(local / A.ntiles_w);
-            nt = (int)(local - (long)mt * A.ntiles_w);
-        }
-        base += __shfl(incl, kWave - 1);
-    }
-    total = base;
-    return e >= 0;
-}
 
 // LDS of one slab stage (50176 bytes).
 //   tok   : [term hi/lo][16-token block] 16 rows x 128 bytes; the 16-byte chunk c
@@ -396,22 +403,36 @@ __global__ __launch_bounds__(kPreThreads) void ffn_pre_kernel(PreArgs A) {
     const int wv = __builtin_amdgcn_readfirstlane(tid / kWave);
     const int wm = wv & 3, wn = wv >> 2;     // token quarter (32 tokens), weight half
 
-    // total tiles, then this workgroup's tile (XCD-aware numbering)
-    int e, mt, nt;
-    long total;
-    pre_find_tile(A, 0, e, mt, nt, total);
+    // total tiles, then this workgroup's tile (XCD-aware numbering), from the
+    // token-tile map by scalar loads
+    const MOE_CONST int32_t *map = as_scalar(A.tile_map);
+    const long total = (long)map[0] * A.ntiles_w;
     const long per = (total + 7) / 8;
     const long q = (long)(blockIdx.x & 7) * per + (blockIdx.x >> 3);
     if ((long)(blockIdx.x >> 3) >= per || q >= total) return;
-    pre_find_tile(A, q, e, mt, nt, total);
+    const int m = (int)(q / A.ntiles_w);
+    const int nt = (int)(q - (long)m * A.ntiles_w);
+    const int md = map[1 + m];
+    const int e = md & 0xFFFF, mt = md >> 16;
 
-    const int row0 = A.offsets[e];
-    const int n_e = A.offsets[e + 1] - row0;
+    const MOE_CONST int32_t *offs = as_scalar(A.offsets);
+    const int row0 = offs[e];
+    const int n_e = offs[e + 1] - row0;
     const int tok0 = mt * kPreTok;
-    const moe_expert_w W = A.experts[e];
-    const uint8_t *wcodes = reinterpret_cast<const uint8_t *>(STAGE == 1 ? W.w13 : W.w2);
-    const uint8_t *wscales = STAGE == 1 ? W.s13 : W.s2;
+    const MOE_CONST moe_expert_w *W = as_scalar(A.experts) + e;
+    const uint8_t *wcodes = reinterpret_cast<const uint8_t *>(STAGE == 1 ? W->w13 : W->w2);
+    const uint8_t *wscales = reinterpret_cast<const uint8_t *>(STAGE == 1 ? W->s13 : W->s2);
     const int nslab = A.K / 128;
+    // stage 2: output rows (pair indices) of this lane's two tokens, loaded
+    // before the copies so that the epilogue does not wait for them
+    int prow_tb[2] = {0, 0};
+    if (STAGE == 2) {
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb) {
+            const int r = tok0 + 32 * wm + 16 * tb + (lane & 15);
+            prow_tb[tb] = r < n_e ? A.sorted_pair[row0 + r] : 0;
+        }
+    }
 
     PreSrc src;
     {
@@ -501,23 +522,30 @@ __global__ __launch_bounds__(kPreThreads) void ffn_pre_kernel(PreArgs A) {
             }
         }
     } else {
+        // all values packed before the first store (so no store's registers
+        // are reused, and waited for, while others are still being written)
+        uint2 pk[2][8];
+        if (!YF32) {
+#pragma unroll
+            for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+                for (int b = 0; b < 8; ++b) {
+                    pk[tb][b].x = pack_bf16x2(acc[b][tb][0], acc[b][tb][1]);
+                    pk[tb][b].y = pack_bf16x2(acc[b][tb][2], acc[b][tb][3]);
+                }
+        }
 #pragma unroll
         for (int tb = 0; tb < 2; ++tb) {
             const int r = tok0 + 32 * wm + 16 * tb + (lane & 15);
             if (r >= n_e) continue;
-            const size_t prow =
-                (size_t)A.sorted_pair[row0 + r] * A.H + nt * 256 + 128 * wn + 4 * g4;
+            const size_t prow = (size_t)prow_tb[tb] * A.H + nt * 256 + 128 * wn + 4 * g4;
 #pragma unroll
             for (int b = 0; b < 8; ++b) {
                 const size_t off = prow + 16 * b;
-                if (YF32) {
+                if (YF32)
                     *reinterpret_cast<f32x4 *>(reinterpret_cast<float *>(A.out) + off) = acc[b][tb];
-                } else {
-                    uint2 pk;
-                    pk.x = pack_bf16x2(acc[b][tb][0], acc[b][tb][1]);
-                    pk.y = pack_bf16x2(acc[b][tb][2], acc[b][tb][3]);
-                    *reinterpret_cast<uint2 *>(reinterpret_cast<uint16_t *>(A.out) + off) = pk;
-                }
+                else
+                    *reinterpret_cast<uint2 *>(reinterpret_cast<uint16_t *>(A.out) + off) = pk[tb][b];
             }
         }
     }
@@ -533,9 +561,13 @@ static size_t al256(size_t b) { return (b + 255) & ~(size_t)255; }
 
 // Workspace of the tiled path: the activation's two terms and scales
 // [n_pairs][I] and the token rows' [T][H].
-size_t prefill_ws_bytes(long n_pairs, long T, int H, int I) {
+static size_t tile_map_bytes(long n_pairs, int E) {
+    return al256(((size_t)n_pairs / kPreTok + E + 1) * sizeof(int32_t));
+}
+
+size_t prefill_ws_bytes(long n_pairs, long T, int H, int I, int E) {
     return 2 * al256((size_t)n_pairs * I) + al256((size_t)n_pairs * I / 32) +
-           2 * al256((size_t)T * H) + al256((size_t)T * H / 32);
+           2 * al256((size_t)T * H) + al256((size_t)T * H / 32) + tile_map_bytes(n_pairs, E);
 }
 
 template <int STAGE, bool YF32>
@@ -562,20 +594,21 @@ int ffn_prefill(const uint16_t *x, const int32_t *sorted_pair, const int32_t *of
     uint8_t *xhi = asc + al256((size_t)n * I / 32);
     uint8_t *xlo = xhi + al256((size_t)T * H);
     uint8_t *xsc = xlo + al256((size_t)T * H);
+    int32_t *map = reinterpret_cast<int32_t *>(xsc + al256((size_t)T * H / 32));
 
     const long nblk = (long)T * H / 32;
-    const long grid = (nblk + 255) / 256;
+    const long grid = (nblk + 255) / 256 + 1;   // + the tile-map workgroup
     if (grid > 0x7FFFFFFFL) return MOE_EUNSUPPORTED;
     MOE_LAUNCH(K_PRE_SPLIT, split_rows_kernel, dim3((unsigned)grid), dim3(256), 0, s, x, nblk,
-                                 xhi, xlo, xsc);
+                                 xhi, xlo, xsc, offsets, E, map);
     int rc = check_launch();
     if (rc) return rc;
 
-    PreArgs a1{xhi, xlo, xsc, sorted_pair, offsets, experts, nullptr, ahi, alo, asc,
+    PreArgs a1{xhi, xlo, xsc, sorted_pair, offsets, experts, nullptr, ahi, alo, asc, map,
                k, H, H, I, E, I / 128};
     rc = launch_pre<1, false>(s, a1, n);
     if (rc) return rc;
-    PreArgs a2{ahi, alo, asc, sorted_pair, offsets, experts, y, nullptr, nullptr, nullptr,
+    PreArgs a2{ahi, alo, asc, sorted_pair, offsets, experts, y, nullptr, nullptr, nullptr, map,
                k, I, H, I, E, H / 256};
     return y_is_fp32 ? launch_pre<2, true>(s, a2, n) : launch_pre<2, false>(s, a2, n);
 }

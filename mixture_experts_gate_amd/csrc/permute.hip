@@ -180,27 +180,41 @@ __global__ __launch_bounds__(kChunk) void permute_rank_kernel(
 
 // Large path, pass 2 (one workgroup): per expert, exclusive prefix over the
 // chunks; offsets by a scan of the expert totals; hist becomes the scatter base.
+// P = 1024 / E threads share an expert's column: each sums a contiguous run of
+// chunks (independent loads), the runs' totals are prefixed in LDS, then each
+// thread rewrites its run.
 __global__ __launch_bounds__(kChunk) void permute_scan_kernel(int nb, int E,
                                                               int32_t *__restrict__ hist,
                                                               int32_t *__restrict__ offsets) {
     __shared__ int tot[kMaxE];
     __shared__ int off[kMaxE + 1];
     __shared__ int scratch[32];
+    __shared__ int part[kChunk];
     const int tid = threadIdx.x;
-    for (int x = tid; x < E; x += kChunk) {
-        int run = 0;
-        for (int b = 0; b < nb; ++b) {
+    const int P = E < kChunk ? kChunk / E : 1;
+    const int x = tid / P, p = tid - x * P;
+    const int per = (nb + P - 1) / P;
+    const int b0 = min(nb, p * per), b1 = min(nb, b0 + per);
+    int sum = 0;
+    if (x < E)
+        for (int b = b0; b < b1; ++b) sum += hist[(size_t)b * E + x];
+    part[tid] = sum;
+    __syncthreads();
+    int pre = 0;                       // this run's exclusive prefix within the column
+    if (x < E)
+        for (int q = 0; q < p; ++q) pre += part[x * P + q];
+    if (x < E && p == P - 1) tot[x] = pre + sum;
+    __syncthreads();
+    block_exclusive_scan(tot, off, E, scratch);
+    for (int y = tid; y <= E; y += kChunk) offsets[y] = off[y];
+    if (x < E) {
+        int run = off[x] + pre;
+        for (int b = b0; b < b1; ++b) {
             const int c = hist[(size_t)b * E + x];
             hist[(size_t)b * E + x] = run;
             run += c;
         }
-        tot[x] = run;
     }
-    __syncthreads();
-    block_exclusive_scan(tot, off, E, scratch);
-    for (int x = tid; x <= E; x += kChunk) offsets[x] = off[x];
-    for (int x = tid; x < E; x += kChunk)
-        for (int b = 0; b < nb; ++b) hist[(size_t)b * E + x] += off[x];
 }
 
 // Large path, pass 3: scatter.

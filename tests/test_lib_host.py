@@ -54,8 +54,10 @@ def test_workspace_sizes(lib):
     pb, fb = lib.moe_workspace_size(8192, 8, 2048, 768, 128)
     assert pb >= (64 * 128 + 65536) * 4
     assert fb >= 65536 * 768 * 2
-    # tiled path: two FP8 terms + block scales of the activation and of x
-    assert fb >= 2 * 65536 * 768 + 65536 * 768 // 32 + 2 * 8192 * 2048 + 8192 * 2048 // 32
+    # tiled path: two FP8 terms + block scales of the activation and of x, and
+    # the token-tile map (at most n_pairs / 128 + E tiles)
+    assert fb >= (2 * 65536 * 768 + 65536 * 768 // 32 + 2 * 8192 * 2048 + 8192 * 2048 // 32
+                  + (65536 // 128 + 128 + 1) * 4)
     with pytest.raises(lib.MoeError):
         lib.moe_workspace_size(-1, 8, 2048, 768, 128)
 
