@@ -19,11 +19,12 @@
 // by a row pass; the activation a = silu(g) * u is split by the gate/up
 // kernel's epilogue as it is produced.
 //
-// Tile (one 512-thread workgroup: 8 wavefronts, two per SIMD, each 32 tokens x
-// 128 weight rows): 128 tokens x 256 weight rows of one expert over the full
-// contraction K, in 128-column slabs copied straight from global memory into a
-// 3-stage LDS ring (two slabs in flight while one is multiplied; one barrier
-// per slab). Every operand lands in LDS in the order the matrix core reads it,
+// Tile (one 256-thread workgroup: 4 wavefronts, one per SIMD, each 32 tokens x
+// 128 weight rows; two workgroups share a compute unit): 64 tokens x 256
+// weight rows of one expert over the full contraction K, in 128-column slabs
+// copied straight from global memory into a 2-stage LDS ring (one slab in
+// flight while one is multiplied; one barrier per slab). 64-token tiles halve
+// the padding of each expert's last tile. Every operand lands in LDS in the order the matrix core reads it,
 // so each fragment read is one contiguous 16-byte-per-lane LDS read:
 //   - weights (operand A, kernel MXFP4 layout): 16 row blocks of 16 rows x 128
 //     columns (1 KB codes + 64 B scales each), copied as they are;
@@ -41,8 +42,8 @@
 
 namespace moe {
 
-constexpr int kPreTok = 128;      // tokens per tile
-constexpr int kPreThreads = 512;
+constexpr int kPreTok = 64;       // tokens per tile
+constexpr int kPreThreads = 256;  // four wavefronts; two workgroups share a compute unit
 constexpr int kLoShift = 5;       // lo term scale = hi scale / 2^5
 
 typedef __attribute__((ext_vector_type(8))) int i32x8;
@@ -189,19 +190,20 @@ struct PreArgs {
     int ntiles_w;                     // weight tiles per expert
 };
 
-// LDS of one slab stage (50176 bytes).
+// LDS of one slab stage (34048 bytes; two stages per workgroup, so two
+// workgroups fit a compute unit's 160 KB).
 //   tok   : [term hi/lo][16-token block] 16 rows x 128 bytes; the 16-byte chunk c
 //           of row r sits at position c ^ ((r / 2) % 8), so the 16 lanes that
 //           read one chunk of 16 rows hit 16 different 16-byte bank groups;
-//   tsc   : the 128 tokens' 4 scale bytes of this slab;
+//   tsc   : the 64 tokens' 4 scale bytes of this slab;
 //   wcode / wscale: the tile's 16 weight blocks, kernel layout.
 struct PreStage {
-    uint8_t tok[2][8][2048];
+    uint8_t tok[2][4][2048];
     uint8_t wcode[16][1024];
     uint8_t tsc[kPreTok][4];
     uint8_t wscale[16][64];
 };
-constexpr int kPreStages = 3;     // computing s, landing s+1 and s+2
+constexpr int kPreStages = 2;     // computing s, landing s+1
 
 __device__ __forceinline__ int tok_swz(int r) { return (r >> 1) & 7; }
 
@@ -228,18 +230,14 @@ __device__ __forceinline__ void wait_vm() {
 // token row, s * 4 to a scale row, s * 1024 / s * 64 to a weight block).
 struct PreSrc {
     const uint8_t *thi[2], *tlo[2];   // token block w, rows 8u + lane/8: the lane's 16-byte chunk
-    const uint8_t *tsc;               // wavefronts 5, 6: scale row of token 64(w-5) + lane
-    const uint8_t *wc[2];             // blocks 2w, 2w+1: codes + 16 lane
-    const uint8_t *ws;                // wavefront 7: scales of block lane/4 + 16 (lane%4)
+    const uint8_t *tsc;               // wavefront 0: scale row of token lane
+    const uint8_t *wc[4];             // blocks 4w .. 4w+3: codes + 16 lane
+    const uint8_t *ws;                // wavefront 1: scales of block lane/4 + 16 (lane%4)
 };
 
-// Copies per slab issued by wavefront w (what its vmcnt waits count).
-__device__ __forceinline__ int pre_copies(int w) { return w >= 5 ? 7 : 6; }
-
-// This wavefront's copies of slab s into stage st (8 wavefronts): its token
-// block's two terms (8 rows x 128 bytes per copy), weight blocks 2w and 2w+1,
-// on wavefronts 5 and 6 half of the token scales, on wavefront 7 the 16 weight
-// blocks' scale rows.
+// This wavefront's copies of slab s into stage st (4 wavefronts): its token
+// block's two terms (8 rows x 128 bytes per copy), weight blocks 4w .. 4w+3,
+// on wavefront 0 the token scales, on wavefront 1 the 16 weight blocks' scale rows.
 __device__ __forceinline__ void pre_issue(PreStage &st, int s, int w, const PreSrc &p) {
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
@@ -247,9 +245,9 @@ __device__ __forceinline__ void pre_issue(PreStage &st, int s, int w, const PreS
         lds_dma16(p.tlo[u] + s * 128, &st.tok[1][w][u * 1024]);
     }
 #pragma unroll
-    for (int u = 0; u < 2; ++u) lds_dma16(p.wc[u] + (size_t)s * 1024, &st.wcode[2 * w + u][0]);
-    if (w == 5 || w == 6) lds_dma4(p.tsc + s * 4, &st.tsc[64 * (w - 5)][0]);
-    if (w == 7) lds_dma16(p.ws + (size_t)s * 64, &st.wscale[0][0]);
+    for (int u = 0; u < 4; ++u) lds_dma16(p.wc[u] + (size_t)s * 1024, &st.wcode[4 * w + u][0]);
+    if (w == 0) lds_dma4(p.tsc + s * 4, &st.tsc[0][0]);
+    if (w == 1) lds_dma16(p.ws + (size_t)s * 64, &st.wscale[0][0]);
 }
 
 // One slab's operands for one wavefront: its 8 weight blocks and its two
@@ -338,61 +336,25 @@ __device__ __forceinline__ void bare_barrier() {
     asm volatile("" ::: "memory");
 }
 
-// Ping-pong schedule. The two wavefronts of a SIMD belong to different
-// groups (waves 0-3 and 4-7) that run half a period apart: while one issues
-// a slab's 32 MFMAs (C), the other issues its copies and LDS reads (M), so
-// the matrix core always has work. With half-periods h = 0, 1, ..:
-//   group 0: M(j) at h = 2j, C(j) at h = 2j + 1
-//   group 1: M(j) at h = 2j + 1, C(j) at h = 2j + 2
-// M(j) reads slab j into registers and, for j >= 1, issues this wavefront's
-// copies of slab j + 2 into the stage slab j - 1 came from (both groups have
-// read slab j - 1 by then). A barrier ends every half-period up to 2n - 2;
-// before the one ending h = 2j + 1 every wavefront has seen its copies of
-// slab j + 1 land (group 0 reads it next) and group 1 has its reads of slab j
-// back (the stage is refilled after it).
-template <int STAGE, int GRP>
+// Double-buffered slab loop; slab j sits in stage j % 2. At the top of slab j
+// this wavefront's copies of slab j have landed (they are the only ones in
+// flight), and after the barrier every wavefront's have, and every wavefront
+// has finished reading slab j - 1, whose stage then receives slab j + 1. The
+// two workgroups on a compute unit interleave: one's copies, fragment reads
+// and barrier waits overlap the other's matrix instructions.
+template <int STAGE>
 __device__ __forceinline__ void pre_mainloop(PreStage (&lds)[kPreStages], f32x4 (&acc)[8][2],
                                              int n, int wv, int wm, int wn, int lane,
                                              const PreSrc &src) {
     PreFrag F;
     const TokPos tp(lane);
-    auto wait_next = [&](int j) {            // end of h = 2j + 1: slab j + 1 landed
-        if (j + 2 < n) {
-            if (pre_copies(wv) == 7) wait_vm<7>();
-            else wait_vm<6>();
-        } else {
-            wait_vm<0>();
-        }
-    };
-    if (GRP == 0) pre_read<STAGE>(lds[0], F, wm, wn, lane, tp);    // M(0)
-    bare_barrier();                                                  // end of h = 0
-    int st = 0;                               // stage of slab j
     for (int j = 0; j < n; ++j) {
-        const int st1 = st == kPreStages - 1 ? 0 : st + 1;
-        const int st2 = st1 == kPreStages - 1 ? 0 : st1 + 1;       // stage of slab j + 2
-        if (GRP == 0) {
-            pre_math(F, acc);                                        // C(j), h = 2j + 1
-            if (j + 1 < n) {
-                wait_next(j);
-                bare_barrier();
-                // M(j + 1), h = 2j + 2: slab j + 3 goes where slab j was
-                if (j + 3 < n) pre_issue(lds[st], j + 3, wv, src);
-                pre_read<STAGE>(lds[st1], F, wm, wn, lane, tp);
-                bare_barrier();
-            }
-        } else {
-            // M(j), h = 2j + 1
-            if (j >= 1 && j + 2 < n) pre_issue(lds[st2], j + 2, wv, src);
-            pre_read<STAGE>(lds[st], F, wm, wn, lane, tp);
-            __builtin_amdgcn_s_waitcnt(0xC07F);                      // lgkmcnt(0)
-            if (j + 1 < n) {
-                wait_next(j);
-                bare_barrier();
-            }
-            pre_math(F, acc);                                        // C(j), h = 2j + 2
-            if (j + 1 < n) bare_barrier();
-        }
-        st = st1;
+        const int st = j & 1;
+        wait_vm<0>();
+        bare_barrier();
+        if (j + 1 < n) pre_issue(lds[st ^ 1], j + 1, wv, src);
+        pre_read<STAGE>(lds[st], F, wm, wn, lane, tp);
+        pre_math(F, acc);
     }
 }
 
@@ -401,7 +363,7 @@ __global__ __launch_bounds__(kPreThreads) void ffn_pre_kernel(PreArgs A) {
     __shared__ __attribute__((aligned(16))) PreStage lds[kPreStages];
     const int tid = threadIdx.x, lane = lane_id();
     const int wv = __builtin_amdgcn_readfirstlane(tid / kWave);
-    const int wm = wv & 3, wn = wv >> 2;     // token quarter (32 tokens), weight half
+    const int wm = wv & 1, wn = wv >> 1;     // token half (32 tokens), weight half
 
     // total tiles, then this workgroup's tile (XCD-aware numbering), from the
     // token-tile map by scalar loads
@@ -449,10 +411,10 @@ __global__ __launch_bounds__(kPreThreads) void ffn_pre_kernel(PreArgs A) {
             src.thi[u] = A.bhi + row * A.K + 16 * chunk;
             src.tlo[u] = A.blo + row * A.K + 16 * chunk;
         }
-        src.tsc = A.bsc + token_row(tok0 + 64 * (wv == 6 ? 1 : 0) + lane) * (A.K / 32);
+        src.tsc = A.bsc + token_row(tok0 + lane) * (A.K / 32);
 #pragma unroll
-        for (int u = 0; u < 2; ++u)
-            src.wc[u] = wcodes + (size_t)pre_block<STAGE>(A, nt, 2 * wv + u) * nslab * 1024 +
+        for (int u = 0; u < 4; ++u)
+            src.wc[u] = wcodes + (size_t)pre_block<STAGE>(A, nt, 4 * wv + u) * nslab * 1024 +
                         16 * lane;
         src.ws = wscales + (size_t)pre_block<STAGE>(A, nt, lane >> 2) * nslab * 64 +
                  16 * (lane & 3);
@@ -464,19 +426,8 @@ __global__ __launch_bounds__(kPreThreads) void ffn_pre_kernel(PreArgs A) {
 #pragma unroll
         for (int tb = 0; tb < 2; ++tb) acc[b][tb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
-    for (int i = 0; i < kPreStages && i < nslab; ++i) pre_issue(lds[i], i, wv, src);
-    // slab 0 landed: the later prologue slabs' copies may remain
-    const int later = nslab - 1 < kPreStages - 1 ? nslab - 1 : kPreStages - 1;
-    const int n_later = later * pre_copies(wv);
-    if (n_later == 0) wait_vm<0>();
-    else if (n_later == 6) wait_vm<6>();
-    else if (n_later == 7) wait_vm<7>();
-    else if (n_later == 12) wait_vm<12>();
-    else wait_vm<14>();
-    bare_barrier();
-
-    if (wv < 4) pre_mainloop<STAGE, 0>(lds, acc, nslab, wv, wm, wn, lane, src);
-    else pre_mainloop<STAGE, 1>(lds, acc, nslab, wv, wm, wn, lane, src);
+    pre_issue(lds[0], 0, wv, src);
+    pre_mainloop<STAGE>(lds, acc, nslab, wv, wm, wn, lane, src);
 
     // epilogue: for token block tb the lane holds token 32wm + 16tb + lane%16 and,
     // in weight block b, rows 4(lane/16) + i (i < 4) of the block
