@@ -188,6 +188,7 @@ struct PreArgs {
     const int32_t *tile_map;          // token-tile map (build_tile_map)
     int k, K, H, I, E;
     int ntiles_w;                     // weight tiles per expert
+    int nt_group;                     // consecutive weight tiles per workgroup (divides ntiles_w)
 };
 
 // LDS of one slab stage (34048 bytes; two stages per workgroup, so two
@@ -238,16 +239,20 @@ struct PreSrc {
 // This wavefront's copies of slab s into stage st (4 wavefronts): its token
 // block's two terms (8 rows x 128 bytes per copy), weight blocks 4w .. 4w+3,
 // on wavefront 0 the token scales, on wavefront 1 the 16 weight blocks' scale rows.
-__device__ __forceinline__ void pre_issue(PreStage &st, int s, int w, const PreSrc &p) {
+// woff: byte offset of this weight tile's codes from the group's first tile's
+// (its scales sit at woff / 16).
+__device__ __forceinline__ void pre_issue(PreStage &st, int s, int w, const PreSrc &p,
+                                          size_t woff) {
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
         lds_dma16(p.thi[u] + s * 128, &st.tok[0][w][u * 1024]);
         lds_dma16(p.tlo[u] + s * 128, &st.tok[1][w][u * 1024]);
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u) lds_dma16(p.wc[u] + (size_t)s * 1024, &st.wcode[4 * w + u][0]);
+    for (int u = 0; u < 4; ++u)
+        lds_dma16(p.wc[u] + woff + (size_t)s * 1024, &st.wcode[4 * w + u][0]);
     if (w == 0) lds_dma4(p.tsc + s * 4, &st.tsc[0][0]);
-    if (w == 1) lds_dma16(p.ws + (size_t)s * 64, &st.wscale[0][0]);
+    if (w == 1) lds_dma16(p.ws + woff / 16 + (size_t)s * 64, &st.wscale[0][0]);
 }
 
 // One slab's operands for one wavefront: its 8 weight blocks and its two
@@ -336,101 +341,39 @@ __device__ __forceinline__ void bare_barrier() {
     asm volatile("" ::: "memory");
 }
 
-// Double-buffered slab loop; slab j sits in stage j % 2. At the top of slab j
-// this wavefront's copies of slab j have landed (they are the only ones in
-// flight), and after the barrier every wavefront's have, and every wavefront
-// has finished reading slab j - 1, whose stage then receives slab j + 1. The
-// two workgroups on a compute unit interleave: one's copies, fragment reads
-// and barrier waits overlap the other's matrix instructions.
+// Double-buffered slab loop over one weight tile; the ring runs on across the
+// workgroup's tiles, slab g (counted over the group) sitting in stage g % 2.
+// At the top of a slab this wavefront's copies of it have landed (they are
+// the only loads in flight), and after the barrier every wavefront's have, and
+// every wavefront has finished reading the previous slab, whose stage then
+// receives the next one (the next tile's first slab after a tile's last). The
+// two workgroups on a compute unit interleave: one's copies, fragment reads,
+// barrier waits and epilogue overlap the other's matrix instructions.
 template <int STAGE>
 __device__ __forceinline__ void pre_mainloop(PreStage (&lds)[kPreStages], f32x4 (&acc)[8][2],
-                                             int n, int wv, int wm, int wn, int lane,
-                                             const PreSrc &src) {
+                                             int n, int g0, int wv, int wm, int wn, int lane,
+                                             const PreSrc &src, size_t woff, size_t woff_next,
+                                             bool has_next) {
     PreFrag F;
     const TokPos tp(lane);
     for (int j = 0; j < n; ++j) {
-        const int st = j & 1;
+        const int st = (g0 + j) & 1;
         wait_vm<0>();
         bare_barrier();
-        if (j + 1 < n) pre_issue(lds[st ^ 1], j + 1, wv, src);
+        if (j + 1 < n) pre_issue(lds[st ^ 1], j + 1, wv, src, woff);
+        else if (has_next) pre_issue(lds[st ^ 1], 0, wv, src, woff_next);
         pre_read<STAGE>(lds[st], F, wm, wn, lane, tp);
         pre_math(F, acc);
     }
 }
 
+// Epilogue of weight tile nt: for token block tb the lane holds token
+// 32wm + 16tb + lane%16 and, in weight block b, rows 4(lane/16) + i (i < 4) of
+// the block.
 template <int STAGE, bool YF32>
-__global__ __launch_bounds__(kPreThreads) void ffn_pre_kernel(PreArgs A) {
-    __shared__ __attribute__((aligned(16))) PreStage lds[kPreStages];
-    const int tid = threadIdx.x, lane = lane_id();
-    const int wv = __builtin_amdgcn_readfirstlane(tid / kWave);
-    const int wm = wv & 1, wn = wv >> 1;     // token half (32 tokens), weight half
-
-    // total tiles, then this workgroup's tile (XCD-aware numbering), from the
-    // token-tile map by scalar loads
-    const MOE_CONST int32_t *map = as_scalar(A.tile_map);
-    const long total = (long)map[0] * A.ntiles_w;
-    const long per = (total + 7) / 8;
-    const long q = (long)(blockIdx.x & 7) * per + (blockIdx.x >> 3);
-    if ((long)(blockIdx.x >> 3) >= per || q >= total) return;
-    const int m = (int)(q / A.ntiles_w);
-    const int nt = (int)(q - (long)m * A.ntiles_w);
-    const int md = map[1 + m];
-    const int e = md & 0xFFFF, mt = md >> 16;
-
-    const MOE_CONST int32_t *offs = as_scalar(A.offsets);
-    const int row0 = offs[e];
-    const int n_e = offs[e + 1] - row0;
-    const int tok0 = mt * kPreTok;
-    const MOE_CONST moe_expert_w *W = as_scalar(A.experts) + e;
-    const uint8_t *wcodes = reinterpret_cast<const uint8_t *>(STAGE == 1 ? W->w13 : W->w2);
-    const uint8_t *wscales = reinterpret_cast<const uint8_t *>(STAGE == 1 ? W->s13 : W->s2);
-    const int nslab = A.K / 128;
-    // stage 2: output rows (pair indices) of this lane's two tokens, loaded
-    // before the copies so that the epilogue does not wait for them
-    int prow_tb[2] = {0, 0};
-    if (STAGE == 2) {
-#pragma unroll
-        for (int tb = 0; tb < 2; ++tb) {
-            const int r = tok0 + 32 * wm + 16 * tb + (lane & 15);
-            prow_tb[tb] = r < n_e ? A.sorted_pair[row0 + r] : 0;
-        }
-    }
-
-    PreSrc src;
-    {
-        auto token_row = [&](int r) -> long {   // operand row of tile row r
-            r = r < n_e ? r : n_e - 1;             // rows past the expert's end repeat its last row
-            return STAGE == 1 ? (long)(A.sorted_pair[row0 + r] / A.k) : (long)(row0 + r);
-        };
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            // token block wv, row 8u + lane/8; lane position lane%8 holds chunk pos ^ swizzle
-            const int rb = 8 * u + (lane >> 3);
-            const long row = token_row(tok0 + 16 * wv + rb);
-            const int chunk = (lane & 7) ^ tok_swz(rb);
-            src.thi[u] = A.bhi + row * A.K + 16 * chunk;
-            src.tlo[u] = A.blo + row * A.K + 16 * chunk;
-        }
-        src.tsc = A.bsc + token_row(tok0 + lane) * (A.K / 32);
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-            src.wc[u] = wcodes + (size_t)pre_block<STAGE>(A, nt, 4 * wv + u) * nslab * 1024 +
-                        16 * lane;
-        src.ws = wscales + (size_t)pre_block<STAGE>(A, nt, lane >> 2) * nslab * 64 +
-                 16 * (lane & 3);
-    }
-
-    f32x4 acc[8][2];
-#pragma unroll
-    for (int b = 0; b < 8; ++b)
-#pragma unroll
-        for (int tb = 0; tb < 2; ++tb) acc[b][tb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-
-    pre_issue(lds[0], 0, wv, src);
-    pre_mainloop<STAGE>(lds, acc, nslab, wv, wm, wn, lane, src);
-
-    // epilogue: for token block tb the lane holds token 32wm + 16tb + lane%16 and,
-    // in weight block b, rows 4(lane/16) + i (i < 4) of the block
+__device__ __forceinline__ void pre_epilogue(const PreArgs &A, const f32x4 (&acc)[8][2], int nt,
+                                             int tok0, int row0, int n_e, int wm, int wn,
+                                             int lane, const int (&prow_tb)[2]) {
     const int g4 = lane >> 4;
     if (STAGE == 1) {
         // blocks b < 4: gate rows, b + 4: the matching up rows -> activation
@@ -502,6 +445,91 @@ __global__ __launch_bounds__(kPreThreads) void ffn_pre_kernel(PreArgs A) {
     }
 }
 
+template <int STAGE, bool YF32>
+__global__ __launch_bounds__(kPreThreads) void ffn_pre_kernel(PreArgs A) {
+    __shared__ __attribute__((aligned(16))) PreStage lds[kPreStages];
+    const int tid = threadIdx.x, lane = lane_id();
+    const int wv = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const int wm = wv & 1, wn = wv >> 1;     // token half (32 tokens), weight half
+
+    // total tile groups (nt_group consecutive weight tiles of one token tile),
+    // then this workgroup's group (XCD-aware numbering), from the token-tile
+    // map by scalar loads
+    const MOE_CONST int32_t *map = as_scalar(A.tile_map);
+    const int gpm = A.ntiles_w / A.nt_group;          // groups per token tile
+    const long total = (long)map[0] * gpm;
+    const long per = (total + 7) / 8;
+    const long q = (long)(blockIdx.x & 7) * per + (blockIdx.x >> 3);
+    if ((long)(blockIdx.x >> 3) >= per || q >= total) return;
+    const int m = (int)(q / gpm);
+    const int nt = (int)(q - (long)m * gpm) * A.nt_group;   // first weight tile of the group
+    const int md = map[1 + m];
+    const int e = md & 0xFFFF, mt = md >> 16;
+
+    const MOE_CONST int32_t *offs = as_scalar(A.offsets);
+    const int row0 = offs[e];
+    const int n_e = offs[e + 1] - row0;
+    const int tok0 = mt * kPreTok;
+    const MOE_CONST moe_expert_w *W = as_scalar(A.experts) + e;
+    const uint8_t *wcodes = reinterpret_cast<const uint8_t *>(STAGE == 1 ? W->w13 : W->w2);
+    const uint8_t *wscales = reinterpret_cast<const uint8_t *>(STAGE == 1 ? W->s13 : W->s2);
+    const int nslab = A.K / 128;
+    // stage 2: output rows (pair indices) of this lane's two tokens, loaded
+    // before the copies so that the epilogue does not wait for them
+    int prow_tb[2] = {0, 0};
+    if (STAGE == 2) {
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb) {
+            const int r = tok0 + 32 * wm + 16 * tb + (lane & 15);
+            prow_tb[tb] = r < n_e ? A.sorted_pair[row0 + r] : 0;
+        }
+    }
+
+    PreSrc src;
+    {
+        auto token_row = [&](int r) -> long {   // operand row of tile row r
+            r = r < n_e ? r : n_e - 1;             // rows past the expert's end repeat its last row
+            return STAGE == 1 ? (long)(A.sorted_pair[row0 + r] / A.k) : (long)(row0 + r);
+        };
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            // token block wv, row 8u + lane/8; lane position lane%8 holds chunk pos ^ swizzle
+            const int rb = 8 * u + (lane >> 3);
+            const long row = token_row(tok0 + 16 * wv + rb);
+            const int chunk = (lane & 7) ^ tok_swz(rb);
+            src.thi[u] = A.bhi + row * A.K + 16 * chunk;
+            src.tlo[u] = A.blo + row * A.K + 16 * chunk;
+        }
+        src.tsc = A.bsc + token_row(tok0 + lane) * (A.K / 32);
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            src.wc[u] = wcodes + (size_t)pre_block<STAGE>(A, nt, 4 * wv + u) * nslab * 1024 +
+                        16 * lane;
+        src.ws = wscales + (size_t)pre_block<STAGE>(A, nt, lane >> 2) * nslab * 64 +
+                 16 * (lane & 3);
+    }
+
+    f32x4 acc[8][2];
+#pragma unroll
+    for (int b = 0; b < 8; ++b)
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb) acc[b][tb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+    // weight tile nt + t starts (STAGE 1 ? 8 : 16) blocks after tile nt
+    const size_t wstep = (size_t)(STAGE == 1 ? 8 : 16) * nslab * 1024;
+    pre_issue(lds[0], 0, wv, src, 0);
+    for (int t = 0; t < A.nt_group; ++t) {
+        pre_mainloop<STAGE>(lds, acc, nslab, t * nslab, wv, wm, wn, lane, src, t * wstep,
+                            (t + 1) * wstep, t + 1 < A.nt_group);
+        pre_epilogue<STAGE, YF32>(A, acc, nt + t, tok0, row0, n_e, wm, wn, lane, prow_tb);
+#pragma unroll
+        for (int b = 0; b < 8; ++b)
+#pragma unroll
+            for (int tb = 0; tb < 2; ++tb) acc[b][tb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+}
+
+
 // Tiled path needs whole 128-row weight tiles in stage 1 (I % 128) and
 // 256-row tiles in stage 2 (H % 256), and whole 128-column slabs.
 bool ffn_prefill_supported(int fmt, int H, int I) {
@@ -521,11 +549,21 @@ size_t prefill_ws_bytes(long n_pairs, long T, int H, int I, int E) {
            2 * al256((size_t)T * H) + al256((size_t)T * H / 32) + tile_map_bytes(n_pairs, E);
 }
 
+#ifndef MOE_PRE_GROUP1
+#define MOE_PRE_GROUP1 1
+#endif
+#ifndef MOE_PRE_GROUP2
+#define MOE_PRE_GROUP2 2
+#endif
 template <int STAGE, bool YF32>
 static int launch_pre(hipStream_t s, PreArgs A, long n_pairs) {
-    // upper bound on tiles: sum_e ceil(count_e / 128) <= n_pairs / 128 + E
+    // weight tiles per workgroup: stage 2's short contraction (I / 128 slabs
+    // per tile) runs two tiles per workgroup so the copy ring spans more slabs
+    const int want = STAGE == 1 ? MOE_PRE_GROUP1 : MOE_PRE_GROUP2;
+    A.nt_group = A.ntiles_w % want == 0 ? want : 1;
+    // upper bound on token tiles: sum_e ceil(count_e / 64) <= n_pairs / 64 + E
     const long mt_max = n_pairs / kPreTok + A.E;
-    const long tiles_max = mt_max * A.ntiles_w;
+    const long tiles_max = mt_max * (A.ntiles_w / A.nt_group);
     const long grid = ((tiles_max + 7) / 8) * 8;
     if (grid > 0x7FFFFFFFL) return MOE_EUNSUPPORTED;
     MOE_LAUNCH(STAGE == 1 ? K_PRE_GATE_UP : K_PRE_DOWN, (ffn_pre_kernel<STAGE, YF32>), dim3((unsigned)grid),
@@ -556,11 +594,11 @@ int ffn_prefill(const uint16_t *x, const int32_t *sorted_pair, const int32_t *of
     if (rc) return rc;
 
     PreArgs a1{xhi, xlo, xsc, sorted_pair, offsets, experts, nullptr, ahi, alo, asc, map,
-               k, H, H, I, E, I / 128};
+               k, H, H, I, E, I / 128, 1};
     rc = launch_pre<1, false>(s, a1, n);
     if (rc) return rc;
     PreArgs a2{ahi, alo, asc, sorted_pair, offsets, experts, y, nullptr, nullptr, nullptr, map,
-               k, I, H, I, E, H / 256};
+               k, I, H, I, E, H / 256, 1};
     return y_is_fp32 ? launch_pre<2, true>(s, a2, n) : launch_pre<2, false>(s, a2, n);
 }
 
