@@ -355,6 +355,25 @@ def test_ffn_paths_agree_with_oracle(lib, orc, path):
     _check_layer_sampled(orc, w, T, x, lg, L, out, n_sample=20)
 
 
+@pytest.mark.parametrize("path", [1, 2])
+def test_ffn_paths_odd_tile_counts(lib, orc, path):
+    """H = 768, I = 384: three 256-row down tiles (the tiled path's two-tile
+    workgroups fall back to one), 6- and 3-slab contractions, skewed routing."""
+    _announce(f"ffn: forced path {path}, H=768 I=384 E=16 k=4 T=400")
+    cfg = synth.LayerConfig("odd_tiles", 768, 16, 4, 384, "mxfp4", 0, "uniform", (400,),
+                            "gauss_mxfp4", seed=7)
+    w = Workload(cfg)
+    T = 400
+    x = synth.activations(cfg, T, step=1)
+    lg = _perm_case(T, 16, 4, "skew")
+    lib.moe_set_option(lib.MOE_OPT_FFN_PATH, path)
+    try:
+        L, out = run_layer(w, T, x, logits=lg)
+    finally:
+        lib.moe_set_option(lib.MOE_OPT_FFN_PATH, 0)
+    _check_layer_sampled(orc, w, T, x, lg, L, out, n_sample=16)
+
+
 def test_shared_expert_call_is_plain_swiglu(lib, orc):
     _announce("ffn: E=1, k=1 identity call (shared-expert form)")
     w = workload(4)
