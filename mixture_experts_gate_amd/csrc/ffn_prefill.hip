@@ -349,11 +349,14 @@ __device__ __forceinline__ void bare_barrier() {
 // receives the next one (the next tile's first slab after a tile's last). The
 // two workgroups on a compute unit interleave: one's copies, fragment reads,
 // barrier waits and epilogue overlap the other's matrix instructions.
-template <int STAGE>
+// `first` runs once, after the first slab's barrier and copies: the previous
+// tile's deferred output stores go there, so that the wait at the top of the
+// first slab does not also wait for them to complete.
+template <int STAGE, class First>
 __device__ __forceinline__ void pre_mainloop(PreStage (&lds)[kPreStages], f32x4 (&acc)[8][2],
                                              int n, int g0, int wv, int wm, int wn, int lane,
                                              const PreSrc &src, size_t woff, size_t woff_next,
-                                             bool has_next) {
+                                             bool has_next, First &&first) {
     PreFrag F;
     const TokPos tp(lane);
     for (int j = 0; j < n; ++j) {
@@ -362,6 +365,7 @@ __device__ __forceinline__ void pre_mainloop(PreStage (&lds)[kPreStages], f32x4 
         bare_barrier();
         if (j + 1 < n) pre_issue(lds[st ^ 1], j + 1, wv, src, woff);
         else if (has_next) pre_issue(lds[st ^ 1], 0, wv, src, woff_next);
+        if (j == 0) first();
         pre_read<STAGE>(lds[st], F, wm, wn, lane, tp);
         pre_math(F, acc);
     }
@@ -370,6 +374,38 @@ __device__ __forceinline__ void pre_mainloop(PreStage (&lds)[kPreStages], f32x4 
 // Epilogue of weight tile nt: for token block tb the lane holds token
 // 32wm + 16tb + lane%16 and, in weight block b, rows 4(lane/16) + i (i < 4) of
 // the block.
+// Stage 2, bf16 y: a tile's outputs packed, and stored later (pre_store_y).
+struct PreOut {
+    uint2 pk[2][8];
+    int nt;
+};
+
+__device__ __forceinline__ void pre_pack_y(const f32x4 (&acc)[8][2], int nt, PreOut &o) {
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+        for (int b = 0; b < 8; ++b) {
+            o.pk[tb][b].x = pack_bf16x2(acc[b][tb][0], acc[b][tb][1]);
+            o.pk[tb][b].y = pack_bf16x2(acc[b][tb][2], acc[b][tb][3]);
+        }
+    o.nt = nt;
+}
+
+__device__ __forceinline__ void pre_store_y(const PreArgs &A, const PreOut &o, int tok0, int n_e,
+                                            int wm, int wn, int lane, const int (&prow_tb)[2]) {
+    const int g4 = lane >> 4;
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb) {
+        const int r = tok0 + 32 * wm + 16 * tb + (lane & 15);
+        if (r >= n_e) continue;
+        const size_t prow = (size_t)prow_tb[tb] * A.H + o.nt * 256 + 128 * wn + 4 * g4;
+#pragma unroll
+        for (int b = 0; b < 8; ++b)
+            *reinterpret_cast<uint2 *>(reinterpret_cast<uint16_t *>(A.out) + prow + 16 * b) =
+                o.pk[tb][b];
+    }
+}
+
 template <int STAGE, bool YF32>
 __device__ __forceinline__ void pre_epilogue(const PreArgs &A, const f32x4 (&acc)[8][2], int nt,
                                              int tok0, int row0, int n_e, int wm, int wn,
@@ -518,15 +554,29 @@ __global__ __launch_bounds__(kPreThreads) void ffn_pre_kernel(PreArgs A) {
     // weight tile nt + t starts (STAGE 1 ? 8 : 16) blocks after tile nt
     const size_t wstep = (size_t)(STAGE == 1 ? 8 : 16) * nslab * 1024;
     pre_issue(lds[0], 0, wv, src, 0);
+    // stage 2 with bf16 y: a tile's outputs are stored after the next tile's
+    // first slab barrier (or at the end), not before it
+    constexpr bool kDefer = STAGE == 2 && !YF32;
+    PreOut pend;
+    bool pending = false;
     for (int t = 0; t < A.nt_group; ++t) {
         pre_mainloop<STAGE>(lds, acc, nslab, t * nslab, wv, wm, wn, lane, src, t * wstep,
-                            (t + 1) * wstep, t + 1 < A.nt_group);
-        pre_epilogue<STAGE, YF32>(A, acc, nt + t, tok0, row0, n_e, wm, wn, lane, prow_tb);
+                            (t + 1) * wstep, t + 1 < A.nt_group, [&]() {
+                                if (kDefer && pending)
+                                    pre_store_y(A, pend, tok0, n_e, wm, wn, lane, prow_tb);
+                            });
+        if (kDefer) {
+            pre_pack_y(acc, nt + t, pend);
+            pending = true;
+        } else {
+            pre_epilogue<STAGE, YF32>(A, acc, nt + t, tok0, row0, n_e, wm, wn, lane, prow_tb);
+        }
 #pragma unroll
         for (int b = 0; b < 8; ++b)
 #pragma unroll
             for (int tb = 0; tb < 2; ++tb) acc[b][tb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     }
+    if (kDefer && pending) pre_store_y(A, pend, tok0, n_e, wm, wn, lane, prow_tb);
 }
 
 
