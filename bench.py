@@ -200,21 +200,24 @@ def algorithmic_bytes(wl, U):
     """Bytes each kernel must move at minimum (weights of touched experts read
     once, activations read once, outputs written once). With a shared expert
     the layer adds its weights and its output; the per-kernel figures are those
-    of the routed launches."""
+    of one step: with a shared expert, the FFN kernels run once for the routed
+    experts and once for the shared one, and their figures cover both."""
     c, T, lay = wl.cfg, wl.T, wl.lay
     H, I, E, k = c.H, c.I, c.E, c.k
     w13 = lay.w2 - lay.w13           # W13 codes + scales of one expert
     w2 = lay.nbytes - lay.w2         # W2 codes + scales
     n = T * k
     sh = (lay.nbytes + T * H * 2) if c.n_shared else 0
+    s13 = (w13 + T * H * 2 + T * I * 2) if c.n_shared else 0
+    s2 = (w2 + T * I * 2 + T * H * 2) if c.n_shared else 0
     return {
         "route": T * E * 4 + n * 8,
         "permute_small": n * 4 + n * 8 + (E + 1) * 4,
-        "ffn_decode_gate_up": U * w13 + T * H * 2 + n * I * 2,
-        "ffn_decode_down": U * w2 + n * I * 2 + n * H * 2,
-        "ffn_prefill_gate_up": U * w13 + T * H * 2 + n * I * 2,
-        "ffn_prefill_down": U * w2 + n * I * 2 + n * H * 2,
-        "combine": n * H * 2 + n * 4 + T * H * 2,
+        "ffn_decode_gate_up": U * w13 + T * H * 2 + n * I * 2 + s13,
+        "ffn_decode_down": U * w2 + n * I * 2 + n * H * 2 + s2,
+        "ffn_prefill_gate_up": U * w13 + T * H * 2 + n * I * 2 + s13,
+        "ffn_prefill_down": U * w2 + n * I * 2 + n * H * 2 + s2,
+        "combine": n * H * 2 + n * 4 + T * H * 2 + (T * H * 2 if c.n_shared else 0),
         "layer": U * lay.nbytes + 2 * T * H * 2 + T * E * 4 + n * 8 + sh,
     }
 
@@ -242,10 +245,13 @@ def run_workload(torch, cfg, T, steps, warmup, dev, pool=None, dexp=None, shared
         "layer_tflops": flops / (ms_step / 1000.0) / 1e12,
         "kernels": kt,
     }
+    ksteps = kernel_steps or min(steps, 64)
     for name, v in kt.items():
+        # per step: the launches of one step together move ab[name] bytes
+        v["us_per_step"] = v["avg_us"] * v["launches"] / ksteps
         if name in ab:
             v["algorithmic_bytes"] = ab[name]
-            v["GBs"] = ab[name] / (v["avg_us"] * 1e-6) / 1e9
+            v["GBs"] = ab[name] / (v["us_per_step"] * 1e-6) / 1e9
     return wl, res
 
 
