@@ -157,6 +157,7 @@ int moe_route_permute(const uint16_t *x_bf16, const uint16_t *wg_bf16, const flo
  * no pair are never read. x_bf16 [T][H]. fmt: MOE_W_MXFP4 (kernel layout,
  * H and I multiples of 128) or MOE_W_BF16 (H and I multiples of 32).
  * ws: device workspace of at least the ffn size from moe_workspace_size.
+ * Requires E <= 512.
  * The shared (always-on) expert is this call with E = 1, k = 1,
  * sorted_pair = 0..T-1 and offsets = {0, T}.
  */

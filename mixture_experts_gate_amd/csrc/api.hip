@@ -177,7 +177,10 @@ extern "C" int moe_expert_ffn(const uint16_t *x_bf16, const int32_t *sorted_pair
                               const int32_t *offsets, const moe_expert_w *experts, int fmt, int T,
                               int k, int H, int I, int E, void *y, int y_is_fp32, void *ws,
                               size_t ws_bytes, void *stream) {
-    if (T < 0 || k < 1 || E < 1 || H < 32 || I < 32 || H % 32 || I % 32) return MOE_EINVAL;
+    // E <= 512: the weight-streaming kernels keep the set of active experts
+    // as a 512-bit mask
+    if (T < 0 || k < 1 || E < 1 || E > 512 || H < 32 || I < 32 || H % 32 || I % 32)
+        return MOE_EINVAL;
     if (fmt != MOE_W_MXFP4 && fmt != MOE_W_BF16) return MOE_EINVAL;
     if (fmt == MOE_W_MXFP4 && (H % 128 || I % 128)) return MOE_EINVAL;
     if (T == 0) return MOE_OK;

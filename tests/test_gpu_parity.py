@@ -400,6 +400,39 @@ def test_layer_deterministic(lib):
     assert torch.equal(a[0], o2) and torch.equal(a[1], L2.y) and torch.equal(a[2], L2.sorted_pair)
 
 
+def test_layer_graph_replays(lib):
+    """Graph replays of the layer (config 4 with its shared expert on a side
+    stream, T=64) repeat the eager result exactly, with eager calls on the same
+    buffers between the replays."""
+    _announce("graph replays of config 4 T=64 against the eager result")
+    from mixture_experts_gate_amd.layer import MoeLayer
+    w = workload(4)
+    T = 64
+    x = to_dev_bf16(synth.activations(w.cfg, T, step=6))
+    lg = to_dev(synth.router_logits(w.cfg, T, step=6))
+    L = MoeLayer(w.cfg.H, w.E, w.cfg.k, w.cfg.I, w.cfg.fmt, T, shared=True, device=DEV)
+    L.prepare_shared(T)
+    ref = L.forward(T, x, w.dev.table, logits=lg, shared_table=w.dev_shared.table).clone()
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        L.forward(T, x, w.dev.table, logits=lg, shared_table=w.dev_shared.table)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        out = L.forward(T, x, w.dev.table, logits=lg, shared_table=w.dev_shared.table)
+    for r in range(4):
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref), f"replay {r} differs from the eager result"
+        # eager work on the same buffers between replays
+        L.forward(T, x, w.dev.table, logits=lg, shared_table=w.dev_shared.table)
+        torch.cuda.synchronize()
+        assert torch.equal(L.out[:T], ref)
+
+
 def test_pack_mxfp4_layout(lib):
     """The kernel layout as the header states it, built independently in numpy
     from random interchange bytes."""

@@ -77,6 +77,9 @@ def test_argument_errors_before_any_device_work(lib):
     # workspace too small
     assert L.moe_expert_ffn(dummy, dummy, dummy, dummy, 1, 4, 2, 64, 64, 8, dummy, 0, dummy,
                             16, None) == lib.MOE_EINVAL
+    # more experts than the FFN supports
+    assert L.moe_expert_ffn(dummy, dummy, dummy, dummy, 1, 4, 2, 128, 128, 513, dummy, 0, dummy,
+                            1 << 30, None) == lib.MOE_EINVAL
     # bad weight format
     assert L.moe_expert_ffn(dummy, dummy, dummy, dummy, 7, 4, 2, 64, 64, 8, dummy, 0, dummy,
                             1 << 20, None) == lib.MOE_EINVAL
