@@ -256,6 +256,33 @@ int expert_cache_reserve(moe_cache **cache, void *pool, size_t pool_bytes, size_
 int expert_cache_prefetch(moe_cache *cache, int layer, const int32_t *ids, int n,
                           void *compute_stream, const moe_expert_w **table_out);
 
+/*
+ * expert_cache_resize -- move the cache to a pool of another size at run time
+ * (the expert-cache side of re-allocating device memory between the expert
+ * cache and other uses without reloading weights).
+ * new_pool: caller-owned device buffer of new_pool_bytes; either the current
+ *       pool itself (shrink or grow in place: its first new_pool_bytes bytes)
+ *       or a buffer that does not overlap the current pool.
+ * The min(residents, new slot count) most recently used residents stay
+ * resident, moved by device-to-device copies on the copy stream (a resident
+ * keeps its slot index when it is below the new slot count, the others take
+ * the lowest free indices, most recent first); the rest are dropped. LRU
+ * order among the kept residents is unchanged; free slots become the least
+ * recently used, in ascending index order. The copy stream first waits for
+ * the work enqueued on compute_stream before this call; on return,
+ * compute_stream waits for the copies and table updates.
+ * Tables returned by earlier prefetch calls must not be read by compute
+ * enqueued after this call (prefetch again). A separate old pool may be
+ * released once compute_stream has passed this call.
+ * moved (may be NULL): number of experts copied.
+ * Returns MOE_ENOMEM if the new pool holds fewer slots than n_experts, and
+ * MOE_EINVAL for a partial overlap, with the cache unchanged; after a HIP
+ * error during the copies the cache stays on the old pool without the
+ * residents that did not fit.
+ */
+int expert_cache_resize(moe_cache *cache, void *new_pool, size_t new_pool_bytes,
+                        void *compute_stream, int *moved);
+
 /* expert_cache_evict -- drop experts of `layer` from the cache (NULL ids =
  * the whole layer). Their slots become free for later misses. */
 int expert_cache_evict(moe_cache *cache, int layer, const int32_t *ids, int n);

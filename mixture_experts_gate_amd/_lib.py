@@ -24,7 +24,7 @@ EXPORTS = [
     "moe_combine", "moe_workspace_size", "moe_set_option", "moe_get_option", "moe_kernel_name",
     "moe_timing_query", "moe_pack_mxfp4", "moe_route_permute",
     "expert_cache_reserve", "expert_cache_prefetch", "expert_cache_evict", "expert_cache_stats",
-    "expert_cache_slots", "expert_cache_slot_of", "expert_cache_destroy",
+    "expert_cache_slots", "expert_cache_slot_of", "expert_cache_destroy", "expert_cache_resize",
 ]
 
 
@@ -71,6 +71,7 @@ def load(path: str | None = None):
         "expert_cache_reserve": (I, [C.POINTER(P), P, Z, Z, I, I, P, Z, Z, Z, Z, P]),
         "expert_cache_prefetch": (I, [P, I, P, I, P, C.POINTER(P)]),
         "expert_cache_evict": (I, [P, I, P, I]),
+        "expert_cache_resize": (I, [P, P, Z, P, C.POINTER(I)]),
         "expert_cache_stats": (I, [P, C.POINTER(C.c_longlong), C.POINTER(C.c_longlong),
                                    C.POINTER(C.c_longlong)]),
         "expert_cache_slots": (I, [P]),
@@ -237,6 +238,15 @@ def expert_cache_stats(cache):
     h, m, b = C.c_longlong(0), C.c_longlong(0), C.c_longlong(0)
     _check("expert_cache_stats", load().expert_cache_stats(cache, C.byref(h), C.byref(m), C.byref(b)))
     return h.value, m.value, b.value
+
+
+def expert_cache_resize(cache, new_pool, new_pool_bytes, compute_stream=None):
+    """Move the cache to `new_pool` (tensor or address); returns the number of
+    experts copied device to device."""
+    moved = C.c_int(0)
+    _check("expert_cache_resize", load().expert_cache_resize(
+        cache, _ptr(new_pool), new_pool_bytes, _stream(compute_stream), C.byref(moved)))
+    return moved.value
 
 
 def expert_cache_slots(cache):

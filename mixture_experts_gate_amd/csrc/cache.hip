@@ -269,6 +269,115 @@ extern "C" int expert_cache_prefetch(moe_cache *c, int layer, const int32_t *ids
     return MOE_OK;
 }
 
+// Elastic resize (the expert-cache half of re-allocating device memory between
+// the expert cache and other uses at run time, aimodeling.com/en page, "Three
+// Engineering Cores"; winzheng.com page, "FreeToken's Three-Layer Mechanism"):
+// the most recently used residents that fit move to the new pool by
+// device-to-device copies, the rest are dropped; nothing is read from the host.
+// A kept resident keeps its slot index when it is below the new slot count;
+// the others take the lowest free indices, most recent first. Free slots go
+// to the least recently used end in ascending index order.
+extern "C" int expert_cache_resize(moe_cache *c, void *new_pool, size_t new_pool_bytes,
+                                   void *compute_stream, int *moved) {
+    if (!c || !new_pool) return MOE_EINVAL;
+    const size_t n2 = new_pool_bytes / c->slot_bytes;
+    if (n2 > 0x7FFFFFFF) return MOE_EINVAL;
+    if (n2 < (size_t)c->E) return MOE_ENOMEM;
+    char *np = reinterpret_cast<char *>(new_pool);
+    const bool same = np == c->pool;
+    if (!same) {
+        const char *o0 = c->pool, *o1 = c->pool + (size_t)c->nslots * c->slot_bytes;
+        const char *n0 = np, *n1 = np + n2 * c->slot_bytes;
+        if (n0 < o1 && o0 < n1) return MOE_EINVAL;     // partial overlap
+    }
+    const int N2 = (int)n2;
+    // residents from most to least recently used; keep the first N2
+    std::vector<int> kept;
+    for (int s = c->head; s >= 0; s = c->next[s])
+        if (c->key_of[s] >= 0) kept.push_back(s);
+    std::vector<int> drop;
+    if ((int)kept.size() > N2) {
+        drop.assign(kept.begin() + N2, kept.end());
+        kept.resize(N2);
+    }
+    // new slot of every kept resident
+    std::vector<char> used(N2, 0);
+    for (int s : kept)
+        if (s < N2) used[s] = 1;
+    std::vector<int> dst(kept.size());
+    int freep = 0;
+    for (size_t i = 0; i < kept.size(); ++i) {
+        const int s = kept[i];
+        if (s < N2) {
+            dst[i] = s;
+        } else {
+            while (used[freep]) ++freep;
+            used[freep] = 1;
+            dst[i] = freep;
+        }
+    }
+    hipStream_t cs = (hipStream_t)compute_stream;
+    // compute enqueued before this call may still read the old slots
+    c->retire_events();
+    hipEvent_t ev = c->get_event();
+    if (!ev) return MOE_EHIP;
+    int rc = check_hip(hipEventRecord(ev, cs));
+    if (!rc) rc = check_hip(hipStreamWaitEvent(c->copy_stream, ev, 0));
+    c->spare_ev.push_back(ev);      // reusable: the wait is enqueued
+    if (rc) return rc;
+    // dropped residents leave first: their slots may be copy destinations
+    for (int s : drop) {
+        c->slot_of[c->key_of[s]] = -1;
+        c->key_of[s] = -1;
+        c->unlink(s);
+        c->push_back(s);
+    }
+    int nmoved = 0;
+    for (size_t i = 0; i < kept.size(); ++i) {
+        if (same && dst[i] == kept[i]) continue;
+        rc = check_hip(hipMemcpyAsync(np + (size_t)dst[i] * c->slot_bytes,
+                                      c->pool + (size_t)kept[i] * c->slot_bytes, c->expert_bytes,
+                                      hipMemcpyDeviceToDevice, c->copy_stream));
+        if (rc) return rc;     // still on the old pool: sources are never destinations
+        ++nmoved;
+    }
+    // metadata of the new pool
+    std::vector<int> key2(N2, -1);
+    for (size_t i = 0; i < kept.size(); ++i) key2[dst[i]] = c->key_of[kept[i]];
+    c->pool = np;
+    c->nslots = N2;
+    c->key_of = key2;
+    c->prev.assign(N2, -1);
+    c->next.assign(N2, -1);
+    c->last_gen.assign(N2, 0);
+    c->head = c->tail = -1;
+    for (size_t i = 0; i < kept.size(); ++i) {
+        c->slot_of[key2[dst[i]]] = dst[i];
+        c->push_back(dst[i]);
+    }
+    for (int s = 0; s < N2; ++s)
+        if (!used[s]) c->push_back(s);
+    // table entries of the residents point into the new pool
+    TableUpdate up;
+    up.n = 0;
+    for (size_t i = 0; i < kept.size(); ++i) {
+        up.key[up.n] = key2[dst[i]];
+        up.slot[up.n] = dst[i];
+        if (++up.n == kTableBatch || i + 1 == kept.size()) {
+            MOE_LAUNCH(K_CACHE_TABLE, cache_table_kernel, dim3(1), dim3(256), 0, c->copy_stream,
+                       c->d_table, (const char *)c->pool, c->slot_bytes, c->lay[0], c->lay[1],
+                       c->lay[2], c->lay[3], up);
+            if ((rc = check_launch())) return rc;
+            up.n = 0;
+        }
+    }
+    rc = check_hip(hipEventRecord(c->ready, c->copy_stream));
+    if (!rc) rc = check_hip(hipStreamWaitEvent(cs, c->ready, 0));
+    if (rc) return rc;
+    if (moved) *moved = nmoved;
+    return MOE_OK;
+}
+
 extern "C" int expert_cache_evict(moe_cache *c, int layer, const int32_t *ids, int n) {
     if (!c || layer < 0 || layer >= c->L || (ids && n < 0)) return MOE_EINVAL;
     const long base_key = (long)layer * c->E;

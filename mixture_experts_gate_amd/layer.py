@@ -248,6 +248,26 @@ class ExpertCache:
     def slots(self):
         return _lib.expert_cache_slots(self.handle)
 
+    def resize(self, pool_bytes, in_place=False, compute_stream=None):
+        """Give the cache a pool of `pool_bytes` without reloading from the host:
+        in place (shrink, or grow within the allocated pool) or into a new pool
+        tensor, after which the old one is released once the copy stream has
+        read it. Returns the number of experts moved. Tables from earlier
+        prefetch calls are invalid afterwards."""
+        import torch
+        nbytes = pool_bytes // self.slot_bytes * self.slot_bytes
+        if in_place:
+            if nbytes > self.pool.numel():
+                raise ValueError("in-place growth beyond the allocated pool")
+            new = self.pool
+        else:
+            new = torch.empty(nbytes, dtype=torch.uint8, device=self.pool.device)
+        moved = _lib.expert_cache_resize(self.handle, new, nbytes, compute_stream)
+        if not in_place:
+            self.pool.record_stream(self.copy_stream)   # read by the migration copies
+            self.pool = new
+        return moved
+
     def slot_of(self, layer, expert):
         return _lib.expert_cache_slot_of(self.handle, layer, expert)
 

@@ -83,6 +83,36 @@ class LruModel:
             self.last[s] = g
             self.misses += 1
 
+    def resize(self, n2, same_pool):
+        """Keep the n2 most recently used residents: a kept slot below n2 stays,
+        the others take the lowest free indices (most recent first); free slots
+        follow at the least recently used end in ascending order."""
+        res = [s for s in self.order if self.key_of[s] >= 0]
+        kept, dropped = res[:n2], res[n2:]
+        for s in dropped:
+            del self.slot_of[self.key_of[s]]
+        used = [False] * n2
+        for s in kept:
+            if s < n2:
+                used[s] = True
+        dst, f = [], 0
+        for s in kept:
+            if s < n2:
+                dst.append(s)
+            else:
+                while used[f]:
+                    f += 1
+                used[f] = True
+                dst.append(f)
+        key2 = [-1] * n2
+        for s, d in zip(kept, dst):
+            key2[d] = self.key_of[s]
+        self.key_of = key2
+        self.slot_of = {k: d for d, k in enumerate(key2) if k >= 0}
+        self.order = dst + [s for s in range(n2) if not used[s]]
+        self.last = [0] * n2
+        return sum(1 for s, d in zip(kept, dst) if s != d or not same_pool)
+
     def evict(self, layer, ids):
         for e in (ids if ids is not None else range(self.E)):
             s = self.slot_of.pop(layer * self.E + int(e), None)
@@ -245,5 +275,90 @@ def test_streaming_next_layer_during_compute_is_bitwise(env):
             assert torch.equal(y.cpu(), want[l]), l
         h, m, b = c.stats()
         assert m >= 3 * env["L"] * E - E     # every layer change misses (two layers fit)
+    finally:
+        c.close()
+
+
+def test_resize_trace_matches_brute_force(env):
+    """Prefetches, evictions and resizes (shrink and grow, in place and into a
+    new pool) against the model; after each resize the residents' slots hold
+    the host bytes, so nothing had to be reloaded."""
+    torch = env["torch"]
+    nb = env["lay"].nbytes
+    slot = (nb + 255) // 256 * 256
+    c = _cache(env, 30)
+    model = LruModel(30, E)
+    rng = np.random.default_rng(8)
+    sizes = [(20, True), (34, False), (16, False), (26, True), (40, False), (E, True)]
+    try:
+        for step in range(60):
+            layer = int(rng.integers(env["L"]))
+            if step % 10 == 9:
+                n2, inplace = sizes[(step // 10) % len(sizes)]
+                if inplace and n2 * slot > c.pool.numel():
+                    inplace = False
+                h0, m0, b0 = c.stats()
+                moved = c.resize(n2 * slot, in_place=inplace)
+                want_moved = model.resize(n2, inplace)
+                assert moved == want_moved, step
+                assert c.slots() == n2
+                assert c.stats() == (h0, m0, b0)        # no host traffic
+                torch.cuda.synchronize()
+                for l in range(env["L"]):
+                    for e in range(E):
+                        s = c.slot_of(l, e)
+                        assert s == model.slot_of.get(l * E + e, -1), (step, l, e)
+                        if s >= 0:
+                            got = c.slot_bytes_view(s, nb).cpu()
+                            assert torch.equal(got, env["store"].host[l * E + e]), (step, l, e)
+                continue
+            ids = None if step % 7 == 0 else rng.integers(0, E, size=int(rng.integers(1, 12)))
+            c.prefetch(layer, ids)
+            model.prefetch(layer, ids)
+            if step % 13 == 12:
+                ev = rng.choice(E, size=2, replace=False)
+                c.evict(layer, ev)
+                model.evict(layer, ev)
+            for l in range(env["L"]):
+                for e in range(E):
+                    assert c.slot_of(l, e) == model.slot_of.get(l * E + e, -1), (step, l, e)
+            assert c.stats()[:2] == (model.hits, model.misses), step
+        torch.cuda.synchronize()
+    finally:
+        c.close()
+
+
+def test_resize_between_layers_is_bitwise(env):
+    """Stack passes with the pool shrunk to one layer and grown back in between:
+    outputs equal the resident outputs bit for bit, and the residents kept by a
+    resize are hits afterwards."""
+    torch = env["torch"]
+    from mixture_experts_gate_amd.layer import expert_table
+    lay = env["lay"]
+    slot = (lay.nbytes + 255) // 256 * 256
+    T = 64
+    res_tabs = [expert_table(r.data_ptr(), E, lay) for r in env["resident"]]
+    want = _layer_outputs(env, res_tabs, T, seed=31)
+    c = _cache(env, 3 * E)
+    try:
+        for step in range(2 * env["L"]):
+            l = step % env["L"]
+            if step == 3:
+                c.resize(E * slot)                      # one layer's worth, new pool
+            if step == 5:
+                c.resize(3 * E * slot)                  # grow back, new pool
+            if step == 6:
+                c.resize(2 * E * slot, in_place=True)   # shrink in place
+            tab = c.prefetch(l, None)
+            got = _layer_outputs(env, [tab], T, seed=31)[0]
+            torch.cuda.synchronize()
+            assert torch.equal(got, want[l]), (step, l)
+        # the layer used right before a resize stays resident through it
+        c.prefetch(1, None)
+        before = c.stats()
+        c.resize(E * slot)
+        c.prefetch(1, None)
+        after = c.stats()
+        assert after[1] == before[1] and after[0] == before[0] + E
     finally:
         c.close()

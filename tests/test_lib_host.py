@@ -103,3 +103,4 @@ def test_cache_reserve_argument_errors(lib):
                                   None) == lib.MOE_EINVAL
     assert L.expert_cache_destroy(None) == lib.MOE_EINVAL
     assert L.expert_cache_slots(None) == lib.MOE_EINVAL
+    assert L.expert_cache_resize(None, 0x1000, 1 << 20, None, None) == lib.MOE_EINVAL
