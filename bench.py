@@ -375,11 +375,13 @@ def h2d_peak(torch, dev, nbytes=1 << 30):
     return gbs
 
 
-def run_stack_cached(torch, st, runs, pool_bytes):
+def run_stack_cached(torch, st, runs, pool_bytes, resize_T=1, resize_steps=32):
     """The stack through a pool_bytes LRU expert cache fed from pinned host
     memory: per layer, route on the GPU, read the ids back, prefetch the misses
     (hipMemcpyAsync on the copy stream), then the expert FFN, shared expert and
-    combine. Shared experts stay resident. runs: [(T, warmup, steps)]."""
+    combine. Shared experts stay resident. runs: [(T, warmup, steps)]. After the
+    timed steps at T = resize_T the pool is resized to half and back, each
+    followed by resize_steps steps."""
     import numpy as np
     from mixture_experts_gate_amd import synth
     from mixture_experts_gate_amd.layer import (ExpertCache, HostExperts, MoeLayer, expert_table,
@@ -393,7 +395,8 @@ def run_stack_cached(torch, st, runs, pool_bytes):
     out = {"h2d_link_GBs": link, "pool_bytes": pool_bytes}
     for T, warmup, steps in runs:
         cache = ExpertCache(store, st.L, c.E, pool_bytes, device=dev)
-        lg = st.logits(torch, T, range(warmup + steps))
+        extra = 2 * resize_steps if T == resize_T else 0
+        lg = st.logits(torch, T, range(warmup + steps + extra))
         x0 = torch.from_numpy(synth.activations(c, T).view("int16")).to(dev)
         layers = [MoeLayer(c.H, c.E, c.k, c.I, c.fmt, T, shared=True, device=dev) for _ in (0, 1)]
         for ly in layers:
@@ -431,6 +434,35 @@ def run_stack_cached(torch, st, runs, pool_bytes):
         out[f"T{T}"] = r
         log(f"stack cached T={T}: {r['tokens_per_s']:.1f} tok/s, hit {r['hit_rate']:.3f}, "
             f"H2D {r['h2d_GBs']:.1f} GB/s ({r['h2d_frac_of_link']*100:.0f}% of the copy rate)")
+        if T == resize_T:
+            # elastic resize: the pool shrinks to half into a new buffer (the
+            # other half could go to other uses), runs, then grows back
+            nxt = warmup + steps
+            r["resize"] = []
+            for frac in (0.5, 1.0):
+                torch.cuda.synchronize()
+                t0 = time.perf_counter()
+                moved = cache.resize(int(pool_bytes * frac))
+                torch.cuda.synchronize()
+                el = time.perf_counter() - t0
+                h0, m0, _ = cache.stats()
+                for i in range(nxt, nxt + resize_steps):
+                    step(i)
+                torch.cuda.synchronize()
+                nxt += resize_steps
+                h1, m1, _ = cache.stats()
+                mb = moved * lay.nbytes
+                q = {"pool_bytes": int(pool_bytes * frac), "slots": cache.slots(),
+                     "experts_moved": moved, "moved_bytes": mb, "ms": 1000.0 * el,
+                     "d2d_GBs_read_plus_write": 2 * mb / el / 1e9,
+                     "d2d_hbm_frac": 2 * mb / el / 1e9 / HBM_PEAK_GBS,
+                     "hit_rate_next_steps": (h1 - h0) / max(h1 - h0 + m1 - m0, 1),
+                     "next_steps": resize_steps}
+                r["resize"].append(q)
+                log(f"stack cached T={T}: resize to {q['pool_bytes']/1e9:.0f} GB moved {moved} experts "
+                    f"({mb/1e9:.1f} GB) in {q['ms']:.1f} ms "
+                    f"({q['d2d_hbm_frac']*100:.0f}% of HBM), hit rate over the next "
+                    f"{resize_steps} steps {q['hit_rate_next_steps']:.3f}")
         cache.close()
         del cache
     del store

@@ -32,7 +32,8 @@ static double g_ms[K_COUNT];
 static const char *const g_kernel_names[K_COUNT] = {
     "route", "permute_small", "permute_rank", "permute_scan", "permute_scatter", "permute_empty",
     "ffn_decode_gate_up", "ffn_decode_down", "ffn_prefill_gate_up", "ffn_prefill_down",
-    "combine", "cache_table", "pack_mxfp4", "route_permute", "ffn_prefill_split"};
+    "combine", "cache_table", "pack_mxfp4", "route_permute", "ffn_prefill_split",
+    "cache_move"};
 
 static hipEvent_t pool_event() {
     if (!g_evpool.empty()) {

@@ -49,6 +49,41 @@ __global__ void cache_table_kernel(moe_expert_w *table, const char *pool, size_t
     }
 }
 
+// Slot moves of a resize, by value: move i copies slot src[i] of the old pool
+// to slot dst[i] of the new one (sources and destinations never overlap).
+constexpr int kMoveBatch = 240;
+struct SlotMoves {
+    int n;
+    int src[kMoveBatch];
+    int dst[kMoveBatch];
+};
+
+// grid (chunks per slot, moves): each workgroup copies 64 KB of one slot with
+// 16-byte non-temporal loads and stores, 16 in flight per lane.
+constexpr int kMoveChunk = 65536;
+__global__ __launch_bounds__(256) void cache_move_kernel(const char *old_pool, char *new_pool,
+                                                         size_t slot_bytes, SlotMoves mv) {
+    const int i = blockIdx.y;
+    const size_t base = (size_t)blockIdx.x * kMoveChunk;
+    if (i >= mv.n || base >= slot_bytes) return;
+    const u32x4 *src = reinterpret_cast<const u32x4 *>(old_pool + (size_t)mv.src[i] * slot_bytes + base);
+    u32x4 *dst = reinterpret_cast<u32x4 *>(new_pool + (size_t)mv.dst[i] * slot_bytes + base);
+    const size_t left = slot_bytes - base;
+    const int n16 = (int)((left < (size_t)kMoveChunk ? left : (size_t)kMoveChunk) / 16);
+    constexpr int kUnroll = kMoveChunk / 16 / 256;
+    u32x4 v[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+        const int j = u * 256 + (int)threadIdx.x;
+        if (j < n16) v[u] = __builtin_nontemporal_load(src + j);
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+        const int j = u * 256 + (int)threadIdx.x;
+        if (j < n16) __builtin_nontemporal_store(v[u], dst + j);
+    }
+}
+
 }  // namespace moe
 
 using namespace moe;
@@ -333,13 +368,23 @@ extern "C" int expert_cache_resize(moe_cache *c, void *new_pool, size_t new_pool
         c->push_back(s);
     }
     int nmoved = 0;
+    SlotMoves mv;
+    mv.n = 0;
+    const unsigned chunks = (unsigned)((c->slot_bytes + kMoveChunk - 1) / kMoveChunk);
     for (size_t i = 0; i < kept.size(); ++i) {
-        if (same && dst[i] == kept[i]) continue;
-        rc = check_hip(hipMemcpyAsync(np + (size_t)dst[i] * c->slot_bytes,
-                                      c->pool + (size_t)kept[i] * c->slot_bytes, c->expert_bytes,
-                                      hipMemcpyDeviceToDevice, c->copy_stream));
-        if (rc) return rc;     // still on the old pool: sources are never destinations
-        ++nmoved;
+        if (!(same && dst[i] == kept[i])) {
+            mv.src[mv.n] = kept[i];
+            mv.dst[mv.n] = dst[i];
+            ++mv.n;
+            ++nmoved;
+        }
+        if (mv.n > 0 && (mv.n == kMoveBatch || i + 1 == kept.size())) {
+            MOE_LAUNCH(K_CACHE_MOVE, cache_move_kernel, dim3(chunks, (unsigned)mv.n), dim3(256), 0,
+                       c->copy_stream, (const char *)c->pool, np, c->slot_bytes, mv);
+            // on failure the cache stays on the old pool: sources are never destinations
+            if ((rc = check_launch())) return rc;
+            mv.n = 0;
+        }
     }
     // metadata of the new pool
     std::vector<int> key2(N2, -1);

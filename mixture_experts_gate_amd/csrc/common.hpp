@@ -44,7 +44,8 @@ int ffn_path_option();
 // Kernel ids for the optional launch timing (moe_timing_query).
 enum KernelId {
     K_ROUTE = 0, K_PERM_SMALL, K_PERM_RANK, K_PERM_SCAN, K_PERM_SCATTER, K_PERM_EMPTY,
-    K_DEC_GATE_UP, K_DEC_DOWN, K_PRE_GATE_UP, K_PRE_DOWN, K_COMBINE, K_CACHE_TABLE, K_PACK, K_ROUTE_PERMUTE, K_PRE_SPLIT, K_COUNT
+    K_DEC_GATE_UP, K_DEC_DOWN, K_PRE_GATE_UP, K_PRE_DOWN, K_COMBINE, K_CACHE_TABLE, K_PACK, K_ROUTE_PERMUTE, K_PRE_SPLIT,
+    K_CACHE_MOVE, K_COUNT
 };
 
 bool timing_enabled();
