@@ -109,6 +109,21 @@ def blob_layout(H: int, I: int, fmt: str) -> BlobLayout:
         w2 = s13 + 2 * I * H // 32
         s2 = w2 + H * I // 2
         end = s2 + H * I // 32
+    elif fmt == "nvfp4":
+        # codes, E4M3 block scales (one per 16), then a 16-byte field with
+        # the matrix's fp32 scale
+        w13 = 0
+        s13 = w13 + 2 * I * H // 2
+        w2 = s13 + 2 * I * H // 16 + 16
+        s2 = w2 + H * I // 2
+        end = s2 + H * I // 16 + 16
+    elif fmt == "fp8":
+        # one-byte E4M3 codes, then a 16-byte field with the matrix's fp32 scale
+        w13 = 0
+        s13 = w13 + 2 * I * H
+        w2 = s13 + 16
+        s2 = w2 + H * I
+        end = s2 + 16
     elif fmt == "bf16":
         w13 = 0
         w2 = 2 * I * H * 2
@@ -163,6 +178,60 @@ def encode_mxfp4(w: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
     return packed, scales
 
 
+def _round_e2m1(q: np.ndarray) -> np.ndarray:
+    """Values (already divided by their scale) -> E2M1 codes, round to nearest
+    even on the grid 0, 0.5, 1, 1.5, 2, 3, 4, 6, saturating at 6."""
+    a = np.abs(q)
+    r = np.where(a < 2.0, np.rint(a * 2.0) / 2.0,
+                 np.where(a < 4.0, np.rint(a), np.rint(a / 2.0) * 2.0))
+    r = np.minimum(r, 6.0)
+    mag = _MAG2_TO_CODE[(r * 2.0).astype(np.int64)]
+    sign = (np.signbit(q) & (mag != 0)).astype(np.uint8) << 3
+    return (mag | sign).astype(np.uint8)
+
+
+def _to_e4m3(a: np.ndarray) -> np.ndarray:
+    """fp32 -> E4M3 codes (torch's float8_e4m3fn conversion, round to nearest
+    even; inputs are kept inside the finite range by the callers)."""
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(torch.float8_e4m3fn)
+    return t.view(torch.uint8).numpy()
+
+
+def _from_e4m3(c: np.ndarray) -> np.ndarray:
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(c, dtype=np.uint8)).view(
+        torch.float8_e4m3fn).to(torch.float32).numpy()
+
+
+def encode_nvfp4(w: np.ndarray) -> tuple[np.ndarray, np.ndarray, np.float32]:
+    """Quantise fp32 rows [R][K] to NVFP4: a per-matrix fp32 scale
+    g = amax / (6 * 448), E4M3 block scales s = amax_block / (6 g) per 16
+    elements along K, E2M1 codes of w / (s g) (round to nearest even, saturating).
+    Returns (codes [R][K/2] with the even element in the low nibble, block
+    scales [R][K/16] as E4M3 bytes, g)."""
+    w = np.asarray(w, dtype=np.float32)
+    R, K = w.shape
+    amax = float(np.abs(w).max())
+    g = np.float32(amax / (6.0 * 448.0)) if amax > 0 else np.float32(1.0)
+    blocks = w.reshape(R, K // 16, 16)
+    bmax = np.abs(blocks).max(axis=2)
+    sc = _to_e4m3(np.minimum(bmax / (6.0 * g), 448.0).astype(np.float32))
+    sv = _from_e4m3(sc).astype(np.float32) * g
+    q = np.where(sv[:, :, None] > 0, blocks / np.where(sv > 0, sv, 1.0)[:, :, None], 0.0)
+    codes = _round_e2m1(q.astype(np.float32)).reshape(R, K)
+    packed = (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
+    return packed, sc.reshape(R, K // 16), g
+
+
+def encode_fp8(w: np.ndarray) -> tuple[np.ndarray, np.float32]:
+    """Quantise fp32 rows [R][K] to E4M3 codes of w / g, g = amax / 448."""
+    w = np.asarray(w, dtype=np.float32)
+    amax = float(np.abs(w).max())
+    g = np.float32(amax / 448.0) if amax > 0 else np.float32(1.0)
+    return _to_e4m3(np.clip(w / g, -448.0, 448.0)), g
+
+
 def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
     """Round fp32 to bf16 bit patterns (torch's RNE conversion)."""
     import torch
@@ -187,6 +256,37 @@ def _gauss_mxfp4_blob(rng: np.random.Generator, H: int, I: int, sigma: float) ->
     out[lay.s13:lay.w2] = s13.reshape(-1)
     out[lay.w2:lay.s2] = c2.reshape(-1)
     out[lay.s2:lay.nbytes] = s2.reshape(-1)
+    return out
+
+
+def _scale_field(g) -> np.ndarray:
+    f = np.zeros(16, dtype=np.uint8)
+    f[:4] = np.array([g], dtype=np.float32).view(np.uint8)
+    return f
+
+
+def _gauss_nvfp4_blob(rng: np.random.Generator, H: int, I: int, sigma: float) -> np.ndarray:
+    lay = blob_layout(H, I, "nvfp4")
+    out = np.empty(lay.nbytes, dtype=np.uint8)
+    for (rows, cols, o_c, o_s, o_end) in ((2 * I, H, lay.w13, lay.s13, lay.w2),
+                                          (H, I, lay.w2, lay.s2, lay.nbytes)):
+        w = rng.standard_normal((rows, cols), dtype=np.float32) * np.float32(sigma)
+        c, sc, g = encode_nvfp4(w)
+        out[o_c:o_s] = c.reshape(-1)
+        out[o_s:o_s + rows * cols // 16] = sc.reshape(-1)
+        out[o_s + rows * cols // 16:o_end] = _scale_field(g)
+    return out
+
+
+def _gauss_fp8_blob(rng: np.random.Generator, H: int, I: int, sigma: float) -> np.ndarray:
+    lay = blob_layout(H, I, "fp8")
+    out = np.empty(lay.nbytes, dtype=np.uint8)
+    for (rows, cols, o_c, o_s, o_end) in ((2 * I, H, lay.w13, lay.s13, lay.w2),
+                                          (H, I, lay.w2, lay.s2, lay.nbytes)):
+        w = rng.standard_normal((rows, cols), dtype=np.float32) * np.float32(sigma)
+        c, g = encode_fp8(w)
+        out[o_c:o_s] = c.reshape(-1)
+        out[o_s:o_end] = _scale_field(g)
     return out
 
 
@@ -257,6 +357,10 @@ def expert_blob(cfg: LayerConfig, layer: int, expert: int, shared: bool = False,
         return _marginal_mxfp4_blob(rng, H, I, WEIGHT_SIGMA)
     if cfg.weights == "gauss_bf16":
         return _gauss_bf16_blob(rng, H, I, WEIGHT_SIGMA)
+    if cfg.weights == "gauss_nvfp4":
+        return _gauss_nvfp4_blob(rng, H, I, WEIGHT_SIGMA)
+    if cfg.weights == "gauss_fp8":
+        return _gauss_fp8_blob(rng, H, I, WEIGHT_SIGMA)
     raise ValueError(cfg.weights)
 
 
@@ -358,7 +462,8 @@ def expected_unique_experts(E: int, k: int, T: int) -> float:
 
 
 __all__ = [
-    "LayerConfig", "CONFIGS", "BlobLayout", "blob_layout", "encode_mxfp4", "f32_to_bf16_bits",
+    "LayerConfig", "CONFIGS", "BlobLayout", "blob_layout", "encode_mxfp4", "encode_nvfp4",
+    "encode_fp8", "f32_to_bf16_bits",
     "expert_blob", "expert_pool", "shared_expert", "activations", "gate_weights",
     "router_logits", "zipf_permutation", "tie_logits", "pool_bytes", "expected_unique_experts",
 ]

@@ -48,6 +48,12 @@ def lib():
         L.orc_e8m0.argtypes = [C.c_int]
         L.orc_mxfp4_decode.restype = None
         L.orc_mxfp4_decode.argtypes = [P, P, C.c_long, C.c_long, P]
+        L.orc_e4m3.restype = C.c_double
+        L.orc_e4m3.argtypes = [C.c_int]
+        L.orc_nvfp4_decode.restype = None
+        L.orc_nvfp4_decode.argtypes = [P, P, C.c_float, C.c_long, C.c_long, P]
+        L.orc_fp8_decode.restype = None
+        L.orc_fp8_decode.argtypes = [P, C.c_float, C.c_long, C.c_long, P]
         L.orc_gate_logits_f32.restype = None
         L.orc_gate_logits_f32.argtypes = [P, P, C.c_int, C.c_int, C.c_int, P]
         L.orc_gate_logits_f64.restype = None
@@ -98,6 +104,27 @@ def mxfp4_decode(codes: np.ndarray, scales: np.ndarray, R: int, K: int) -> np.nd
     scales = _c(scales, np.uint8)
     out = np.empty((R, K), dtype=np.float64)
     lib().orc_mxfp4_decode(_p(codes), _p(scales), R, K, _p(out))
+    return out
+
+
+def e4m3(code: int) -> float:
+    return lib().orc_e4m3(int(code))
+
+
+def nvfp4_decode(codes: np.ndarray, scales: np.ndarray, g: float, R: int, K: int) -> np.ndarray:
+    """Rows [R][K] from E2M1 codes [R][K/2], E4M3 block scales [R][K/16] and the
+    matrix's fp32 scale g."""
+    out = np.empty((R, K), dtype=np.float64)
+    codes = _c(codes, np.uint8)
+    scales = _c(scales, np.uint8)
+    lib().orc_nvfp4_decode(_p(codes), _p(scales), float(g), R, K, _p(out))
+    return out
+
+
+def fp8_decode(codes: np.ndarray, g: float, R: int, K: int) -> np.ndarray:
+    out = np.empty((R, K), dtype=np.float64)
+    codes = _c(codes, np.uint8)
+    lib().orc_fp8_decode(_p(codes), float(g), R, K, _p(out))
     return out
 
 
@@ -169,7 +196,7 @@ def _expert_table(blobs: np.ndarray, layout):
 
 
 def _fmt_code(layout) -> int:
-    return {"bf16": 0, "mxfp4": 1}[layout.fmt]
+    return {"bf16": 0, "mxfp4": 1, "nvfp4": 2, "fp8": 3}[layout.fmt]
 
 
 def ffn_rows(x: np.ndarray, blobs: np.ndarray, layout, row_token, row_expert, want_act=False):

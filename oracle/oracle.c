@@ -9,8 +9,8 @@
  * describe: each token is sent to a few routed experts (winzheng.com page,
  * "Why Now": six routed experts per token per decoder layer, the rest of the
  * FP4-quantised pool idle), each expert being a SwiGLU feed-forward block whose
- * weights are stored in MXFP4 or BF16 (aimodeling.com/en page, "Reported
- * Numbers and Ecosystem Position": MXFP4, NVFP4, FP8 and BF16 formats).
+ * weights are stored in MXFP4, NVFP4, FP8 or BF16 (aimodeling.com/en page,
+ * "Reported Numbers and Ecosystem Position", lists these formats).
  * The pages do not spell out the routing function, the FFN form or the
  * combine; the readings taken are:
  *   - routing selects the k largest logits (ties: lower expert index first) and
@@ -101,6 +101,45 @@ void orc_mxfp4_decode(const uint8_t *codes, const uint8_t *scales, long R, long 
             int code = (c % 2 == 0) ? (byte & 15) : (byte >> 4);
             out[r * K + c] = elem[code] * scale[scales[r * (K / 32) + c / 32]];
         }
+}
+
+/* E4M3 (OCP 8-bit floating point, the variant without infinities): 1 sign,
+ * 4 exponent bits (bias 7), 3 mantissa bits; exponent field 0 is subnormal
+ * (m/8 * 2^-6); S.1111.111 is NaN, so the largest finite value is 448. */
+double orc_e4m3(int code) {
+    int s = (code >> 7) & 1, e = (code >> 3) & 15, m = code & 7;
+    double v;
+    if (e == 15 && m == 7) return NAN;
+    if (e == 0) v = ldexp((double)m / 8.0, -6);
+    else v = ldexp(1.0 + (double)m / 8.0, e - 7);
+    return s ? -v : v;
+}
+
+/* Decode rows [R][K] of NVFP4 (aimodeling.com/en page, "Reported Numbers and
+ * Ecosystem Position", lists NVFP4 among the weight formats): E2M1 codes
+ * [R][K/2] (even element in the low nibble), one E4M3 scale per 16
+ * consecutive elements of a row (scales [R][K/16]), and one fp32 scale g for
+ * the matrix: value = e2m1 * e4m3(scale) * g. */
+void orc_nvfp4_decode(const uint8_t *codes, const uint8_t *scales, float g, long R, long K,
+                      double *out) {
+    for (long r = 0; r < R; ++r)
+        for (long c = 0; c < K; ++c) {
+            uint8_t byte = codes[r * (K / 2) + c / 2];
+            int code = (c % 2 == 0) ? (byte & 15) : (byte >> 4);
+            out[r * K + c] = orc_e2m1(code) * orc_e4m3(scales[r * (K / 16) + c / 16]) * (double)g;
+        }
+}
+
+/* Decode rows [R][K] of FP8 weights: E4M3 codes [R][K] times the matrix's
+ * fp32 scale g. */
+void orc_fp8_decode(const uint8_t *codes, float g, long R, long K, double *out) {
+    for (long i = 0; i < R * K; ++i) out[i] = orc_e4m3(codes[i]) * (double)g;
+}
+
+static float read_f32(const uint8_t *p) {
+    float f;
+    memcpy(&f, p, 4);
+    return f;
 }
 
 static void decode_bf16_rows(const uint16_t *w, long n, double *out) {
@@ -222,7 +261,9 @@ int orc_permute(const int32_t *ids, int T, int k, int E,
 /* ---------------------------------------------------------------- FFN ---- */
 
 /* Host-side view of one expert blob: W13 [2I][H] (rows 0..I-1 gate, I..2I-1
- * up) and W2 [H][I], each either bf16 (scales unused) or MXFP4 codes+scales. */
+ * up) and W2 [H][I], each bf16 (scales unused), MXFP4 codes + E8M0 scales,
+ * NVFP4 codes + E4M3 scales followed by the matrix's fp32 scale, or FP8
+ * codes with the scale pointer at the matrix's fp32 scale. */
 typedef struct {
     const void *w13;
     const uint8_t *s13;
@@ -234,9 +275,17 @@ static void decode_expert(const orc_expert *x, int fmt, int H, int I, double *w1
     if (fmt == 0) {
         decode_bf16_rows((const uint16_t *)x->w13, (long)2 * I * H, w13);
         decode_bf16_rows((const uint16_t *)x->w2, (long)H * I, w2);
-    } else {
+    } else if (fmt == 1) {
         orc_mxfp4_decode((const uint8_t *)x->w13, x->s13, 2L * I, H, w13);
         orc_mxfp4_decode((const uint8_t *)x->w2, x->s2, H, I, w2);
+    } else if (fmt == 2) {
+        orc_nvfp4_decode((const uint8_t *)x->w13, x->s13, read_f32(x->s13 + 2L * I * H / 16),
+                         2L * I, H, w13);
+        orc_nvfp4_decode((const uint8_t *)x->w2, x->s2, read_f32(x->s2 + (long)H * I / 16), H, I,
+                         w2);
+    } else {
+        orc_fp8_decode((const uint8_t *)x->w13, read_f32(x->s13), 2L * I, H, w13);
+        orc_fp8_decode((const uint8_t *)x->w2, read_f32(x->s2), H, I, w2);
     }
 }
 
@@ -247,7 +296,8 @@ static void decode_expert(const orc_expert *x, int fmt, int H, int I, double *w1
  *   y_n = sum_i a_i W2[n][i]
  * Everything in double. y: [nrows][H]; act (optional): [nrows][I].
  * Each expert is decoded once, then all of its rows are evaluated.
- * fmt: 0 = bf16, 1 = MXFP4. Returns -1 on a bad expert index or allocation. */
+ * fmt: 0 = bf16, 1 = MXFP4, 2 = NVFP4, 3 = FP8. Returns -1 on a bad expert
+ * index or allocation. */
 int orc_ffn_rows(const uint16_t *x, int H, int I, int fmt, const orc_expert *experts, int E,
                  long nrows, const int32_t *row_token, const int32_t *row_expert,
                  double *y, double *act) {

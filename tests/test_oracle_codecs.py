@@ -128,3 +128,101 @@ def test_bf16_to_f64_exact(orc):
         t = torch.from_numpy(np.array([bits], dtype=np.uint16).view(np.int16))
         want = float(t.view(torch.bfloat16).float())
         assert orc.bf16_to_f64(bits) == want
+
+
+# ------------------------------------------------------------ E4M3, NVFP4, FP8 --
+
+def _torch_e4m3(codes):
+    """torch's float8_e4m3fn -> float64 (library routine)."""
+    t = torch.from_numpy(np.ascontiguousarray(codes, dtype=np.uint8))
+    return t.view(torch.float8_e4m3fn).double().numpy()
+
+
+def test_e4m3_all_codes_match_torch(orc):
+    want = _torch_e4m3(np.arange(256, dtype=np.uint8))
+    for c in range(256):
+        got = orc.e4m3(c)
+        if c & 0x7F == 0x7F:
+            assert math.isnan(got) and math.isnan(want[c]), c
+        else:
+            assert got == want[c], (c, got, want[c])
+            assert math.copysign(1.0, got) == math.copysign(1.0, want[c]), c
+
+
+@pytest.mark.parametrize("code,value", [
+    (0x38, 1.0), (0x3C, 1.5), (0x40, 2.0), (0x7E, 448.0), (0x01, 2.0 ** -9),
+    (0x07, 7 * 2.0 ** -9), (0x08, 2.0 ** -6), (0xB8, -1.0), (0x30, 0.5),
+])
+def test_e4m3_closed_forms(orc, code, value):
+    """(1 + m/8) 2^(e-7) for normal codes, m/8 2^-6 for subnormal ones."""
+    assert orc.e4m3(code) == value
+
+
+def test_nvfp4_worked_example(orc):
+    """Two 16-element blocks of one row, hand-computed: block 0 has scale 0x38
+    (1.0), block 1 has 0x44 (3.0); matrix scale 0.5."""
+    codes = np.zeros(16, np.uint8)
+    codes[0] = 0x1 | (0x2 << 4)          # elements 0, 1: 0.5, 1.0
+    codes[7] = 0xF | (0x7 << 4)          # elements 14, 15: -6, 6
+    codes[8] = 0x3 | (0xB << 4)          # elements 16, 17: 1.5, -1.5
+    codes[15] = 0x5 | (0x0 << 4)         # elements 30, 31: 3, 0
+    scales = np.array([0x38, 0x44], np.uint8)
+    got = orc.nvfp4_decode(codes, scales, 0.5, 1, 32)[0]
+    want = np.zeros(32)
+    want[0], want[1], want[14], want[15] = 0.25, 0.5, -3.0, 3.0
+    want[16], want[17], want[30] = 2.25, -2.25, 4.5
+    assert np.array_equal(got, want)
+
+
+def test_nvfp4_block_structure(orc):
+    """Changing the scale byte of block b of row r changes exactly elements
+    16b..16b+15 of row r, by the ratio of the two scales; g scales everything."""
+    rng = np.random.default_rng(5)
+    R, K = 3, 64
+    codes = rng.integers(0, 256, size=(R, K // 2), dtype=np.uint8)
+    scales = rng.integers(0x20, 0x50, size=(R, K // 16), dtype=np.uint8)
+    base = orc.nvfp4_decode(codes, scales, 1.0, R, K)
+    assert np.array_equal(orc.nvfp4_decode(codes, scales, 0.25, R, K), base * 0.25)
+    for r, b in ((0, 0), (1, 3), (2, 2)):
+        s2 = scales.copy()
+        s2[r, b] = 0x38 if scales[r, b] != 0x38 else 0x40
+        d = orc.nvfp4_decode(codes, s2, 1.0, R, K)
+        changed = np.zeros((R, K), bool)
+        changed[r, 16 * b:16 * b + 16] = True
+        assert np.array_equal(d[~changed], base[~changed])
+        ratio = orc.e4m3(s2[r, b]) / orc.e4m3(scales[r, b])
+        assert np.array_equal(d[changed], base[changed] * ratio)
+
+
+def test_nvfp4_encoder_roundtrip_error_bound(orc):
+    """The generator's quantiser and the oracle's decoder agree on layout: every
+    decoded value lies within one E2M1 grid unit (at the block's decoded scale)
+    of the input."""
+    rng = np.random.default_rng(13)
+    w = rng.standard_normal((16, 256)).astype(np.float32) * np.float32(0.02)
+    codes, scales, g = synth.encode_nvfp4(w)
+    dec = orc.nvfp4_decode(codes, scales, g, 16, 256)
+    unit = np.repeat(_torch_e4m3(scales), 16, axis=1) * float(g)
+    assert (np.abs(dec - w) <= unit + 1e-12).all()
+    # and much closer on average than a wrong block mapping would be
+    assert np.abs(dec - w).mean() < 0.2 * np.abs(w).mean()
+
+
+def test_fp8_decode_matches_torch(orc):
+    rng = np.random.default_rng(17)
+    R, K = 5, 64
+    codes = rng.integers(0, 256, size=(R, K), dtype=np.uint8)
+    codes[(codes & 0x7F) == 0x7F] = 0x38          # no NaN codes in weights
+    got = orc.fp8_decode(codes, 0.375, R, K)
+    assert np.array_equal(got, _torch_e4m3(codes) * 0.375)
+
+
+def test_fp8_encoder_roundtrip_error_bound(orc):
+    rng = np.random.default_rng(19)
+    w = rng.standard_normal((8, 128)).astype(np.float32) * np.float32(0.02)
+    codes, g = synth.encode_fp8(w)
+    dec = orc.fp8_decode(codes, g, 8, 128)
+    # E4M3 keeps 4 significant bits: relative error <= 2^-4 above the subnormals
+    big = np.abs(w) > float(g) * 2.0 ** -6
+    assert (np.abs(dec - w)[big] <= 2.0 ** -4 * np.abs(w)[big] + 1e-12).all()
+    assert (np.abs(dec - w)[~big] <= float(g) * 2.0 ** -10 + 1e-12).all()

@@ -206,13 +206,35 @@ def _dequant_blob(blob, lay):
         s = np.repeat(scales.reshape(R, K // 32).astype(np.float64), 32, axis=1)
         return torch.from_numpy(lut[c] * np.exp2(s - 127))
 
+    def e4m3(codes):   # torch's float8_e4m3fn conversion (library routine)
+        t = torch.from_numpy(np.ascontiguousarray(codes, dtype=np.uint8))
+        return t.view(torch.float8_e4m3fn).double()
+
+    def f32_at(b, o):
+        return float(np.frombuffer(b[o:o + 4].tobytes(), dtype=np.float32)[0])
+
+    def nv(codes, scales, g, R, K):
+        c = np.empty((R, K), np.int64)
+        cc = codes.reshape(R, K // 2)
+        c[:, 0::2], c[:, 1::2] = cc & 15, cc >> 4
+        s = torch.repeat_interleave(e4m3(scales.reshape(R, K // 16)), 16, dim=1)
+        return torch.from_numpy(lut[c]) * s * g
+
     H, I = lay.H, lay.I
     if lay.fmt == "bf16":
         w13 = _bits_to_f64(blob[lay.w13:lay.w2].view(np.uint16).reshape(2 * I, H))
         w2 = _bits_to_f64(blob[lay.w2:lay.nbytes].view(np.uint16).reshape(H, I))
-    else:
+    elif lay.fmt == "mxfp4":
         w13 = mx(blob[lay.w13:lay.s13], blob[lay.s13:lay.w2], 2 * I, H)
         w2 = mx(blob[lay.w2:lay.s2], blob[lay.s2:lay.nbytes], H, I)
+    elif lay.fmt == "nvfp4":
+        n13, n2 = 2 * I * H // 16, H * I // 16
+        w13 = nv(blob[lay.w13:lay.s13], blob[lay.s13:lay.s13 + n13], f32_at(blob, lay.s13 + n13),
+                 2 * I, H)
+        w2 = nv(blob[lay.w2:lay.s2], blob[lay.s2:lay.s2 + n2], f32_at(blob, lay.s2 + n2), H, I)
+    else:
+        w13 = e4m3(blob[lay.w13:lay.s13]).reshape(2 * I, H) * f32_at(blob, lay.s13)
+        w2 = e4m3(blob[lay.w2:lay.s2]).reshape(H, I) * f32_at(blob, lay.s2)
     return w13, w2
 
 
@@ -223,11 +245,13 @@ def _torch_swiglu(x64, w13, w2, I):
 
 
 def _small_cfg(fmt, H=256, E=6, k=2, I=160, T=8):
-    weights = "gauss_bf16" if fmt == "bf16" else "gauss_mxfp4"
-    return synth.LayerConfig("small", H, E, k, I, fmt, 0, "uniform", (T,), weights, seed=9)
+    return synth.LayerConfig("small", H, E, k, I, fmt, 0, "uniform", (T,), "gauss_" + fmt, seed=9)
 
 
-@pytest.mark.parametrize("fmt", ["bf16", "mxfp4"])
+FORMATS = ["bf16", "mxfp4", "nvfp4", "fp8"]
+
+
+@pytest.mark.parametrize("fmt", FORMATS)
 def test_single_expert_layer_is_plain_swiglu(orc, fmt):
     """E=1, k=1: the layer reduces to one SwiGLU FFN; compare with torch fp64 matmul."""
     cfg = _small_cfg(fmt, E=1, k=1)
@@ -245,7 +269,7 @@ def test_single_expert_layer_is_plain_swiglu(orc, fmt):
     assert np.array_equal(r["out_bf16"], ob)
 
 
-@pytest.mark.parametrize("fmt", ["bf16", "mxfp4"])
+@pytest.mark.parametrize("fmt", FORMATS)
 def test_dense_all_experts_equals_sparse(orc, fmt):
     """Brute force: every expert on every token, masked by the routing weights."""
     cfg = _small_cfg(fmt, E=6, k=3, T=8)
