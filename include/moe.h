@@ -49,6 +49,23 @@
  *               16rb + l%16, columns 128s + 32(l/16) + 0..31.
  *     Sizes equal the interchange layout's. Requires H and I to be multiples
  *     of 128.
+ *   MOE_W_NVFP4 (aimodeling.com/en page, "Reported Numbers and Ecosystem
+ *     Position", lists NVFP4 among the weight formats): value = E2M1 code x
+ *     E4M3 block scale x one fp32 scale per matrix; one E4M3 scale per 16
+ *     consecutive elements of a row. Interchange layout: codes as MXFP4, then
+ *     scales [rows][K/16] (one byte each), then the matrix's fp32 scale in 16
+ *     bytes (the scale pointer s13 / s2 points at the block scales; the fp32
+ *     scale sits at s + rows*K/16). Kernel layout: codes as the kernel MXFP4
+ *     layout; block scales 128 bytes per block at (rb*nslab + s)*128, bytes
+ *     2l and 2l+1 holding the scales of columns 128s + 32(l/16) + 0..15 and
+ *     + 16..31 of row 16rb + l%16; the fp32 scale stays at s + rows*K/16.
+ *   MOE_W_FP8 (same page, FP8): value = E4M3 code x one fp32 scale per matrix.
+ *     Interchange layout: rows of one-byte codes, then the fp32 scale in 16
+ *     bytes (s13 / s2 point at it). Kernel layout: 2048-byte blocks at
+ *     (rb*nslab + s)*2048; bytes 32l..32l+31 are row 16rb + l%16, columns
+ *     128s + 32(l/16) + 0..31.
+ *   E4M3 is the OCP 8-bit format with 4 exponent bits (bias 7) and 3 mantissa
+ *   bits, no infinities, NaN = S.1111.111, largest finite 448.
  *   MOE_W_BF16: rows of bf16, row-major; scale pointers are ignored.
  * All weight matrix starts must be 16-byte aligned.
  */
@@ -71,7 +88,7 @@ typedef enum {
     MOE_EBUSY = -5          /* resource in use */
 } moe_err;
 
-typedef enum { MOE_W_BF16 = 0, MOE_W_MXFP4 = 1 } moe_wfmt;
+typedef enum { MOE_W_BF16 = 0, MOE_W_MXFP4 = 1, MOE_W_NVFP4 = 2, MOE_W_FP8 = 3 } moe_wfmt;
 
 /* One expert's weights. w13/w2 point to codes (MXFP4) or bf16 values; s13/s2
  * to E8M0 scales (MXFP4 only). */
@@ -154,8 +171,12 @@ int moe_route_permute(const uint16_t *x_bf16, const uint16_t *wg_bf16, const flo
  * FP8 x FP4 matrix cores as two E4M3 terms hi + lo with one E8M0 scale per
  * 32 elements: |hi + lo - v| <= 2^-8 |v| + 2^-22 max|block| for every v.
  * experts: device array [E] of moe_expert_w; entries of experts that receive
- * no pair are never read. x_bf16 [T][H]. fmt: MOE_W_MXFP4 (kernel layout,
- * H and I multiples of 128) or MOE_W_BF16 (H and I multiples of 32).
+ * no pair are never read. x_bf16 [T][H]. fmt: MOE_W_MXFP4, MOE_W_NVFP4 or
+ * MOE_W_FP8 (kernel layouts, H and I multiples of 128) or MOE_W_BF16 (H and
+ * I multiples of 32). NVFP4 and FP8 always run the weight-streaming kernels
+ * (the tiled kernels' matrix-core instruction takes only E8M0 block scales);
+ * there the weights enter the bf16 products as bf16(code x block scale),
+ * which is exact, and the per-matrix fp32 scale multiplies the fp32 sums.
  * ws: device workspace of at least the ffn size from moe_workspace_size.
  * Requires E <= 512.
  * The shared (always-on) expert is this call with E = 1, k = 1,
@@ -186,6 +207,15 @@ int moe_combine(const void *y, int y_is_fp32, const float *topk_w, const void *y
 int moe_pack_mxfp4(const void *src, void *dst, int n, size_t src_stride, size_t dst_stride,
                    int H, int I, size_t lay_w13, size_t lay_s13, size_t lay_w2, size_t lay_s2,
                    void *stream);
+
+/*
+ * moe_pack_weights -- moe_pack_mxfp4 for any of MOE_W_MXFP4, MOE_W_NVFP4 and
+ * MOE_W_FP8: interchange -> kernel layout of n blobs (same arguments; the
+ * per-matrix fp32 scales are copied as they are).
+ */
+int moe_pack_weights(int fmt, const void *src, void *dst, int n, size_t src_stride,
+                     size_t dst_stride, int H, int I, size_t lay_w13, size_t lay_s13,
+                     size_t lay_w2, size_t lay_s2, void *stream);
 
 /* Device workspace bytes needed by moe_permute and moe_expert_ffn for these
  * sizes (host call, no device work). Either output pointer may be NULL. */

@@ -14,7 +14,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libmoe.so")
 
 MOE_OK, MOE_EINVAL, MOE_ENOMEM, MOE_EHIP, MOE_EUNSUPPORTED, MOE_EBUSY = 0, -1, -2, -3, -4, -5
-MOE_W_BF16, MOE_W_MXFP4 = 0, 1
+MOE_W_BF16, MOE_W_MXFP4, MOE_W_NVFP4, MOE_W_FP8 = 0, 1, 2, 3
 MOE_OPT_FFN_PATH = 1
 MOE_OPT_TIMING = 2
 
@@ -22,7 +22,7 @@ MOE_OPT_TIMING = 2
 EXPORTS = [
     "moe_strerror", "moe_last_hip_error", "moe_route", "moe_permute", "moe_expert_ffn",
     "moe_combine", "moe_workspace_size", "moe_set_option", "moe_get_option", "moe_kernel_name",
-    "moe_timing_query", "moe_pack_mxfp4", "moe_route_permute",
+    "moe_timing_query", "moe_pack_mxfp4", "moe_pack_weights", "moe_route_permute",
     "expert_cache_reserve", "expert_cache_prefetch", "expert_cache_evict", "expert_cache_stats",
     "expert_cache_slots", "expert_cache_slot_of", "expert_cache_destroy", "expert_cache_resize",
 ]
@@ -68,6 +68,7 @@ def load(path: str | None = None):
         "moe_kernel_name": (C.c_char_p, [I]),
         "moe_timing_query": (I, [I, C.POINTER(C.c_longlong), C.POINTER(C.c_double)]),
         "moe_pack_mxfp4": (I, [P, P, I, Z, Z, I, I, Z, Z, Z, Z, P]),
+        "moe_pack_weights": (I, [I, P, P, I, Z, Z, I, I, Z, Z, Z, Z, P]),
         "expert_cache_reserve": (I, [C.POINTER(P), P, Z, Z, I, I, P, Z, Z, Z, Z, P]),
         "expert_cache_prefetch": (I, [P, I, P, I, P, C.POINTER(P)]),
         "expert_cache_evict": (I, [P, I, P, I]),
@@ -152,6 +153,12 @@ def moe_pack_mxfp4(src, dst, n, src_stride, dst_stride, H, I, layout, stream=Non
     return _check("moe_pack_mxfp4", load().moe_pack_mxfp4(
         _ptr(src), _ptr(dst), n, src_stride, dst_stride, H, I, layout.w13, layout.s13, layout.w2,
         layout.s2, _stream(stream)))
+
+
+def moe_pack_weights(fmt, src, dst, n, src_stride, dst_stride, H, I, layout, stream=None):
+    return _check("moe_pack_weights", load().moe_pack_weights(
+        fmt, _ptr(src), _ptr(dst), n, src_stride, dst_stride, H, I, layout.w13, layout.s13,
+        layout.w2, layout.s2, _stream(stream)))
 
 
 def moe_workspace_size(T, k, H, I, E):

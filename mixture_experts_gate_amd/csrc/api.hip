@@ -182,8 +182,9 @@ extern "C" int moe_expert_ffn(const uint16_t *x_bf16, const int32_t *sorted_pair
     // as a 512-bit mask
     if (T < 0 || k < 1 || E < 1 || E > 512 || H < 32 || I < 32 || H % 32 || I % 32)
         return MOE_EINVAL;
-    if (fmt != MOE_W_MXFP4 && fmt != MOE_W_BF16) return MOE_EINVAL;
-    if (fmt == MOE_W_MXFP4 && (H % 128 || I % 128)) return MOE_EINVAL;
+    if (fmt != MOE_W_MXFP4 && fmt != MOE_W_BF16 && fmt != MOE_W_NVFP4 && fmt != MOE_W_FP8)
+        return MOE_EINVAL;
+    if (fmt != MOE_W_BF16 && (H % 128 || I % 128)) return MOE_EINVAL;
     if (T == 0) return MOE_OK;
     if (!x_bf16 || !sorted_pair || !offsets || !experts || !y || !ws) return MOE_EINVAL;
     const long n = (long)T * k;

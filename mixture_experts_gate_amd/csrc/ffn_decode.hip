@@ -87,6 +87,71 @@ struct WFrag<MOE_W_MXFP4> {
     __device__ __forceinline__ bf16x8 get(int j) const { return dequant8_fp4(q[j], e8m0_to_f32(s)); }
 };
 
+// NVFP4: the lane's 32 codes span two 16-element blocks (dwords 0-1 and 2-3),
+// each with an E4M3 scale. The convert applies only a power of two, so a
+// block scale v is split into 2^floor(log2 v) (in the convert) and its
+// mantissa factor in [1, 2) (one fp32 multiply per element); both products
+// are exact, as is the bf16 rounding of code x scale (at most 6 significant
+// bits). The matrix's fp32 scale multiplies the sums instead (epilogue).
+template <>
+struct WFrag<MOE_W_NVFP4> {
+    u32x4 q;
+    uint32_t s;     // two E4M3 block-scale bytes
+    __device__ __forceinline__ void pin() { asm volatile("" : "+v"(q), "+v"(s)); }
+    __device__ __forceinline__ void load_block(buf_rsrc codes, buf_rsrc scales, uint32_t chunk,
+                                               int lane, bool ok) {
+        q = buf_load_nt16(codes, ok ? chunk * 1024u + lane * 16 : kBufOff);
+        s = __builtin_amdgcn_raw_buffer_load_b16(scales, ok ? chunk * 128u + lane * 2 : kBufOff,
+                                                 0, kBufNt);
+    }
+    __device__ __forceinline__ bf16x8 get(int j) const {
+        typedef __attribute__((ext_vector_type(2))) float f32x2;
+        const uint32_t sb = (j >> 1) ? (s >> 8) : s;
+        const float v = __builtin_amdgcn_cvt_f32_fp8((int)sb, 0);         // block scale
+        const uint32_t b = __float_as_uint(v);
+        const float p2 = __uint_as_float(b & 0x7F800000u);
+        const float mf = v == 0.0f ? 0.0f : __uint_as_float((b & 0x007FFFFFu) | 0x3F800000u);
+        const f32x2 f0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q[j], p2, 0);
+        const f32x2 f1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q[j], p2, 1);
+        const f32x2 f2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q[j], p2, 2);
+        const f32x2 f3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q[j], p2, 3);
+        bf16x8 r = {(__bf16)(f0[0] * mf), (__bf16)(f0[1] * mf), (__bf16)(f1[0] * mf),
+                    (__bf16)(f1[1] * mf), (__bf16)(f2[0] * mf), (__bf16)(f2[1] * mf),
+                    (__bf16)(f3[0] * mf), (__bf16)(f3[1] * mf)};
+        return r;
+    }
+};
+
+// FP8 E4M3: 32 one-byte codes per lane (two 16-byte loads); codes enter the
+// products exactly (scale 1) and the matrix's fp32 scale multiplies the sums.
+template <>
+struct WFrag<MOE_W_FP8> {
+    u32x4 q[2];
+    __device__ __forceinline__ void pin() { asm volatile("" : "+v"(q[0]), "+v"(q[1])); }
+    __device__ __forceinline__ void load_block(buf_rsrc codes, buf_rsrc, uint32_t chunk, int lane,
+                                               bool ok) {
+        q[0] = buf_load_nt16(codes, ok ? chunk * 2048u + lane * 32 : kBufOff);
+        q[1] = buf_load_nt16(codes, ok ? chunk * 2048u + lane * 32 + 16 : kBufOff);
+    }
+    __device__ __forceinline__ bf16x8 get(int j) const {
+        const u32x4 &w = q[j >> 1];
+        const uint32_t lo = w[(j & 1) * 2], hi = w[(j & 1) * 2 + 1];
+        const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false);
+        const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true);
+        const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false);
+        const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true);
+        bf16x8 r = {a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+        return r;
+    }
+};
+
+// Formats whose kernel layout is the 16 x 128 block tiling.
+constexpr bool blocked_fmt(int fmt) {
+    return fmt == MOE_W_MXFP4 || fmt == MOE_W_NVFP4 || fmt == MOE_W_FP8;
+}
+// Formats with one fp32 scale per matrix, applied to the sums.
+constexpr bool tensor_scaled(int fmt) { return fmt == MOE_W_NVFP4 || fmt == MOE_W_FP8; }
+
 template <>
 struct WFrag<MOE_W_BF16> {
     u32x4 q[4];
@@ -162,15 +227,24 @@ struct DecArgs {
 
 // Expert-level state of the tile being processed (wavefront-uniform: read
 // with scalar loads, so fetching it never waits for the weights in flight).
-struct ExpertState {
+// the matrix's fp32 scale, a member only for the formats that have one
+template <bool HAS>
+struct TensorScale {
+    float g;
+};
+template <>
+struct TensorScale<false> {};
+
+template <int FMT>
+struct ExpertState : TensorScale<tensor_scaled(FMT)> {
     int a, e, row0, n_e;
     const uint8_t *w, *s;           // matrix base (W13 or W2) and its scales
-    buf_rsrc wr, sr;                // the same as ranged buffer resources (MXFP4)
+    buf_rsrc wr, sr;                // the same as ranged buffer resources (block formats)
 };
 
-template <int STAGE>
+template <int STAGE, int FMT>
 __device__ __forceinline__ void expert_state(const DecArgs &A, const ActiveSet &act, int a,
-                                             ExpertState &st) {
+                                             ExpertState<FMT> &st) {
     st.a = a;
     st.e = act.nth(a);
     const MOE_CONST int32_t *off = as_scalar(A.offsets);
@@ -180,8 +254,11 @@ __device__ __forceinline__ void expert_state(const DecArgs &A, const ActiveSet &
     st.w = reinterpret_cast<const uint8_t *>(STAGE == 1 ? W->w13 : W->w2);
     st.s = reinterpret_cast<const uint8_t *>(STAGE == 1 ? W->s13 : W->s2);
     const uint32_t elems = (uint32_t)(STAGE == 1 ? 2 * A.I : A.H) * (uint32_t)A.K;
-    st.wr = make_rsrc(st.w, elems / 2);
-    st.sr = make_rsrc(st.s, elems / 32);
+    st.wr = make_rsrc(st.w, FMT == MOE_W_FP8 ? elems : elems / 2);
+    st.sr = make_rsrc(st.s, FMT == MOE_W_NVFP4 ? elems / 16 : elems / 32);
+    if constexpr (FMT == MOE_W_NVFP4)
+        st.g = *as_scalar(reinterpret_cast<const float *>(st.s + elems / 16));
+    if constexpr (FMT == MOE_W_FP8) st.g = *as_scalar(reinterpret_cast<const float *>(st.s));
 }
 
 // 16-row block index (within the stage's matrix) of block b of tile rt.
@@ -198,9 +275,9 @@ __device__ __forceinline__ long tile_block(const DecArgs &A, int rt, int b) {
 // FULL: the KS wavefronts x SPW slabs cover the K slabs exactly (no bounds checks).
 // `on` = false issues the same loads switched off (MXFP4; see buf_rsrc).
 template <int FMT, int STAGE, int SPW, int NB, bool FULL>
-__device__ __forceinline__ void load_tile(const DecArgs &A, const ExpertState &st, int rt, int wv,
+__device__ __forceinline__ void load_tile(const DecArgs &A, const ExpertState<FMT> &st, int rt, int wv,
                                           int lane, WFrag<FMT> (&f)[SPW][NB], bool on = true) {
-    if constexpr (FMT == MOE_W_MXFP4) {
+    if constexpr (blocked_fmt(FMT)) {
         const int nslab = A.K / 128;
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
@@ -230,8 +307,8 @@ __device__ __forceinline__ void load_tile(const DecArgs &A, const ExpertState &s
 
 // Token operand of pass p (rows p*16 .. p*16+15 of the expert), K slabs of
 // this wavefront; for stage 2 also the pair index each row's output goes to.
-template <int STAGE, int SPW>
-__device__ __forceinline__ void load_tokens(const DecArgs &A, const ExpertState &st, int p, int wv,
+template <int STAGE, int SPW, class ES>
+__device__ __forceinline__ void load_tokens(const DecArgs &A, const ES &st, int p, int wv,
                                             int m, int c, u32x4 (&xr)[SPW][4], int &pidx) {
     const int nblk = A.K / 32;
     const int r = p * kPass + m;
@@ -265,8 +342,8 @@ template <int FMT, int STAGE, int SPW, int KS, int NB, bool YF32, bool FULL, int
 __device__ __forceinline__ void dec_step(const DecArgs &A, const ActiveSet &act,
                                          float (&red)[2][KS > 1 ? KS - 1 : 1][NB][4][kWave],
                                          WFrag<FMT> (&wc)[SPW][NB], WFrag<FMT> (&wn)[SPW][NB],
-                                         u32x4 (&xr)[SPW][4], const ExpertState &cur,
-                                         const ExpertState &prev, ExpertState &nxt,
+                                         u32x4 (&xr)[SPW][4], const ExpertState<FMT> &cur,
+                                         const ExpertState<FMT> &prev, ExpertState<FMT> &nxt,
                                          int &pidx, int &x_key, int &buf, int rt, TilePos pn,
                                          bool pf, int lane, int wv, int m, int c) {
 
@@ -280,7 +357,7 @@ __device__ __forceinline__ void dec_step(const DecArgs &A, const ActiveSet &act,
         // `prev` holds the state of the tile before it. Issued, switched off,
         // also past the end (see buf_rsrc).
         const int an = pf ? pn.a : prev.a;
-        if (an != prev.a) expert_state<STAGE>(A, act, an, nxt);
+        if (an != prev.a) expert_state<STAGE, FMT>(A, act, an, nxt);
         else nxt = prev;
         load_tile<FMT, STAGE, SPW, NB, FULL>(A, nxt, pf ? pn.rt : 0, wv, lane, wn, pf);
         for (int p = 0; p * kPass < cur.n_e; ++p) {
@@ -322,6 +399,12 @@ __device__ __forceinline__ void dec_step(const DecArgs &A, const ActiveSet &act,
                     for (int i = 0; i < 4; ++i)
 #pragma unroll
                         for (int w = 0; w < KS - 1; ++w) acc[b][i] += red[buf][w][b][i][lane];
+                if constexpr (tensor_scaled(FMT)) {
+#pragma unroll
+                    for (int b = 0; b < NB; ++b)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) acc[b][i] *= cur.g;
+                }
                 const int r = p * kPass + m;
                 if (r < cur.n_e) {
                     if (STAGE == 1) {
@@ -391,16 +474,16 @@ __global__ __launch_bounds__(kWave *KS) void ffn_dec_kernel(DecArgs A) {
     // between them, so nothing waits for a prefetch before it is needed).
     // Slots past the end repeat the last tile's position and load nothing.
     constexpr int D = STAGE == 2 ? kDepth2 : kDepth;
-    ExpertState es[D];
+    ExpertState<FMT> es[D];
     TilePos pos[D];
     WFrag<FMT> wr[D][SPW][NB];
     pos[0] = TilePos{t0 / A.nrt, t0 % A.nrt};
-    expert_state<STAGE>(A, act, pos[0].a, es[0]);
+    expert_state<STAGE, FMT>(A, act, pos[0].a, es[0]);
 #pragma unroll
     for (int d = 1; d < D - 1; ++d) {
         pos[d] = d < n ? advance(pos[d - 1], sa, srt, A.nrt) : pos[d - 1];
         if (pos[d].a == es[d - 1].a) es[d] = es[d - 1];
-        else expert_state<STAGE>(A, act, pos[d].a, es[d]);
+        else expert_state<STAGE, FMT>(A, act, pos[d].a, es[d]);
     }
     // the first tile's token operand is requested before any weights, so that
     // resolving its row indices does not wait behind the weight prefetch
@@ -519,6 +602,12 @@ int ffn_decode(const uint16_t *x, const int32_t *sorted_pair, const int32_t *off
     if (fmt == MOE_W_MXFP4)
         return ffn_decode_fmt<MOE_W_MXFP4>(x, sorted_pair, offsets, experts, T, k, H, I, E, y,
                                            y_is_fp32, act, s);
+    if (fmt == MOE_W_NVFP4)
+        return ffn_decode_fmt<MOE_W_NVFP4>(x, sorted_pair, offsets, experts, T, k, H, I, E, y,
+                                           y_is_fp32, act, s);
+    if (fmt == MOE_W_FP8)
+        return ffn_decode_fmt<MOE_W_FP8>(x, sorted_pair, offsets, experts, T, k, H, I, E, y,
+                                         y_is_fp32, act, s);
     return ffn_decode_fmt<MOE_W_BF16>(x, sorted_pair, offsets, experts, T, k, H, I, E, y,
                                       y_is_fp32, act, s);
 }

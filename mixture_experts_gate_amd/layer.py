@@ -12,7 +12,8 @@ import torch
 from . import _lib
 from .synth import blob_layout
 
-FMT = {"bf16": _lib.MOE_W_BF16, "mxfp4": _lib.MOE_W_MXFP4}
+FMT = {"bf16": _lib.MOE_W_BF16, "mxfp4": _lib.MOE_W_MXFP4, "nvfp4": _lib.MOE_W_NVFP4,
+       "fp8": _lib.MOE_W_FP8}
 
 
 def expert_table(base_ptr: int, n: int, layout, stride: int | None = None, device="cuda"):
@@ -30,17 +31,17 @@ def expert_table(base_ptr: int, n: int, layout, stride: int | None = None, devic
 
 def pack_to_device(pool: np.ndarray, layout, device="cuda"):
     """Upload expert blobs [n][nbytes] in the interchange layout and return a
-    device tensor of the same shape in the kernel layout (MXFP4 blocks packed
-    by the library; bf16 blobs are used as they are)."""
+    device tensor of the same shape in the kernel layout (MXFP4, NVFP4 and FP8
+    blocks packed by the library; bf16 blobs are used as they are)."""
     host = torch.from_numpy(np.ascontiguousarray(pool, dtype=np.uint8))
     if host.dim() == 1:
         host = host[None, :]
     src = host.to(device)
-    if layout.fmt != "mxfp4":
+    if layout.fmt == "bf16":
         return src
     dst = torch.empty_like(src)
     n, nb = src.shape
-    _lib.moe_pack_mxfp4(src, dst, n, nb, nb, layout.H, layout.I, layout)
+    _lib.moe_pack_weights(FMT[layout.fmt], src, dst, n, nb, nb, layout.H, layout.I, layout)
     torch.cuda.synchronize()
     del src
     return dst

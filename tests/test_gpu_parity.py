@@ -461,3 +461,72 @@ def test_pack_mxfp4_layout(lib):
     lib.moe_pack_mxfp4(d_src, d_dst, n, lay.nbytes, lay.nbytes, H, I, lay)
     torch.cuda.synchronize()
     assert np.array_equal(d_dst.cpu().numpy(), want)
+
+
+# ------------------------------------------------------- NVFP4 and FP8 weights --
+
+_FMT_CASES = [
+    # (fmt, H, I, E, k, T, logits kind)
+    ("nvfp4", 1024, 512, 16, 4, 1, "uniform"),
+    ("nvfp4", 1024, 512, 16, 4, 64, "uniform"),
+    ("nvfp4", 768, 384, 16, 4, 200, "skew"),
+    ("fp8", 1024, 512, 16, 4, 1, "uniform"),
+    ("fp8", 1024, 512, 16, 4, 64, "uniform"),
+    ("fp8", 768, 384, 16, 4, 200, "skew"),
+]
+
+
+@pytest.mark.parametrize("fmt,H,I,E,k,T,kind", _FMT_CASES,
+                         ids=[f"{c[0]}-H{c[1]}-I{c[2]}-T{c[5]}-{c[6]}" for c in _FMT_CASES])
+def test_layer_nvfp4_fp8_weights(lib, orc, fmt, H, I, E, k, T, kind):
+    """Layers whose experts are stored in NVFP4 or FP8 (weight-streaming
+    kernels), against the oracle's exact decode: small and large batches,
+    skewed routing with several token passes per expert, 6/3- and 8/4-slab
+    contractions."""
+    _announce(f"layer: {fmt} weights H={H} I={I} E={E} k={k} T={T} ({kind})")
+    cfg = synth.LayerConfig(f"{fmt}_test", H, E, k, I, fmt, 0, "uniform", (T,), "gauss_" + fmt,
+                            seed=23)
+    w = Workload(cfg)
+    x = synth.activations(cfg, T, step=2)
+    lg = synth.router_logits(cfg, T, step=2) if kind == "uniform" else _perm_case(T, E, k, kind)
+    L, out = run_layer(w, T, x, logits=lg)
+    _check_layer_full(orc, w, T, x, L, out, logits=lg)
+
+
+@pytest.mark.parametrize("fmt", ["nvfp4", "fp8"])
+def test_pack_nvfp4_fp8_layout(lib, fmt):
+    """The kernel layouts of NVFP4 and FP8 as the header states them, built
+    independently in numpy from random interchange bytes."""
+    _announce(f"pack: interchange -> kernel {fmt} layout")
+    H, I, n = 256, 384, 3
+    lay = synth.blob_layout(H, I, fmt)
+    rng = np.random.default_rng(22)
+    src = rng.integers(0, 256, size=(n, lay.nbytes), dtype=np.uint8)
+
+    def nv(codes, scales, R, K):
+        nslab = K // 128
+        c = codes.reshape(R // 16, 16, nslab, 4, 16)           # rb, row, s, cb, byte
+        oc = c.transpose(0, 2, 3, 1, 4).reshape(-1)
+        sc = scales.reshape(R // 16, 16, nslab, 4, 2).transpose(0, 2, 3, 1, 4).reshape(-1)
+        return oc, sc
+
+    def f8(codes, R, K):
+        nslab = K // 128
+        c = codes.reshape(R // 16, 16, nslab, 4, 32)           # rb, row, s, cb, byte
+        return c.transpose(0, 2, 3, 1, 4).reshape(-1)
+
+    want = src.copy()       # the fp32 scale fields stay where they are
+    for e in range(n):
+        b = src[e]
+        for (R, K, oc, os_) in ((2 * I, H, lay.w13, lay.s13), (H, I, lay.w2, lay.s2)):
+            if fmt == "nvfp4":
+                c, sc = nv(b[oc:os_], b[os_:os_ + R * K // 16], R, K)
+                want[e, oc:os_], want[e, os_:os_ + R * K // 16] = c, sc
+            else:
+                want[e, oc:os_] = f8(b[oc:os_], R, K)
+    d_src = to_dev(src)
+    d_dst = torch.zeros_like(d_src)
+    lib.moe_pack_weights(lib.MOE_W_NVFP4 if fmt == "nvfp4" else lib.MOE_W_FP8, d_src, d_dst, n,
+                         lay.nbytes, lay.nbytes, H, I, lay)
+    torch.cuda.synchronize()
+    assert np.array_equal(d_dst.cpu().numpy(), want)
