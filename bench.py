@@ -56,7 +56,7 @@ def parse():
                     help="short run for profilers: headline workload, no sweep, no CPU leg")
     ap.add_argument("--no-stack", action="store_true", help="skip the 43-layer stack runs")
     ap.add_argument("--only", default="",
-                    help="comma list of sweep parts to run: decode,prefill,cfg4,stack")
+                    help="comma list of sweep parts to run: decode,formats,prefill,cfg4,stack")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run one plain 512 MiB device copy (HBM counter calibration)")
     return ap.parse_args()
@@ -544,6 +544,23 @@ def main():
                                 pool=wl.pool, dexp=wl.dexp)
             sweep[f"decode_T{T}"] = r
             log(f"T={T}: {r['tokens_per_s']:.0f} tok/s, {r['ms_per_step']*1000:.1f} us/step")
+    if not args.no_sweep and want("formats"):
+        # the decode layer's shapes and routing with NVFP4 and FP8 expert weights
+        import dataclasses
+        for f in ("nvfp4", "fp8"):
+            cf = dataclasses.replace(c2, name=f"decode_{f}", fmt=f, weights="marginal_" + f)
+            fw, r = run_workload(torch, cf, args.T, max(args.steps // 2, 32), args.warmup, dev)
+            gu = r["kernels"].get("ffn_decode_gate_up", {})
+            r["roofline_gate_up"] = {"bound": "hbm", "achieved": gu.get("GBs"),
+                                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                     "frac": (gu.get("GBs") or 0.0) / HBM_PEAK_GBS}
+            sweep[f"decode_{f}_T{args.T}"] = r
+            log(f"{f} weights T={args.T}: {r['tokens_per_s']:.0f} tok/s, "
+                f"{r['ms_per_step']*1000:.1f} us/step, gate/up {gu.get('GBs', 0):.0f} GB/s "
+                f"({r['roofline_gate_up']['frac']*100:.1f}% of HBM), layer HBM "
+                f"{r['layer_hbm_frac']*100:.1f}%")
+            del fw
+            torch.cuda.empty_cache()
     if not args.no_sweep and want("prefill"):
         # the prefill workload runs the same layer (same weights) at T=8192
         _, r = run_workload(torch, synth.CONFIGS[3], 8192, 16, 3, dev, pool=wl.pool,

@@ -130,8 +130,9 @@ struct WFrag<MOE_W_FP8> {
     __device__ __forceinline__ void pin() { asm volatile("" : "+v"(q[0]), "+v"(q[1])); }
     __device__ __forceinline__ void load_block(buf_rsrc codes, buf_rsrc, uint32_t chunk, int lane,
                                                bool ok) {
-        q[0] = buf_load_nt16(codes, ok ? chunk * 2048u + lane * 32 : kBufOff);
-        q[1] = buf_load_nt16(codes, ok ? chunk * 2048u + lane * 32 + 16 : kBufOff);
+        const uint32_t o = ok ? chunk * 2048u + lane * 32 : kBufOff;
+        q[0] = buf_load_nt16(codes, o);
+        q[1] = buf_load_nt16(codes, o + 16);
     }
     __device__ __forceinline__ bf16x8 get(int j) const {
         const u32x4 &w = q[j >> 1];

@@ -345,6 +345,59 @@ def _marginal_mxfp4_blob(rng: np.random.Generator, H: int, I: int, sigma: float)
     return out
 
 
+def _marginal_tables_fmt(fmt: str, sigma: float):
+    """As _marginal_tables for NVFP4 (codes, block scales, matrix scale) and
+    FP8 (codes, matrix scale)."""
+    key = (fmt, float(sigma))
+    if key in _MARGINAL_CACHE:
+        return _MARGINAL_CACHE[key]
+    rng = _rng(12345, 98)
+    sample = rng.standard_normal((1024, 1024), dtype=np.float32) * np.float32(sigma)
+
+    def lut_from(values: np.ndarray, nvals: int) -> np.ndarray:
+        hist = np.bincount(values.reshape(-1).astype(np.int64), minlength=nvals).astype(np.float64)
+        cdf = np.cumsum(hist) / hist.sum()
+        u = (np.arange(256) + 0.5) / 256.0
+        return np.searchsorted(cdf, u).astype(np.uint8)
+
+    if fmt == "nvfp4":
+        packed, sc, g = encode_nvfp4(sample)
+        codes = np.concatenate([packed & 15, packed >> 4]).reshape(-1)
+        tabs = (lut_from(codes, 16), lut_from(sc, 256), g)
+    else:
+        codes, g = encode_fp8(sample)
+        tabs = (lut_from(codes, 256), None, g)
+    _MARGINAL_CACHE[key] = tabs
+    return tabs
+
+
+def _marginal_nvfp4_blob(rng: np.random.Generator, H: int, I: int, sigma: float) -> np.ndarray:
+    """Fast NVFP4 blob: independent codes and block scales from the marginals
+    of quantised N(0, sigma), the sample's matrix scale."""
+    lay = blob_layout(H, I, "nvfp4")
+    code_lut, scale_lut, g = _marginal_tables_fmt("nvfp4", sigma)
+    out = np.empty(lay.nbytes, dtype=np.uint8)
+    for (rows, cols, o_c, o_s, o_end) in ((2 * I, H, lay.w13, lay.s13, lay.w2),
+                                          (H, I, lay.w2, lay.s2, lay.nbytes)):
+        r = rng.integers(0, 256, size=(2, rows * cols // 2), dtype=np.uint8)
+        out[o_c:o_s] = code_lut[r[0]] | (code_lut[r[1]] << 4)
+        ns = rows * cols // 16
+        out[o_s:o_s + ns] = scale_lut[rng.integers(0, 256, size=ns, dtype=np.uint8)]
+        out[o_s + ns:o_end] = _scale_field(g)
+    return out
+
+
+def _marginal_fp8_blob(rng: np.random.Generator, H: int, I: int, sigma: float) -> np.ndarray:
+    lay = blob_layout(H, I, "fp8")
+    code_lut, _, g = _marginal_tables_fmt("fp8", sigma)
+    out = np.empty(lay.nbytes, dtype=np.uint8)
+    for (rows, cols, o_c, o_s, o_end) in ((2 * I, H, lay.w13, lay.s13, lay.w2),
+                                          (H, I, lay.w2, lay.s2, lay.nbytes)):
+        out[o_c:o_s] = code_lut[rng.integers(0, 256, size=rows * cols, dtype=np.uint8)]
+        out[o_s:o_end] = _scale_field(g)
+    return out
+
+
 def expert_blob(cfg: LayerConfig, layer: int, expert: int, shared: bool = False,
                 H: int | None = None, I: int | None = None) -> np.ndarray:
     """One expert's blob (uint8 [nbytes]) in the storage layout of ``blob_layout``."""
@@ -361,6 +414,10 @@ def expert_blob(cfg: LayerConfig, layer: int, expert: int, shared: bool = False,
         return _gauss_nvfp4_blob(rng, H, I, WEIGHT_SIGMA)
     if cfg.weights == "gauss_fp8":
         return _gauss_fp8_blob(rng, H, I, WEIGHT_SIGMA)
+    if cfg.weights == "marginal_nvfp4":
+        return _marginal_nvfp4_blob(rng, H, I, WEIGHT_SIGMA)
+    if cfg.weights == "marginal_fp8":
+        return _marginal_fp8_blob(rng, H, I, WEIGHT_SIGMA)
     raise ValueError(cfg.weights)
 
 
