@@ -89,10 +89,15 @@ struct WFrag<MOE_W_MXFP4> {
 
 // NVFP4: the lane's 32 codes span two 16-element blocks (dwords 0-1 and 2-3),
 // each with an E4M3 scale. The convert applies only a power of two, so a
-// block scale v is split into 2^floor(log2 v) (in the convert) and its
-// mantissa factor in [1, 2) (one fp32 multiply per element); both products
-// are exact, as is the bf16 rounding of code x scale (at most 6 significant
-// bits). The matrix's fp32 scale multiplies the sums instead (epilogue).
+// block scale v is split into 2^floor(log2 v) (in the convert, to fp16) and
+// its mantissa factor in [1, 2) (one packed fp16 multiply per two elements).
+// code x v has at most 6 significant bits and lies in [2^-10, 2880], so it is
+// exact in fp16; these weights run through the fp16 matrix instruction (the
+// token operand is carried in fp16 too). The matrix's fp32 scale multiplies
+// the sums instead (epilogue).
+typedef __attribute__((ext_vector_type(2))) _Float16 f16x2;
+typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
+
 template <>
 struct WFrag<MOE_W_NVFP4> {
     u32x4 q;
@@ -104,20 +109,19 @@ struct WFrag<MOE_W_NVFP4> {
         s = __builtin_amdgcn_raw_buffer_load_b16(scales, ok ? chunk * 128u + lane * 2 : kBufOff,
                                                  0, kBufNt);
     }
-    __device__ __forceinline__ bf16x8 get(int j) const {
-        typedef __attribute__((ext_vector_type(2))) float f32x2;
+    __device__ __forceinline__ f16x8 get(int j) const {
         const uint32_t sb = (j >> 1) ? (s >> 8) : s;
         const float v = __builtin_amdgcn_cvt_f32_fp8((int)sb, 0);         // block scale
         const uint32_t b = __float_as_uint(v);
         const float p2 = __uint_as_float(b & 0x7F800000u);
-        const float mf = v == 0.0f ? 0.0f : __uint_as_float((b & 0x007FFFFFu) | 0x3F800000u);
-        const f32x2 f0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q[j], p2, 0);
-        const f32x2 f1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q[j], p2, 1);
-        const f32x2 f2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q[j], p2, 2);
-        const f32x2 f3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q[j], p2, 3);
-        bf16x8 r = {(__bf16)(f0[0] * mf), (__bf16)(f0[1] * mf), (__bf16)(f1[0] * mf),
-                    (__bf16)(f1[1] * mf), (__bf16)(f2[0] * mf), (__bf16)(f2[1] * mf),
-                    (__bf16)(f3[0] * mf), (__bf16)(f3[1] * mf)};
+        const _Float16 mh =
+            v == 0.0f ? (_Float16)0.0f : (_Float16)__uint_as_float((b & 0x007FFFFFu) | 0x3F800000u);
+        const f16x2 m2 = {mh, mh};
+        const f16x2 a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(q[j], p2, 0) * m2;
+        const f16x2 c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(q[j], p2, 1) * m2;
+        const f16x2 d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(q[j], p2, 2) * m2;
+        const f16x2 e = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(q[j], p2, 3) * m2;
+        f16x8 r = {a[0], a[1], c[0], c[1], d[0], d[1], e[0], e[1]};
         return r;
     }
 };
@@ -152,6 +156,19 @@ constexpr bool blocked_fmt(int fmt) {
 }
 // Formats with one fp32 scale per matrix, applied to the sums.
 constexpr bool tensor_scaled(int fmt) { return fmt == MOE_W_NVFP4 || fmt == MOE_W_FP8; }
+// Formats whose products run in fp16 (weights, tokens and the activation).
+constexpr bool f16_path(int fmt) { return fmt == MOE_W_NVFP4; }
+
+// 8 bf16 (one u32x4) -> 8 fp16, in place; exact for magnitudes in
+// [2^-14, 65504] (fp16 keeps more significand bits than bf16).
+__device__ __forceinline__ void bf16x8_to_f16(u32x4 &v) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float lo = __uint_as_float(v[i] << 16), hi = __uint_as_float(v[i] & 0xFFFF0000u);
+        const f16x2 h = {(_Float16)lo, (_Float16)hi};
+        v[i] = __builtin_bit_cast(uint32_t, h);
+    }
+}
 
 template <>
 struct WFrag<MOE_W_BF16> {
@@ -345,14 +362,15 @@ __device__ __forceinline__ void dec_step(const DecArgs &A, const ActiveSet &act,
                                          WFrag<FMT> (&wc)[SPW][NB], WFrag<FMT> (&wn)[SPW][NB],
                                          u32x4 (&xr)[SPW][4], const ExpertState<FMT> &cur,
                                          const ExpertState<FMT> &prev, ExpertState<FMT> &nxt,
-                                         int &pidx, int &x_key, int &buf, int rt, TilePos pn,
-                                         bool pf, int lane, int wv, int m, int c) {
+                                         int &pidx, int &x_key, bool &x_raw, int &buf, int rt,
+                                         TilePos pn, bool pf, int lane, int wv, int m, int c) {
 
         // token operand for the first pass of this tile (loaded before the next
         // prefetch, so that waiting for it does not wait for the prefetched weights)
         if (x_key != cur.a * 4096) {
             load_tokens<STAGE, SPW>(A, cur, 0, wv, m, c, xr, pidx);
             x_key = cur.a * 4096;
+            x_raw = true;
         }
         // prefetch the tile D - 1 steps ahead (position pn, present if pf);
         // `prev` holds the state of the tile before it. Issued, switched off,
@@ -365,6 +383,18 @@ __device__ __forceinline__ void dec_step(const DecArgs &A, const ActiveSet &act,
             if (p > 0) {   // more than 16 tokens: next 16 of this expert
                 load_tokens<STAGE, SPW>(A, cur, p, wv, m, c, xr, pidx);
                 x_key = cur.a * 4096 + p;
+                x_raw = true;
+            }
+            // fp16 products: bf16 tokens (stage 1) are converted once per load
+            // (after the prefetch was issued, so the wait for them leaves it in flight)
+            if constexpr (f16_path(FMT) && STAGE == 1) {
+                if (x_raw) {
+#pragma unroll
+                    for (int s = 0; s < SPW; ++s)
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) bf16x8_to_f16(xr[s][j]);
+                    x_raw = false;
+                }
             }
             f32x4 acc[NB];
 #pragma unroll
@@ -377,11 +407,19 @@ __device__ __forceinline__ void dec_step(const DecArgs &A, const ActiveSet &act,
             for (int s = 0; s < SPW; ++s)
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    const bf16x8 bx = as_bf16x8(xr[s][j]);
+                    if constexpr (f16_path(FMT)) {
+                        const f16x8 hx = __builtin_bit_cast(f16x8, xr[s][j]);
 #pragma unroll
-                    for (int b = 0; b < NB; ++b)
-                        acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wc[s][b].get(j), bx,
-                                                                        acc[b], 0, 0, 0);
+                        for (int b = 0; b < NB; ++b)
+                            acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wc[s][b].get(j), hx,
+                                                                           acc[b], 0, 0, 0);
+                    } else {
+                        const bf16x8 bx = as_bf16x8(xr[s][j]);
+#pragma unroll
+                        for (int b = 0; b < NB; ++b)
+                            acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wc[s][b].get(j), bx,
+                                                                            acc[b], 0, 0, 0);
+                    }
                 }
             // partial sums of the K split meet in LDS (double-buffered: one barrier per pass)
             if (KS > 1) {
@@ -414,10 +452,19 @@ __device__ __forceinline__ void dec_step(const DecArgs &A, const ActiveSet &act,
 #pragma unroll
                         for (int b = 0; b < H2; ++b) {
                             uint2 pk;
-                            pk.x = pack_bf16x2(silu_mul(acc[b][0], acc[b + H2][0]),
-                                               silu_mul(acc[b][1], acc[b + H2][1]));
-                            pk.y = pack_bf16x2(silu_mul(acc[b][2], acc[b + H2][2]),
-                                               silu_mul(acc[b][3], acc[b + H2][3]));
+                            // the activation in the stage-2 operand type (bf16, or fp16)
+                            auto pack2 = [](float lo, float hi) -> uint32_t {
+                                if constexpr (f16_path(FMT)) {
+                                    const f16x2 h = {(_Float16)lo, (_Float16)hi};
+                                    return __builtin_bit_cast(uint32_t, h);
+                                } else {
+                                    return pack_bf16x2(lo, hi);
+                                }
+                            };
+                            pk.x = pack2(silu_mul(acc[b][0], acc[b + H2][0]),
+                                         silu_mul(acc[b][1], acc[b + H2][1]));
+                            pk.y = pack2(silu_mul(acc[b][2], acc[b + H2][2]),
+                                         silu_mul(acc[b][3], acc[b + H2][3]));
                             *reinterpret_cast<uint2 *>(actp + (rt * H2 + b) * 16 + 4 * c) = pk;
                         }
                     } else {
@@ -492,6 +539,7 @@ __global__ __launch_bounds__(kWave *KS) void ffn_dec_kernel(DecArgs A) {
     int pidx = 0;
     load_tokens<STAGE, SPW>(A, es[0], 0, wv, m, c, xr, pidx);
     int x_key = es[0].a * 4096;
+    bool x_raw = true;      // tokens just loaded (not yet in the product type)
     int buf = 0;
 #pragma unroll
     for (int d = 0; d < D - 1; ++d)
@@ -505,7 +553,7 @@ __global__ __launch_bounds__(kWave *KS) void ffn_dec_kernel(DecArgs A) {
                 const bool pf = i + d + D - 1 < n;
                 pos[fd] = pf ? advance(pos[pd], sa, srt, A.nrt) : pos[pd];
                 dec_step<FMT, STAGE, SPW, KS, NB, YF32, FULL, D>(
-                    A, act, red, wr[d], wr[fd], xr, es[d], es[pd], es[fd], pidx, x_key, buf,
+                    A, act, red, wr[d], wr[fd], xr, es[d], es[pd], es[fd], pidx, x_key, x_raw, buf,
                     pos[d].rt, pos[fd], pf, lane, wv, m, c);
             }
         }
