@@ -608,7 +608,9 @@ static int launch_dec(hipStream_t s, DecArgs A, long slots) {
 // Tiles: stage 1 = 16 gate + 16 up rows (NB = 2); stage 2 = NB2 x 16 rows.
 template <int FMT, int STAGE, bool YF32>
 static int launch_stage(int slabs, hipStream_t s, const DecArgs &A, long slots) {
-    const bool nb4 = STAGE == 2 && A.H % 64 == 0;
+    // 64-row down tiles, unless that leaves fewer tiles than two workgroups
+    // per compute unit (a handful of experts at small batches): then 32
+    const bool nb4 = STAGE == 2 && A.H % 64 == 0 && slots * (A.H / 64) >= 2L * num_cus();
 #define MOE_ST(SPW_, KS_, FULL_)                                                              \
     return nb4 ? launch_dec<FMT, STAGE, SPW_, KS_, (STAGE == 2 ? 4 : 2), YF32, FULL_>(s, A, slots) \
                : launch_dec<FMT, STAGE, SPW_, KS_, 2, YF32, FULL_>(s, A, slots)
