@@ -362,3 +362,36 @@ def test_resize_between_layers_is_bitwise(env):
         assert after[1] == before[1] and after[0] == before[0] + E
     finally:
         c.close()
+
+
+def test_resize_errors_leave_the_cache_unchanged(env):
+    """A pool with fewer slots than one layer's experts is refused (ENOMEM), and
+    so is a new pool that partly overlaps the current one (EINVAL); neither
+    changes the slots, the counters or the residents' bytes."""
+    torch = env["torch"]
+    lib = env["lib"]
+    nb = env["lay"].nbytes
+    slot = (nb + 255) // 256 * 256
+    c = _cache(env, 2 * E)
+    try:
+        c.prefetch(0, None)
+        c.prefetch(1, np.arange(5))
+        torch.cuda.synchronize()
+        before = [[c.slot_of(l, e) for e in range(E)] for l in range(env["L"])]
+        stats = c.stats()
+        with pytest.raises(lib.MoeError) as ei:
+            c.resize((E - 1) * slot)
+        assert ei.value.code == lib.MOE_ENOMEM
+        overlap = c.pool.data_ptr() + slot            # starts inside the current pool
+        with pytest.raises(lib.MoeError) as ei:
+            lib.expert_cache_resize(c.handle, overlap, E * slot)
+        assert ei.value.code == lib.MOE_EINVAL
+        assert [[c.slot_of(l, e) for e in range(E)] for l in range(env["L"])] == before
+        assert c.stats() == stats and c.slots() == 2 * E
+        for l in range(env["L"]):
+            for e in range(E):
+                s = c.slot_of(l, e)
+                if s >= 0:
+                    assert torch.equal(c.slot_bytes_view(s, nb).cpu(), env["store"].host[l * E + e])
+    finally:
+        c.close()

@@ -80,6 +80,17 @@ def test_argument_errors_before_any_device_work(lib):
     # more experts than the FFN supports
     assert L.moe_expert_ffn(dummy, dummy, dummy, dummy, 1, 4, 2, 128, 128, 513, dummy, 0, dummy,
                             1 << 30, None) == lib.MOE_EINVAL
+    # packing: unknown format, K not a multiple of 128, null pointers
+    assert L.moe_pack_weights(0, dummy, dummy, 1, 1 << 20, 1 << 20, 256, 256, 0, 0, 0, 0,
+                              None) == lib.MOE_EINVAL
+    assert L.moe_pack_weights(2, dummy, dummy, 1, 1 << 20, 1 << 20, 256, 192, 0, 0, 0, 0,
+                              None) == lib.MOE_EINVAL
+    assert L.moe_pack_weights(3, None, dummy, 1, 1 << 20, 1 << 20, 256, 256, 0, 0, 0, 0,
+                              None) == lib.MOE_EINVAL
+    assert L.moe_pack_weights(3, None, None, 0, 0, 0, 256, 256, 0, 0, 0, 0, None) == lib.MOE_OK
+    # NVFP4 / FP8 FFN calls need H, I multiples of 128
+    assert L.moe_expert_ffn(dummy, dummy, dummy, dummy, 2, 4, 2, 192, 128, 8, dummy, 0, dummy,
+                            1 << 30, None) == lib.MOE_EINVAL
     # bad weight format
     assert L.moe_expert_ffn(dummy, dummy, dummy, dummy, 7, 4, 2, 64, 64, 8, dummy, 0, dummy,
                             1 << 20, None) == lib.MOE_EINVAL
