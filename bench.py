@@ -559,6 +559,17 @@ def main():
                 f"{r['ms_per_step']*1000:.1f} us/step, gate/up {gu.get('GBs', 0):.0f} GB/s "
                 f"({r['roofline_gate_up']['frac']*100:.1f}% of HBM), layer HBM "
                 f"{r['layer_hbm_frac']*100:.1f}%")
+            if f == "fp8":
+                # the prefill workload (T=8192, its routing) with the same FP8 weights:
+                # the tiled kernels with E4M3 weights
+                cp = dataclasses.replace(synth.CONFIGS[3], name="prefill_fp8", fmt=f,
+                                         weights="marginal_" + f)
+                _, rp = run_workload(torch, cp, 8192, 16, 3, dev, pool=fw.pool, dexp=fw.dexp,
+                                     kernel_steps=8)
+                rp["mfma_frac_bf16_peak"] = rp["layer_tflops"] / BF16_PEAK_TFLOPS
+                sweep["prefill_fp8_T8192"] = rp
+                log(f"fp8 weights T=8192: {rp['tokens_per_s']:.0f} tok/s, "
+                    f"{rp['layer_tflops']:.1f} TFLOP/s")
             del fw
             torch.cuda.empty_cache()
     if not args.no_sweep and want("prefill"):

@@ -173,10 +173,11 @@ int moe_route_permute(const uint16_t *x_bf16, const uint16_t *wg_bf16, const flo
  * experts: device array [E] of moe_expert_w; entries of experts that receive
  * no pair are never read. x_bf16 [T][H]. fmt: MOE_W_MXFP4, MOE_W_NVFP4 or
  * MOE_W_FP8 (kernel layouts, H and I multiples of 128) or MOE_W_BF16 (H and
- * I multiples of 32). NVFP4 and FP8 always run the weight-streaming kernels
- * (the tiled kernels' matrix-core instruction takes only E8M0 block scales);
- * there the weights enter the products as code x block scale, which is
- * exact, and the per-matrix fp32 scale multiplies the fp32 sums. FP8 products
+ * I multiples of 32). NVFP4 always runs the weight-streaming kernels (the
+ * tiled kernels' matrix-core instruction takes only E8M0 block scales over 32
+ * elements); FP8 runs either, the tiled kernels with unit block scales. The
+ * weights enter the products as code x block scale, which is exact, and the
+ * per-matrix fp32 scale multiplies the fp32 sums. Weight-streaming FP8 products
  * are bf16 x bf16 as for the other formats; NVFP4 products are fp16 x fp16:
  * x and the activation are carried in fp16 (exact for bf16 x with magnitude
  * in [2^-14, 65504]), so NVFP4 layers need activations below 65504.

@@ -198,9 +198,14 @@ struct PreArgs {
 //           read one chunk of 16 rows hit 16 different 16-byte bank groups;
 //   tsc   : the 64 tokens' 4 scale bytes of this slab;
 //   wcode / wscale: the tile's 16 weight blocks, kernel layout.
+// FP8 weights (one byte per element) take 2 KB per weight block: the stage
+// is then 50 KB and one workgroup fits a compute unit.
+constexpr int wblock_bytes(int fmt) { return fmt == MOE_W_FP8 ? 2048 : 1024; }
+
+template <int FMT>
 struct PreStage {
     uint8_t tok[2][4][2048];
-    uint8_t wcode[16][1024];
+    uint8_t wcode[16][wblock_bytes(FMT)];
     uint8_t tsc[kPreTok][4];
     uint8_t wscale[16][64];
 };
@@ -241,24 +246,31 @@ struct PreSrc {
 // on wavefront 0 the token scales, on wavefront 1 the 16 weight blocks' scale rows.
 // woff: byte offset of this weight tile's codes from the group's first tile's
 // (its scales sit at woff / 16).
-__device__ __forceinline__ void pre_issue(PreStage &st, int s, int w, const PreSrc &p,
+template <int FMT>
+__device__ __forceinline__ void pre_issue(PreStage<FMT> &st, int s, int w, const PreSrc &p,
                                           size_t woff) {
+    constexpr int WB = wblock_bytes(FMT);
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
         lds_dma16(p.thi[u] + s * 128, &st.tok[0][w][u * 1024]);
         lds_dma16(p.tlo[u] + s * 128, &st.tok[1][w][u * 1024]);
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
-        lds_dma16(p.wc[u] + woff + (size_t)s * 1024, &st.wcode[4 * w + u][0]);
+    for (int u = 0; u < 4; ++u) {
+        lds_dma16(p.wc[u] + woff + (size_t)s * WB, &st.wcode[4 * w + u][0]);
+        if (WB == 2048) lds_dma16(p.wc[u] + woff + (size_t)s * WB + 1024, &st.wcode[4 * w + u][1024]);
+    }
     if (w == 0) lds_dma4(p.tsc + s * 4, &st.tsc[0][0]);
-    if (w == 1) lds_dma16(p.ws + woff / 16 + (size_t)s * 64, &st.wscale[0][0]);
+    if (FMT == MOE_W_MXFP4 && w == 1)
+        lds_dma16(p.ws + woff / 16 + (size_t)s * 64, &st.wscale[0][0]);
 }
 
 // One slab's operands for one wavefront: its 8 weight blocks and its two
 // 16-token blocks (both terms, both halves), with the lane's scale bytes.
+template <int FMT>
 struct PreFrag {
     u32x4 w[8];
+    u32x4 w2[FMT == MOE_W_FP8 ? 8 : 1];   // FP8: the lane's second 16 bytes of each block
     uint32_t ws[8];
     i32x8 t[2][2];                // [token block][term]; elements 0-3 / 4-7 = column half 0 / 1
     uint32_t ts[2];
@@ -284,14 +296,26 @@ struct TokPos {
     }
 };
 
-template <int STAGE>
-__device__ __forceinline__ void pre_read(const PreStage &st, PreFrag &f, int wm, int wn, int lane,
-                                         const TokPos &tp) {
+template <int STAGE, int FMT>
+__device__ __forceinline__ void pre_read(const PreStage<FMT> &st, PreFrag<FMT> &f, int wm, int wn,
+                                         int lane, const TokPos &tp) {
 #pragma unroll
     for (int b = 0; b < 8; ++b) {
         const int lb = lds_block<STAGE>(wn, b);
-        f.w[b] = *reinterpret_cast<const u32x4 *>(&st.wcode[lb][16 * lane]);
-        f.ws[b] = st.wscale[lb][lane];
+        if constexpr (FMT == MOE_W_FP8) {
+            // an 8-bit operand lane holds columns 16g..16g+15 (bytes 0-15) and
+            // 64+16g.. (bytes 16-31), g = lane / 16, like the token operand;
+            // the block stores each row's columns 32h..32h+31 as one 32-byte
+            // piece at (16h + row) * 32
+            const int r = lane & 15, g = lane >> 4;
+            const int a0 = ((g >> 1) * 16 + r) * 32 + 16 * (g & 1);
+            const int a1 = ((2 + (g >> 1)) * 16 + r) * 32 + 16 * (g & 1);
+            f.w[b] = *reinterpret_cast<const u32x4 *>(&st.wcode[lb][a0]);
+            f.w2[b] = *reinterpret_cast<const u32x4 *>(&st.wcode[lb][a1]);
+        } else {
+            f.w[b] = *reinterpret_cast<const u32x4 *>(&st.wcode[lb][16 * lane]);
+            f.ws[b] = st.wscale[lb][lane];
+        }
     }
 #pragma unroll
     for (int tb = 0; tb < 2; ++tb) {
@@ -305,20 +329,32 @@ __device__ __forceinline__ void pre_read(const PreStage &st, PreFrag &f, int wm,
     }
 }
 
-__device__ __forceinline__ void pre_math(const PreFrag &f, f32x4 (&acc)[8][2]) {
+template <int FMT>
+__device__ __forceinline__ void pre_math(const PreFrag<FMT> &f, f32x4 (&acc)[8][2]) {
 #pragma unroll
     for (int term = 0; term < 2; ++term)
 #pragma unroll
         for (int b = 0; b < 8; ++b) {
-            // E2M1 operand: only the low four dwords are read
             const i32x4 w4 = __builtin_bit_cast(i32x4, f.w[b]);
-            const i32x8 a = __builtin_shufflevector(w4, w4, 0, 1, 2, 3, -1, -1, -1, -1);
+            i32x8 a;
+            if constexpr (FMT == MOE_W_FP8) {
+                const i32x4 w4b = __builtin_bit_cast(i32x4, f.w2[b]);
+                a = __builtin_shufflevector(w4, w4b, 0, 1, 2, 3, 4, 5, 6, 7);
+            } else {
+                // E2M1 operand: only the low four dwords are read
+                a = __builtin_shufflevector(w4, w4, 0, 1, 2, 3, -1, -1, -1, -1);
+            }
 #pragma unroll
             for (int tb = 0; tb < 2; ++tb) {
                 const int tsc = (int)f.ts[tb] - (term ? kLoShift : 0);
-                // A: E2M1 (format 4), B: E4M3 (format 0)
-                acc[b][tb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                    a, f.t[tb][term], acc[b][tb], 4, 0, 0, (int)f.ws[b], 0, tsc);
+                // A: E2M1 (format 4) with its E8M0 block scale, or E4M3 (format
+                // 0) with unit scale 127; B: E4M3 (format 0)
+                if constexpr (FMT == MOE_W_FP8)
+                    acc[b][tb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                        a, f.t[tb][term], acc[b][tb], 0, 0, 0, 127, 0, tsc);
+                else
+                    acc[b][tb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                        a, f.t[tb][term], acc[b][tb], 4, 0, 0, (int)f.ws[b], 0, tsc);
             }
         }
 }
@@ -352,22 +388,22 @@ __device__ __forceinline__ void bare_barrier() {
 // `first` runs once, after the first slab's barrier and copies: the previous
 // tile's deferred output stores go there, so that the wait at the top of the
 // first slab does not also wait for them to complete.
-template <int STAGE, class First>
-__device__ __forceinline__ void pre_mainloop(PreStage (&lds)[kPreStages], f32x4 (&acc)[8][2],
+template <int STAGE, int FMT, class First>
+__device__ __forceinline__ void pre_mainloop(PreStage<FMT> (&lds)[kPreStages], f32x4 (&acc)[8][2],
                                              int n, int g0, int wv, int wm, int wn, int lane,
                                              const PreSrc &src, size_t woff, size_t woff_next,
                                              bool has_next, First &&first) {
-    PreFrag F;
+    PreFrag<FMT> F;
     const TokPos tp(lane);
     for (int j = 0; j < n; ++j) {
         const int st = (g0 + j) & 1;
         wait_vm<0>();
         bare_barrier();
-        if (j + 1 < n) pre_issue(lds[st ^ 1], j + 1, wv, src, woff);
-        else if (has_next) pre_issue(lds[st ^ 1], 0, wv, src, woff_next);
+        if (j + 1 < n) pre_issue<FMT>(lds[st ^ 1], j + 1, wv, src, woff);
+        else if (has_next) pre_issue<FMT>(lds[st ^ 1], 0, wv, src, woff_next);
         if (j == 0) first();
-        pre_read<STAGE>(lds[st], F, wm, wn, lane, tp);
-        pre_math(F, acc);
+        pre_read<STAGE, FMT>(lds[st], F, wm, wn, lane, tp);
+        pre_math<FMT>(F, acc);
     }
 }
 
@@ -481,9 +517,10 @@ __device__ __forceinline__ void pre_epilogue(const PreArgs &A, const f32x4 (&acc
     }
 }
 
-template <int STAGE, bool YF32>
+template <int STAGE, bool YF32, int FMT>
 __global__ __launch_bounds__(kPreThreads) void ffn_pre_kernel(PreArgs A) {
-    __shared__ __attribute__((aligned(16))) PreStage lds[kPreStages];
+    __shared__ __attribute__((aligned(16))) PreStage<FMT> lds[kPreStages];
+    constexpr int WB = wblock_bytes(FMT);
     const int tid = threadIdx.x, lane = lane_id();
     const int wv = __builtin_amdgcn_readfirstlane(tid / kWave);
     const int wm = wv & 1, wn = wv >> 1;     // token half (32 tokens), weight half
@@ -539,7 +576,7 @@ __global__ __launch_bounds__(kPreThreads) void ffn_pre_kernel(PreArgs A) {
         src.tsc = A.bsc + token_row(tok0 + lane) * (A.K / 32);
 #pragma unroll
         for (int u = 0; u < 4; ++u)
-            src.wc[u] = wcodes + (size_t)pre_block<STAGE>(A, nt, 4 * wv + u) * nslab * 1024 +
+            src.wc[u] = wcodes + (size_t)pre_block<STAGE>(A, nt, 4 * wv + u) * nslab * WB +
                         16 * lane;
         src.ws = wscales + (size_t)pre_block<STAGE>(A, nt, lane >> 2) * nslab * 64 +
                  16 * (lane & 3);
@@ -552,19 +589,27 @@ __global__ __launch_bounds__(kPreThreads) void ffn_pre_kernel(PreArgs A) {
         for (int tb = 0; tb < 2; ++tb) acc[b][tb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
     // weight tile nt + t starts (STAGE 1 ? 8 : 16) blocks after tile nt
-    const size_t wstep = (size_t)(STAGE == 1 ? 8 : 16) * nslab * 1024;
-    pre_issue(lds[0], 0, wv, src, 0);
+    const size_t wstep = (size_t)(STAGE == 1 ? 8 : 16) * nslab * WB;
+    // FP8: the matrix's fp32 scale multiplies the sums (the blocks use unit scales)
+    const float gsc = FMT == MOE_W_FP8 ? *as_scalar(reinterpret_cast<const float *>(wscales)) : 1.0f;
+    pre_issue<FMT>(lds[0], 0, wv, src, 0);
     // stage 2 with bf16 y: a tile's outputs are stored after the next tile's
     // first slab barrier (or at the end), not before it
     constexpr bool kDefer = STAGE == 2 && !YF32;
     PreOut pend;
     bool pending = false;
     for (int t = 0; t < A.nt_group; ++t) {
-        pre_mainloop<STAGE>(lds, acc, nslab, t * nslab, wv, wm, wn, lane, src, t * wstep,
+        pre_mainloop<STAGE, FMT>(lds, acc, nslab, t * nslab, wv, wm, wn, lane, src, t * wstep,
                             (t + 1) * wstep, t + 1 < A.nt_group, [&]() {
                                 if (kDefer && pending)
                                     pre_store_y(A, pend, tok0, n_e, wm, wn, lane, prow_tb);
                             });
+        if (FMT == MOE_W_FP8) {
+#pragma unroll
+            for (int b = 0; b < 8; ++b)
+#pragma unroll
+                for (int tb = 0; tb < 2; ++tb) acc[b][tb] *= gsc;
+        }
         if (kDefer) {
             pre_pack_y(acc, nt + t, pend);
             pending = true;
@@ -583,7 +628,7 @@ __global__ __launch_bounds__(kPreThreads) void ffn_pre_kernel(PreArgs A) {
 // Tiled path needs whole 128-row weight tiles in stage 1 (I % 128) and
 // 256-row tiles in stage 2 (H % 256), and whole 128-column slabs.
 bool ffn_prefill_supported(int fmt, int H, int I) {
-    return fmt == MOE_W_MXFP4 && I % 128 == 0 && H % 256 == 0;
+    return (fmt == MOE_W_MXFP4 || fmt == MOE_W_FP8) && I % 128 == 0 && H % 256 == 0;
 }
 
 static size_t al256(size_t b) { return (b + 255) & ~(size_t)255; }
@@ -605,7 +650,7 @@ size_t prefill_ws_bytes(long n_pairs, long T, int H, int I, int E) {
 #ifndef MOE_PRE_GROUP2
 #define MOE_PRE_GROUP2 2
 #endif
-template <int STAGE, bool YF32>
+template <int STAGE, bool YF32, int FMT>
 static int launch_pre(hipStream_t s, PreArgs A, long n_pairs) {
     // weight tiles per workgroup: stage 2's short contraction (I / 128 slabs
     // per tile) runs two tiles per workgroup so the copy ring spans more slabs
@@ -616,7 +661,7 @@ static int launch_pre(hipStream_t s, PreArgs A, long n_pairs) {
     const long tiles_max = mt_max * (A.ntiles_w / A.nt_group);
     const long grid = ((tiles_max + 7) / 8) * 8;
     if (grid > 0x7FFFFFFFL) return MOE_EUNSUPPORTED;
-    MOE_LAUNCH(STAGE == 1 ? K_PRE_GATE_UP : K_PRE_DOWN, (ffn_pre_kernel<STAGE, YF32>), dim3((unsigned)grid),
+    MOE_LAUNCH(STAGE == 1 ? K_PRE_GATE_UP : K_PRE_DOWN, (ffn_pre_kernel<STAGE, YF32, FMT>), dim3((unsigned)grid),
                                  dim3(kPreThreads), 0, s, A);
     return check_launch();
 }
@@ -645,11 +690,18 @@ int ffn_prefill(const uint16_t *x, const int32_t *sorted_pair, const int32_t *of
 
     PreArgs a1{xhi, xlo, xsc, sorted_pair, offsets, experts, nullptr, ahi, alo, asc, map,
                k, H, H, I, E, I / 128, 1};
-    rc = launch_pre<1, false>(s, a1, n);
-    if (rc) return rc;
     PreArgs a2{ahi, alo, asc, sorted_pair, offsets, experts, y, nullptr, nullptr, nullptr, map,
                k, I, H, I, E, H / 256, 1};
-    return y_is_fp32 ? launch_pre<2, true>(s, a2, n) : launch_pre<2, false>(s, a2, n);
+    if (fmt == MOE_W_FP8) {
+        rc = launch_pre<1, false, MOE_W_FP8>(s, a1, n);
+        if (rc) return rc;
+        return y_is_fp32 ? launch_pre<2, true, MOE_W_FP8>(s, a2, n)
+                         : launch_pre<2, false, MOE_W_FP8>(s, a2, n);
+    }
+    rc = launch_pre<1, false, MOE_W_MXFP4>(s, a1, n);
+    if (rc) return rc;
+    return y_is_fp32 ? launch_pre<2, true, MOE_W_MXFP4>(s, a2, n)
+                     : launch_pre<2, false, MOE_W_MXFP4>(s, a2, n);
 }
 
 }  // namespace moe

@@ -530,3 +530,25 @@ def test_pack_nvfp4_fp8_layout(lib, fmt):
                          lay.nbytes, lay.nbytes, H, I, lay)
     torch.cuda.synchronize()
     assert np.array_equal(d_dst.cpu().numpy(), want)
+
+
+@pytest.mark.parametrize("H,I,E,k,T,kind,path", [
+    (768, 384, 16, 4, 400, "skew", 2),       # forced onto the tiled kernels; 3 down tiles
+    (1024, 512, 16, 4, 2048, "uniform", 0),  # chosen by size
+])
+def test_fp8_weights_tiled_path(lib, orc, H, I, E, k, T, kind, path):
+    """FP8 experts on the tiled (matrix-core) kernels: E4M3 weights with unit
+    block scales and the matrix scale on the sums, against the oracle on
+    sampled tokens (the last one included)."""
+    _announce(f"layer: fp8 weights, tiled path, H={H} I={I} E={E} k={k} T={T} ({kind})")
+    cfg = synth.LayerConfig("fp8_tiled", H, E, k, I, "fp8", 0, "uniform", (T,), "gauss_fp8",
+                            seed=29)
+    w = Workload(cfg)
+    x = synth.activations(cfg, T, step=3)
+    lg = synth.router_logits(cfg, T, step=3) if kind == "uniform" else _perm_case(T, E, k, kind)
+    lib.moe_set_option(lib.MOE_OPT_FFN_PATH, path)
+    try:
+        L, out = run_layer(w, T, x, logits=lg)
+    finally:
+        lib.moe_set_option(lib.MOE_OPT_FFN_PATH, 0)
+    _check_layer_sampled(orc, w, T, x, lg, L, out, n_sample=12)
