@@ -622,7 +622,11 @@ static int launch_stage(int slabs, hipStream_t s, const DecArgs &A, long slots) 
         case 6: MOE_ST(2, 3, true);
         case 8: MOE_ST(2, 4, true);
         case 12: MOE_ST(3, 4, true);
-        case 16: MOE_ST(4, 4, true);
+        case 16:
+            // gate/up with fewer tiles than two workgroups per compute unit (a
+            // handful of experts): 8 wavefronts per tile shorten each tile
+            if (STAGE == 1 && slots * (A.I / 16) < 2L * num_cus()) MOE_ST(2, 8, true);
+            MOE_ST(4, 4, true);
         case 24: MOE_ST(3, 8, true);
         case 32: MOE_ST(4, 8, true);
         default: break;
