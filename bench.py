@@ -409,9 +409,8 @@ def run_stack_cached(torch, st, runs, pool_bytes, resize_T=1, resize_steps=32):
                 ly.route_permute(T, logits=lg[i][l], write_logits=False)
                 ids = ly.topk_ids[:T].cpu().numpy().ravel()
                 tab = cache.prefetch(l, ids)
-                ly.ffn(T, x, tab)
-                ly.shared_ffn(T, x, stabs[l])
-                ly.combine(T, with_shared=True)
+                ysh = ly.ffn_with_shared(T, x, tab, stabs[l])
+                ly.combine(T, y_shared=ysh)
                 x = ly.out[:T]
 
         for i in range(warmup):

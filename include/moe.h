@@ -148,9 +148,10 @@ int moe_permute(const int32_t *topk_ids, int T, int k, int E, int32_t *offsets,
 
 /*
  * moe_route_permute -- moe_route followed by moe_permute, with the same
- * arguments and results as the two calls. For T <= 16 (and E <= 512) both run
- * in one single-workgroup kernel that keeps the chosen ids on chip; larger
- * batches make the two calls. ws / ws_bytes as for moe_permute.
+ * arguments and results as the two calls. For T <= 16 with the gate computed
+ * here, or T <= 8 with logits_in given (and E <= 512), both run in one
+ * single-workgroup kernel that keeps the chosen ids on chip; larger batches
+ * make the two calls. ws / ws_bytes as for moe_permute.
  */
 int moe_route_permute(const uint16_t *x_bf16, const uint16_t *wg_bf16, const float *logits_in,
                       float *logits_out, int T, int H, int E, int k, int renormalize,
@@ -189,6 +190,29 @@ int moe_route_permute(const uint16_t *x_bf16, const uint16_t *wg_bf16, const flo
 int moe_expert_ffn(const uint16_t *x_bf16, const int32_t *sorted_pair, const int32_t *offsets,
                    const moe_expert_w *experts, int fmt, int T, int k, int H, int I, int E,
                    void *y, int y_is_fp32, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * moe_expert_ffn_shared -- moe_expert_ffn for the routed experts together with
+ * the always-on shared expert, in the same launches: the shared expert is one
+ * more expert whose rows are all T tokens.
+ *   y[p] for p < T*k as moe_expert_ffn; y[T*k + t] = W2_s (silu(W1_s x_t) *
+ *   (W3_s x_t)) with the shared expert's weights `shared` (device pointer to
+ *   one moe_expert_w, same format and sizes as the routed experts).
+ * y: [T*k + T][H], bf16 (y_is_fp32 = 0) or fp32; moe_combine takes rows T*k ..
+ * as its y_shared. Numerics as moe_expert_ffn's weight-streaming kernels.
+ * ws: device workspace of at least the ffn size from moe_workspace_size(T,
+ * k + 1, H, I, E) (the activation holds the shared expert's rows too).
+ * Runs where moe_expert_ffn would choose the weight-streaming kernels (small
+ * batches, where a separate shared-expert launch leaves compute units idle
+ * behind the routed one). Where it would choose the tiled kernels (or
+ * MOE_OPT_FFN_PATH forces them) it returns MOE_EUNSUPPORTED before any device
+ * work; the caller then makes the shared expert its own moe_expert_ffn call.
+ * Other errors as moe_expert_ffn (shared == NULL is MOE_EINVAL).
+ */
+int moe_expert_ffn_shared(const uint16_t *x_bf16, const int32_t *sorted_pair,
+                          const int32_t *offsets, const moe_expert_w *experts,
+                          const moe_expert_w *shared, int fmt, int T, int k, int H, int I, int E,
+                          void *y, int y_is_fp32, void *ws, size_t ws_bytes, void *stream);
 
 /*
  * moe_combine -- weighted sum of each token's k expert outputs.

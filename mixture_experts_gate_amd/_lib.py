@@ -21,6 +21,7 @@ MOE_OPT_TIMING = 2
 # every symbol include/moe.h declares
 EXPORTS = [
     "moe_strerror", "moe_last_hip_error", "moe_route", "moe_permute", "moe_expert_ffn",
+    "moe_expert_ffn_shared",
     "moe_combine", "moe_workspace_size", "moe_set_option", "moe_get_option", "moe_kernel_name",
     "moe_timing_query", "moe_pack_mxfp4", "moe_pack_weights", "moe_route_permute",
     "expert_cache_reserve", "expert_cache_prefetch", "expert_cache_evict", "expert_cache_stats",
@@ -61,6 +62,7 @@ def load(path: str | None = None):
         "moe_permute": (I, [P, I, I, I, P, P, P, P, Z, P]),
         "moe_route_permute": (I, [P, P, P, P, I, I, I, I, I, P, P, P, P, P, P, Z, P]),
         "moe_expert_ffn": (I, [P, P, P, P, I, I, I, I, I, I, P, I, P, Z, P]),
+        "moe_expert_ffn_shared": (I, [P, P, P, P, P, I, I, I, I, I, I, P, I, P, Z, P]),
         "moe_combine": (I, [P, I, P, P, I, I, I, P, P]),
         "moe_workspace_size": (I, [I, I, I, I, I, C.POINTER(Z), C.POINTER(Z)]),
         "moe_set_option": (I, [I, I]),
@@ -141,6 +143,19 @@ def moe_expert_ffn(x_bf16, sorted_pair, offsets, experts, fmt, T, k, H, I, E, y,
     return _check("moe_expert_ffn", load().moe_expert_ffn(
         _ptr(x_bf16), _ptr(sorted_pair), _ptr(offsets), _ptr(experts), fmt, T, k, H, I, E, _ptr(y),
         int(bool(y_is_fp32)), _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def moe_expert_ffn_shared(x_bf16, sorted_pair, offsets, experts, shared, fmt, T, k, H, I, E, y,
+                          y_is_fp32, ws, ws_bytes, stream=None, check=True):
+    """Routed + shared expert FFN in the same launches (y has T*k + T rows).
+    check=False returns MOE_EUNSUPPORTED instead of raising, so that the
+    caller can run the shared expert as its own call on the tiled path."""
+    rc = load().moe_expert_ffn_shared(
+        _ptr(x_bf16), _ptr(sorted_pair), _ptr(offsets), _ptr(experts), _ptr(shared), fmt, T, k, H,
+        I, E, _ptr(y), int(bool(y_is_fp32)), _ptr(ws), ws_bytes, _stream(stream))
+    if not check and rc == MOE_EUNSUPPORTED:
+        return rc
+    return _check("moe_expert_ffn_shared", rc)
 
 
 def moe_combine(y, y_is_fp32, topk_w, y_shared, T, k, H, out_bf16, stream=None):

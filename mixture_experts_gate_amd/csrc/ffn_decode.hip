@@ -194,12 +194,16 @@ __device__ __forceinline__ const uint8_t *srow(const uint8_t *base, long r, int 
 
 // Experts that received at least one pair, as a bitmask (E <= 512), computed
 // by the whole wavefront from one round of loads; lookups afterwards are
-// scalar.
+// scalar. With a shared expert it is one more active expert, the last, with
+// expert index E and all T tokens as its rows.
 struct ActiveSet {
     uint64_t w[8];
-    int count;
+    int count;               // active experts, the shared one included
+    int routed;              // active routed experts
+    int e_shared;            // expert index standing for the shared expert (E)
     bool multi_pass;         // some expert has more rows than one token pass
-    __device__ __forceinline__ void init(const int32_t *__restrict__ offsets, int E) {
+    __device__ __forceinline__ void init(const int32_t *__restrict__ offsets, int E,
+                                         bool shared, int T) {
         count = 0;
         int cnt[8];
 #pragma unroll
@@ -214,10 +218,17 @@ struct ActiveSet {
             many |= __ballot(cnt[i] > kPass);
             count += __popcll(w[i]);
         }
+        routed = count;
+        e_shared = E;
+        if (shared) {
+            count += 1;
+            if (T > kPass) many = 1;
+        }
         multi_pass = many != 0;
     }
     // index of the a-th (0-based) active expert; a < count
     __device__ __forceinline__ int nth(int a) const {
+        if (a >= routed) return e_shared;
         int base = 0;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
@@ -241,6 +252,9 @@ struct DecArgs {
     const moe_expert_w *experts;
     void *out;                      // act (stage 1) or y (stage 2)
     int k, K, H, I, E, nrt;         // nrt: tiles per expert
+    const moe_expert_w *shared;     // shared expert (NULL: none): expert index E, rows =
+                                    // tokens 0..T-1 after the routed rows, y rows T*k + t
+    int T;
 };
 
 // Expert-level state of the tile being processed (wavefront-uniform: read
@@ -266,9 +280,10 @@ __device__ __forceinline__ void expert_state(const DecArgs &A, const ActiveSet &
     st.a = a;
     st.e = act.nth(a);
     const MOE_CONST int32_t *off = as_scalar(A.offsets);
-    st.row0 = off[st.e];
-    st.n_e = off[st.e + 1] - st.row0;
-    const MOE_CONST moe_expert_w *W = as_scalar(A.experts) + st.e;
+    const bool sh = st.e == A.E;              // the shared expert
+    st.row0 = off[st.e];                      // shared: its rows follow the routed ones
+    st.n_e = sh ? A.T : off[st.e + 1] - st.row0;
+    const MOE_CONST moe_expert_w *W = sh ? as_scalar(A.shared) : as_scalar(A.experts) + st.e;
     st.w = reinterpret_cast<const uint8_t *>(STAGE == 1 ? W->w13 : W->w2);
     st.s = reinterpret_cast<const uint8_t *>(STAGE == 1 ? W->s13 : W->s2);
     const uint32_t elems = (uint32_t)(STAGE == 1 ? 2 * A.I : A.H) * (uint32_t)A.K;
@@ -332,7 +347,10 @@ __device__ __forceinline__ void load_tokens(const DecArgs &A, const ES &st, int 
     const int r = p * kPass + m;
     const bool has = r < st.n_e;
     const uint16_t *row;
-    if (STAGE == 1) {
+    const bool sh = st.e == A.E;   // shared expert: row r is token r, output row T*k + r
+    if (STAGE == 1 && sh) {
+        row = A.src + (size_t)(has ? r : 0) * A.K;
+    } else if (STAGE == 1) {
         // the pass's 16 pair indices by scalar loads; lane m takes the m-th
         const MOE_CONST int32_t *sp = as_scalar(A.sorted_pair) + st.row0 + p * kPass;
         int pair = 0;
@@ -342,7 +360,7 @@ __device__ __forceinline__ void load_tokens(const DecArgs &A, const ES &st, int 
         row = A.src + (size_t)(pair / A.k) * A.K;
     } else {
         row = A.src + (size_t)(st.row0 + (has ? r : 0)) * A.K;
-        pidx = has ? A.sorted_pair[st.row0 + r] : 0;
+        pidx = !has ? 0 : sh ? A.T * A.k + r : A.sorted_pair[st.row0 + r];
     }
 #pragma unroll
     for (int s = 0; s < SPW; ++s) {
@@ -496,7 +514,7 @@ __global__ __launch_bounds__(kWave *KS) void ffn_dec_kernel(DecArgs A) {
     const int m = lane & 15, c = lane >> 4;
 
     ActiveSet act;
-    act.init(A.offsets, A.E);
+    act.init(A.offsets, A.E, A.shared != nullptr, A.T);
     // Tiles are active-expert-major. Workgroups take contiguous ranges, which
     // keep an expert's token operand in registers across its tiles, unless some
     // expert has more rows than one token pass: then workgroup b takes tiles b,
@@ -639,32 +657,30 @@ static int launch_stage(int slabs, hipStream_t s, const DecArgs &A, long slots) 
 
 template <int FMT>
 static int ffn_decode_fmt(const uint16_t *x, const int32_t *sorted_pair, const int32_t *offsets,
-                          const moe_expert_w *experts, int T, int k, int H, int I, int E, void *y,
-                          int y_is_fp32, uint16_t *act, hipStream_t s) {
+                          const moe_expert_w *experts, const moe_expert_w *shared, int T, int k,
+                          int H, int I, int E, void *y, int y_is_fp32, uint16_t *act,
+                          hipStream_t s) {
     const long n_pairs = (long)T * k;
-    const long slots = n_pairs < E ? n_pairs : E;
-    DecArgs a1{x, sorted_pair, offsets, experts, act, k, H, H, I, E, 0};
+    const long slots = (n_pairs < E ? n_pairs : E) + (shared ? 1 : 0);
+    DecArgs a1{x, sorted_pair, offsets, experts, act, k, H, H, I, E, 0, shared, T};
     int rc = launch_stage<FMT, 1, false>((H + 127) / 128, s, a1, slots);
     if (rc) return rc;
-    DecArgs a2{act, sorted_pair, offsets, experts, y, k, I, H, I, E, 0};
+    DecArgs a2{act, sorted_pair, offsets, experts, y, k, I, H, I, E, 0, shared, T};
     if (y_is_fp32) return launch_stage<FMT, 2, true>((I + 127) / 128, s, a2, slots);
     return launch_stage<FMT, 2, false>((I + 127) / 128, s, a2, slots);
 }
 
 int ffn_decode(const uint16_t *x, const int32_t *sorted_pair, const int32_t *offsets,
-               const moe_expert_w *experts, int fmt, int T, int k, int H, int I, int E, void *y,
-               int y_is_fp32, uint16_t *act, hipStream_t s) {
-    if (fmt == MOE_W_MXFP4)
-        return ffn_decode_fmt<MOE_W_MXFP4>(x, sorted_pair, offsets, experts, T, k, H, I, E, y,
-                                           y_is_fp32, act, s);
-    if (fmt == MOE_W_NVFP4)
-        return ffn_decode_fmt<MOE_W_NVFP4>(x, sorted_pair, offsets, experts, T, k, H, I, E, y,
-                                           y_is_fp32, act, s);
-    if (fmt == MOE_W_FP8)
-        return ffn_decode_fmt<MOE_W_FP8>(x, sorted_pair, offsets, experts, T, k, H, I, E, y,
-                                         y_is_fp32, act, s);
-    return ffn_decode_fmt<MOE_W_BF16>(x, sorted_pair, offsets, experts, T, k, H, I, E, y,
-                                      y_is_fp32, act, s);
+               const moe_expert_w *experts, const moe_expert_w *shared, int fmt, int T, int k,
+               int H, int I, int E, void *y, int y_is_fp32, uint16_t *act, hipStream_t s) {
+#define MOE_DEC_FMT(F)                                                                         \
+    return ffn_decode_fmt<F>(x, sorted_pair, offsets, experts, shared, T, k, H, I, E, y,       \
+                             y_is_fp32, act, s)
+    if (fmt == MOE_W_MXFP4) MOE_DEC_FMT(MOE_W_MXFP4);
+    if (fmt == MOE_W_NVFP4) MOE_DEC_FMT(MOE_W_NVFP4);
+    if (fmt == MOE_W_FP8) MOE_DEC_FMT(MOE_W_FP8);
+    MOE_DEC_FMT(MOE_W_BF16);
+#undef MOE_DEC_FMT
 }
 
 }  // namespace moe

@@ -14,7 +14,8 @@ constexpr int kChunk = 1024;            // pairs per chunk (one per thread)
 constexpr int kWavesPerChunk = kChunk / kWave;
 constexpr int kMaxE = 512;
 constexpr int kSmallMax = 4 * kChunk;   // pairs handled by the one-workgroup kernel
-constexpr int kFusedMaxT = 16;          // tokens routed by the fused kernel (one per wavefront)
+constexpr int kFusedMaxT = 16;          // fused router + permutation, gate computed in the kernel
+constexpr int kFusedMaxLogitsT = 8;     // fused router + permutation, logits given
 
 // Multisplit rank of this lane's expert e within its wavefront. Returns the
 // number of lower lanes with the same e; *count = lanes with the same e.
@@ -137,9 +138,11 @@ __global__ __launch_bounds__(kChunk) void permute_small_kernel(
     permute_block(ids, n, E, offsets, sorted_pair, pair_row, lds);
 }
 
-// Router + permutation in one workgroup (T <= kFusedMaxT): wavefront w routes
-// token w; the chosen ids stay in LDS for the permutation. (With more tokens a
-// single workgroup routes them serially and the two separate kernels win.)
+// Router + permutation in one workgroup (T <= kFusedMaxT, or kFusedMaxLogitsT
+// when logits are given): wavefront w routes token w; the chosen ids stay in
+// LDS for the permutation. Beyond that the router's selection rounds (about 85
+// dependent vector instructions per token and round) need more than one
+// compute unit, and the separate router and permutation kernels win.
 template <int VPL>
 __global__ __launch_bounds__(kChunk) void route_permute_kernel(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ wg,
@@ -289,7 +292,8 @@ extern "C" int moe_route_permute(const uint16_t *x_bf16, const uint16_t *wg_bf16
     if (T < 0 || E < 1 || E > kMaxE || k < 1 || k > E || k > kWave || !offsets) return MOE_EINVAL;
     if (!logits_in && T > 0 && (!x_bf16 || !wg_bf16 || H < 8 || H % 8)) return MOE_EINVAL;
     const long n = (long)T * k;
-    if (T == 0 || T > kFusedMaxT || n > kSmallMax) {
+    const int max_t = logits_in ? kFusedMaxLogitsT : kFusedMaxT;
+    if (T == 0 || T > max_t || n > kSmallMax) {
         int rc = moe_route(x_bf16, wg_bf16, logits_in, logits_out, T, H, E, k, renormalize,
                            topk_ids, topk_w, stream);
         if (rc) return rc;

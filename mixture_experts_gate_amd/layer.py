@@ -84,12 +84,15 @@ class MoeLayer:
         self.offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
         self.sorted_pair = torch.empty(max(n, 1), dtype=torch.int32, device=dev)
         self.pair_row = torch.empty(max(n, 1), dtype=torch.int32, device=dev)
-        pb, fb = _lib.moe_workspace_size(T_max, k, H, I, E)
+        # with a shared expert the weight-streaming kernels keep its T rows of
+        # activation after the routed ones, and y holds its T output rows
+        pb, _ = _lib.moe_workspace_size(T_max, k, H, I, E)
+        _, fb = _lib.moe_workspace_size(T_max, k + 1 if shared else k, H, I, E)
         self.ws_perm_bytes = max(pb, 256)
         self.ws_ffn_bytes = fb
         self.ws_perm = torch.empty(self.ws_perm_bytes, dtype=torch.uint8, device=dev)
         self.ws_ffn = torch.empty(fb, dtype=torch.uint8, device=dev)
-        self.y = torch.empty((max(n, 1), H), dtype=ydt, device=dev)
+        self.y = torch.empty((max(n + (T_max if shared else 0), 1), H), dtype=ydt, device=dev)
         self.out = torch.empty((T_max, H), dtype=torch.bfloat16, device=dev)
         if shared:
             self.sh_pair = torch.arange(T_max, dtype=torch.int32, device=dev)
@@ -123,33 +126,25 @@ class MoeLayer:
                             self.I, self.E, self.y, self.y_fp32, self.ws_ffn, self.ws_ffn_bytes,
                             stream)
 
-    def combine(self, T, with_shared=False, stream=None):
-        _lib.moe_combine(self.y, self.y_fp32, self.topk_w, self.y_sh if with_shared else None, T,
-                         self.k, self.H, self.out, stream)
+    def combine(self, T, with_shared=False, stream=None, y_shared=None):
+        """y_shared: the shared expert's rows (from ffn_with_shared); with_shared
+        alone takes them from the separate shared-expert buffer."""
+        if y_shared is None and with_shared:
+            y_shared = self.y_sh
+        _lib.moe_combine(self.y, self.y_fp32, self.topk_w, y_shared, T, self.k, self.H, self.out,
+                         stream)
 
     # whole layer -----------------------------------------------------------
     def forward(self, T, x, table, logits=None, wg=None, shared_table=None, renormalize=True,
-                stream=None, write_logits=False, fused_routing=True):
+                stream=None, write_logits=False, fused_routing=True, fuse_shared=True):
         """route -> permute -> expert FFN (+ shared expert) -> combine; returns out[:T].
         fused_routing: route and permute with the one-call entry (one kernel for
-        small batches) instead of the two separate calls."""
+        small batches) instead of the two separate calls.
+        fuse_shared: run the shared expert in the routed FFN's launches
+        (moe_expert_ffn_shared) where the weight-streaming kernels run; else,
+        and where the tiled kernels run, it is its own call on a side stream."""
         if T > self.T_max:
             raise ValueError("T exceeds the buffers' T_max")
-        if shared_table is not None:
-            # the shared expert needs only x: it runs on a side stream, forked
-            # before routing and joined before the combine, so that it overlaps
-            # routing and the routed experts
-            if self._sh_T != T:
-                self.prepare_shared(T)
-            main = stream if stream is not None else torch.cuda.current_stream()
-            if self._side is None:
-                self._side = torch.cuda.Stream(device=main.device)
-                self._fork = torch.cuda.Event()
-                self._join = torch.cuda.Event()
-            self._fork.record(main)
-            self._side.wait_event(self._fork)
-            self.shared_ffn(T, x, shared_table, self._side)
-            self._join.record(self._side)
         wl = write_logits or logits is None
         if fused_routing:
             self.route_permute(T, x=x, wg=wg, logits=logits, renormalize=renormalize,
@@ -158,11 +153,44 @@ class MoeLayer:
             self.route(T, x=x, wg=wg, logits=logits, renormalize=renormalize, stream=stream,
                        write_logits=wl)
             self.permute(T, stream)
-        self.ffn(T, x, table, stream)
-        if shared_table is not None:
-            main.wait_event(self._join)
-        self.combine(T, with_shared=shared_table is not None, stream=stream)
+        if shared_table is None:
+            self.ffn(T, x, table, stream)
+            self.combine(T, stream=stream)
+            return self.out[:T]
+        ysh = self.ffn_with_shared(T, x, table, shared_table, stream, fuse=fuse_shared)
+        self.combine(T, stream=stream, y_shared=ysh)
         return self.out[:T]
+
+    def ffn_with_shared(self, T, x, table, shared_table, stream=None, fuse=True):
+        """Routed and shared expert FFN; returns the shared expert's output rows
+        [T][H] for the combine. With fuse, where the weight-streaming kernels
+        run, the shared expert is one more expert of the routed launches (its
+        rows land in y after the routed pairs); otherwise it is its own call on
+        a side stream, forked before the routed FFN and joined after it."""
+        if not self.shared:
+            raise ValueError("layer was built without shared-expert buffers")
+        n = T * self.k
+        if fuse:
+            rc = _lib.moe_expert_ffn_shared(x, self.sorted_pair, self.offsets, table, shared_table,
+                                            self.fmt, T, self.k, self.H, self.I, self.E, self.y,
+                                            self.y_fp32, self.ws_ffn, self.ws_ffn_bytes, stream,
+                                            check=False)
+            if rc != _lib.MOE_EUNSUPPORTED:
+                return self.y[n:n + T]
+        if self._sh_T != T:
+            self.prepare_shared(T)
+        main = stream if stream is not None else torch.cuda.current_stream()
+        if self._side is None:
+            self._side = torch.cuda.Stream(device=main.device)
+            self._fork = torch.cuda.Event()
+            self._join = torch.cuda.Event()
+        self._fork.record(main)
+        self._side.wait_event(self._fork)
+        self.shared_ffn(T, x, shared_table, self._side)
+        self._join.record(self._side)
+        self.ffn(T, x, table, stream)
+        main.wait_event(self._join)
+        return self.y_sh[:T]
 
     def prepare_shared(self, T):
         """Write the shared expert's offsets {0, T} (outside any timed or captured region)."""

@@ -69,7 +69,7 @@ def workload(c, E=None):
 
 
 def run_layer(w: Workload, T, x, logits=None, wg=None, y_fp32=False, renormalize=True,
-              fused=True):
+              fused=True, fuse_shared=True):
     from mixture_experts_gate_amd.layer import MoeLayer
     cfg = w.cfg
     L = MoeLayer(cfg.H, w.E, cfg.k, cfg.I, cfg.fmt, T, shared=bool(cfg.n_shared), y_fp32=y_fp32,
@@ -79,7 +79,8 @@ def run_layer(w: Workload, T, x, logits=None, wg=None, y_fp32=False, renormalize
                     logits=None if logits is None else to_dev(logits),
                     wg=None if wg is None else to_dev_bf16(wg),
                     shared_table=w.dev_shared.table if w.dev_shared else None,
-                    renormalize=renormalize, write_logits=True, fused_routing=fused)
+                    renormalize=renormalize, write_logits=True, fused_routing=fused,
+                    fuse_shared=fuse_shared)
     torch.cuda.synchronize()
     return L, out
 
@@ -196,7 +197,8 @@ PERM_CASES = [(1, 128, 8, "uniform"), (8, 128, 8, "uniform"), (64, 128, 8, "unif
               (16, 8, 2, "uniform"), (500, 256, 6, "skew"), (513, 512, 4, "uniform"),
               (4096, 256, 6, "uniform"), (8192, 128, 8, "uniform"), (6000, 64, 3, "skew"),
               (1, 1, 1, "uniform"), (3, 7, 7, "uniform"), (33, 128, 8, "uniform"),
-              (48, 64, 4, "skew"), (64, 512, 6, "skew")]
+              (48, 64, 4, "skew"), (64, 512, 6, "skew"), (100, 128, 8, "skew"),
+              (256, 128, 8, "uniform"), (250, 64, 4, "skew"), (257, 128, 8, "uniform")]
 
 
 @pytest.mark.parametrize("T,E,k,kind", PERM_CASES)
@@ -400,11 +402,12 @@ def test_layer_deterministic(lib):
     assert torch.equal(a[0], o2) and torch.equal(a[1], L2.y) and torch.equal(a[2], L2.sorted_pair)
 
 
-def test_layer_graph_replays(lib):
-    """Graph replays of the layer (config 4 with its shared expert on a side
-    stream, T=64) repeat the eager result exactly, with eager calls on the same
-    buffers between the replays."""
-    _announce("graph replays of config 4 T=64 against the eager result")
+@pytest.mark.parametrize("fuse_shared", [True, False])
+def test_layer_graph_replays(lib, fuse_shared):
+    """Graph replays of the layer (config 4, T=64, its shared expert in the
+    routed launches or as its own call on a side stream) repeat the eager
+    result exactly, with eager calls on the same buffers between the replays."""
+    _announce(f"graph replays of config 4 T=64 against the eager result (fused={fuse_shared})")
     from mixture_experts_gate_amd.layer import MoeLayer
     w = workload(4)
     T = 64
@@ -412,23 +415,27 @@ def test_layer_graph_replays(lib):
     lg = to_dev(synth.router_logits(w.cfg, T, step=6))
     L = MoeLayer(w.cfg.H, w.E, w.cfg.k, w.cfg.I, w.cfg.fmt, T, shared=True, device=DEV)
     L.prepare_shared(T)
-    ref = L.forward(T, x, w.dev.table, logits=lg, shared_table=w.dev_shared.table).clone()
+    ref = L.forward(T, x, w.dev.table, logits=lg, shared_table=w.dev_shared.table,
+                    fuse_shared=fuse_shared).clone()
     torch.cuda.synchronize()
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
-        L.forward(T, x, w.dev.table, logits=lg, shared_table=w.dev_shared.table)
+        L.forward(T, x, w.dev.table, logits=lg, shared_table=w.dev_shared.table,
+                  fuse_shared=fuse_shared)
     torch.cuda.current_stream().wait_stream(s)
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
-        out = L.forward(T, x, w.dev.table, logits=lg, shared_table=w.dev_shared.table)
+        out = L.forward(T, x, w.dev.table, logits=lg, shared_table=w.dev_shared.table,
+                        fuse_shared=fuse_shared)
     for r in range(4):
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(out, ref), f"replay {r} differs from the eager result"
         # eager work on the same buffers between replays
-        L.forward(T, x, w.dev.table, logits=lg, shared_table=w.dev_shared.table)
+        L.forward(T, x, w.dev.table, logits=lg, shared_table=w.dev_shared.table,
+                  fuse_shared=fuse_shared)
         torch.cuda.synchronize()
         assert torch.equal(L.out[:T], ref)
 
@@ -490,6 +497,63 @@ def test_layer_nvfp4_fp8_weights(lib, orc, fmt, H, I, E, k, T, kind):
     x = synth.activations(cfg, T, step=2)
     lg = synth.router_logits(cfg, T, step=2) if kind == "uniform" else _perm_case(T, E, k, kind)
     L, out = run_layer(w, T, x, logits=lg)
+    _check_layer_full(orc, w, T, x, L, out, logits=lg)
+
+
+_SHARED_CASES = [("mxfp4", 1, "uniform", False), ("mxfp4", 7, "uniform", False),
+                 ("mxfp4", 17, "skew", False), ("mxfp4", 40, "uniform", True),
+                 ("bf16", 9, "uniform", False), ("nvfp4", 20, "uniform", False),
+                 ("fp8", 33, "skew", False)]
+
+
+@pytest.mark.parametrize("fmt,T,kind,y_fp32", _SHARED_CASES,
+                         ids=[f"{c[0]}-T{c[1]}-{c[2]}{'-f32' if c[3] else ''}"
+                              for c in _SHARED_CASES])
+def test_ffn_shared_in_routed_launch(lib, orc, fmt, T, kind, y_fp32):
+    """The shared expert as one more expert of the routed launches
+    (moe_expert_ffn_shared): every routed row and every shared row against the
+    oracle, the layer output too, and the same layer with the shared expert as
+    its own call. T > 16 takes the shared expert through several token passes."""
+    _announce(f"ffn+shared one launch: {fmt} T={T} {kind} y_fp32={y_fp32}")
+    H, I, E, k = 512, 256, 16, 4
+    cfg = synth.LayerConfig(f"shared_{fmt}", H, E, k, I, fmt, 1, "uniform", (T,), "gauss_" + fmt,
+                            seed=31)
+    w = Workload(cfg)
+    x = synth.activations(cfg, T, step=4)
+    lg = synth.router_logits(cfg, T, step=4) if kind == "uniform" else _perm_case(T, E, k, kind)
+    L, out = run_layer(w, T, x, logits=lg, y_fp32=y_fp32)
+    ref = _check_layer_full(orc, w, T, x, L, out, logits=lg)
+    ysh_ref = orc.ffn_rows(x, w.shared[None], w.lay, np.arange(T, dtype=np.int32),
+                           np.zeros(T, np.int32))
+    ysh = L.y[T * k:T * k + T].float().cpu().numpy()
+    assert_close(ysh, ysh_ref, f"shared expert rows (T={T})")
+    L2, out2 = run_layer(w, T, x, logits=lg, y_fp32=y_fp32, fuse_shared=False)
+    assert_close(bf16_dev_to_f64(out2), ref["out_f64"], f"layer output, separate shared call")
+    assert_close(L2.y_sh[:T].float().cpu().numpy(), ysh_ref, "shared rows, separate call")
+
+
+def test_ffn_shared_tiled_path_unsupported(lib, orc):
+    """Where the tiled kernels would run, moe_expert_ffn_shared declines before
+    any device work and the layer runs the shared expert as its own call."""
+    _announce("ffn+shared: tiled path forced -> EUNSUPPORTED, layer falls back")
+    H, I, E, k, T = 512, 256, 16, 4, 24
+    cfg = synth.LayerConfig("shared_tiled", H, E, k, I, "mxfp4", 1, "uniform", (T,),
+                            "gauss_mxfp4", seed=32)
+    w = Workload(cfg)
+    x = synth.activations(cfg, T, step=1)
+    lg = synth.router_logits(cfg, T, step=1)
+    from mixture_experts_gate_amd.layer import MoeLayer
+    M = MoeLayer(H, E, k, I, "mxfp4", T, shared=True, device=DEV)
+    M.route_permute(T, logits=to_dev(lg))
+    lib.moe_set_option(lib.MOE_OPT_FFN_PATH, 2)
+    try:
+        rc = lib.moe_expert_ffn_shared(to_dev_bf16(x), M.sorted_pair, M.offsets, w.dev.table,
+                                       w.dev_shared.table, M.fmt, T, k, H, I, E, M.y, False,
+                                       M.ws_ffn, M.ws_ffn_bytes, check=False)
+        assert rc == lib.MOE_EUNSUPPORTED
+        L, out = run_layer(w, T, x, logits=lg)
+    finally:
+        lib.moe_set_option(lib.MOE_OPT_FFN_PATH, 0)
     _check_layer_full(orc, w, T, x, L, out, logits=lg)
 
 

@@ -101,6 +101,31 @@ def test_argument_errors_before_any_device_work(lib):
     assert L.moe_route(None, None, None, None, 0, 64, 8, 2, 1, None, None, None) == lib.MOE_OK
 
 
+def test_ffn_shared_argument_errors(lib):
+    """moe_expert_ffn_shared: a missing shared expert, a workspace sized for the
+    routed rows only, and a forced tiled path are refused before device work."""
+    L = lib.load()
+    dummy = 0x1000  # never dereferenced: validation fails first
+    T, k, H, I, E = 8, 4, 256, 128, 16
+    _, fb_k = lib.moe_workspace_size(T, k, H, I, E)
+    _, fb_k1 = lib.moe_workspace_size(T, k + 1, H, I, E)
+    assert fb_k1 > fb_k
+    assert L.moe_expert_ffn_shared(dummy, dummy, dummy, dummy, None, 1, T, k, H, I, E, dummy, 0,
+                                   dummy, fb_k1, None) == lib.MOE_EINVAL
+    assert L.moe_expert_ffn_shared(dummy, dummy, dummy, dummy, dummy, 1, T, k, H, I, E, dummy, 0,
+                                   dummy, fb_k, None) == lib.MOE_EINVAL
+    assert L.moe_expert_ffn_shared(dummy, dummy, dummy, dummy, dummy, 1, T, k, H, I, 513, dummy,
+                                   0, dummy, 1 << 30, None) == lib.MOE_EINVAL
+    assert L.moe_expert_ffn_shared(None, None, None, None, None, 1, 0, k, H, I, E, None, 0, None,
+                                   0, None) == lib.MOE_OK
+    lib.moe_set_option(lib.MOE_OPT_FFN_PATH, 2)
+    try:
+        assert L.moe_expert_ffn_shared(dummy, dummy, dummy, dummy, dummy, 1, T, k, H, I, E, dummy,
+                                       0, dummy, fb_k1, None) == lib.MOE_EUNSUPPORTED
+    finally:
+        lib.moe_set_option(lib.MOE_OPT_FFN_PATH, 0)
+
+
 def test_cache_reserve_argument_errors(lib):
     L = lib.load()
     h = C.c_void_p(0)
