@@ -77,8 +77,12 @@ static void timing_drain() {
 
 size_t permute_ws_bytes(long n, int E);
 int ffn_decode(const uint16_t *x, const int32_t *sorted_pair, const int32_t *offsets,
-               const moe_expert_w *experts, const moe_expert_w *shared, int fmt, int T, int k,
-               int H, int I, int E, void *y, int y_is_fp32, uint16_t *act, hipStream_t s);
+               const moe_expert_w *experts, int fmt, int T, int k, int H, int I, int E, void *y,
+               int y_is_fp32, uint16_t *act, hipStream_t s);
+int ffn_decode_shared(const uint16_t *x, const int32_t *sorted_pair, const int32_t *offsets,
+                      const moe_expert_w *experts, const moe_expert_w *shared, int fmt, int T,
+                      int k, int H, int I, int E, void *y, int y_is_fp32, uint16_t *act,
+                      hipStream_t s);
 int ffn_prefill(const uint16_t *x, const int32_t *sorted_pair, const int32_t *offsets,
                 const moe_expert_w *experts, int fmt, int T, int k, int H, int I, int E, void *y,
                 int y_is_fp32, void *ws, hipStream_t s);
@@ -195,8 +199,8 @@ extern "C" int moe_expert_ffn(const uint16_t *x_bf16, const int32_t *sorted_pair
     if (use_prefill(n, E, fmt, H, I))
         return ffn_prefill(x_bf16, sorted_pair, offsets, experts, fmt, T, k, H, I, E, y, y_is_fp32,
                            ws, s);
-    return ffn_decode(x_bf16, sorted_pair, offsets, experts, nullptr, fmt, T, k, H, I, E, y,
-                      y_is_fp32, act, s);
+    return ffn_decode(x_bf16, sorted_pair, offsets, experts, fmt, T, k, H, I, E, y, y_is_fp32,
+                      act, s);
 }
 
 extern "C" int moe_expert_ffn_shared(const uint16_t *x_bf16, const int32_t *sorted_pair,
@@ -217,6 +221,7 @@ extern "C" int moe_expert_ffn_shared(const uint16_t *x_bf16, const int32_t *sort
     if (ws_bytes < ffn_ws_bytes((long)T * (k + 1), T, H, I, E)) return MOE_EINVAL;
     // the tiled kernels take the shared expert as its own call
     if (use_prefill(n, E, fmt, H, I)) return MOE_EUNSUPPORTED;
-    return ffn_decode(x_bf16, sorted_pair, offsets, experts, shared, fmt, T, k, H, I, E, y,
-                      y_is_fp32, reinterpret_cast<uint16_t *>(ws), (hipStream_t)stream);
+    return ffn_decode_shared(x_bf16, sorted_pair, offsets, experts, shared, fmt, T, k, H, I, E,
+                             y, y_is_fp32, reinterpret_cast<uint16_t *>(ws),
+                             (hipStream_t)stream);
 }

@@ -192,6 +192,15 @@ __device__ __forceinline__ const uint8_t *srow(const uint8_t *base, long r, int 
     return base ? base + r * (K / 32) : nullptr;
 }
 
+// The shared expert of a launch that carries one: expert index E, its rows
+// the T tokens after the routed rows, its outputs y rows T*k + t. A second
+// kernel argument, so that launches without it keep the argument layout (and
+// scalar registers) they had.
+struct ShArgs {
+    const moe_expert_w *shared;
+    int T;
+};
+
 // Experts that received at least one pair, as a bitmask (E <= 512), computed
 // by the whole wavefront from one round of loads; lookups afterwards are
 // scalar. With a shared expert it is one more active expert, the last, with
@@ -201,9 +210,12 @@ struct ActiveSet {
     int count;               // active experts, the shared one included
     int routed;              // active routed experts
     int e_shared;            // expert index standing for the shared expert (E)
+    const moe_expert_w *sh_w;  // shared expert's weights and rows (SH launches only)
+    int sh_T;
     bool multi_pass;         // some expert has more rows than one token pass
+    template <bool SH>
     __device__ __forceinline__ void init(const int32_t *__restrict__ offsets, int E,
-                                         bool shared, int T) {
+                                         const ShArgs &S) {
         count = 0;
         int cnt[8];
 #pragma unroll
@@ -220,15 +232,20 @@ struct ActiveSet {
         }
         routed = count;
         e_shared = E;
-        if (shared) {
+        if constexpr (SH) {
             count += 1;
-            if (T > kPass) many = 1;
+            sh_w = S.shared;
+            sh_T = S.T;
+            if (S.T > kPass) many = 1;
         }
         multi_pass = many != 0;
     }
     // index of the a-th (0-based) active expert; a < count
+    template <bool SH>
     __device__ __forceinline__ int nth(int a) const {
-        if (a >= routed) return e_shared;
+        if constexpr (SH) {
+            if (a >= routed) return e_shared;
+        }
         int base = 0;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
@@ -252,10 +269,8 @@ struct DecArgs {
     const moe_expert_w *experts;
     void *out;                      // act (stage 1) or y (stage 2)
     int k, K, H, I, E, nrt;         // nrt: tiles per expert
-    const moe_expert_w *shared;     // shared expert (NULL: none): expert index E, rows =
-                                    // tokens 0..T-1 after the routed rows, y rows T*k + t
-    int T;
 };
+
 
 // Expert-level state of the tile being processed (wavefront-uniform: read
 // with scalar loads, so fetching it never waits for the weights in flight).
@@ -274,16 +289,17 @@ struct ExpertState : TensorScale<tensor_scaled(FMT)> {
     buf_rsrc wr, sr;                // the same as ranged buffer resources (block formats)
 };
 
-template <int STAGE, int FMT>
+// SH: the launch carries the shared expert (compiled out otherwise).
+template <int STAGE, int FMT, bool SH>
 __device__ __forceinline__ void expert_state(const DecArgs &A, const ActiveSet &act, int a,
                                              ExpertState<FMT> &st) {
     st.a = a;
-    st.e = act.nth(a);
+    st.e = act.template nth<SH>(a);
     const MOE_CONST int32_t *off = as_scalar(A.offsets);
-    const bool sh = st.e == A.E;              // the shared expert
+    const bool sh = SH && st.e == A.E;        // the shared expert
     st.row0 = off[st.e];                      // shared: its rows follow the routed ones
-    st.n_e = sh ? A.T : off[st.e + 1] - st.row0;
-    const MOE_CONST moe_expert_w *W = sh ? as_scalar(A.shared) : as_scalar(A.experts) + st.e;
+    st.n_e = sh ? act.sh_T : off[st.e + 1] - st.row0;
+    const MOE_CONST moe_expert_w *W = sh ? as_scalar(act.sh_w) : as_scalar(A.experts) + st.e;
     st.w = reinterpret_cast<const uint8_t *>(STAGE == 1 ? W->w13 : W->w2);
     st.s = reinterpret_cast<const uint8_t *>(STAGE == 1 ? W->s13 : W->s2);
     const uint32_t elems = (uint32_t)(STAGE == 1 ? 2 * A.I : A.H) * (uint32_t)A.K;
@@ -340,27 +356,28 @@ __device__ __forceinline__ void load_tile(const DecArgs &A, const ExpertState<FM
 
 // Token operand of pass p (rows p*16 .. p*16+15 of the expert), K slabs of
 // this wavefront; for stage 2 also the pair index each row's output goes to.
-template <int STAGE, int SPW, class ES>
+template <int STAGE, int SPW, bool SH, class ES>
 __device__ __forceinline__ void load_tokens(const DecArgs &A, const ES &st, int p, int wv,
                                             int m, int c, u32x4 (&xr)[SPW][4], int &pidx) {
     const int nblk = A.K / 32;
     const int r = p * kPass + m;
     const bool has = r < st.n_e;
     const uint16_t *row;
-    const bool sh = st.e == A.E;   // shared expert: row r is token r, output row T*k + r
-    if (STAGE == 1 && sh) {
-        row = A.src + (size_t)(has ? r : 0) * A.K;
-    } else if (STAGE == 1) {
-        // the pass's 16 pair indices by scalar loads; lane m takes the m-th
-        const MOE_CONST int32_t *sp = as_scalar(A.sorted_pair) + st.row0 + p * kPass;
+    const bool sh = SH && st.e == A.E;   // shared expert: row r is token r, output row T*k + r
+    if (STAGE == 1) {
+        // the pass's 16 pair indices by scalar loads; lane m takes the m-th.
+        // (The shared expert reads the first entries instead, in bounds since
+        // T <= T*k, and takes token r: a select, no branch around the loads.)
+        const MOE_CONST int32_t *sp = as_scalar(A.sorted_pair) + (sh ? 0 : st.row0 + p * kPass);
         int pair = 0;
 #pragma unroll
         for (int i = 0; i < kPass; ++i)
             if (p * kPass + i < st.n_e) pair = m == i ? sp[i] : pair;
-        row = A.src + (size_t)(pair / A.k) * A.K;
+        row = A.src + (size_t)(sh ? r : pair / A.k) * A.K;
     } else {
         row = A.src + (size_t)(st.row0 + (has ? r : 0)) * A.K;
-        pidx = !has ? 0 : sh ? A.T * A.k + r : A.sorted_pair[st.row0 + r];
+        // (the shared expert's n_e is T, so its outputs start at row n_e * k = T*k)
+        pidx = !has ? 0 : sh ? st.n_e * A.k + r : A.sorted_pair[st.row0 + r];
     }
 #pragma unroll
     for (int s = 0; s < SPW; ++s) {
@@ -374,7 +391,7 @@ __device__ __forceinline__ void load_tokens(const DecArgs &A, const ES &st, int 
 
 // One tile: token operand if the expert changed, prefetch of the next tile's
 // weights into `wn`, multiply from `wc`, K-split reduction, epilogue.
-template <int FMT, int STAGE, int SPW, int KS, int NB, bool YF32, bool FULL, int D>
+template <int FMT, int STAGE, int SPW, int KS, int NB, bool YF32, bool FULL, int D, bool SH>
 __device__ __forceinline__ void dec_step(const DecArgs &A, const ActiveSet &act,
                                          float (&red)[2][KS > 1 ? KS - 1 : 1][NB][4][kWave],
                                          WFrag<FMT> (&wc)[SPW][NB], WFrag<FMT> (&wn)[SPW][NB],
@@ -386,7 +403,7 @@ __device__ __forceinline__ void dec_step(const DecArgs &A, const ActiveSet &act,
         // token operand for the first pass of this tile (loaded before the next
         // prefetch, so that waiting for it does not wait for the prefetched weights)
         if (x_key != cur.a * 4096) {
-            load_tokens<STAGE, SPW>(A, cur, 0, wv, m, c, xr, pidx);
+            load_tokens<STAGE, SPW, SH>(A, cur, 0, wv, m, c, xr, pidx);
             x_key = cur.a * 4096;
             x_raw = true;
         }
@@ -394,12 +411,12 @@ __device__ __forceinline__ void dec_step(const DecArgs &A, const ActiveSet &act,
         // `prev` holds the state of the tile before it. Issued, switched off,
         // also past the end (see buf_rsrc).
         const int an = pf ? pn.a : prev.a;
-        if (an != prev.a) expert_state<STAGE, FMT>(A, act, an, nxt);
+        if (an != prev.a) expert_state<STAGE, FMT, SH>(A, act, an, nxt);
         else nxt = prev;
         load_tile<FMT, STAGE, SPW, NB, FULL>(A, nxt, pf ? pn.rt : 0, wv, lane, wn, pf);
         for (int p = 0; p * kPass < cur.n_e; ++p) {
             if (p > 0) {   // more than 16 tokens: next 16 of this expert
-                load_tokens<STAGE, SPW>(A, cur, p, wv, m, c, xr, pidx);
+                load_tokens<STAGE, SPW, SH>(A, cur, p, wv, m, c, xr, pidx);
                 x_key = cur.a * 4096 + p;
                 x_raw = true;
             }
@@ -506,15 +523,15 @@ __device__ __forceinline__ void dec_step(const DecArgs &A, const ActiveSet &act,
         }
 }
 
-template <int FMT, int STAGE, int SPW, int KS, int NB, bool YF32, bool FULL>
-__global__ __launch_bounds__(kWave *KS) void ffn_dec_kernel(DecArgs A) {
-    __shared__ float red[2][KS > 1 ? KS - 1 : 1][NB][4][kWave];
+template <int FMT, int STAGE, int SPW, int KS, int NB, bool YF32, bool FULL, bool SH>
+__device__ __forceinline__ void ffn_dec_body(const DecArgs &A, const ShArgs &S,
+                                             float (&red)[2][KS > 1 ? KS - 1 : 1][NB][4][kWave]) {
     const int lane = lane_id();
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);   // wavefront-uniform
     const int m = lane & 15, c = lane >> 4;
 
     ActiveSet act;
-    act.init(A.offsets, A.E, A.shared != nullptr, A.T);
+    act.template init<SH>(A.offsets, A.E, S);
     // Tiles are active-expert-major. Workgroups take contiguous ranges, which
     // keep an expert's token operand in registers across its tiles, unless some
     // expert has more rows than one token pass: then workgroup b takes tiles b,
@@ -544,18 +561,18 @@ __global__ __launch_bounds__(kWave *KS) void ffn_dec_kernel(DecArgs A) {
     TilePos pos[D];
     WFrag<FMT> wr[D][SPW][NB];
     pos[0] = TilePos{t0 / A.nrt, t0 % A.nrt};
-    expert_state<STAGE, FMT>(A, act, pos[0].a, es[0]);
+    expert_state<STAGE, FMT, SH>(A, act, pos[0].a, es[0]);
 #pragma unroll
     for (int d = 1; d < D - 1; ++d) {
         pos[d] = d < n ? advance(pos[d - 1], sa, srt, A.nrt) : pos[d - 1];
         if (pos[d].a == es[d - 1].a) es[d] = es[d - 1];
-        else expert_state<STAGE, FMT>(A, act, pos[d].a, es[d]);
+        else expert_state<STAGE, FMT, SH>(A, act, pos[d].a, es[d]);
     }
     // the first tile's token operand is requested before any weights, so that
     // resolving its row indices does not wait behind the weight prefetch
     u32x4 xr[SPW][4];
     int pidx = 0;
-    load_tokens<STAGE, SPW>(A, es[0], 0, wv, m, c, xr, pidx);
+    load_tokens<STAGE, SPW, SH>(A, es[0], 0, wv, m, c, xr, pidx);
     int x_key = es[0].a * 4096;
     bool x_raw = true;      // tokens just loaded (not yet in the product type)
     int buf = 0;
@@ -570,12 +587,25 @@ __global__ __launch_bounds__(kWave *KS) void ffn_dec_kernel(DecArgs A) {
                 const int fd = (d + D - 1) % D, pd = (d + D - 2) % D;
                 const bool pf = i + d + D - 1 < n;
                 pos[fd] = pf ? advance(pos[pd], sa, srt, A.nrt) : pos[pd];
-                dec_step<FMT, STAGE, SPW, KS, NB, YF32, FULL, D>(
+                dec_step<FMT, STAGE, SPW, KS, NB, YF32, FULL, D, SH>(
                     A, act, red, wr[d], wr[fd], xr, es[d], es[pd], es[fd], pidx, x_key, x_raw, buf,
                     pos[d].rt, pos[fd], pf, lane, wv, m, c);
             }
         }
     }
+}
+
+template <int FMT, int STAGE, int SPW, int KS, int NB, bool YF32, bool FULL>
+__global__ __launch_bounds__(kWave *KS) void ffn_dec_kernel(DecArgs A) {
+    __shared__ float red[2][KS > 1 ? KS - 1 : 1][NB][4][kWave];
+    ffn_dec_body<FMT, STAGE, SPW, KS, NB, YF32, FULL, false>(A, ShArgs{nullptr, 0}, red);
+}
+
+// the same with the shared expert as one more expert of the launch
+template <int FMT, int STAGE, int SPW, int KS, int NB, bool YF32, bool FULL>
+__global__ __launch_bounds__(kWave *KS) void ffn_dec_kernel_sh(DecArgs A, ShArgs S) {
+    __shared__ float red[2][KS > 1 ? KS - 1 : 1][NB][4][kWave];
+    ffn_dec_body<FMT, STAGE, SPW, KS, NB, YF32, FULL, true>(A, S, red);
 }
 
 // ------------------------------------------------------------- launchers --
@@ -605,33 +635,44 @@ static unsigned resident_grid(K kernel, int threads) {
 #ifndef MOE_DEC_WG_PER_CU
 #define MOE_DEC_WG_PER_CU 0
 #endif
-template <int FMT, int STAGE, int SPW, int KS, int NB, bool YF32, bool FULL>
-static int launch_dec(hipStream_t s, DecArgs A, long slots) {
+template <int FMT, int STAGE, int SPW, int KS, int NB, bool YF32, bool FULL, bool SH>
+static int launch_dec(hipStream_t s, DecArgs A, const ShArgs &S, long slots) {
     static unsigned full = 0;
-    if (!full)
-        full = MOE_DEC_WG_PER_CU ? MOE_DEC_WG_PER_CU * num_cus()
-                                 : resident_grid(ffn_dec_kernel<FMT, STAGE, SPW, KS, NB, YF32, FULL>, kWave * KS);
+    if (!full) {
+        unsigned res;
+        if constexpr (SH)
+            res = resident_grid(ffn_dec_kernel_sh<FMT, STAGE, SPW, KS, NB, YF32, FULL>, kWave * KS);
+        else
+            res = resident_grid(ffn_dec_kernel<FMT, STAGE, SPW, KS, NB, YF32, FULL>, kWave * KS);
+        full = MOE_DEC_WG_PER_CU ? MOE_DEC_WG_PER_CU * num_cus() : res;
+    }
     // tiles per expert
     A.nrt = STAGE == 1 ? A.I / (8 * NB) : A.H / (16 * NB);
     const long max_tiles = slots * A.nrt;
     const unsigned grid = (unsigned)(max_tiles < (long)full ? max_tiles : (long)full);
     if (grid == 0) return MOE_OK;
-    MOE_LAUNCH(STAGE == 1 ? K_DEC_GATE_UP : K_DEC_DOWN, (ffn_dec_kernel<FMT, STAGE, SPW, KS, NB, YF32, FULL>), dim3(grid),
-                                 dim3(kWave * KS), 0, s, A);
+    if constexpr (SH)
+        MOE_LAUNCH(STAGE == 1 ? K_DEC_GATE_UP : K_DEC_DOWN,
+                   (ffn_dec_kernel_sh<FMT, STAGE, SPW, KS, NB, YF32, FULL>), dim3(grid),
+                   dim3(kWave * KS), 0, s, A, S);
+    else
+        MOE_LAUNCH(STAGE == 1 ? K_DEC_GATE_UP : K_DEC_DOWN,
+                   (ffn_dec_kernel<FMT, STAGE, SPW, KS, NB, YF32, FULL>), dim3(grid),
+                   dim3(kWave * KS), 0, s, A);
     return check_launch();
 }
 
 // K split: KS wavefronts x SPW 128-column slabs each. Exact splits for the
 // slab counts of the supported shapes; otherwise a bounds-checked split.
 // Tiles: stage 1 = 16 gate + 16 up rows (NB = 2); stage 2 = NB2 x 16 rows.
-template <int FMT, int STAGE, bool YF32>
-static int launch_stage(int slabs, hipStream_t s, const DecArgs &A, long slots) {
+template <int FMT, int STAGE, bool YF32, bool SH>
+static int launch_stage(int slabs, hipStream_t s, const DecArgs &A, const ShArgs &S, long slots) {
     // 64-row down tiles, unless that leaves fewer tiles than two workgroups
     // per compute unit (a handful of experts at small batches): then 32
     const bool nb4 = STAGE == 2 && A.H % 64 == 0 && slots * (A.H / 64) >= 2L * num_cus();
 #define MOE_ST(SPW_, KS_, FULL_)                                                              \
-    return nb4 ? launch_dec<FMT, STAGE, SPW_, KS_, (STAGE == 2 ? 4 : 2), YF32, FULL_>(s, A, slots) \
-               : launch_dec<FMT, STAGE, SPW_, KS_, 2, YF32, FULL_>(s, A, slots)
+    return nb4 ? launch_dec<FMT, STAGE, SPW_, KS_, (STAGE == 2 ? 4 : 2), YF32, FULL_, SH>(s, A, S, slots) \
+               : launch_dec<FMT, STAGE, SPW_, KS_, 2, YF32, FULL_, SH>(s, A, S, slots)
     switch (slabs) {
         case 1: MOE_ST(1, 1, true);
         case 2: MOE_ST(1, 2, true);
@@ -655,32 +696,50 @@ static int launch_stage(int slabs, hipStream_t s, const DecArgs &A, long slots) 
     return MOE_EUNSUPPORTED;
 }
 
-template <int FMT>
+template <int FMT, bool SH>
 static int ffn_decode_fmt(const uint16_t *x, const int32_t *sorted_pair, const int32_t *offsets,
                           const moe_expert_w *experts, const moe_expert_w *shared, int T, int k,
                           int H, int I, int E, void *y, int y_is_fp32, uint16_t *act,
                           hipStream_t s) {
     const long n_pairs = (long)T * k;
-    const long slots = (n_pairs < E ? n_pairs : E) + (shared ? 1 : 0);
-    DecArgs a1{x, sorted_pair, offsets, experts, act, k, H, H, I, E, 0, shared, T};
-    int rc = launch_stage<FMT, 1, false>((H + 127) / 128, s, a1, slots);
+    const long slots = (n_pairs < E ? n_pairs : E) + (SH ? 1 : 0);
+    const ShArgs S{shared, T};
+    DecArgs a1{x, sorted_pair, offsets, experts, act, k, H, H, I, E, 0};
+    int rc = launch_stage<FMT, 1, false, SH>((H + 127) / 128, s, a1, S, slots);
     if (rc) return rc;
-    DecArgs a2{act, sorted_pair, offsets, experts, y, k, I, H, I, E, 0, shared, T};
-    if (y_is_fp32) return launch_stage<FMT, 2, true>((I + 127) / 128, s, a2, slots);
-    return launch_stage<FMT, 2, false>((I + 127) / 128, s, a2, slots);
+    DecArgs a2{act, sorted_pair, offsets, experts, y, k, I, H, I, E, 0};
+    if (y_is_fp32) return launch_stage<FMT, 2, true, SH>((I + 127) / 128, s, a2, S, slots);
+    return launch_stage<FMT, 2, false, SH>((I + 127) / 128, s, a2, S, slots);
 }
 
+#define MOE_DEC_FMT(F, SH)                                                                     \
+    return ffn_decode_fmt<F, SH>(x, sorted_pair, offsets, experts, shared, T, k, H, I, E, y,   \
+                                 y_is_fp32, act, s)
+#define MOE_DEC_DISPATCH(SH)                                                                   \
+    if (fmt == MOE_W_MXFP4) MOE_DEC_FMT(MOE_W_MXFP4, SH);                                      \
+    if (fmt == MOE_W_NVFP4) MOE_DEC_FMT(MOE_W_NVFP4, SH);                                      \
+    if (fmt == MOE_W_FP8) MOE_DEC_FMT(MOE_W_FP8, SH);                                          \
+    MOE_DEC_FMT(MOE_W_BF16, SH)
+
+// The kernels with the shared-expert path are instantiated in a translation
+// unit of their own (ffn_decode_shared.hip), so that the two sets compile in
+// parallel and the routed-only kernels carry none of that path.
+#ifndef MOE_DEC_SHARED_UNIT
 int ffn_decode(const uint16_t *x, const int32_t *sorted_pair, const int32_t *offsets,
-               const moe_expert_w *experts, const moe_expert_w *shared, int fmt, int T, int k,
-               int H, int I, int E, void *y, int y_is_fp32, uint16_t *act, hipStream_t s) {
-#define MOE_DEC_FMT(F)                                                                         \
-    return ffn_decode_fmt<F>(x, sorted_pair, offsets, experts, shared, T, k, H, I, E, y,       \
-                             y_is_fp32, act, s)
-    if (fmt == MOE_W_MXFP4) MOE_DEC_FMT(MOE_W_MXFP4);
-    if (fmt == MOE_W_NVFP4) MOE_DEC_FMT(MOE_W_NVFP4);
-    if (fmt == MOE_W_FP8) MOE_DEC_FMT(MOE_W_FP8);
-    MOE_DEC_FMT(MOE_W_BF16);
-#undef MOE_DEC_FMT
+               const moe_expert_w *experts, int fmt, int T, int k, int H, int I, int E, void *y,
+               int y_is_fp32, uint16_t *act, hipStream_t s) {
+    const moe_expert_w *shared = nullptr;
+    MOE_DEC_DISPATCH(false);
 }
+#else
+int ffn_decode_shared(const uint16_t *x, const int32_t *sorted_pair, const int32_t *offsets,
+                      const moe_expert_w *experts, const moe_expert_w *shared, int fmt, int T,
+                      int k, int H, int I, int E, void *y, int y_is_fp32, uint16_t *act,
+                      hipStream_t s) {
+    MOE_DEC_DISPATCH(true);
+}
+#endif
+#undef MOE_DEC_DISPATCH
+#undef MOE_DEC_FMT
 
 }  // namespace moe

@@ -532,6 +532,27 @@ def test_ffn_shared_in_routed_launch(lib, orc, fmt, T, kind, y_fp32):
     assert_close(L2.y_sh[:T].float().cpu().numpy(), ysh_ref, "shared rows, separate call")
 
 
+@pytest.mark.parametrize("T,k,shared", [(200, 1, False), (200, 1, True), (45, 2, True)])
+def test_decode_multipass_one_hot_expert(lib, orc, T, k, shared):
+    """Weight-streaming kernels with every token's first choice on one expert
+    (up to 13 token passes per tile): the tile ranges cut at equal cost shares
+    and the alternating pass order must still cover every row exactly once."""
+    _announce(f"decode multi-pass: T={T} k={k} one hot expert, shared={shared}")
+    H, I, E = 256, 128, 16
+    cfg = synth.LayerConfig("one_hot", H, E, k, I, "mxfp4", int(shared), "uniform", (T,),
+                            "gauss_mxfp4", seed=33)
+    w = Workload(cfg)
+    x = synth.activations(cfg, T, step=7)
+    lg = np.random.default_rng(T).random((T, E), dtype=np.float32)
+    lg[:, 5] += 10.0
+    lib.moe_set_option(lib.MOE_OPT_FFN_PATH, 1)
+    try:
+        L, out = run_layer(w, T, x, logits=lg)
+    finally:
+        lib.moe_set_option(lib.MOE_OPT_FFN_PATH, 0)
+    _check_layer_full(orc, w, T, x, L, out, logits=lg)
+
+
 def test_ffn_shared_tiled_path_unsupported(lib, orc):
     """Where the tiled kernels would run, moe_expert_ffn_shared declines before
     any device work and the layer runs the shared expert as its own call."""
