@@ -193,8 +193,10 @@ int moe_expert_ffn(const uint16_t *x_bf16, const int32_t *sorted_pair, const int
 
 /*
  * moe_expert_ffn_shared -- moe_expert_ffn for the routed experts together with
- * the always-on shared expert, in the same launches: the shared expert is one
- * more expert whose rows are all T tokens.
+ * the always-on shared expert, in the same launches: the shared expert enters
+ * as more experts of the launch, its T tokens in blocks of 16 when no routed
+ * expert has more than 16 rows (every block reads the shared weights; blocks
+ * run close together, so the repeats mostly hit the caches), else as one.
  *   y[p] for p < T*k as moe_expert_ffn; y[T*k + t] = W2_s (silu(W1_s x_t) *
  *   (W3_s x_t)) with the shared expert's weights `shared` (device pointer to
  *   one moe_expert_w, same format and sizes as the routed experts).

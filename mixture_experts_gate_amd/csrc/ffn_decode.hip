@@ -192,13 +192,19 @@ __device__ __forceinline__ const uint8_t *srow(const uint8_t *base, long r, int 
     return base ? base + r * (K / 32) : nullptr;
 }
 
-// The shared expert of a launch that carries one: expert index E, its rows
-// the T tokens after the routed rows, its outputs y rows T*k + t. A second
-// kernel argument, so that launches without it keep the argument layout (and
-// scalar registers) they had.
+// The shared expert of a launch that carries one, as active experts with
+// index E after the routed ones. When no routed expert has more than 16 rows,
+// its T token rows are cut into blocks of one token pass (16 rows), each one
+// more active expert: so the launch keeps its contiguous tile order (one
+// expert over T > 16 rows would switch it to the strided order), and the
+// blocks read the same weights close together in time (mostly from cache).
+// When some routed expert needs several passes anyway, it stays one expert
+// over all T rows. Token t's activation and output row is base + t, base =
+// T*k. A second kernel argument, so that launches without it keep the
+// argument layout (and scalar registers) they had.
 struct ShArgs {
     const moe_expert_w *shared;
-    int T;
+    int T, base;
 };
 
 // Experts that received at least one pair, as a bitmask (E <= 512), computed
@@ -209,10 +215,9 @@ struct ActiveSet {
     uint64_t w[8];
     int count;               // active experts, the shared one included
     int routed;              // active routed experts
-    int e_shared;            // expert index standing for the shared expert (E)
-    const moe_expert_w *sh_w;  // shared expert's weights and rows (SH launches only)
+    const moe_expert_w *sh_w;  // shared expert's weights and tokens (SH launches)
     int sh_T;
-    bool multi_pass;         // some expert has more rows than one token pass
+    bool multi_pass;         // some routed expert has more rows than one token pass
     template <bool SH>
     __device__ __forceinline__ void init(const int32_t *__restrict__ offsets, int E,
                                          const ShArgs &S) {
@@ -231,20 +236,21 @@ struct ActiveSet {
             count += __popcll(w[i]);
         }
         routed = count;
-        e_shared = E;
+        multi_pass = many != 0;
+        // the shared expert: blocks of 16 tokens, or one block over all T when
+        // the launch has several passes anyway (shared_block)
         if constexpr (SH) {
-            count += 1;
+            count += multi_pass ? 1 : (S.T + kPass - 1) / kPass;
             sh_w = S.shared;
             sh_T = S.T;
-            if (S.T > kPass) many = 1;
         }
-        multi_pass = many != 0;
     }
     // index of the a-th (0-based) active expert; a < count
+    // (a shared-expert block: E)
     template <bool SH>
-    __device__ __forceinline__ int nth(int a) const {
+    __device__ __forceinline__ int nth(int a, int E) const {
         if constexpr (SH) {
-            if (a >= routed) return e_shared;
+            if (a >= routed) return E;
         }
         int base = 0;
 #pragma unroll
@@ -289,16 +295,20 @@ struct ExpertState : TensorScale<tensor_scaled(FMT)> {
     buf_rsrc wr, sr;                // the same as ranged buffer resources (block formats)
 };
 
-// SH: the launch carries the shared expert (compiled out otherwise).
+// SH: the launch carries the shared expert (compiled out otherwise). Only its
+// weights and token count stay in registers (the gate/up kernels run at the
+// scalar-register limit); block size and row base are derived where used.
 template <int STAGE, int FMT, bool SH>
-__device__ __forceinline__ void expert_state(const DecArgs &A, const ActiveSet &act, int a,
-                                             ExpertState<FMT> &st) {
+__device__ __forceinline__ void expert_state(const DecArgs &A, const ShArgs &S,
+                                             const ActiveSet &act, int a, ExpertState<FMT> &st) {
     st.a = a;
-    st.e = act.template nth<SH>(a);
+    st.e = act.template nth<SH>(a, A.E);
     const MOE_CONST int32_t *off = as_scalar(A.offsets);
-    const bool sh = SH && st.e == A.E;        // the shared expert
-    st.row0 = off[st.e];                      // shared: its rows follow the routed ones
-    st.n_e = sh ? act.sh_T : off[st.e + 1] - st.row0;
+    const bool sh = SH && st.e == A.E;        // a block of the shared expert's tokens
+    const int bs = act.multi_pass ? act.sh_T : kPass;   // (its rows per block)
+    const int j = a - act.routed;             // (which block)
+    st.row0 = sh ? act.sh_T * A.k + j * bs : off[st.e];
+    st.n_e = sh ? min(bs, act.sh_T - j * bs) : off[st.e + 1] - st.row0;
     const MOE_CONST moe_expert_w *W = sh ? as_scalar(act.sh_w) : as_scalar(A.experts) + st.e;
     st.w = reinterpret_cast<const uint8_t *>(STAGE == 1 ? W->w13 : W->w2);
     st.s = reinterpret_cast<const uint8_t *>(STAGE == 1 ? W->s13 : W->s2);
@@ -357,27 +367,29 @@ __device__ __forceinline__ void load_tile(const DecArgs &A, const ExpertState<FM
 // Token operand of pass p (rows p*16 .. p*16+15 of the expert), K slabs of
 // this wavefront; for stage 2 also the pair index each row's output goes to.
 template <int STAGE, int SPW, bool SH, class ES>
-__device__ __forceinline__ void load_tokens(const DecArgs &A, const ES &st, int p, int wv,
-                                            int m, int c, u32x4 (&xr)[SPW][4], int &pidx) {
+__device__ __forceinline__ void load_tokens(const DecArgs &A, const ShArgs &S, const ES &st,
+                                            int p, int wv, int m, int c, u32x4 (&xr)[SPW][4],
+                                            int &pidx) {
     const int nblk = A.K / 32;
     const int r = p * kPass + m;
     const bool has = r < st.n_e;
     const uint16_t *row;
-    const bool sh = SH && st.e == A.E;   // shared expert: row r is token r, output row T*k + r
+    // shared-expert block: row r is token row0 - base + r; its output row is row0 + r
+    const bool sh = SH && st.e == A.E;
     if (STAGE == 1) {
         // the pass's 16 pair indices by scalar loads; lane m takes the m-th.
-        // (The shared expert reads the first entries instead, in bounds since
-        // T <= T*k, and takes token r: a select, no branch around the loads.)
+        // (A shared-expert block reads the first entries instead, in bounds
+        // since p * 16 + i < n_e <= T <= T*k, and takes its token: a select,
+        // no branch around the loads.)
         const MOE_CONST int32_t *sp = as_scalar(A.sorted_pair) + (sh ? 0 : st.row0 + p * kPass);
         int pair = 0;
 #pragma unroll
         for (int i = 0; i < kPass; ++i)
             if (p * kPass + i < st.n_e) pair = m == i ? sp[i] : pair;
-        row = A.src + (size_t)(sh ? r : pair / A.k) * A.K;
+        row = A.src + (size_t)(sh ? st.row0 - S.T * A.k + r : pair / A.k) * A.K;
     } else {
         row = A.src + (size_t)(st.row0 + (has ? r : 0)) * A.K;
-        // (the shared expert's n_e is T, so its outputs start at row n_e * k = T*k)
-        pidx = !has ? 0 : sh ? st.n_e * A.k + r : A.sorted_pair[st.row0 + r];
+        pidx = !has ? 0 : sh ? st.row0 + r : A.sorted_pair[st.row0 + r];
     }
 #pragma unroll
     for (int s = 0; s < SPW; ++s) {
@@ -392,7 +404,7 @@ __device__ __forceinline__ void load_tokens(const DecArgs &A, const ES &st, int 
 // One tile: token operand if the expert changed, prefetch of the next tile's
 // weights into `wn`, multiply from `wc`, K-split reduction, epilogue.
 template <int FMT, int STAGE, int SPW, int KS, int NB, bool YF32, bool FULL, int D, bool SH>
-__device__ __forceinline__ void dec_step(const DecArgs &A, const ActiveSet &act,
+__device__ __forceinline__ void dec_step(const DecArgs &A, const ShArgs &S, const ActiveSet &act,
                                          float (&red)[2][KS > 1 ? KS - 1 : 1][NB][4][kWave],
                                          WFrag<FMT> (&wc)[SPW][NB], WFrag<FMT> (&wn)[SPW][NB],
                                          u32x4 (&xr)[SPW][4], const ExpertState<FMT> &cur,
@@ -403,7 +415,7 @@ __device__ __forceinline__ void dec_step(const DecArgs &A, const ActiveSet &act,
         // token operand for the first pass of this tile (loaded before the next
         // prefetch, so that waiting for it does not wait for the prefetched weights)
         if (x_key != cur.a * 4096) {
-            load_tokens<STAGE, SPW, SH>(A, cur, 0, wv, m, c, xr, pidx);
+            load_tokens<STAGE, SPW, SH>(A, S, cur, 0, wv, m, c, xr, pidx);
             x_key = cur.a * 4096;
             x_raw = true;
         }
@@ -411,12 +423,12 @@ __device__ __forceinline__ void dec_step(const DecArgs &A, const ActiveSet &act,
         // `prev` holds the state of the tile before it. Issued, switched off,
         // also past the end (see buf_rsrc).
         const int an = pf ? pn.a : prev.a;
-        if (an != prev.a) expert_state<STAGE, FMT, SH>(A, act, an, nxt);
+        if (an != prev.a) expert_state<STAGE, FMT, SH>(A, S, act, an, nxt);
         else nxt = prev;
         load_tile<FMT, STAGE, SPW, NB, FULL>(A, nxt, pf ? pn.rt : 0, wv, lane, wn, pf);
         for (int p = 0; p * kPass < cur.n_e; ++p) {
             if (p > 0) {   // more than 16 tokens: next 16 of this expert
-                load_tokens<STAGE, SPW, SH>(A, cur, p, wv, m, c, xr, pidx);
+                load_tokens<STAGE, SPW, SH>(A, S, cur, p, wv, m, c, xr, pidx);
                 x_key = cur.a * 4096 + p;
                 x_raw = true;
             }
@@ -561,18 +573,18 @@ __device__ __forceinline__ void ffn_dec_body(const DecArgs &A, const ShArgs &S,
     TilePos pos[D];
     WFrag<FMT> wr[D][SPW][NB];
     pos[0] = TilePos{t0 / A.nrt, t0 % A.nrt};
-    expert_state<STAGE, FMT, SH>(A, act, pos[0].a, es[0]);
+    expert_state<STAGE, FMT, SH>(A, S, act, pos[0].a, es[0]);
 #pragma unroll
     for (int d = 1; d < D - 1; ++d) {
         pos[d] = d < n ? advance(pos[d - 1], sa, srt, A.nrt) : pos[d - 1];
         if (pos[d].a == es[d - 1].a) es[d] = es[d - 1];
-        else expert_state<STAGE, FMT, SH>(A, act, pos[d].a, es[d]);
+        else expert_state<STAGE, FMT, SH>(A, S, act, pos[d].a, es[d]);
     }
     // the first tile's token operand is requested before any weights, so that
     // resolving its row indices does not wait behind the weight prefetch
     u32x4 xr[SPW][4];
     int pidx = 0;
-    load_tokens<STAGE, SPW, SH>(A, es[0], 0, wv, m, c, xr, pidx);
+    load_tokens<STAGE, SPW, SH>(A, S, es[0], 0, wv, m, c, xr, pidx);
     int x_key = es[0].a * 4096;
     bool x_raw = true;      // tokens just loaded (not yet in the product type)
     int buf = 0;
@@ -588,7 +600,7 @@ __device__ __forceinline__ void ffn_dec_body(const DecArgs &A, const ShArgs &S,
                 const bool pf = i + d + D - 1 < n;
                 pos[fd] = pf ? advance(pos[pd], sa, srt, A.nrt) : pos[pd];
                 dec_step<FMT, STAGE, SPW, KS, NB, YF32, FULL, D, SH>(
-                    A, act, red, wr[d], wr[fd], xr, es[d], es[pd], es[fd], pidx, x_key, x_raw, buf,
+                    A, S, act, red, wr[d], wr[fd], xr, es[d], es[pd], es[fd], pidx, x_key, x_raw, buf,
                     pos[d].rt, pos[fd], pf, lane, wv, m, c);
             }
         }
@@ -702,8 +714,9 @@ static int ffn_decode_fmt(const uint16_t *x, const int32_t *sorted_pair, const i
                           int H, int I, int E, void *y, int y_is_fp32, uint16_t *act,
                           hipStream_t s) {
     const long n_pairs = (long)T * k;
-    const long slots = (n_pairs < E ? n_pairs : E) + (SH ? 1 : 0);
-    const ShArgs S{shared, T};
+    // a shared expert adds one active expert per 16 tokens
+    const long slots = (n_pairs < E ? n_pairs : E) + (SH ? (T + kPass - 1) / kPass : 0);
+    const ShArgs S{shared, T, T * k};
     DecArgs a1{x, sorted_pair, offsets, experts, act, k, H, H, I, E, 0};
     int rc = launch_stage<FMT, 1, false, SH>((H + 127) / 128, s, a1, S, slots);
     if (rc) return rc;
