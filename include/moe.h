@@ -150,8 +150,9 @@ int moe_permute(const int32_t *topk_ids, int T, int k, int E, int32_t *offsets,
  * moe_route_permute -- moe_route followed by moe_permute, with the same
  * arguments and results as the two calls. For T <= 16 with the gate computed
  * here, or T <= 8 with logits_in given (and E <= 512), both run in one
- * single-workgroup kernel that keeps the chosen ids on chip; larger batches
- * make the two calls. ws / ws_bytes as for moe_permute.
+ * single-workgroup kernel that keeps the chosen ids on chip (up to 64 pairs
+ * one wavefront ranks them in registers); larger batches make the two calls.
+ * ws / ws_bytes as for moe_permute.
  */
 int moe_route_permute(const uint16_t *x_bf16, const uint16_t *wg_bf16, const float *logits_in,
                       float *logits_out, int T, int H, int E, int k, int renormalize,

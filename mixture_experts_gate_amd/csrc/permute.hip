@@ -163,6 +163,68 @@ __global__ __launch_bounds__(kChunk) void route_permute_kernel(
     permute_block(ids_lds, T * k, E, offsets, sorted_pair, pair_row, plds);
 }
 
+// Router + permutation for tiny batches (at most 64 pairs, one wavefront per
+// token): wavefront t routes token t; wavefront 0 then ranks the pairs in its
+// lanes (lane p holds pair p): the multisplit rank within each expert, a
+// histogram in LDS (one writer per expert), and the offsets by a wavefront
+// scan with nine experts per lane (E <= 512, offsets[0..E]). Wavefront-local
+// LDS writes and reads need no barrier: one wavefront's LDS operations run in
+// order.
+constexpr int kTinyPer = 9;             // experts per lane in the tiny kernel's scan
+static_assert(kTinyPer * 64 >= kMaxE + 1, "tiny kernel scan must cover offsets[0..E]");
+template <int VPL>
+__global__ __launch_bounds__(kChunk) void route_permute_tiny_kernel(
+    const uint16_t *__restrict__ x, const uint16_t *__restrict__ wg,
+    const float *__restrict__ logits_in, float *__restrict__ logits_out, int T, int H, int E,
+    int k, int renormalize, int32_t *__restrict__ topk_ids, float *__restrict__ topk_w,
+    int32_t *__restrict__ offsets, int32_t *__restrict__ sorted_pair,
+    int32_t *__restrict__ pair_row) {
+    __shared__ int ids_lds[kWave];
+    __shared__ int cnt[kTinyPer * kWave];   // histogram, then exclusive offsets
+    const int w = threadIdx.x / kWave, lane = lane_id();
+    const int n = T * k;
+    if (w < T) {
+        const int id = route_token<VPL>(w, x, wg, logits_in, logits_out, H, E, k, renormalize,
+                                        topk_ids, topk_w);
+        if (lane < k) ids_lds[w * k + lane] = id;
+    }
+    for (int e = threadIdx.x; e < kTinyPer * kWave; e += blockDim.x) cnt[e] = 0;
+    __syncthreads();
+    if (w != 0) return;
+    const int e = lane < n ? ids_lds[lane] : -1;
+    const bool valid = e >= 0 && e < E;
+    int same;
+    const int r = wave_rank(valid, e, id_bits(E), &same);
+    if (valid && r == 0) cnt[e] = same;
+    __builtin_amdgcn_wave_barrier();
+    int c[kTinyPer], tot = 0;
+#pragma unroll
+    for (int i = 0; i < kTinyPer; ++i) {
+        c[i] = cnt[kTinyPer * lane + i];
+        tot += c[i];
+    }
+    int incl = tot;
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+        const int o = __shfl_up(incl, d);
+        if (lane >= d) incl += o;
+    }
+    int base = incl - tot;
+#pragma unroll
+    for (int i = 0; i < kTinyPer; ++i) {
+        const int ex = kTinyPer * lane + i;
+        cnt[ex] = base;
+        if (ex <= E) offsets[ex] = base;
+        base += c[i];
+    }
+    __builtin_amdgcn_wave_barrier();
+    if (valid) {
+        const int pos = cnt[e] + r;
+        sorted_pair[pos] = lane;
+        pair_row[lane] = pos;
+    }
+}
+
 // Large path, pass 1: per-chunk ranks and histograms.
 __global__ __launch_bounds__(kChunk) void permute_rank_kernel(
     const int32_t *__restrict__ ids, int n, int E, int32_t *__restrict__ hist /*[nb][E]*/,
@@ -302,6 +364,20 @@ extern "C" int moe_route_permute(const uint16_t *x_bf16, const uint16_t *wg_bf16
     }
     if (!topk_ids || !topk_w || !sorted_pair || !pair_row) return MOE_EINVAL;
     hipStream_t s = (hipStream_t)stream;
+    if (n <= kWave) {
+        // at most 64 pairs: one wavefront per token, the ranking in registers
+        // (kTinyPer * 64 >= E + 1 offsets)
+#define MOE_RPT(VPL)                                                                           \
+    MOE_LAUNCH(K_ROUTE_PERMUTE, route_permute_tiny_kernel<VPL>, dim3(1), dim3(kWave * T), 0, s, \
+               x_bf16, wg_bf16, logits_in, logits_out, T, H, E, k, renormalize, topk_ids,       \
+               topk_w, offsets, sorted_pair, pair_row)
+        if (E <= 64) MOE_RPT(1);
+        else if (E <= 128) MOE_RPT(2);
+        else if (E <= 256) MOE_RPT(4);
+        else MOE_RPT(8);
+#undef MOE_RPT
+        return check_launch();
+    }
     const size_t lds = ((size_t)n + permute_block_lds_ints(E)) * sizeof(int);
 #define MOE_RP(VPL)                                                                            \
     MOE_LAUNCH(K_ROUTE_PERMUTE, route_permute_kernel<VPL>, dim3(1), dim3(kChunk), lds, s, x_bf16, \

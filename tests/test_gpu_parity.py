@@ -198,7 +198,9 @@ PERM_CASES = [(1, 128, 8, "uniform"), (8, 128, 8, "uniform"), (64, 128, 8, "unif
               (4096, 256, 6, "uniform"), (8192, 128, 8, "uniform"), (6000, 64, 3, "skew"),
               (1, 1, 1, "uniform"), (3, 7, 7, "uniform"), (33, 128, 8, "uniform"),
               (48, 64, 4, "skew"), (64, 512, 6, "skew"), (100, 128, 8, "skew"),
-              (256, 128, 8, "uniform"), (250, 64, 4, "skew"), (257, 128, 8, "uniform")]
+              (256, 128, 8, "uniform"), (250, 64, 4, "skew"), (257, 128, 8, "uniform"),
+              (2, 512, 6, "uniform"), (5, 512, 8, "skew"), (8, 33, 8, "uniform"),
+              (4, 64, 16, "skew")]
 
 
 @pytest.mark.parametrize("T,E,k,kind", PERM_CASES)
