@@ -327,6 +327,26 @@ def test_layer_large_sparse_cfg4(lib, orc, T):
     _check_layer_sampled(orc, w, T, x, lg, L, out, n_sample=8)
 
 
+def test_layer_cfg4_uniform_shared_blocks(lib, orc):
+    """Config 4's shapes with uniform routing at T=40: no routed expert over 16
+    rows, so the shared expert enters the routed launches as three 16-token
+    blocks (the 8-wavefront gate/up and 64-row down kernels with the shared
+    path), sampled tokens against the oracle."""
+    _announce("layer: config 4 shapes, uniform routing, T=40 (shared expert in blocks)")
+    w = workload(4)
+    T = 40
+    x = synth.activations(w.cfg, T, step=9)
+    lg = np.random.default_rng(40).random((T, w.E), dtype=np.float32)
+    L, out = run_layer(w, T, x, logits=lg)
+    ids, _, _ = orc.topk(lg, w.cfg.k)
+    assert np.bincount(ids.ravel(), minlength=w.E).max() <= 16
+    _check_layer_sampled(orc, w, T, x, lg, L, out, n_sample=8)
+    toks = np.array([0, 17, 39], dtype=np.int32)
+    ysh_ref = orc.ffn_rows(x, w.shared[None], w.lay, toks, np.zeros(len(toks), np.int32))
+    ysh = L.y[T * w.cfg.k + toks].float().cpu().numpy()
+    assert_close(ysh, ysh_ref, "shared expert rows (three blocks)")
+
+
 def test_layer_large_sparse_cfg4_T4096(lib, orc):
     _announce("layer: config 4, T=4096")
     w = workload(4)
