@@ -186,7 +186,8 @@ int moe_route_permute(const uint16_t *x_bf16, const uint16_t *wg_bf16, const flo
  * ws: device workspace of at least the ffn size from moe_workspace_size.
  * Requires E <= 512.
  * The shared (always-on) expert is this call with E = 1, k = 1,
- * sorted_pair = 0..T-1 and offsets = {0, T}.
+ * sorted_pair = 0..T-1 and offsets = {0, T}; moe_expert_ffn_shared runs it
+ * inside the routed launches instead where the weight-streaming kernels run.
  */
 int moe_expert_ffn(const uint16_t *x_bf16, const int32_t *sorted_pair, const int32_t *offsets,
                    const moe_expert_w *experts, int fmt, int T, int k, int H, int I, int E,
