@@ -59,6 +59,8 @@ def parse():
                     help="comma list of sweep parts to run: decode,formats,prefill,cfg4,stack")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run one plain 512 MiB device copy (HBM counter calibration)")
+    ap.add_argument("--cfg4-T", default="1,64,4096",
+                    help="comma list of the large sparse layer's batch sizes to run")
     return ap.parse_args()
 
 
@@ -582,7 +584,10 @@ def main():
         c4 = synth.CONFIGS[4]
         log("config 4: generating 256 experts + shared ...")
         w4 = None
+        c4_T = {int(v) for v in args.cfg4_T.split(",") if v}
         for T, steps in ((1, 100), (64, 100), (4096, 8)):
+            if T not in c4_T:
+                continue
             w, r = run_workload(torch, c4, T, steps, 3, dev, replicas=2,
                                 pool=None if w4 is None else w4.pool,
                                 dexp=None if w4 is None else w4.dexp,
