@@ -84,7 +84,7 @@ typedef enum {
     MOE_EINVAL = -1,        /* bad argument (size, null pointer, small workspace) */
     MOE_ENOMEM = -2,        /* not enough cache slots / host memory */
     MOE_EHIP = -3,          /* a HIP call failed; see moe_last_hip_error() */
-    MOE_EUNSUPPORTED = -4,  /* valid request this build does not handle */
+    MOE_EUNSUPPORTED = -4,  /* valid request the library does not handle */
     MOE_EBUSY = -5          /* resource in use */
 } moe_err;
 
