@@ -6,9 +6,10 @@
  * feed-forward block with block-scaled FP4 weights, and the k expert outputs
  * are mixed by the router's weights. The FreeToken pages describe this
  * sparsity as what makes edge serving of very large models possible
- * (winzheng.com page, "Why Now of All Times": six routed experts per token in
- * each of 43 decoder layers, an FP4 expert pool of about 140 GB that can live
- * in host memory and be loaded on demand) and list MXFP4, NVFP4, FP8 and BF16
+ * (winzheng.com page, "Why Now of All Times": per token, each of the 43
+ * decoder layers uses six routed experts, and since the FP4-quantised pool is
+ * far larger than device memory, most experts stay on the host and are copied
+ * in when routed to) and list MXFP4, NVFP4, FP8 and BF16
  * weights (aimodeling.com/en page, "Reported Numbers and Ecosystem Position").
  * The expert cache calls follow the pages' global LRU expert cache and
  * full-layer double-buffered prefill streaming (winzheng.com page,
@@ -90,8 +91,10 @@ typedef enum {
 
 typedef enum { MOE_W_BF16 = 0, MOE_W_MXFP4 = 1, MOE_W_NVFP4 = 2, MOE_W_FP8 = 3 } moe_wfmt;
 
-/* One expert's weights. w13/w2 point to codes (MXFP4) or bf16 values; s13/s2
- * to E8M0 scales (MXFP4 only). */
+/* One expert's weights. w13/w2 point to the codes (MXFP4, NVFP4, FP8) or the
+ * bf16 values; s13/s2 point to the scale section of each matrix: E8M0 block
+ * scales (MXFP4), E4M3 block scales followed by the fp32 matrix scale (NVFP4),
+ * or the fp32 matrix scale alone (FP8); ignored for bf16. */
 typedef struct {
     const void *w13;
     const uint8_t *s13;

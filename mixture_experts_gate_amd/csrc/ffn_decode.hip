@@ -413,10 +413,11 @@ __device__ __forceinline__ void dec_step(const DecArgs &A, const ShArgs &S, cons
                                          TilePos pn, bool pf, int lane, int wv, int m, int c) {
 
         // token operand for the first pass of this tile (loaded before the next
-        // prefetch, so that waiting for it does not wait for the prefetched weights)
-        if (x_key != cur.a * 4096) {
+        // prefetch, so that waiting for it does not wait for the prefetched weights).
+        // x_key: the active expert whose first pass the registers hold, or -1
+        if (x_key != cur.a) {
             load_tokens<STAGE, SPW, SH>(A, S, cur, 0, wv, m, c, xr, pidx);
-            x_key = cur.a * 4096;
+            x_key = cur.a;
             x_raw = true;
         }
         // prefetch the tile D - 1 steps ahead (position pn, present if pf);
@@ -429,7 +430,7 @@ __device__ __forceinline__ void dec_step(const DecArgs &A, const ShArgs &S, cons
         for (int p = 0; p * kPass < cur.n_e; ++p) {
             if (p > 0) {   // more than 16 tokens: next 16 of this expert
                 load_tokens<STAGE, SPW, SH>(A, S, cur, p, wv, m, c, xr, pidx);
-                x_key = cur.a * 4096 + p;
+                x_key = -1;     // a later pass: the next tile reloads its first
                 x_raw = true;
             }
             // fp16 products: bf16 tokens (stage 1) are converted once per load
@@ -585,7 +586,7 @@ __device__ __forceinline__ void ffn_dec_body(const DecArgs &A, const ShArgs &S,
     u32x4 xr[SPW][4];
     int pidx = 0;
     load_tokens<STAGE, SPW, SH>(A, S, es[0], 0, wv, m, c, xr, pidx);
-    int x_key = es[0].a * 4096;
+    int x_key = es[0].a;
     bool x_raw = true;      // tokens just loaded (not yet in the product type)
     int buf = 0;
 #pragma unroll

@@ -96,7 +96,7 @@ __device__ __forceinline__ void split_quad(const float (&v)[4], float inv, uint3
 
 // Row split of bf16 rows [rows][K] into hi [rows][K], lo [rows][K] and hi
 // scale bytes [rows][K/32]. One thread per 32-element block.
-// Token-tile map of the tiled kernels: map[0] = M, the number of 128-token
+// Token-tile map of the tiled kernels: map[0] = M, the number of 64-token
 // tiles over all experts; map[1 + m] = e | (mt << 16) for the m-th tile in
 // expert order (tile mt of expert e). One 256-thread workgroup.
 __device__ void build_tile_map(const int32_t *__restrict__ offsets, int E,

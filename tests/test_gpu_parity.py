@@ -319,12 +319,18 @@ def test_layer_prefill_cfg3(lib, orc):
 
 @pytest.mark.parametrize("T", [1, 64])
 def test_layer_large_sparse_cfg4(lib, orc, T):
-    _announce(f"layer: config 4 (shared expert, Zipf), T={T}")
+    """Config 4 (Zipf routing, shared expert) at decode sizes, every token
+    against the oracle: at T=64 the hottest experts take several 16-row token
+    passes, and checking all tokens covers every row of every pass."""
+    _announce(f"layer: config 4 (shared expert, Zipf), T={T}, all tokens")
     w = workload(4)
     x = synth.activations(w.cfg, T)
     lg = synth.router_logits(w.cfg, T)
     L, out = run_layer(w, T, x, logits=lg)
-    _check_layer_sampled(orc, w, T, x, lg, L, out, n_sample=8)
+    ids, _, _ = orc.topk(lg, w.cfg.k)
+    if T == 64:
+        assert np.bincount(ids.ravel(), minlength=w.E).max() > 16   # multi-pass experts
+    _check_layer_sampled(orc, w, T, x, lg, L, out, n_sample=T)
 
 
 def test_layer_cfg4_uniform_shared_blocks(lib, orc):
@@ -347,14 +353,54 @@ def test_layer_cfg4_uniform_shared_blocks(lib, orc):
     assert_close(ysh, ysh_ref, "shared expert rows (three blocks)")
 
 
+def _tile_rows(off, hot, n_rest, tile, rng):
+    """Sorted rows to check on the tiled path: the first and last row of every
+    `tile`-row tile of the `hot` experts with most rows, and the first and last
+    row of `n_rest` other non-empty experts (their last, partial tiles)."""
+    cnt = np.diff(off)
+    order = np.argsort(-cnt, kind="stable")
+    rows = set()
+    for e in order[:hot]:
+        for t0 in range(off[e], off[e + 1], tile):
+            rows.update((t0, min(t0 + tile, off[e + 1]) - 1))
+    rest = [e for e in order[hot:] if cnt[e] > 0]
+    pick = rng.choice(len(rest), size=min(n_rest, len(rest)), replace=False)
+    for i in pick:
+        e = rest[i]
+        rows.update((off[e], off[e + 1] - 1))
+    coldest = [e for e in order[::-1] if cnt[e] > 0][0]
+    rows.update((off[coldest], off[coldest + 1] - 1))
+    return np.array(sorted(rows), dtype=np.int64)
+
+
+def _check_rows(orc, w, x, L, rows, off, sp):
+    """Expert outputs y of the given sorted rows against the oracle, row by row."""
+    k = w.cfg.k
+    e_of = np.searchsorted(off, rows, side="right") - 1
+    pairs = sp[rows]
+    y_ref = orc.ffn_rows(x, w.pool, w.lay, (pairs // k).astype(np.int32),
+                         e_of.astype(np.int32))
+    yg = L.y[torch.from_numpy(pairs).to(DEV)].float().cpu().numpy()
+    assert_close(yg, y_ref, f"expert outputs y of {len(rows)} rows chosen by tile")
+
+
 def test_layer_large_sparse_cfg4_T4096(lib, orc):
-    _announce("layer: config 4, T=4096")
+    """Config 4 at T=4096 (tiled kernels, Zipf routing: the hottest expert holds
+    about 3000 rows, the coldest a handful): routing and permutation in full;
+    expert outputs of the first and last row of every 64-row tile of the three
+    hottest experts and of the first and last rows of 40 other experts (their
+    partial last tiles) and the coldest; the layer output on sampled tokens."""
+    _announce("layer: config 4, T=4096, rows chosen by tile")
     w = workload(4)
     T = 4096
     x = synth.activations(w.cfg, T)
     lg = synth.router_logits(w.cfg, T)
     L, out = run_layer(w, T, x, logits=lg)
     _check_layer_sampled(orc, w, T, x, lg, L, out, n_sample=8)
+    ids, _, _ = orc.topk(lg, w.cfg.k)
+    off, sp, _ = orc.permute(ids, w.E)
+    rows = _tile_rows(off, 3, 40, 64, np.random.default_rng(4096))
+    _check_rows(orc, w, x, L, rows, off, sp)
 
 
 @pytest.mark.parametrize("path", [1, 2])
@@ -413,15 +459,26 @@ def test_shared_expert_call_is_plain_swiglu(lib, orc):
     assert_close(M.y_sh[:T].float().cpu().numpy(), ref, "shared expert y")
 
 
-def test_layer_deterministic(lib):
-    _announce("determinism: config 2 T=64 twice")
-    w = workload(2)
-    x = synth.activations(w.cfg, 64, step=3)
-    lg = synth.router_logits(w.cfg, 64, step=3)
-    L1, o1 = run_layer(w, 64, x, logits=lg)
-    a = (o1.clone(), L1.y.clone(), L1.sorted_pair.clone())
-    L2, o2 = run_layer(w, 64, x, logits=lg)
-    assert torch.equal(a[0], o2) and torch.equal(a[1], L2.y) and torch.equal(a[2], L2.sorted_pair)
+@pytest.mark.parametrize("c,T", [(1, 16), (2, 1), (2, 64), (3, 8192), (4, 64), (4, 4096)])
+def test_layer_deterministic(lib, c, T):
+    """The same layer call twice gives bit-identical routing, permutation,
+    expert outputs and layer output (no order-deciding atomics anywhere):
+    the weight-streaming kernels, the tiled kernels (configs 3 and 4 at large
+    T) and the shared expert in both forms."""
+    _announce(f"determinism: config {c} T={T} twice")
+    w = workload(c)
+    x = synth.activations(w.cfg, T, step=3)
+    if c == 1:
+        kw = dict(wg=synth.gate_weights(w.cfg))
+    else:
+        kw = dict(logits=synth.router_logits(w.cfg, T, step=3))
+    L1, o1 = run_layer(w, T, x, **kw)
+    a = (o1.clone(), L1.y.clone(), L1.sorted_pair.clone(), L1.pair_row.clone(),
+         L1.offsets.clone(), L1.topk_w.clone())
+    L2, o2 = run_layer(w, T, x, **kw)
+    b = (o2, L2.y, L2.sorted_pair, L2.pair_row, L2.offsets, L2.topk_w)
+    for u, v in zip(a, b):
+        assert torch.equal(u, v)
 
 
 @pytest.mark.parametrize("fuse_shared", [True, False])
@@ -496,6 +553,12 @@ def test_pack_mxfp4_layout(lib):
 
 _FMT_CASES = [
     # (fmt, H, I, E, k, T, logits kind)
+    # the decode layer's shapes (16- and 6-slab contractions, 64-row down tiles
+    # at T=64, 32-row tiles and 8-wavefront gate/up at T=1)
+    ("nvfp4", 2048, 768, 128, 8, 64, "uniform"),
+    ("nvfp4", 2048, 768, 128, 8, 1, "uniform"),
+    ("fp8", 2048, 768, 128, 8, 64, "uniform"),
+    ("fp8", 2048, 768, 128, 8, 1, "uniform"),
     ("nvfp4", 1024, 512, 16, 4, 1, "uniform"),
     ("nvfp4", 1024, 512, 16, 4, 64, "uniform"),
     ("nvfp4", 768, 384, 16, 4, 200, "skew"),
@@ -557,8 +620,9 @@ def test_ffn_shared_in_routed_launch(lib, orc, fmt, T, kind, y_fp32):
 @pytest.mark.parametrize("T,k,shared", [(200, 1, False), (200, 1, True), (45, 2, True)])
 def test_decode_multipass_one_hot_expert(lib, orc, T, k, shared):
     """Weight-streaming kernels with every token's first choice on one expert
-    (up to 13 token passes per tile): the tile ranges cut at equal cost shares
-    and the alternating pass order must still cover every row exactly once."""
+    (up to 13 token passes per tile): the strided tile order taken when an
+    expert needs several passes must still cover every row exactly once, and
+    the token operand must be reloaded for the next tile after a later pass."""
     _announce(f"decode multi-pass: T={T} k={k} one hot expert, shared={shared}")
     H, I, E = 256, 128, 16
     cfg = synth.LayerConfig("one_hot", H, E, k, I, "mxfp4", int(shared), "uniform", (T,),
@@ -642,6 +706,7 @@ def test_pack_nvfp4_fp8_layout(lib, fmt):
 @pytest.mark.parametrize("H,I,E,k,T,kind,path", [
     (768, 384, 16, 4, 400, "skew", 2),       # forced onto the tiled kernels; 3 down tiles
     (1024, 512, 16, 4, 2048, "uniform", 0),  # chosen by size
+    (2048, 768, 128, 8, 8192, "prefill", 0), # the prefill workload's shapes: 16/6 slabs
 ])
 def test_fp8_weights_tiled_path(lib, orc, H, I, E, k, T, kind, path):
     """FP8 experts on the tiled (matrix-core) kernels: E4M3 weights with unit
@@ -652,10 +717,20 @@ def test_fp8_weights_tiled_path(lib, orc, H, I, E, k, T, kind, path):
                             seed=29)
     w = Workload(cfg)
     x = synth.activations(cfg, T, step=3)
-    lg = synth.router_logits(cfg, T, step=3) if kind == "uniform" else _perm_case(T, E, k, kind)
+    if kind == "uniform":
+        lg = synth.router_logits(cfg, T, step=3)
+    elif kind == "prefill":     # the prefill workload's routing (biased Gumbel, dead experts)
+        lg = synth.router_logits(synth.CONFIGS[3], T)
+    else:
+        lg = _perm_case(T, E, k, kind)
     lib.moe_set_option(lib.MOE_OPT_FFN_PATH, path)
     try:
         L, out = run_layer(w, T, x, logits=lg)
     finally:
         lib.moe_set_option(lib.MOE_OPT_FFN_PATH, 0)
     _check_layer_sampled(orc, w, T, x, lg, L, out, n_sample=12)
+    if kind == "prefill":
+        ids, _, _ = orc.topk(lg, k)
+        off, sp, _ = orc.permute(ids, E)
+        rows = _tile_rows(off, 2, 24, 64, np.random.default_rng(T))
+        _check_rows(orc, w, x, L, rows, off, sp)
