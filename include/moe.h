@@ -222,6 +222,27 @@ int moe_expert_ffn_shared(const uint16_t *x_bf16, const int32_t *sorted_pair,
                           void *y, int y_is_fp32, void *ws, size_t ws_bytes, void *stream);
 
 /*
+ * moe_expert_ffn_noalloc -- moe_expert_ffn without a caller workspace, for
+ * callers that cannot allocate device memory (code under stream/graph
+ * capture, tight serving loops, harnesses that forbid allocation).
+ * Arguments, results, numerics and errors as moe_expert_ffn, minus ws and
+ * ws_bytes: the workspace is a device array of MOE_FFN_NOALLOC_MAX_WS bytes
+ * inside this library, one per device, reserved when the library's kernels
+ * are loaded on that device and held until the process ends. The call itself
+ * allocates nothing. Requests whose workspace (the ffn size from
+ * moe_workspace_size) exceeds MOE_FFN_NOALLOC_MAX_WS return MOE_ENOMEM before
+ * any device work. The array is used on the calling thread's current device
+ * (stream must belong to it). All calls on one device share the array: calls
+ * whose work may overlap on the device (different streams without ordering
+ * between them) race and give undefined results; calls ordered on one stream
+ * are safe. Nothing in the array needs to start at a particular value.
+ */
+#define MOE_FFN_NOALLOC_MAX_WS ((size_t)64 << 20)
+int moe_expert_ffn_noalloc(const uint16_t *x_bf16, const int32_t *sorted_pair,
+                           const int32_t *offsets, const moe_expert_w *experts, int fmt, int T,
+                           int k, int H, int I, int E, void *y, int y_is_fp32, void *stream);
+
+/*
  * moe_combine -- weighted sum of each token's k expert outputs.
  *   out[t][n] = bf16_rne( sum_{j<k} topk_w[t][j] * y[t*k+j][n] + y_shared[t][n] )
  * summed in fp32 with j ascending; y_shared [T][H] (same dtype as y) is

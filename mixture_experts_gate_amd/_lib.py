@@ -21,7 +21,7 @@ MOE_OPT_TIMING = 2
 # every symbol include/moe.h declares
 EXPORTS = [
     "moe_strerror", "moe_last_hip_error", "moe_route", "moe_permute", "moe_expert_ffn",
-    "moe_expert_ffn_shared",
+    "moe_expert_ffn_shared", "moe_expert_ffn_noalloc",
     "moe_combine", "moe_workspace_size", "moe_set_option", "moe_get_option", "moe_kernel_name",
     "moe_timing_query", "moe_pack_mxfp4", "moe_pack_weights", "moe_route_permute",
     "expert_cache_reserve", "expert_cache_prefetch", "expert_cache_evict", "expert_cache_stats",
@@ -63,6 +63,7 @@ def load(path: str | None = None):
         "moe_route_permute": (I, [P, P, P, P, I, I, I, I, I, P, P, P, P, P, P, Z, P]),
         "moe_expert_ffn": (I, [P, P, P, P, I, I, I, I, I, I, P, I, P, Z, P]),
         "moe_expert_ffn_shared": (I, [P, P, P, P, P, I, I, I, I, I, I, P, I, P, Z, P]),
+        "moe_expert_ffn_noalloc": (I, [P, P, P, P, I, I, I, I, I, I, P, I, P]),
         "moe_combine": (I, [P, I, P, P, I, I, I, P, P]),
         "moe_workspace_size": (I, [I, I, I, I, I, C.POINTER(Z), C.POINTER(Z)]),
         "moe_set_option": (I, [I, I]),
@@ -156,6 +157,17 @@ def moe_expert_ffn_shared(x_bf16, sorted_pair, offsets, experts, shared, fmt, T,
     if not check and rc == MOE_EUNSUPPORTED:
         return rc
     return _check("moe_expert_ffn_shared", rc)
+
+
+FFN_NOALLOC_MAX_WS = 64 << 20
+
+
+def moe_expert_ffn_noalloc(x_bf16, sorted_pair, offsets, experts, fmt, T, k, H, I, E, y,
+                           y_is_fp32, stream=None):
+    """moe_expert_ffn with the library's own per-device workspace array."""
+    return _check("moe_expert_ffn_noalloc", load().moe_expert_ffn_noalloc(
+        _ptr(x_bf16), _ptr(sorted_pair), _ptr(offsets), _ptr(experts), fmt, T, k, H, I, E, _ptr(y),
+        int(bool(y_is_fp32)), _stream(stream)))
 
 
 def moe_combine(y, y_is_fp32, topk_w, y_shared, T, k, H, out_bf16, stream=None):

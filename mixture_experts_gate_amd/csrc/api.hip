@@ -178,10 +178,12 @@ extern "C" int moe_workspace_size(int T, int k, int H, int I, int E, size_t *per
     return MOE_OK;
 }
 
-extern "C" int moe_expert_ffn(const uint16_t *x_bf16, const int32_t *sorted_pair,
-                              const int32_t *offsets, const moe_expert_w *experts, int fmt, int T,
-                              int k, int H, int I, int E, void *y, int y_is_fp32, void *ws,
-                              size_t ws_bytes, void *stream) {
+namespace moe {
+// The expert FFN behind moe_expert_ffn (and its variant without a caller
+// workspace): argument checks, then the weight-streaming or tiled kernels.
+int expert_ffn_call(const uint16_t *x_bf16, const int32_t *sorted_pair, const int32_t *offsets,
+                    const moe_expert_w *experts, int fmt, int T, int k, int H, int I, int E,
+                    void *y, int y_is_fp32, void *ws, size_t ws_bytes, void *stream) {
     // E <= 512: the weight-streaming kernels keep the set of active experts
     // as a 512-bit mask
     if (T < 0 || k < 1 || E < 1 || E > 512 || H < 32 || I < 32 || H % 32 || I % 32)
@@ -201,6 +203,15 @@ extern "C" int moe_expert_ffn(const uint16_t *x_bf16, const int32_t *sorted_pair
                            ws, s);
     return ffn_decode(x_bf16, sorted_pair, offsets, experts, fmt, T, k, H, I, E, y, y_is_fp32,
                       act, s);
+}
+}  // namespace moe
+
+extern "C" int moe_expert_ffn(const uint16_t *x_bf16, const int32_t *sorted_pair,
+                              const int32_t *offsets, const moe_expert_w *experts, int fmt, int T,
+                              int k, int H, int I, int E, void *y, int y_is_fp32, void *ws,
+                              size_t ws_bytes, void *stream) {
+    return expert_ffn_call(x_bf16, sorted_pair, offsets, experts, fmt, T, k, H, I, E, y,
+                           y_is_fp32, ws, ws_bytes, stream);
 }
 
 extern "C" int moe_expert_ffn_shared(const uint16_t *x_bf16, const int32_t *sorted_pair,
