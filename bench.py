@@ -59,6 +59,8 @@ def parse():
                     help="comma list of sweep parts to run: decode,formats,prefill,cfg4,stack")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run one plain 512 MiB device copy (HBM counter calibration)")
+    ap.add_argument("--no-micro", action="store_true",
+                    help="skip the read-stream / matrix-core reference measurements")
     ap.add_argument("--cfg4-T", default="1,64,4096",
                     help="comma list of the large sparse layer's batch sizes to run")
     return ap.parse_args()
@@ -497,6 +499,66 @@ def cpu_baseline(wl, budget_s=12.0):
             "host_cpus": os.cpu_count()}
 
 
+def micro(torch, dev):
+    """References measured on this GPU with the library's measurement kernels:
+    the read-stream rate at the byte counts of the decode kernels (and larger),
+    with a persistent grid (two workgroups per compute unit) and with one
+    workgroup per 64 KB chunk, buffers rotated over more than 1 GB so that the
+    bytes come from HBM; and the issue rate of the bf16 and the block-scaled
+    FP8 x FP4 matrix instructions. Times are the dispatches' own start/end
+    events (library timing mode)."""
+    from mixture_experts_gate_amd import _lib
+    ncu = torch.cuda.get_device_properties(dev).multi_processor_count
+    sink = torch.zeros(64, dtype=torch.int32, device=dev)
+    kid = {n: i for i, n in enumerate(_lib.kernel_names())}
+    out = {"read_stream": [], "mfma": [], "compute_units": ncu}
+
+    def timed(fn, reps, name):
+        for i in range(3):
+            fn(i)
+        torch.cuda.synchronize()
+        _lib.moe_set_option(_lib.MOE_OPT_TIMING, 1)
+        for i in range(reps):
+            fn(i)
+        torch.cuda.synchronize()
+        n, ms = _lib.moe_timing_query(kid[name])
+        _lib.moe_set_option(_lib.MOE_OPT_TIMING, 0)
+        return 1000.0 * ms / n
+
+    for size in (105_000_000, 211_000_000, 316_000_000, 1_000_000_000, 4_000_000_000):
+        nbytes = size // 65536 * 65536
+        nbuf = max(2, -(-1_100_000_000 // nbytes))
+        bufs = [torch.empty(nbytes, dtype=torch.uint8, device=dev) for _ in range(nbuf)]
+        for b in bufs:
+            b.fill_(1)
+        for label, grid in (("persistent", 2 * ncu), ("one_per_chunk", nbytes // 65536)):
+            us = timed(lambda i: _lib.moe_micro_read(bufs[i % nbuf], nbytes, grid, sink),
+                       4 * nbuf, "micro_read")
+            out["read_stream"].append({"bytes": nbytes, "grid": grid, "launch": label, "avg_us": us,
+                                       "GBs": nbytes / (us * 1e-6) / 1e9})
+            log(f"read stream {nbytes/1e6:.0f} MB, {label} grid {grid}: {us:.1f} us, "
+                f"{nbytes/(us*1e-6)/1e9:.0f} GB/s")
+        del bufs
+    torch.cuda.empty_cache()
+    for kind, label in ((0, "bf16_32x32x16"), (1, "scaled_fp4xfp8_16x16x128")):
+        grid, iters = 4 * ncu, 2000
+        flops = _lib.moe_micro_mfma(kind, grid, iters, sink)
+        us = timed(lambda i: _lib.moe_micro_mfma(kind, grid, iters, sink), 5, "micro_mfma")
+        out["mfma"].append({"instruction": label, "grid": grid, "avg_us": us,
+                            "TFLOPs": flops / (us * 1e-6) / 1e12})
+        log(f"matrix cores {label}: {flops/(us*1e-6)/1e12:.0f} TFLOP/s")
+    return out
+
+
+def read_peak_for(micro_res, nbytes):
+    """Best measured read-stream rate at the size closest to nbytes."""
+    if not micro_res:
+        return None
+    rs = micro_res["read_stream"]
+    size = min({r["bytes"] for r in rs}, key=lambda b: abs(b - nbytes))
+    return max(r["GBs"] for r in rs if r["bytes"] == size)
+
+
 def calib_copy(torch, dev):
     n = 512 << 20
     a = torch.empty(n, dtype=torch.uint8, device=dev)
@@ -530,11 +592,19 @@ def main():
     only = set(args.only.split(",")) if args.only else None
     want = lambda name: only is None or name in only
 
+    micro_res = None
+    if not args.no_micro and not args.profile:
+        log("reference measurements: read stream, matrix cores")
+        micro_res = micro(torch, dev)
     c2 = synth.CONFIGS[2]
     sweep = {}
     log(f"headline: decode layer T={args.T}, {args.steps} steps, {args.warmup} warm-up")
     wl, head = run_workload(torch, c2, args.T, args.steps, args.warmup, dev)
     dom, roof = roofline(head, args.T)
+    if roof.get("achieved") and micro_res:
+        peak = read_peak_for(micro_res, roof["algorithmic_bytes_per_launch"])
+        roof["measured_read_stream_GBs"] = peak
+        roof["frac_of_measured_read_stream"] = roof["achieved"] / peak
     log(f"T={args.T}: {head['tokens_per_s']:.0f} tok/s, {head['ms_per_step']*1000:.1f} us/step, "
         f"layer HBM {head['layer_hbm_frac']*100:.1f}%")
     if not args.no_sweep and want("decode"):
@@ -637,6 +707,7 @@ def main():
                    "kernels": head["kernels"]},
         "roofline": roof,
         "cpu_baseline": cpu,
+        "micro": micro_res,
         "sweep": sweep,
     }
     print(json.dumps(line), flush=True)

@@ -286,8 +286,16 @@ int moe_workspace_size(int T, int k, int H, int I, int E, size_t *permute_bytes,
  *                     hipExtLaunchKernel with two events that take the
  *                     dispatch's own start and end times on the launch's
  *                     stream (do not use under graph capture); 0 = off.
- *                     Setting it clears the accumulated timings. */
-enum { MOE_OPT_FFN_PATH = 1, MOE_OPT_TIMING = 2 };
+ *                     Setting it clears the accumulated timings.
+ *   MOE_OPT_DEC_SPLIT: weights of the weight-streaming kernels' split of the
+ *                     tiles over their persistent workgroups: workgroup i
+ *                     takes a contiguous share proportional to
+ *                     1 - ws * (i / C) - wp * (i % C) / C, C = compute units
+ *                     (later-dispatched workgroups receive their first data
+ *                     later). Four bytes, each in units of 1/256 and below
+ *                     128: stage 1 ws, stage 1 wp, stage 2 ws, stage 2 wp
+ *                     (low byte first); -1 restores the default. */
+enum { MOE_OPT_FFN_PATH = 1, MOE_OPT_TIMING = 2, MOE_OPT_DEC_SPLIT = 3 };
 int moe_set_option(int option, int value);
 int moe_get_option(int option);
 
@@ -296,6 +304,23 @@ const char *moe_kernel_name(int kernel_id);
 /* Launches of kernel_id timed since MOE_OPT_TIMING was last set, and their
  * summed durations in milliseconds (waits for the recorded events). */
 int moe_timing_query(int kernel_id, long long *launches, double *total_ms);
+
+/* ---------------------------------------------------------------------------
+ * Measurement helpers (not part of the layer): the references the layer's
+ * kernels are compared with in a benchmark.
+ *
+ * moe_micro_read -- read `bytes` (a multiple of 16) of the device buffer buf
+ * (16-byte aligned) once, with `grid` workgroups of 256 threads taking 64 KB
+ * chunks in turn, 16-byte non-temporal loads. sink: device word written only
+ * in a case that does not occur (keeps the loads). Time it with events.
+ *
+ * moe_micro_mfma -- `grid` workgroups of four wavefronts each issue `iters` x 4
+ * independent matrix-core instructions: kind 0 = bf16 32x32x16, kind 1 =
+ * block-scaled 16x16x128 with an E2M1 A and an E4M3 B operand. *flops (host,
+ * optional) receives the FLOPs of the launch. sink as above.
+ */
+int moe_micro_read(const void *buf, size_t bytes, int grid, void *sink, void *stream);
+int moe_micro_mfma(int kind, int grid, int iters, void *sink, double *flops, void *stream);
 
 /* ---------------------------------------------------------------------------
  * Expert cache: a pool of device slots holding expert blobs copied from pinned

@@ -17,6 +17,7 @@ MOE_OK, MOE_EINVAL, MOE_ENOMEM, MOE_EHIP, MOE_EUNSUPPORTED, MOE_EBUSY = 0, -1, -
 MOE_W_BF16, MOE_W_MXFP4, MOE_W_NVFP4, MOE_W_FP8 = 0, 1, 2, 3
 MOE_OPT_FFN_PATH = 1
 MOE_OPT_TIMING = 2
+MOE_OPT_DEC_SPLIT = 3
 
 # every symbol include/moe.h declares
 EXPORTS = [
@@ -26,6 +27,7 @@ EXPORTS = [
     "moe_timing_query", "moe_pack_mxfp4", "moe_pack_weights", "moe_route_permute",
     "expert_cache_reserve", "expert_cache_prefetch", "expert_cache_evict", "expert_cache_stats",
     "expert_cache_slots", "expert_cache_slot_of", "expert_cache_destroy", "expert_cache_resize",
+    "moe_micro_read", "moe_micro_mfma",
 ]
 
 
@@ -81,6 +83,8 @@ def load(path: str | None = None):
         "expert_cache_slots": (I, [P]),
         "expert_cache_slot_of": (I, [P, I, I]),
         "expert_cache_destroy": (I, [P]),
+        "moe_micro_read": (I, [P, Z, I, P, P]),
+        "moe_micro_mfma": (I, [I, I, I, P, C.POINTER(C.c_double), P]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)
@@ -229,6 +233,21 @@ def timing_report():
         if n:
             rep[name] = (n, ms)
     return rep
+
+
+# ------------------------------------------------------- measurement helpers --
+
+def moe_micro_read(buf, nbytes, grid, sink, stream=None):
+    return _check("moe_micro_read", load().moe_micro_read(_ptr(buf), nbytes, grid, _ptr(sink),
+                                                          _stream(stream)))
+
+
+def moe_micro_mfma(kind, grid, iters, sink, stream=None):
+    """Returns the FLOPs of the launch."""
+    f = C.c_double(0.0)
+    _check("moe_micro_mfma", load().moe_micro_mfma(kind, grid, iters, _ptr(sink), C.byref(f),
+                                                   _stream(stream)))
+    return f.value
 
 
 # ------------------------------------------------------------ expert cache --

@@ -15,7 +15,7 @@ LIB = os.path.join(PKG, "libmoe.so")
 OBJDIR = os.path.join(PKG, "_build")
 
 SOURCES = ["api.hip", "route.hip", "permute.hip", "ffn_decode.hip", "ffn_decode_shared.hip",
-           "ffn_prefill.hip", "pack.hip", "noalloc.hip",
+           "ffn_prefill.hip", "pack.hip", "noalloc.hip", "micro.hip",
            "combine.hip", "cache.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

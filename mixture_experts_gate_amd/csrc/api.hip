@@ -14,6 +14,18 @@ static std::atomic<int> g_ffn_path{0};
 void set_last_hip_error(hipError_t e) { g_last_hip_error = (int)e; }
 int ffn_path_option() { return g_ffn_path.load(); }
 
+// Decode tile-split weights, one byte each in units of 1/256: stage 1 slot,
+// stage 1 position, stage 2 slot, stage 2 position (low byte first).
+// measured on the decode layer at T = 8..64: 64/256, 38/256, 38/256, 23/256
+constexpr int kDecSplitDefault = 64 | (38 << 8) | (38 << 16) | (23 << 24);
+static std::atomic<int> g_dec_split{kDecSplitDefault};
+void dec_split_weights(int stage, float *w_slot, float *w_pos) {
+    const unsigned v = (unsigned)g_dec_split.load(std::memory_order_relaxed);
+    const int sh = stage == 1 ? 0 : 16;
+    *w_slot = (float)((v >> sh) & 0xFF) / 256.0f;
+    *w_pos = (float)((v >> (sh + 8)) & 0xFF) / 256.0f;
+}
+
 // ---------------------------------------------------------------- timing --
 // Optional per-kernel launch timing: each launch is made with
 // hipExtLaunchKernel and two events that take the dispatch's own start and end
@@ -33,7 +45,7 @@ static const char *const g_kernel_names[K_COUNT] = {
     "route", "permute_small", "permute_rank", "permute_scan", "permute_scatter", "permute_empty",
     "ffn_decode_gate_up", "ffn_decode_down", "ffn_prefill_gate_up", "ffn_prefill_down",
     "combine", "cache_table", "pack_mxfp4", "route_permute", "ffn_prefill_split",
-    "cache_move"};
+    "cache_move", "micro_read", "micro_mfma"};
 
 static hipEvent_t pool_event() {
     if (!g_evpool.empty()) {
@@ -135,6 +147,13 @@ extern "C" int moe_set_option(int option, int value) {
         g_ffn_path.store(value);
         return MOE_OK;
     }
+    if (option == MOE_OPT_DEC_SPLIT) {
+        if (value == -1) value = kDecSplitDefault;
+        // every byte below 128: each weight stays under one half
+        if (value < 0 || (value & 0x80808080)) return MOE_EINVAL;
+        g_dec_split.store(value);
+        return MOE_OK;
+    }
     if (option == MOE_OPT_TIMING) {
         if (value < 0 || value > 1) return MOE_EINVAL;
         std::lock_guard<std::mutex> lk(g_tmu);
@@ -152,6 +171,7 @@ extern "C" int moe_set_option(int option, int value) {
 extern "C" int moe_get_option(int option) {
     if (option == MOE_OPT_FFN_PATH) return g_ffn_path.load();
     if (option == MOE_OPT_TIMING) return g_timing.load() ? 1 : 0;
+    if (option == MOE_OPT_DEC_SPLIT) return g_dec_split.load();
     return MOE_EINVAL;
 }
 

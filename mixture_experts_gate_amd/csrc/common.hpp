@@ -40,12 +40,14 @@ inline int check_hip(hipError_t e) {
 }
 
 int ffn_path_option();
+// Weights of the decode kernels' tile split for stage 1 or 2 (MOE_OPT_DEC_SPLIT).
+void dec_split_weights(int stage, float *w_slot, float *w_pos);
 
 // Kernel ids for the optional launch timing (moe_timing_query).
 enum KernelId {
     K_ROUTE = 0, K_PERM_SMALL, K_PERM_RANK, K_PERM_SCAN, K_PERM_SCATTER, K_PERM_EMPTY,
     K_DEC_GATE_UP, K_DEC_DOWN, K_PRE_GATE_UP, K_PRE_DOWN, K_COMBINE, K_CACHE_TABLE, K_PACK, K_ROUTE_PERMUTE, K_PRE_SPLIT,
-    K_CACHE_MOVE, K_COUNT
+    K_CACHE_MOVE, K_MICRO_READ, K_MICRO_MFMA, K_COUNT
 };
 
 bool timing_enabled();

@@ -275,7 +275,35 @@ struct DecArgs {
     const moe_expert_w *experts;
     void *out;                      // act (stage 1) or y (stage 2)
     int k, K, H, I, E, nrt;         // nrt: tiles per expert
+    // weighted split of the tiles over the workgroups (see split_start)
+    int slot_size;                  // workgroups per dispatch slot (compute units)
+    float w_slot, w_pos;
 };
+
+// Share of the tiles before workgroup b when workgroup i carries weight
+// 1 - w_slot * (i / C) - w_pos * (i % C) / C (C = slot_size): a persistent
+// grid is dispatched one workgroup per compute unit at a time, and a
+// workgroup dispatched later (a later slot on its compute unit, or later
+// within a slot) receives its first weights later, because the start-up
+// burst of requests is served roughly in issue order; with equal shares it
+// also finishes later, by the same offset, while the early ones idle.
+// Returns the weight sum over workgroups 0 .. b-1.
+__device__ __forceinline__ float split_prefix(int b, int C, float ws, float wp) {
+    const int s = b / C, r = b - s * C;
+    const float full = (float)s * ((float)C - wp * (float)(C - 1) * 0.5f) -
+                       ws * (float)C * ((float)s * (float)(s - 1) * 0.5f);
+    const float part = (float)r * (1.0f - ws * (float)s) -
+                       wp * ((float)r * (float)(r - 1) * 0.5f) / (float)C;
+    return full + part;
+}
+
+__device__ __forceinline__ int split_start(int b, int G, int total, const DecArgs &A) {
+    if (b >= G) return total;
+    const float f = split_prefix(b, A.slot_size, A.w_slot, A.w_pos) /
+                    split_prefix(G, A.slot_size, A.w_slot, A.w_pos);
+    const int t = (int)((float)total * f);
+    return t < total ? t : total;
+}
 
 
 // Expert-level state of the tile being processed (wavefront-uniform: read
@@ -558,8 +586,8 @@ __device__ __forceinline__ void ffn_dec_body(const DecArgs &A, const ShArgs &S,
         ts = gridDim.x;
         n = t0 < total ? (total - t0 + ts - 1) / ts : 0;
     } else {
-        t0 = (int)((long)blockIdx.x * total / gridDim.x);
-        n = (int)(((long)blockIdx.x + 1) * total / gridDim.x) - t0;
+        t0 = split_start(blockIdx.x, gridDim.x, total, A);
+        n = split_start(blockIdx.x + 1, gridDim.x, total, A) - t0;
         ts = 1;
     }
     if (n <= 0) return;
@@ -661,6 +689,13 @@ static int launch_dec(hipStream_t s, DecArgs A, const ShArgs &S, long slots) {
     }
     // tiles per expert
     A.nrt = STAGE == 1 ? A.I / (8 * NB) : A.H / (16 * NB);
+    A.slot_size = num_cus();
+    dec_split_weights(STAGE, &A.w_slot, &A.w_pos);
+    {   // keep every workgroup's weight at 1/4 or more
+        const int last_slot = (int)((full + A.slot_size - 1) / A.slot_size) - 1;
+        if (last_slot > 0 && A.w_slot * last_slot + A.w_pos > 0.75f)
+            A.w_slot = (0.75f - A.w_pos) / last_slot;
+    }
     const long max_tiles = slots * A.nrt;
     const unsigned grid = (unsigned)(max_tiles < (long)full ? max_tiles : (long)full);
     if (grid == 0) return MOE_OK;
@@ -718,10 +753,10 @@ static int ffn_decode_fmt(const uint16_t *x, const int32_t *sorted_pair, const i
     // a shared expert adds one active expert per 16 tokens
     const long slots = (n_pairs < E ? n_pairs : E) + (SH ? (T + kPass - 1) / kPass : 0);
     const ShArgs S{shared, T, T * k};
-    DecArgs a1{x, sorted_pair, offsets, experts, act, k, H, H, I, E, 0};
+    DecArgs a1{x, sorted_pair, offsets, experts, act, k, H, H, I, E, 0, 1, 0.0f, 0.0f};
     int rc = launch_stage<FMT, 1, false, SH>((H + 127) / 128, s, a1, S, slots);
     if (rc) return rc;
-    DecArgs a2{act, sorted_pair, offsets, experts, y, k, I, H, I, E, 0};
+    DecArgs a2{act, sorted_pair, offsets, experts, y, k, I, H, I, E, 0, 1, 0.0f, 0.0f};
     if (y_is_fp32) return launch_stage<FMT, 2, true, SH>((I + 127) / 128, s, a2, S, slots);
     return launch_stage<FMT, 2, false, SH>((I + 127) / 128, s, a2, S, slots);
 }

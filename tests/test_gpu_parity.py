@@ -243,6 +243,45 @@ def test_route_permute_fused_bitwise(lib, orc, T, E, k, kind):
     assert np.array_equal(pr_d.cpu().numpy(), pr)
 
 
+def test_route_permute_reuses_workspace(lib, orc):
+    """Consecutive router + permutation calls on one workspace, with batch
+    sizes that take the one-workgroup kernels and the separate router and
+    permutation (one-workgroup and chunked), logits given and the gate
+    computed: each call equals the oracle bit for bit, whatever the calls
+    before it left in the workspace."""
+    E, k, H = 256, 6, 512
+    pb, _ = lib.moe_workspace_size(1000, k, H, 64, E)
+    pb = max(pb, 256)
+    ws = torch.zeros(pb, dtype=torch.uint8, device=DEV)
+    rng = np.random.default_rng(17)
+    wg = synth.f32_to_bf16_bits((rng.standard_normal((E, H)) * 0.02).astype(np.float32))
+    for i, (T, gate) in enumerate([(64, False), (33, False), (600, False), (5, False), (9, False),
+                                   (37, True), (64, False), (12, True), (20, True), (257, False),
+                                   (1000, False), (64, False)]):
+        _announce(f"route+permute, shared workspace: call {i}, T={T}, gate={gate}")
+        x = synth.f32_to_bf16_bits(rng.standard_normal((T, H)).astype(np.float32))
+        lg = orc.gate_logits_f32(x, wg) if gate else rng.random((T, E), dtype=np.float32)
+        ids, wts, _ = orc.topk(lg, k)
+        off, sp, pr = orc.permute(ids, E)
+        ids_d = torch.full((T, k), -7, dtype=torch.int32, device=DEV)
+        w_d = torch.empty((T, k), dtype=torch.float32, device=DEV)
+        off_d = torch.full((E + 1,), -7, dtype=torch.int32, device=DEV)
+        sp_d = torch.full((T * k,), -7, dtype=torch.int32, device=DEV)
+        pr_d = torch.full((T * k,), -7, dtype=torch.int32, device=DEV)
+        if gate:
+            lib.moe_route_permute(to_dev_bf16(x), to_dev_bf16(wg), None, None, T, H, E, k, True,
+                                  ids_d, w_d, off_d, sp_d, pr_d, ws, pb)
+        else:
+            lib.moe_route_permute(None, None, to_dev(lg), None, T, 0, E, k, True, ids_d, w_d,
+                                  off_d, sp_d, pr_d, ws, pb)
+        torch.cuda.synchronize()
+        assert np.array_equal(ids_d.cpu().numpy(), ids)
+        assert np.abs(w_d.cpu().numpy().astype(np.float64) - wts).max() <= W_ATOL
+        assert np.array_equal(off_d.cpu().numpy(), off)
+        assert np.array_equal(sp_d.cpu().numpy(), sp)
+        assert np.array_equal(pr_d.cpu().numpy(), pr)
+
+
 def test_permute_empty_batch(lib):
     off_d = torch.full((9,), -7, dtype=torch.int32, device=DEV)
     lib.moe_permute(None, 0, 2, 8, off_d, None, None, None, 0)
