@@ -8,10 +8,13 @@ inputs resident in HBM. The headline workload is the decode-shaped layer
 router logits) at T=64 tokens. The JSON line's sweep also carries T=1, 8, 32
 and the prefill-shaped T=8192 batch of the same layer; the large sparse layer
 (H=4096, 256 experts + 1 shared, top-6, I=2048, Zipf popularity) at T=1, 64,
-4096; and the 43-layer stack of that layer decoding T=1 and 16 tokens, once
-with every layer resident in HBM and once through a 32 GB LRU expert cache
-fed from pinned host memory (hit rate, H2D bytes and GB/s against the
-measured pinned copy rate).
+4096; and the 43-layer stack of that layer decoding T=1, 2, 4, 8 and 16 tokens,
+once with every layer resident in HBM and once through a 32 GB LRU expert
+cache fed from pinned host memory (hit rate, H2D bytes and GB/s against the
+measured pinned copy rate; T=1 over 1024 steps, four popularity phases);
+full-layer double-buffered prefill streaming of that stack at T=4096 (time
+per layer against the copy alone and the compute alone); references measured
+on the GPU (read stream at the kernels' byte counts, matrix-core issue rates).
 
 Timing: W eager warm-up steps, then K steps replayed from HIP graphs (one
 graph holds 16 consecutive steps), bracketed by device synchronisation.
@@ -23,7 +26,9 @@ average launch time, from the start/end events hipExtLaunchKernel attaches to
 each of its dispatches on the launch stream (library timing mode, a second
 pass of K eager steps); traffic: HBM bytes per launch from the committed
 counter summary (profiles/traffic.json) when it matches the kernel's source.
-cpu_baseline: the CPU oracle (single-threaded C, fp64) on the same layer.
+cpu_baseline: the CPU oracle (single-threaded C, fp64) on the same layer;
+cpu_baseline_sweep: the oracle on every workload (token subsets of the large
+batches, extrapolation labelled), with the host's CPU model.
 """
 from __future__ import annotations
 
@@ -56,11 +61,13 @@ def parse():
                     help="short run for profilers: headline workload, no sweep, no CPU leg")
     ap.add_argument("--no-stack", action="store_true", help="skip the 43-layer stack runs")
     ap.add_argument("--only", default="",
-                    help="comma list of sweep parts to run: decode,formats,prefill,cfg4,stack")
+                    help="comma list of sweep parts to run: decode,formats,prefill,cfg4,stack,stream")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run one plain 512 MiB device copy (HBM counter calibration)")
     ap.add_argument("--no-micro", action="store_true",
                     help="skip the read-stream / matrix-core reference measurements")
+    ap.add_argument("--stack-steps", type=int, default=1024,
+                    help="timed steps of the cached 43-layer stack at T=1")
     ap.add_argument("--cfg4-T", default="1,64,4096",
                     help="comma list of the large sparse layer's batch sizes to run")
     return ap.parse_args()
@@ -297,6 +304,14 @@ class Stack:
         self.shared_blobs = [synth.shared_expert(c, layer=d) for d in range(distinct)]
         self.dev = dev
 
+    def host_store(self):
+        """Pinned host store of the stack's experts: the generated layers, every
+        layer key reading the stored layer it repeats (the copies move the bytes
+        of 43 distinct layers)."""
+        from mixture_experts_gate_amd.layer import HostExperts
+        return HostExperts(self.blobs, self.lay, alias=lambda l, e: (l % self.D) * self.cfg.E + e,
+                           device=self.dev)
+
     def logits(self, torch, T, steps):
         """Router logits of every layer for each of the given steps (fresh Gumbel
         noise per step and layer; the Zipf popularity permutation changes every
@@ -379,28 +394,29 @@ def h2d_peak(torch, dev, nbytes=1 << 30):
     return gbs
 
 
-def run_stack_cached(torch, st, runs, pool_bytes, resize_T=1, resize_steps=32):
+def run_stack_cached(torch, st, runs, pool_bytes, resize_T=1, resize_steps=32, store=None):
     """The stack through a pool_bytes LRU expert cache fed from pinned host
     memory: per layer, route on the GPU, read the ids back, prefetch the misses
     (hipMemcpyAsync on the copy stream), then the expert FFN, shared expert and
-    combine. Shared experts stay resident. runs: [(T, warmup, steps)]. After the
-    timed steps at T = resize_T the pool is resized to half and back, each
-    followed by resize_steps steps."""
-    import numpy as np
+    combine. Shared experts stay resident. runs: [(T, first_step, warmup,
+    steps)]: steps first_step .. first_step + steps - 1 are timed after `warmup`
+    untimed steps just before them (router logits per step index, Zipf
+    popularity re-drawn every 256 steps). After the timed steps at T = resize_T
+    the pool is resized to half and back, each followed by resize_steps steps."""
     from mixture_experts_gate_amd import synth
-    from mixture_experts_gate_amd.layer import (ExpertCache, HostExperts, MoeLayer, expert_table,
-                                                pack_to_device)
+    from mixture_experts_gate_amd.layer import ExpertCache, MoeLayer, expert_table, pack_to_device
     c, lay, dev = st.cfg, st.lay, st.dev
-    store = HostExperts(st.blobs, lay, alias=lambda l, e: (l % st.D) * c.E + e, device=dev)
+    store = store if store is not None else st.host_store()
     spacked = [pack_to_device(b[None, :], lay, dev) for b in st.shared_blobs]
     stabs = [expert_table(spacked[l % st.D].data_ptr(), 1, lay, device=dev) for l in range(st.L)]
     link = h2d_peak(torch, dev)
     log(f"pinned H2D copy rate: {link:.1f} GB/s")
     out = {"h2d_link_GBs": link, "pool_bytes": pool_bytes}
-    for T, warmup, steps in runs:
+    for T, first, warmup, steps in runs:
         cache = ExpertCache(store, st.L, c.E, pool_bytes, device=dev)
         extra = 2 * resize_steps if T == resize_T else 0
-        lg = st.logits(torch, T, range(warmup + steps + extra))
+        s0 = first - warmup
+        lg = st.logits(torch, T, range(s0, first + steps + extra))
         x0 = torch.from_numpy(synth.activations(c, T).view("int16")).to(dev)
         layers = [MoeLayer(c.H, c.E, c.k, c.I, c.fmt, T, shared=True, device=dev) for _ in (0, 1)]
         for ly in layers:
@@ -410,37 +426,44 @@ def run_stack_cached(torch, st, runs, pool_bytes, resize_T=1, resize_steps=32):
             x = x0
             for l in range(st.L):
                 ly = layers[l % 2]
-                ly.route_permute(T, logits=lg[i][l], write_logits=False)
+                ly.route_permute(T, logits=lg[i - s0][l], write_logits=False)
                 ids = ly.topk_ids[:T].cpu().numpy().ravel()
                 tab = cache.prefetch(l, ids)
                 ysh = ly.ffn_with_shared(T, x, tab, stabs[l])
                 ly.combine(T, y_shared=ysh)
                 x = ly.out[:T]
 
-        for i in range(warmup):
+        for i in range(s0, first):
             step(i)
         torch.cuda.synchronize()
         h0, m0, b0 = cache.stats()
         t0 = time.perf_counter()
-        for i in range(warmup, warmup + steps):
+        phases = {}
+        for i in range(first, first + steps):
             step(i)
+            if (i - first) % 64 == 63:
+                log(f"stack cached T={T}: step {i}")
+            phases.setdefault(i // synth.ZIPF_PHASE_STEPS, 0)
+            phases[i // synth.ZIPF_PHASE_STEPS] += 1
         torch.cuda.synchronize()
         el = time.perf_counter() - t0
         h1, m1, b1 = cache.stats()
         hits, misses, nb = h1 - h0, m1 - m0, b1 - b0
-        r = {"T": T, "steps": steps, "warmup": warmup, "slots": cache.slots(),
+        r = {"T": T, "steps": steps, "first_step": first, "warmup": warmup,
+             "slots": cache.slots(),
              "tokens_per_s": T * steps / el, "ms_per_step": 1000.0 * el / steps,
              "hit_rate": hits / max(hits + misses, 1), "misses_per_step": misses / steps,
              "h2d_bytes_per_step": nb / steps, "h2d_GBs": nb / el / 1e9,
              "h2d_frac_of_link": nb / el / 1e9 / link,
-             "steps_cross_popularity_change": (warmup + steps) > 256}
+             "popularity_phases": {str(k): v for k, v in sorted(phases.items())}}
         out[f"T{T}"] = r
-        log(f"stack cached T={T}: {r['tokens_per_s']:.1f} tok/s, hit {r['hit_rate']:.3f}, "
-            f"H2D {r['h2d_GBs']:.1f} GB/s ({r['h2d_frac_of_link']*100:.0f}% of the copy rate)")
+        log(f"stack cached T={T} steps {first}..{first + steps - 1}: {r['tokens_per_s']:.1f} tok/s, "
+            f"hit {r['hit_rate']:.3f}, H2D {r['h2d_GBs']:.1f} GB/s "
+            f"({r['h2d_frac_of_link']*100:.0f}% of the copy rate), phases {r['popularity_phases']}")
         if T == resize_T:
             # elastic resize: the pool shrinks to half into a new buffer (the
             # other half could go to other uses), runs, then grows back
-            nxt = warmup + steps
+            nxt = first + steps
             r["resize"] = []
             for frac in (0.5, 1.0):
                 torch.cuda.synchronize()
@@ -467,9 +490,81 @@ def run_stack_cached(torch, st, runs, pool_bytes, resize_T=1, resize_steps=32):
                     f"({q['d2d_hbm_frac']*100:.0f}% of HBM), hit rate over the next "
                     f"{resize_steps} steps {q['hit_rate_next_steps']:.3f}")
         cache.close()
-        del cache
-    del store
+        del cache, lg
     return out
+
+
+def run_prefill_stream(torch, st, T=4096, n_layers=6, store=None):
+    """Full-layer double-buffered prefill streaming over the stack (the pages'
+    prefill mechanism): every expert of layer l+1 is requested while layer l
+    computes, into a pool of two layers, from pinned host memory. Reported: the
+    time per layer streamed, the compute alone (the same layers with their
+    experts already in the pool), the copy alone (one layer's experts with no
+    compute), the overlap (max(copy, compute) over the streamed time) and the
+    H2D rate against the measured pinned copy rate."""
+    from mixture_experts_gate_amd import synth
+    from mixture_experts_gate_amd.layer import ExpertCache, MoeLayer, expert_table, pack_to_device
+    c, lay, dev = st.cfg, st.lay, st.dev
+    store = store if store is not None else st.host_store()
+    spacked = [pack_to_device(b[None, :], lay, dev) for b in st.shared_blobs]
+    stabs = [expert_table(spacked[l % st.D].data_ptr(), 1, lay, device=dev) for l in range(st.L)]
+    slot = (lay.nbytes + 255) // 256 * 256
+    cache = ExpertCache(store, st.L, c.E, 2 * c.E * slot, device=dev)
+    ly = MoeLayer(c.H, c.E, c.k, c.I, c.fmt, T, shared=True, device=dev)
+    ly.prepare_shared(T)
+    x0 = torch.from_numpy(synth.activations(c, T).view("int16")).to(dev)
+    lg = st.logits(torch, T, (0,))[0]
+    link = h2d_peak(torch, dev)
+    layer_bytes = c.E * lay.nbytes
+
+    def copy_only(l):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        cache.prefetch(l, None)
+        torch.cuda.synchronize()
+        return time.perf_counter() - t0
+
+    def streamed(first, n):
+        x = x0
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        tab = cache.prefetch(first, None)
+        for l in range(first, first + n):
+            ly.forward(T, x, tab, logits=lg[l], shared_table=stabs[l])
+            x = ly.out[:T]
+            if l + 1 < first + n:
+                tab = cache.prefetch(l + 1, None)
+        torch.cuda.synchronize()
+        return time.perf_counter() - t0
+
+    def compute_only(l, reps=5):
+        tab = cache.prefetch(l, None)          # resident from the pass before: all hits
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            ly.forward(T, x0, tab, logits=lg[l], shared_table=stabs[l])
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) / reps
+
+    streamed(0, 2)                                # warm-up
+    t_copy = copy_only(2)
+    t_stream = streamed(3, n_layers)
+    t_comp = compute_only(3 + n_layers - 1)
+    per = t_stream / n_layers
+    h, m, b = cache.stats()
+    cache.close()
+    r = {"T": T, "layers": n_layers, "layer_bytes": layer_bytes, "h2d_link_GBs": link,
+         "ms_per_layer_streamed": 1000.0 * per, "ms_per_layer_compute_only": 1000.0 * t_comp,
+         "ms_per_layer_copy_only": 1000.0 * t_copy,
+         "overlap_efficiency": max(t_copy, t_comp) / per,
+         "h2d_GBs_streamed": layer_bytes / per / 1e9,
+         "h2d_frac_of_link": layer_bytes / per / 1e9 / link,
+         "tokens_per_s": T / per}
+    log(f"prefill streaming T={T}: {r['ms_per_layer_streamed']:.1f} ms/layer streamed, "
+        f"copy alone {r['ms_per_layer_copy_only']:.1f} ms, compute alone "
+        f"{r['ms_per_layer_compute_only']:.2f} ms, overlap {r['overlap_efficiency']:.2f}, "
+        f"H2D {r['h2d_GBs_streamed']:.1f} GB/s ({r['h2d_frac_of_link']*100:.0f}% of the copy rate)")
+    return r
 
 
 def cpu_baseline(wl, budget_s=12.0):
@@ -496,7 +591,7 @@ def cpu_baseline(wl, budget_s=12.0):
     return {"value": wl.T * reps / el, "unit": "tokens/s", "cores": 1, "kind": "oracle",
             "sample": f"{reps} full layer passes at T={wl.T} (same layer, input batch 0), "
                       f"single-threaded C oracle, fp64 accumulation, {el:.1f} s",
-            "host_cpus": os.cpu_count()}
+            "host_cpus": os.cpu_count(), "cpu_model": cpu_model()}
 
 
 def micro(torch, dev):
@@ -557,6 +652,104 @@ def read_peak_for(micro_res, nbytes):
     rs = micro_res["read_stream"]
     size = min({r["bytes"] for r in rs}, key=lambda b: abs(b - nbytes))
     return max(r["GBs"] for r in rs if r["bytes"] == size)
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def cpu_baselines(c2_pool, budget_s=3.0):
+    """The oracle on every workload (one core, pinned): full layers where the
+    oracle finishes in seconds, token subsets of the large batches with the
+    per-token linear extrapolation to the full batch labelled as such (the
+    layer is token-independent once routing is fixed), and a sample of layers
+    of one 43-layer stack step."""
+    import numpy as np
+    import oracle
+    from mixture_experts_gate_amd import synth
+    oracle.build(force=False)
+    try:
+        cpus = sorted(os.sched_getaffinity(0))
+        old = set(cpus)
+        os.sched_setaffinity(0, {cpus[-1]})
+    except (AttributeError, OSError):
+        old = None
+    out = []
+
+    def timed(fn, min_reps=1):
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            fn()
+            reps += 1
+            el = time.perf_counter() - t0
+            if (el >= budget_s and reps >= min_reps) or reps >= 50:
+                return el / reps, reps
+
+    def record(name, T_full, tokens, per_pass, reps, note):
+        r = {"workload": name, "T": T_full, "tokens_timed": tokens, "passes": reps,
+             "s_per_pass": per_pass, "value": tokens / per_pass, "unit": "tokens/s", "cores": 1,
+             "kind": "oracle"}
+        if tokens < T_full:
+            r["extrapolated_full_batch_s"] = per_pass * T_full / tokens
+            r["note"] = ("measured on a token subset; full-batch time extrapolated per token "
+                         "(linear, the layer being token-independent once routing is fixed)")
+        if note:
+            r["sample"] = note
+        out.append(r)
+        log(f"oracle {name}: {r['value']:.2f} tok/s ({reps} passes of {tokens} tokens)")
+
+    c1 = synth.CONFIGS[1]
+    lay1 = synth.blob_layout(c1.H, c1.I, c1.fmt)
+    pool1, x1, wg1 = synth.expert_pool(c1), synth.activations(c1, 16), synth.gate_weights(c1)
+    per, reps = timed(lambda: oracle.moe_layer(x1, lay1, pool1, c1.k, wg=wg1))
+    record("tiny layer T=16 (gate computed)", 16, 16, per, reps, None)
+    c2 = synth.CONFIGS[2]
+    lay2 = synth.blob_layout(c2.H, c2.I, c2.fmt)
+    for T in (1, 8, 32, 64):
+        x, lg = synth.activations(c2, T), synth.router_logits(c2, T)
+        per, reps = timed(lambda: oracle.moe_layer(x, lay2, c2_pool, c2.k, logits=lg))
+        record(f"decode layer T={T}", T, T, per, reps, None)
+    c3 = synth.CONFIGS[3]
+    sub = np.arange(0, 8192, 32)                    # 256 tokens of the prefill batch
+    x3 = synth.activations(c3, 8192)[sub]
+    lg3 = synth.router_logits(c3, 8192)[sub]
+    per, reps = timed(lambda: oracle.moe_layer(x3, lay2, c2_pool, c3.k, logits=lg3))
+    record("prefill layer T=8192", 8192, len(sub), per, reps, "every 32nd token of the batch")
+    c4 = synth.CONFIGS[4]
+    lay4 = synth.blob_layout(c4.H, c4.I, c4.fmt)
+    pool4, sh4 = synth.expert_pool(c4), synth.shared_expert(c4)
+    for T, n in ((1, 1), (64, 16), (4096, 64)):
+        idx = np.arange(0, T, T // n)
+        x, lg = synth.activations(c4, T)[idx], synth.router_logits(c4, T)[idx]
+        per, reps = timed(lambda: oracle.moe_layer(x, lay4, pool4, c4.k, logits=lg,
+                                                   shared_blob=sh4))
+        record(f"large sparse layer T={T}", T, len(idx), per, reps,
+               None if n == T else f"every {T // n}th token of the batch")
+    # one step of the stack at T=1: 8 of its 43 layers (each with its own
+    # experts and logits), scaled to the step
+    c5 = synth.CONFIGS[5]
+    pool5, sh5 = pool4, sh4           # the stack's layers have the large sparse layer's shapes
+    x = synth.activations(c5, 1)
+    t0 = time.perf_counter()
+    for l in range(8):
+        lg = synth.router_logits(c5, 1, layer=l)
+        r = oracle.moe_layer(x, lay4, pool5, c5.k, logits=lg, shared_blob=sh5)
+        x = r["out_bf16"]
+    el = (time.perf_counter() - t0) * c5.layers / 8
+    out.append({"workload": "43-layer stack, one step at T=1", "T": 1, "value": 1.0 / el,
+                "unit": "tokens/s", "cores": 1, "kind": "oracle", "s_per_step": el,
+                "note": "8 of the 43 layers timed, the step scaled by 43/8 (layers cost the same)"})
+    log(f"oracle stack step T=1: {el:.1f} s per step")
+    if old is not None:
+        os.sched_setaffinity(0, old)
+    return {"cpu_model": cpu_model(), "host_cpus": os.cpu_count(), "runs": out}
 
 
 def calib_copy(torch, dev):
@@ -671,18 +864,28 @@ def main():
                 f"layer HBM {r['layer_hbm_frac']*100:.1f}%, {r['layer_tflops']:.1f} TFLOP/s")
         del w4
         torch.cuda.empty_cache()
-    if not args.no_sweep and not args.no_stack and want("stack"):
+    if not args.no_sweep and not args.no_stack and (want("stack") or want("stream")):
         c5 = synth.CONFIGS[5]
         log("config 5: generating 2 distinct layers ...")
         st = Stack(torch, c5, dev, distinct=2)
-        sweep["stack43_resident"] = run_stack_resident(torch, st, (1, 16), 40, 3)
-        sweep["stack43_cache32GB"] = run_stack_cached(torch, st, [(1, 32, 288), (16, 4, 8)],
-                                                      32 * 10**9)
-        del st
-    cpu = None
+        if want("stack"):
+            sweep["stack43_resident"] = run_stack_resident(torch, st, (1, 2, 4, 8, 16), 40, 3)
+        store = st.host_store()
+        if want("stream"):
+            sweep["prefill_stream_T4096"] = run_prefill_stream(torch, st, store=store)
+        if want("stack"):
+            # T=1 over four popularity phases; T=16 across the change at step 256
+            runs = [(1, 32, 32, args.stack_steps), (2, 128, 4, 16), (4, 128, 4, 16),
+                    (8, 128, 4, 16), (16, 248, 4, 16)]
+            sweep["stack43_cache32GB"] = run_stack_cached(torch, st, runs, 32 * 10**9,
+                                                          store=store)
+        del st, store
+    cpu = cpu_all = None
     if not args.no_cpu:
         log("CPU oracle baseline ...")
         cpu = cpu_baseline(wl)
+        if not args.no_sweep:
+            cpu_all = cpu_baselines(wl.pool)
     c = wl.cfg
     line = {
         "metric": "MoE-layer tokens/s at decode T=1..64 & prefill T=8192; % HBM / MFMA roofline",
@@ -707,6 +910,7 @@ def main():
                    "kernels": head["kernels"]},
         "roofline": roof,
         "cpu_baseline": cpu,
+        "cpu_baseline_sweep": cpu_all,
         "micro": micro_res,
         "sweep": sweep,
     }

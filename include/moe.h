@@ -294,8 +294,15 @@ int moe_workspace_size(int T, int k, int H, int I, int E, size_t *permute_bytes,
  *                     (later-dispatched workgroups receive their first data
  *                     later). Four bytes, each in units of 1/256 and below
  *                     128: stage 1 ws, stage 1 wp, stage 2 ws, stage 2 wp
- *                     (low byte first); -1 restores the default. */
-enum { MOE_OPT_FFN_PATH = 1, MOE_OPT_TIMING = 2, MOE_OPT_DEC_SPLIT = 3 };
+ *                     (low byte first); -1 restores the default.
+ *   MOE_OPT_CACHE_FAULT: test knob: n > 0 makes the n-th expert-cache copy
+ *                     from now fail without being issued (the prefetch call
+ *                     returns MOE_EHIP as for a failed hipMemcpyAsync); 0 = off.
+ *   MOE_OPT_CACHE_DELAY_US: test knob: every prefetch that copies first holds
+ *                     its copy stream this many microseconds (a host function
+ *                     that sleeps), as a slow link would; 0 = off. */
+enum { MOE_OPT_FFN_PATH = 1, MOE_OPT_TIMING = 2, MOE_OPT_DEC_SPLIT = 3, MOE_OPT_CACHE_FAULT = 4,
+       MOE_OPT_CACHE_DELAY_US = 5 };
 int moe_set_option(int option, int value);
 int moe_get_option(int option);
 
@@ -356,7 +363,15 @@ int expert_cache_reserve(moe_cache **cache, void *pool, size_t pool_bytes, size_
  *      allowed); NULL means every expert of the layer.
  * Hits refresh the LRU order; each miss takes the least recently used slot
  * that no call since the previous prefetch has handed out, waits (on the copy
- * stream) for the compute work that last used it, and copies the blob into it.
+ * stream) for the compute work that last used it, and copies the blob into it
+ * (free slots count as least recently used, the lowest index first; misses
+ * whose blobs are adjacent in host memory and whose slots are adjacent share
+ * one copy).
+ * If a copy cannot be enqueued (MOE_EHIP), the misses enqueued before it are
+ * resident (their copies are in flight; compute_stream waits for them), and
+ * nothing else of the call takes effect: no hit is refreshed, no other slot
+ * changes, the counters count only the enqueued copies. A failure at the
+ * call's first copy therefore leaves the cache exactly as it was.
  * On return, compute_stream has been made to wait for this layer's copies and
  * table update, and *table_out (if not NULL) is the layer's device table
  * [n_experts] for moe_expert_ffn. Entries of experts not requested may be
@@ -379,7 +394,7 @@ int expert_cache_prefetch(moe_cache *cache, int layer, const int32_t *ids, int n
  * keeps its slot index when it is below the new slot count, the others take
  * the lowest free indices, most recent first); the rest are dropped. LRU
  * order among the kept residents is unchanged; free slots become the least
- * recently used, in ascending index order. The copy stream first waits for
+ * recently used, the lowest index to be taken first. The copy stream first waits for
  * the work enqueued on compute_stream before this call; on return,
  * compute_stream waits for the copies and table updates.
  * Tables returned by earlier prefetch calls must not be read by compute

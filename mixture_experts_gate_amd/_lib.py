@@ -18,6 +18,8 @@ MOE_W_BF16, MOE_W_MXFP4, MOE_W_NVFP4, MOE_W_FP8 = 0, 1, 2, 3
 MOE_OPT_FFN_PATH = 1
 MOE_OPT_TIMING = 2
 MOE_OPT_DEC_SPLIT = 3
+MOE_OPT_CACHE_FAULT = 4
+MOE_OPT_CACHE_DELAY_US = 5
 
 # every symbol include/moe.h declares
 EXPORTS = [

@@ -147,6 +147,8 @@ extern "C" int moe_set_option(int option, int value) {
         g_ffn_path.store(value);
         return MOE_OK;
     }
+    if (option == MOE_OPT_CACHE_FAULT) return cache_set_fault(value);
+    if (option == MOE_OPT_CACHE_DELAY_US) return cache_set_delay(value);
     if (option == MOE_OPT_DEC_SPLIT) {
         if (value == -1) value = kDecSplitDefault;
         // every byte below 128: each weight stays under one half
@@ -172,6 +174,8 @@ extern "C" int moe_get_option(int option) {
     if (option == MOE_OPT_FFN_PATH) return g_ffn_path.load();
     if (option == MOE_OPT_TIMING) return g_timing.load() ? 1 : 0;
     if (option == MOE_OPT_DEC_SPLIT) return g_dec_split.load();
+    if (option == MOE_OPT_CACHE_FAULT) return cache_get_fault();
+    if (option == MOE_OPT_CACHE_DELAY_US) return cache_get_delay();
     return MOE_EINVAL;
 }
 

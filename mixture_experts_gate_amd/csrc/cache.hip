@@ -18,7 +18,10 @@
 // ev[last_gen + 1] of that slot before overwriting it. With room for two
 // layers of experts, prefetching layer l+1 evicts layer l-1 and overlaps the
 // compute of layer l.
+#include <unistd.h>
+
 #include <algorithm>
+#include <atomic>
 #include <deque>
 #include <new>
 #include <vector>
@@ -26,6 +29,37 @@
 #include "common.hpp"
 
 namespace moe {
+
+// Test knobs (MOE_OPT_CACHE_FAULT, MOE_OPT_CACHE_DELAY_US): the n-th
+// host-to-device copy of the cache from now fails without being issued; every
+// prefetch with copies first holds its copy stream for this many microseconds
+// (a host function that sleeps).
+static std::atomic<long long> g_fault_at{0};     // remaining copies before the fault, 0 = off
+static std::atomic<int> g_delay_us{0};
+
+int cache_set_fault(int n) {
+    if (n < 0) return MOE_EINVAL;
+    g_fault_at.store(n);
+    return MOE_OK;
+}
+int cache_get_fault() { return (int)g_fault_at.load(); }
+int cache_set_delay(int us) {
+    if (us < 0 || us > 10000000) return MOE_EINVAL;
+    g_delay_us.store(us);
+    return MOE_OK;
+}
+int cache_get_delay() { return g_delay_us.load(); }
+
+// True if this copy is the one the fault knob designates (counts it down).
+static bool copy_fault_now() {
+    long long v = g_fault_at.load();
+    while (v > 0) {
+        if (g_fault_at.compare_exchange_weak(v, v - 1)) return v == 1;
+    }
+    return false;
+}
+
+static void sleep_host_fn(void *arg) { usleep((useconds_t)(uintptr_t)arg); }
 
 constexpr int kTableBatch = 240;
 
@@ -103,6 +137,7 @@ struct moe_cache {
     std::vector<int> prev, next;        // LRU list over slots; head = most recent
     int head = -1, tail = -1;
     std::vector<long long> last_gen;    // slot -> generation that last handed it out (0 = never)
+    std::vector<long long> pick_gen;    // slot -> generation whose plan took it (scratch)
     long long gen = 0;
     std::deque<hipEvent_t> entry_ev;    // entry_ev[i] belongs to generation ev_front_gen + i
     long long ev_front_gen = 1;
@@ -188,11 +223,13 @@ extern "C" int expert_cache_reserve(moe_cache **cache, void *pool, size_t pool_b
         c->prev.assign(nslots, -1);
         c->next.assign(nslots, -1);
         c->last_gen.assign(nslots, 0);
+        c->pick_gen.assign(nslots, 0);
     } catch (...) {
         delete c;
         return MOE_ENOMEM;
     }
-    for (int s = 0; s < c->nslots; ++s) c->push_back(s);
+    // free slots at the least recently used end, the lowest index taken first
+    for (int s = c->nslots - 1; s >= 0; --s) c->push_back(s);
     int rc = check_hip(hipMalloc(&c->d_table, sizeof(moe_expert_w) * (size_t)nkeys));
     if (!rc) rc = check_hip(hipMemset(c->d_table, 0, sizeof(moe_expert_w) * (size_t)nkeys));
     if (!rc) rc = check_hip(hipEventCreateWithFlags(&c->ready, hipEventDisableTiming));
@@ -238,53 +275,104 @@ extern "C" int expert_cache_prefetch(moe_cache *c, int layer, const int32_t *ids
     c->entry_ev.push_back(ev);      // generation g == ev_front_gen + index
 
     const long base_key = (long)layer * E;
-    // hits first: they are handed out by this call and must not become victims
-    std::vector<int> miss;
+    // Plan, without changing anything: the hits, and for each miss (ascending
+    // expert) the least recently used slot that neither a hit nor an earlier
+    // miss of this call takes.
+    std::vector<int> hit_slot, miss, victim;
     for (int e : want) {
         const int s = c->slot_of[base_key + e];
         if (s >= 0) {
-            ++c->hits;
-            c->unlink(s);
-            c->push_front(s);
-            c->last_gen[s] = g;
+            hit_slot.push_back(s);
+            c->pick_gen[s] = g;
         } else {
             miss.push_back(e);
         }
     }
-    TableUpdate up;
-    up.n = 0;
-    auto flush = [&]() -> int {
-        if (up.n == 0) return MOE_OK;
-        MOE_LAUNCH(K_CACHE_TABLE, cache_table_kernel, dim3(1), dim3(256), 0, c->copy_stream,
-                                     c->d_table, (const char *)c->pool, c->slot_bytes, c->lay[0],
-                                     c->lay[1], c->lay[2], c->lay[3], up);
-        up.n = 0;
-        return check_launch();
-    };
-    for (int e : miss) {
-        // least recently used slot not handed out by this call (tail side)
-        int s = c->tail;
-        while (s >= 0 && c->last_gen[s] == g) s = c->prev[s];
+    for (int s = c->tail; victim.size() < miss.size(); s = c->prev[s]) {
+        while (s >= 0 && c->pick_gen[s] == g) s = c->prev[s];
         if (s < 0) return MOE_ENOMEM;    // cannot happen: want.size() <= nslots
-        const long long lg = c->last_gen[s];
-        if (lg > 0 && lg + 1 > c->done_gen) {
-            // its readers are covered by the entry event of generation lg + 1
-            const long long idx = lg + 1 - c->ev_front_gen;
+        victim.push_back(s);
+        c->pick_gen[s] = g;
+    }
+    // Issue the copies. A copy that cannot be enqueued ends the call: the
+    // misses copied before it are committed below (their copies are in
+    // flight), the rest of the call is not, so a failure at the first copy
+    // leaves the cache, its table and its counters as they were.
+    size_t issued = 0;
+    if (!miss.empty() && g_delay_us.load() > 0) {
+        rc = check_hip(hipLaunchHostFunc(c->copy_stream, sleep_host_fn,
+                                         (void *)(uintptr_t)g_delay_us.load()));
+        if (rc) return rc;
+    }
+    // A victim's readers are covered by the entry event of generation
+    // last_gen + 1; the copy stream waits for it before the copy. A wait
+    // covers every later copy on the stream and entry events complete in
+    // generation order, so one wait per larger generation suffices.
+    // Consecutive misses whose blobs sit back to back in host memory and whose
+    // slots are adjacent go in one copy (a whole layer into the slots of the
+    // layer before it is then a few large copies).
+    long long waited = c->done_gen;
+    while (issued < miss.size() && !rc) {
+        size_t run = 1;
+        while (issued + run < miss.size() &&
+               victim[issued + run] == victim[issued + run - 1] + 1 &&
+               miss[issued + run] == miss[issued + run - 1] + 1 &&
+               (const char *)c->src[base_key + miss[issued + run]] ==
+                   (const char *)c->src[base_key + miss[issued + run - 1]] + c->slot_bytes)
+            ++run;
+        long long need = 0;
+        for (size_t i = issued; i < issued + run; ++i) {
+            const long long lg = c->last_gen[victim[i]];
+            if (lg > 0 && lg + 1 > need) need = lg + 1;
+        }
+        if (need > waited) {
+            const long long idx = need - c->ev_front_gen;
             if (idx >= 0 && idx < (long long)c->entry_ev.size()) {
                 rc = check_hip(hipStreamWaitEvent(c->copy_stream, c->entry_ev[(size_t)idx], 0));
-                if (rc) return rc;
+                if (rc) break;
             }
+            waited = need;
         }
+        // the fault knob counts experts: a run stops short of the designated one
+        size_t ok = 0;
+        while (ok < run && !copy_fault_now()) ++ok;
+        if (ok > 0) {
+            rc = check_hip(hipMemcpyAsync(c->pool + (size_t)victim[issued] * c->slot_bytes,
+                                          c->src[base_key + miss[issued]],
+                                          (ok - 1) * c->slot_bytes + c->expert_bytes,
+                                          hipMemcpyHostToDevice, c->copy_stream));
+            if (rc) break;
+            issued += ok;
+        }
+        if (ok < run) {
+            set_last_hip_error(hipErrorUnknown);
+            rc = MOE_EHIP;
+        }
+    }
+    // Commit: hits (only when the whole call succeeded), then the issued misses.
+    if (!rc) {
+        for (int s : hit_slot) {
+            ++c->hits;
+            c->unlink(s);
+            c->push_front(s);
+            c->last_gen[s] = g;
+        }
+    }
+    TableUpdate up;
+    up.n = 0;
+    int rc_table = MOE_OK;
+    auto flush = [&]() {
+        if (up.n == 0) return;
+        MOE_LAUNCH(K_CACHE_TABLE, cache_table_kernel, dim3(1), dim3(256), 0, c->copy_stream,
+                   c->d_table, (const char *)c->pool, c->slot_bytes, c->lay[0], c->lay[1],
+                   c->lay[2], c->lay[3], up);
+        up.n = 0;
+        if (!rc_table) rc_table = check_launch();
+    };
+    for (size_t i = 0; i < issued; ++i) {
+        const int s = victim[i], e = miss[i];
         const int old = c->key_of[s];
         if (old >= 0) c->slot_of[old] = -1;
-        c->key_of[s] = -1;
-        rc = check_hip(hipMemcpyAsync(c->pool + (size_t)s * c->slot_bytes, c->src[base_key + e],
-                                      c->expert_bytes, hipMemcpyHostToDevice, c->copy_stream));
-        if (rc) {
-            c->unlink(s);
-            c->push_back(s);
-            return rc;
-        }
         c->key_of[s] = (int)(base_key + e);
         c->slot_of[base_key + e] = s;
         c->unlink(s);
@@ -294,11 +382,16 @@ extern "C" int expert_cache_prefetch(moe_cache *c, int layer, const int32_t *ids
         c->h2d_bytes += (long long)c->expert_bytes;
         up.key[up.n] = (int)(base_key + e);
         up.slot[up.n] = s;
-        if (++up.n == kTableBatch && (rc = flush())) return rc;
+        if (++up.n == kTableBatch) flush();
     }
-    if ((rc = flush())) return rc;
-    rc = check_hip(hipEventRecord(c->ready, c->copy_stream));
-    if (!rc) rc = check_hip(hipStreamWaitEvent(cs, c->ready, 0));
+    flush();
+    if (!rc) rc = rc_table;
+    if (issued > 0 || !rc) {
+        // the compute stream waits for whatever was enqueued on the copy stream
+        const int rc2 = check_hip(hipEventRecord(c->ready, c->copy_stream));
+        const int rc3 = rc2 ? rc2 : check_hip(hipStreamWaitEvent(cs, c->ready, 0));
+        if (!rc) rc = rc3;
+    }
     if (rc) return rc;
     if (table_out) *table_out = c->d_table + base_key;
     return MOE_OK;
@@ -311,7 +404,7 @@ extern "C" int expert_cache_prefetch(moe_cache *c, int layer, const int32_t *ids
 // device-to-device copies, the rest are dropped; nothing is read from the host.
 // A kept resident keeps its slot index when it is below the new slot count;
 // the others take the lowest free indices, most recent first. Free slots go
-// to the least recently used end in ascending index order.
+// to the least recently used end, the lowest index to be taken first.
 extern "C" int expert_cache_resize(moe_cache *c, void *new_pool, size_t new_pool_bytes,
                                    void *compute_stream, int *moved) {
     if (!c || !new_pool) return MOE_EINVAL;
@@ -395,12 +488,13 @@ extern "C" int expert_cache_resize(moe_cache *c, void *new_pool, size_t new_pool
     c->prev.assign(N2, -1);
     c->next.assign(N2, -1);
     c->last_gen.assign(N2, 0);
+    c->pick_gen.assign(N2, 0);
     c->head = c->tail = -1;
     for (size_t i = 0; i < kept.size(); ++i) {
         c->slot_of[key2[dst[i]]] = dst[i];
         c->push_back(dst[i]);
     }
-    for (int s = 0; s < N2; ++s)
+    for (int s = N2 - 1; s >= 0; --s)
         if (!used[s]) c->push_back(s);
     // table entries of the residents point into the new pool
     TableUpdate up;

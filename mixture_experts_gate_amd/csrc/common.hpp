@@ -40,6 +40,11 @@ inline int check_hip(hipError_t e) {
 }
 
 int ffn_path_option();
+// Expert-cache test knobs (MOE_OPT_CACHE_FAULT, MOE_OPT_CACHE_DELAY_US).
+int cache_set_fault(int n);
+int cache_get_fault();
+int cache_set_delay(int us);
+int cache_get_delay();
 // Weights of the decode kernels' tile split for stage 1 or 2 (MOE_OPT_DEC_SPLIT).
 void dec_split_weights(int stage, float *w_slot, float *w_pos);
 

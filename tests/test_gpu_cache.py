@@ -47,7 +47,7 @@ class LruModel:
     handed out by the same call."""
 
     def __init__(self, nslots, E):
-        self.order = list(range(nslots))
+        self.order = list(reversed(range(nslots)))      # free slots: lowest index taken first
         self.key_of = [-1] * nslots
         self.slot_of = {}
         self.last = [0] * nslots
@@ -86,7 +86,8 @@ class LruModel:
     def resize(self, n2, same_pool):
         """Keep the n2 most recently used residents: a kept slot below n2 stays,
         the others take the lowest free indices (most recent first); free slots
-        follow at the least recently used end in ascending order."""
+        follow at the least recently used end, the lowest index last (taken
+        first)."""
         res = [s for s in self.order if self.key_of[s] >= 0]
         kept, dropped = res[:n2], res[n2:]
         for s in dropped:
@@ -109,7 +110,7 @@ class LruModel:
             key2[d] = self.key_of[s]
         self.key_of = key2
         self.slot_of = {k: d for d, k in enumerate(key2) if k >= 0}
-        self.order = dst + [s for s in range(n2) if not used[s]]
+        self.order = dst + [s for s in reversed(range(n2)) if not used[s]]
         self.last = [0] * n2
         return sum(1 for s, d in zip(kept, dst) if s != d or not same_pool)
 
@@ -395,3 +396,137 @@ def test_resize_errors_leave_the_cache_unchanged(env):
                     assert torch.equal(c.slot_bytes_view(s, nb).cpu(), env["store"].host[l * E + e])
     finally:
         c.close()
+
+
+# ------------------------------------------------------------ fault injection --
+
+def _slots_all(c, env):
+    return [[c.slot_of(l, e) for e in range(E)] for l in range(env["L"])]
+
+
+def test_injected_copy_failure_leaves_cache_unchanged(env):
+    """A copy that fails at the first copy of a call (injected: not issued)
+    returns MOE_EHIP and leaves slots, LRU order and counters as they were;
+    the trace afterwards still matches the brute-force LRU model. A failure
+    at the third copy keeps exactly the two misses copied before it (their
+    bytes arrive), and a retry of the same request completes the layer."""
+    torch, lib = env["torch"], env["lib"]
+    nb = env["lay"].nbytes
+    nslots = 2 * E
+    c = _cache(env, nslots)
+    model = LruModel(nslots, E)
+    try:
+        for l, ids in ((0, None), (1, np.array([2, 9, 4])), (2, np.arange(10))):
+            c.prefetch(l, ids)
+            model.prefetch(l, ids)
+        torch.cuda.synchronize()
+        before, stats = _slots_all(c, env), c.stats()
+        lib.moe_set_option(lib.MOE_OPT_CACHE_FAULT, 1)
+        with pytest.raises(lib.MoeError) as ei:
+            c.prefetch(3, np.array([1, 5, 6]))          # three misses
+        assert ei.value.code == lib.MOE_EHIP
+        lib.moe_set_option(lib.MOE_OPT_CACHE_FAULT, 1)
+        with pytest.raises(lib.MoeError):
+            c.prefetch(2, np.arange(8, 16))             # hits of layer 2 and misses
+        assert lib.moe_get_option(lib.MOE_OPT_CACHE_FAULT) == 0     # the knob fired
+        assert _slots_all(c, env) == before and c.stats() == stats
+        # the failed calls changed nothing the model does not know about
+        rng = np.random.default_rng(3)
+        for step in range(30):
+            layer = int(rng.integers(env["L"]))
+            ids = None if step % 9 == 0 else rng.integers(0, E, size=int(rng.integers(1, 9)))
+            c.prefetch(layer, ids)
+            model.prefetch(layer, ids)
+            assert _slots_all(c, env) == [[model.slot_of.get(l * E + e, -1) for e in range(E)]
+                                          for l in range(env["L"])], step
+            assert c.stats()[:2] == (model.hits, model.misses)
+        # partial failure: the third copy of the call fails
+        c.evict(3, None)
+        model.evict(3, None)
+        h0, m0, _ = c.stats()
+        lib.moe_set_option(lib.MOE_OPT_CACHE_FAULT, 3)
+        with pytest.raises(lib.MoeError) as ei:
+            c.prefetch(3, np.arange(6))
+        assert ei.value.code == lib.MOE_EHIP
+        torch.cuda.synchronize()
+        got = [c.slot_of(3, e) for e in range(6)]
+        assert all(s >= 0 for s in got[:2]) and all(s == -1 for s in got[2:]), got
+        assert c.stats()[:2] == (h0, m0 + 2)
+        for e in range(2):
+            assert torch.equal(c.slot_bytes_view(got[e], nb).cpu(), env["store"].host[3 * E + e])
+        c.prefetch(3, np.arange(6))
+        h1, m1, _ = c.stats()
+        assert (h1, m1) == (h0 + 2, m0 + 6)
+        torch.cuda.synchronize()
+        for e in range(6):
+            s = c.slot_of(3, e)
+            assert torch.equal(c.slot_bytes_view(s, nb).cpu(), env["store"].host[3 * E + e])
+    finally:
+        lib.moe_set_option(lib.MOE_OPT_CACHE_FAULT, 0)
+        c.close()
+
+
+def _stream_stack(env, c, T, passes, seed):
+    """Double-buffered pass over the stack through cache c: layer l+1 is
+    requested right after layer l's FFN is enqueued. Returns [(layer, y)]."""
+    torch = env["torch"]
+    from mixture_experts_gate_amd.layer import MoeLayer
+    rng = np.random.default_rng(seed)
+    Lyr = MoeLayer(H, E, K, I, "mxfp4", T)
+    x = torch.from_numpy(
+        synth.f32_to_bf16_bits(rng.standard_normal((T, H)).astype(np.float32)).view(np.int16)
+    ).cuda()
+    logits = torch.from_numpy(rng.random((T, E), dtype=np.float32)).cuda()
+    Lyr.route_permute(T, logits=logits, write_logits=False)
+    outs = []
+    tab = c.prefetch(0, None)
+    for step in range(passes * env["L"]):
+        l = step % env["L"]
+        Lyr.ffn(T, x, tab)
+        outs.append((l, Lyr.y[:T * K].clone()))
+        tab = c.prefetch((l + 1) % env["L"], None)
+    torch.cuda.synchronize()
+    return outs
+
+
+def test_delayed_copy_stream_is_bitwise(env):
+    """Every prefetch's copies held back 20 ms on the copy stream (a slow
+    link): the compute of each layer still waits for its own copies and never
+    reads a slot being refilled, so the streamed outputs equal the resident
+    ones bit for bit."""
+    torch, lib = env["torch"], env["lib"]
+    from mixture_experts_gate_amd.layer import expert_table
+    lay = env["lay"]
+    T = 256
+    res_tabs = [expert_table(r.data_ptr(), E, lay) for r in env["resident"]]
+    want = _layer_outputs(env, res_tabs, T, seed=19)
+    c = _cache(env, 2 * E)
+    lib.moe_set_option(lib.MOE_OPT_CACHE_DELAY_US, 20000)
+    try:
+        outs = _stream_stack(env, c, T, 2, seed=19)
+    finally:
+        lib.moe_set_option(lib.MOE_OPT_CACHE_DELAY_US, 0)
+        c.close()
+    for l, y in outs:
+        assert torch.equal(y.cpu(), want[l]), l
+
+
+def test_thrash_at_one_layer_capacity_is_bitwise(env):
+    """A pool of exactly one layer of experts: every request of the next layer
+    replaces every slot (each waits for the previous layer's compute), all
+    misses, and the outputs equal the resident ones bit for bit."""
+    torch = env["torch"]
+    from mixture_experts_gate_amd.layer import expert_table
+    lay = env["lay"]
+    T = 64
+    res_tabs = [expert_table(r.data_ptr(), E, lay) for r in env["resident"]]
+    want = _layer_outputs(env, res_tabs, T, seed=23)
+    c = _cache(env, E)
+    try:
+        outs = _stream_stack(env, c, T, 3, seed=23)
+        h, m, _ = c.stats()
+        assert h == 0 and m == (3 * env["L"] + 1) * E
+    finally:
+        c.close()
+    for l, y in outs:
+        assert torch.equal(y.cpu(), want[l]), l
