@@ -61,7 +61,8 @@ def parse():
                     help="short run for profilers: headline workload, no sweep, no CPU leg")
     ap.add_argument("--no-stack", action="store_true", help="skip the 43-layer stack runs")
     ap.add_argument("--only", default="",
-                    help="comma list of sweep parts to run: decode,formats,prefill,cfg4,stack,stream")
+                    help="comma list of sweep parts to run: "
+                         "decode,formats,prefill,cfg4,stack,stream,qstar")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run one plain 512 MiB device copy (HBM counter calibration)")
     ap.add_argument("--no-micro", action="store_true",
@@ -654,6 +655,138 @@ def read_peak_for(micro_res, nbytes):
     return max(r["GBs"] for r in rs if r["bytes"] == size)
 
 
+def calibrate_host_expert(lay, blob_ptrs, H, I, threads=0):
+    """Host expert kernel cost: seconds per expert (its weights decoded) and per
+    token row, from timing one expert at 1 and 8 rows."""
+    import numpy as np
+    from mixture_experts_gate_amd import _lib
+    rng = np.random.default_rng(0)
+    t = {}
+    for n in (1, 8):
+        x = (rng.standard_normal((n, H)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+        y = np.empty_like(x)
+        _lib.moe_cpu_expert_ffn(_lib.MOE_W_MXFP4, *blob_ptrs, H, I, x, y, threads)
+        reps, t0 = 0, time.perf_counter()
+        while time.perf_counter() - t0 < 0.5:
+            _lib.moe_cpu_expert_ffn(_lib.MOE_W_MXFP4, *blob_ptrs, H, I, x, y, threads)
+            reps += 1
+        t[n] = (time.perf_counter() - t0) / reps
+    per_row = max((t[8] - t[1]) / 7.0, 0.0)
+    return t[1] - per_row, per_row
+
+
+def calibrate_host_fixed(torch, dev, H):
+    """The fixed cost of giving the host any expert in a layer: the rows sent
+    back (pinned copy, scatter, synchronisation) and a wake-up of the host
+    kernel's threads, measured with a one-row call at the smallest shapes."""
+    import numpy as np
+    from mixture_experts_gate_amd import _lib
+    src = torch.zeros((1, H), dtype=torch.bfloat16, device=dev)
+    dst = torch.zeros((8, H), dtype=torch.bfloat16, device=dev)
+    idx = torch.zeros(1, dtype=torch.int32, device=dev)
+    pin = torch.zeros((1, H), dtype=torch.int16, pin_memory=True)
+    blob = np.zeros(128 * 128 * 2, dtype=np.uint8)
+    x = np.zeros((1, 128), dtype=np.uint16)
+    y = np.empty_like(x)
+    p = blob.ctypes.data
+
+    def once():
+        _lib.moe_cpu_expert_ffn(_lib.MOE_W_MXFP4, p, p, p, p, 128, 128, x, y, 0)
+        src.view(torch.int16).copy_(pin, non_blocking=True)
+        _lib.moe_scatter_rows(src, idx, 1, H * 2, dst)
+        torch.cuda.synchronize()
+
+    for _ in range(10):
+        once()
+    t0, reps = time.perf_counter(), 0
+    while time.perf_counter() - t0 < 0.2:
+        once()
+        reps += 1
+    return (time.perf_counter() - t0) / reps
+
+
+def run_qstar(torch, st, store, pool_bytes, T=1, warmup=8, steps=24, links=(None, 14.0, 5.0)):
+    """Bandwidth-adaptive placement (q*) on the cached stack: per layer the
+    misses are computed on the host CPU from their pinned blobs while that is
+    cheaper than copying them at the rate the cache measures, against copying
+    every miss (stream only). Links: the native one and slower ones emulated by
+    holding the copy stream (the pages' desktop PCIe 4.0 and x8 laptop links
+    move the ~140 GB pool in about 5 and over 10 seconds)."""
+    from mixture_experts_gate_amd import _lib, synth
+    from mixture_experts_gate_amd.layer import ExpertCache, MoeLayer, expert_table, pack_to_device
+    c, lay, dev = st.cfg, st.lay, st.dev
+    spacked = [pack_to_device(b[None, :], lay, dev) for b in st.shared_blobs]
+    stabs = [expert_table(spacked[l % st.D].data_ptr(), 1, lay, device=dev) for l in range(st.L)]
+    a, b = calibrate_host_expert(lay, store.blob_ptrs(0), c.H, c.I)
+    f = calibrate_host_fixed(torch, dev, c.H)
+    native = h2d_peak(torch, dev)
+    crossover = lay.nbytes / (a + b) / 1e9
+    log(f"host expert kernel: {a*1e3:.2f} ms per expert + {b*1e3:.3f} ms per row, "
+        f"{f*1e3:.3f} ms fixed per layer; a one-row miss is cheaper on the host below "
+        f"{crossover:.1f} GB/s (link {native:.1f} GB/s)")
+    out = {"host_s_fixed": f, "host_s_per_expert": a, "host_s_per_row": b,
+           "crossover_GBs_one_row": crossover,
+           "native_link_GBs": native, "expert_bytes": lay.nbytes, "runs": []}
+    lg = st.logits(torch, T, range(warmup + steps))
+    x0 = torch.from_numpy(synth.activations(c, T).view("int16")).to(dev)
+    for link in links:
+        thr = 0 if link is None else int(1000.0 / (1.0 / link - 1.0 / native))
+        _lib.moe_set_option(_lib.MOE_OPT_CACHE_THROTTLE_MBS, thr)
+        try:
+            for mode in ("stream", "qstar"):
+                cache = ExpertCache(store, st.L, c.E, pool_bytes, device=dev)
+                ly = MoeLayer(c.H, c.E, c.k, c.I, c.fmt, T, shared=True, device=dev)
+                ly.prepare_shared(T)
+                host_experts = [0]
+
+                def step(i):
+                    x = x0
+                    for l in range(st.L):
+                        if mode == "qstar":
+                            o, mask = ly.forward_cached_qstar(T, x, cache, l, logits=lg[i][l],
+                                                              shared_table=stabs[l],
+                                                              host_s_fixed=f,
+                                                              host_s_per_expert=a,
+                                                              host_s_per_row=b)
+                            host_experts[0] += int(mask.sum())
+                        else:
+                            ly.route_permute(T, logits=lg[i][l], write_logits=False)
+                            ids = ly.topk_ids[:T].cpu().numpy().ravel()
+                            tab = cache.prefetch(l, ids)
+                            ysh = ly.ffn_with_shared(T, x, tab, stabs[l])
+                            ly.combine(T, y_shared=ysh)
+                            o = ly.out[:T]
+                        x = o
+
+                for i in range(warmup):
+                    step(i)
+                torch.cuda.synchronize()
+                h0, m0, b0 = cache.stats()
+                host_experts[0] = 0
+                t0 = time.perf_counter()
+                for i in range(warmup, warmup + steps):
+                    step(i)
+                torch.cuda.synchronize()
+                el = time.perf_counter() - t0
+                h1, m1, b1 = cache.stats()
+                gbs, _ = cache.bandwidth()
+                cache.close()
+                r = {"link": "native" if link is None else f"{link:g} GB/s (emulated)",
+                     "mode": mode, "T": T, "steps": steps, "tokens_per_s": T * steps / el,
+                     "ms_per_step": 1000.0 * el / steps, "measured_link_GBs": gbs,
+                     "copied_per_step": (m1 - m0) / steps,
+                     "host_experts_per_step": host_experts[0] / steps,
+                     "hits_per_step": (h1 - h0) / steps}
+                out["runs"].append(r)
+                log(f"q* leg, link {r['link']}, {mode}: {r['tokens_per_s']:.1f} tok/s, "
+                    f"{r['ms_per_step']:.1f} ms/step, copied {r['copied_per_step']:.1f} and "
+                    f"host {r['host_experts_per_step']:.1f} experts per step, measured link "
+                    f"{gbs:.1f} GB/s")
+        finally:
+            _lib.moe_set_option(_lib.MOE_OPT_CACHE_THROTTLE_MBS, 0)
+    return out
+
+
 def cpu_model():
     try:
         with open("/proc/cpuinfo") as f:
@@ -864,7 +997,8 @@ def main():
                 f"layer HBM {r['layer_hbm_frac']*100:.1f}%, {r['layer_tflops']:.1f} TFLOP/s")
         del w4
         torch.cuda.empty_cache()
-    if not args.no_sweep and not args.no_stack and (want("stack") or want("stream")):
+    if not args.no_sweep and not args.no_stack and (want("stack") or want("stream") or
+                                                    want("qstar")):
         c5 = synth.CONFIGS[5]
         log("config 5: generating 2 distinct layers ...")
         st = Stack(torch, c5, dev, distinct=2)
@@ -879,6 +1013,8 @@ def main():
                     (8, 128, 4, 16), (16, 248, 4, 16)]
             sweep["stack43_cache32GB"] = run_stack_cached(torch, st, runs, 32 * 10**9,
                                                           store=store)
+        if want("qstar"):
+            sweep["stack43_qstar"] = run_qstar(torch, st, store, 32 * 10**9)
         del st, store
     cpu = cpu_all = None
     if not args.no_cpu:

@@ -300,9 +300,13 @@ int moe_workspace_size(int T, int k, int H, int I, int E, size_t *permute_bytes,
  *                     returns MOE_EHIP as for a failed hipMemcpyAsync); 0 = off.
  *   MOE_OPT_CACHE_DELAY_US: test knob: every prefetch that copies first holds
  *                     its copy stream this many microseconds (a host function
- *                     that sleeps), as a slow link would; 0 = off. */
+ *                     that sleeps), as a slow link would; 0 = off.
+ *   MOE_OPT_CACHE_THROTTLE_MBS: test knob: every prefetch that copies also
+ *                     holds its copy stream for (bytes it copies) / (value
+ *                     MB/s) before the copies, so the link looks slower (rate
+ *                     1 / (1/value + 1/link)); 0 = off. */
 enum { MOE_OPT_FFN_PATH = 1, MOE_OPT_TIMING = 2, MOE_OPT_DEC_SPLIT = 3, MOE_OPT_CACHE_FAULT = 4,
-       MOE_OPT_CACHE_DELAY_US = 5 };
+       MOE_OPT_CACHE_DELAY_US = 5, MOE_OPT_CACHE_THROTTLE_MBS = 6 };
 int moe_set_option(int option, int value);
 int moe_get_option(int option);
 
@@ -408,6 +412,79 @@ int expert_cache_prefetch(moe_cache *cache, int layer, const int32_t *ids, int n
  */
 int expert_cache_resize(moe_cache *cache, void *new_pool, size_t new_pool_bytes,
                         void *compute_stream, int *moved);
+
+/*
+ * expert_cache_bandwidth -- the host-to-device rate the cache's copies have
+ * actually achieved (the pages' system keeps measuring the bandwidth it really
+ * gets, winzheng.com page, "FreeToken's Three-Layer Mechanism"): an
+ * exponentially weighted mean (weight 1/4 for the newest) of bytes / time over
+ * the copies of completed prefetch calls, each call's copies timed by two
+ * events on the copy stream (waits for free slots and any contention inside
+ * the call count against the rate). *gbs = 0 until a call with copies has
+ * completed; *samples = the calls folded in. Either pointer may be NULL.
+ */
+int expert_cache_bandwidth(moe_cache *cache, double *gbs, long long *samples);
+
+/*
+ * expert_cache_prefetch_qstar -- expert_cache_prefetch with the pages'
+ * bandwidth-adaptive choice of the side that computes each expert (the q*
+ * policy: GPU or host CPU by the bandwidth actually available; winzheng.com
+ * page, "FreeToken's Three-Layer Mechanism"; aimodeling.com/en page, "Three
+ * Engineering Cores").
+ * ids, rows: (host) [n] requested experts of `layer` and the number of token
+ * rows each has (duplicates add up). A resident expert stays on the device.
+ * A missing one costs expert_bytes / rate on the link, or host_s_per_expert
+ * + rows x host_s_per_row (seconds) on the host, plus host_s_fixed once if
+ * the host takes any expert (its inputs read back, its rows sent), and both
+ * sides work at the same time:
+ * misses move to the host, fewest rows first, while the host's summed time
+ * stays within the copy time left to the link. rate: link_gbs if > 0, else
+ * expert_cache_bandwidth's (no expert goes to the host before it is known).
+ * The device experts are then requested as by expert_cache_prefetch (same
+ * results, errors and table); the host experts are not copied.
+ * host_mask: (host) [n_experts] out: 1 for the experts to compute on the host
+ * (with moe_cpu_expert_ffn from their host blobs), else 0; *n_host (may be
+ * NULL) their number. On error host_mask is not written.
+ */
+int expert_cache_prefetch_qstar(moe_cache *cache, int layer, const int32_t *ids,
+                                const int32_t *rows, int n, double host_s_fixed,
+                                double host_s_per_expert, double host_s_per_row, double link_gbs,
+                                void *compute_stream, const moe_expert_w **table_out,
+                                uint8_t *host_mask, int *n_host);
+
+/*
+ * moe_permute_split -- (host arrays) moe_permute's result restricted to the
+ * experts with host_mask[e] == 0, for moe_expert_ffn on the device: their rows
+ * in the same order, the masked experts' counts zero (dev_offsets [E+1],
+ * dev_sorted_pair [offsets[E]]); and the masked experts' pairs in sorted order
+ * (host_pairs [offsets[E]], *n_host of them), for the host kernel and
+ * moe_scatter_rows.
+ */
+int moe_permute_split(const int32_t *offsets, const int32_t *sorted_pair, int E,
+                      const uint8_t *host_mask, int32_t *dev_offsets, int32_t *dev_sorted_pair,
+                      int32_t *host_pairs, int *n_host);
+
+/*
+ * moe_cpu_expert_ffn -- (host) one expert's SwiGLU FFN on the host CPU, for the
+ * experts the bandwidth-adaptive choice leaves on the host:
+ *   y_rows[r] = W2 (silu(W1 x_r) * (W3 x_r)),  r < n,
+ * x_rows [n][H] and y_rows [n][H] bf16 in host memory; the weights in host
+ * memory in the kernel MXFP4 layout (fmt must be MOE_W_MXFP4; w13/s13/w2/s2 as
+ * in moe_expert_w, e.g. a blob of the cache's pinned host store). fp32
+ * accumulation; the activation is rounded to bf16 between the contractions.
+ * threads: host threads (OpenMP; 0 = the default count). Synchronous.
+ */
+int moe_cpu_expert_ffn(int fmt, const void *w13, const uint8_t *s13, const void *w2,
+                       const uint8_t *s2, int H, int I, const uint16_t *x_rows, int n,
+                       uint16_t *y_rows, int threads);
+
+/*
+ * moe_scatter_rows -- dst row idx[r] = src row r for r < n (device arrays;
+ * rows of row_bytes bytes, a multiple of 16; every idx[r] must index a row of
+ * dst): the host-computed expert rows into y at their pairs.
+ */
+int moe_scatter_rows(const void *src, const int32_t *idx, int n, size_t row_bytes, void *dst,
+                     void *stream);
 
 /* expert_cache_evict -- drop experts of `layer` from the cache (NULL ids =
  * the whole layer). Their slots become free for later misses. */

@@ -20,6 +20,7 @@ MOE_OPT_TIMING = 2
 MOE_OPT_DEC_SPLIT = 3
 MOE_OPT_CACHE_FAULT = 4
 MOE_OPT_CACHE_DELAY_US = 5
+MOE_OPT_CACHE_THROTTLE_MBS = 6
 
 # every symbol include/moe.h declares
 EXPORTS = [
@@ -29,7 +30,8 @@ EXPORTS = [
     "moe_timing_query", "moe_pack_mxfp4", "moe_pack_weights", "moe_route_permute",
     "expert_cache_reserve", "expert_cache_prefetch", "expert_cache_evict", "expert_cache_stats",
     "expert_cache_slots", "expert_cache_slot_of", "expert_cache_destroy", "expert_cache_resize",
-    "moe_micro_read", "moe_micro_mfma",
+    "moe_micro_read", "moe_micro_mfma", "expert_cache_bandwidth", "expert_cache_prefetch_qstar",
+    "moe_permute_split", "moe_cpu_expert_ffn", "moe_scatter_rows",
 ]
 
 
@@ -87,6 +89,12 @@ def load(path: str | None = None):
         "expert_cache_destroy": (I, [P]),
         "moe_micro_read": (I, [P, Z, I, P, P]),
         "moe_micro_mfma": (I, [I, I, I, P, C.POINTER(C.c_double), P]),
+        "expert_cache_bandwidth": (I, [P, C.POINTER(C.c_double), C.POINTER(C.c_longlong)]),
+        "expert_cache_prefetch_qstar": (I, [P, I, P, P, I, C.c_double, C.c_double, C.c_double,
+                                            C.c_double, P, C.POINTER(P), P, C.POINTER(I)]),
+        "moe_permute_split": (I, [P, P, I, P, P, P, P, C.POINTER(I)]),
+        "moe_cpu_expert_ffn": (I, [I, P, P, P, P, I, I, P, I, P, I]),
+        "moe_scatter_rows": (I, [P, P, I, Z, P, P]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)
@@ -302,6 +310,63 @@ def expert_cache_resize(cache, new_pool, new_pool_bytes, compute_stream=None):
     _check("expert_cache_resize", load().expert_cache_resize(
         cache, _ptr(new_pool), new_pool_bytes, _stream(compute_stream), C.byref(moved)))
     return moved.value
+
+
+def expert_cache_bandwidth(cache):
+    """(GB/s, samples) of the cache's measured host-to-device rate."""
+    g, n = C.c_double(0.0), C.c_longlong(0)
+    _check("expert_cache_bandwidth", load().expert_cache_bandwidth(cache, C.byref(g), C.byref(n)))
+    return g.value, n.value
+
+
+def expert_cache_prefetch_qstar(cache, layer, ids, rows, host_s_fixed, host_s_per_expert,
+                                host_s_per_row, n_experts, link_gbs=0.0, compute_stream=None):
+    """Returns (device table address, host mask uint8 [n_experts])."""
+    import numpy as np
+    ids = np.ascontiguousarray(ids, dtype=np.int32)
+    rows = np.ascontiguousarray(rows, dtype=np.int32)
+    mask = np.zeros(n_experts, dtype=np.uint8)
+    tab, nh = C.c_void_p(0), C.c_int(0)
+    _check("expert_cache_prefetch_qstar", load().expert_cache_prefetch_qstar(
+        cache, layer, ids.ctypes.data_as(C.c_void_p), rows.ctypes.data_as(C.c_void_p),
+        int(ids.size), float(host_s_fixed), float(host_s_per_expert), float(host_s_per_row),
+        float(link_gbs),
+        _stream(compute_stream),
+        C.byref(tab), mask.ctypes.data_as(C.c_void_p), C.byref(nh)))
+    return tab.value, mask
+
+
+def moe_permute_split(offsets, sorted_pair, host_mask):
+    """Host arrays -> (dev_offsets, dev_sorted_pair, host_pairs) as numpy int32."""
+    import numpy as np
+    off = np.ascontiguousarray(offsets, dtype=np.int32)
+    sp = np.ascontiguousarray(sorted_pair, dtype=np.int32)
+    mask = np.ascontiguousarray(host_mask, dtype=np.uint8)
+    E = off.size - 1
+    n = int(off[-1])
+    d_off = np.empty(E + 1, dtype=np.int32)
+    d_sp = np.empty(max(n, 1), dtype=np.int32)
+    h_p = np.empty(max(n, 1), dtype=np.int32)
+    nh = C.c_int(0)
+    _check("moe_permute_split", load().moe_permute_split(
+        off.ctypes.data_as(C.c_void_p), sp.ctypes.data_as(C.c_void_p), E,
+        mask.ctypes.data_as(C.c_void_p), d_off.ctypes.data_as(C.c_void_p),
+        d_sp.ctypes.data_as(C.c_void_p), h_p.ctypes.data_as(C.c_void_p), C.byref(nh)))
+    return d_off, d_sp[:int(d_off[-1])], h_p[:nh.value]
+
+
+def moe_cpu_expert_ffn(fmt, w13, s13, w2, s2, H, I, x_rows, y_rows, threads=0):
+    """x_rows, y_rows: host numpy uint16 [n][H] (y written in place); weight
+    pointers: host addresses."""
+    n = int(x_rows.shape[0])
+    return _check("moe_cpu_expert_ffn", load().moe_cpu_expert_ffn(
+        fmt, w13, s13, w2, s2, H, I, x_rows.ctypes.data_as(C.c_void_p), n,
+        y_rows.ctypes.data_as(C.c_void_p), threads))
+
+
+def moe_scatter_rows(src, idx, n, row_bytes, dst, stream=None):
+    return _check("moe_scatter_rows", load().moe_scatter_rows(
+        _ptr(src), _ptr(idx), n, row_bytes, _ptr(dst), _stream(stream)))
 
 
 def expert_cache_slots(cache):

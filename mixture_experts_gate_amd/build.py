@@ -28,7 +28,21 @@ FLAGS = [
 ]
 
 
+# host-only sources (the host side of the bandwidth-adaptive placement)
+HOST_SOURCES = ["cpu_expert.cpp"]
+CXX = os.environ.get("CXX_HOST", "g++")
+HOST_FLAGS = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-fopenmp", "-I", INCLUDE]
+
+
 def _compile(src: str) -> str:
+    if src.endswith(".cpp"):
+        obj = os.path.join(OBJDIR, src.replace(".cpp", ".o"))
+        cmd = [CXX, *HOST_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            sys.stderr.write(r.stdout + r.stderr)
+            raise RuntimeError(f"{CXX} failed on {src}")
+        return obj
     obj = os.path.join(OBJDIR, src.replace(".hip", ".o"))
     cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -41,9 +55,9 @@ def _compile(src: str) -> str:
 def build(jobs: int = 8) -> str:
     os.makedirs(OBJDIR, exist_ok=True)
     with ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(_compile, SOURCES))
+        objs = list(ex.map(_compile, SOURCES + HOST_SOURCES))
     tmp = LIB + f".tmp{os.getpid()}"
-    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs]
+    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs, "-lgomp"]
     subprocess.check_call(cmd)
     os.replace(tmp, LIB)
     return LIB

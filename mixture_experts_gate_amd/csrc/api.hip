@@ -45,7 +45,7 @@ static const char *const g_kernel_names[K_COUNT] = {
     "route", "permute_small", "permute_rank", "permute_scan", "permute_scatter", "permute_empty",
     "ffn_decode_gate_up", "ffn_decode_down", "ffn_prefill_gate_up", "ffn_prefill_down",
     "combine", "cache_table", "pack_mxfp4", "route_permute", "ffn_prefill_split",
-    "cache_move", "micro_read", "micro_mfma"};
+    "cache_move", "micro_read", "micro_mfma", "scatter_rows"};
 
 static hipEvent_t pool_event() {
     if (!g_evpool.empty()) {
@@ -149,6 +149,7 @@ extern "C" int moe_set_option(int option, int value) {
     }
     if (option == MOE_OPT_CACHE_FAULT) return cache_set_fault(value);
     if (option == MOE_OPT_CACHE_DELAY_US) return cache_set_delay(value);
+    if (option == MOE_OPT_CACHE_THROTTLE_MBS) return cache_set_throttle(value);
     if (option == MOE_OPT_DEC_SPLIT) {
         if (value == -1) value = kDecSplitDefault;
         // every byte below 128: each weight stays under one half
@@ -176,6 +177,7 @@ extern "C" int moe_get_option(int option) {
     if (option == MOE_OPT_DEC_SPLIT) return g_dec_split.load();
     if (option == MOE_OPT_CACHE_FAULT) return cache_get_fault();
     if (option == MOE_OPT_CACHE_DELAY_US) return cache_get_delay();
+    if (option == MOE_OPT_CACHE_THROTTLE_MBS) return cache_get_throttle();
     return MOE_EINVAL;
 }
 

@@ -36,6 +36,7 @@ namespace moe {
 // (a host function that sleeps).
 static std::atomic<long long> g_fault_at{0};     // remaining copies before the fault, 0 = off
 static std::atomic<int> g_delay_us{0};
+static std::atomic<int> g_throttle_mbs{0};       // MOE_OPT_CACHE_THROTTLE_MBS, 0 = off
 
 int cache_set_fault(int n) {
     if (n < 0) return MOE_EINVAL;
@@ -49,6 +50,12 @@ int cache_set_delay(int us) {
     return MOE_OK;
 }
 int cache_get_delay() { return g_delay_us.load(); }
+int cache_set_throttle(int mbs) {
+    if (mbs < 0) return MOE_EINVAL;
+    g_throttle_mbs.store(mbs);
+    return MOE_OK;
+}
+int cache_get_throttle() { return g_throttle_mbs.load(); }
 
 // True if this copy is the one the fault knob designates (counts it down).
 static bool copy_fault_now() {
@@ -145,6 +152,41 @@ struct moe_cache {
     std::vector<hipEvent_t> spare_ev;
 
     long long hits = 0, misses = 0, h2d_bytes = 0;
+
+    // Live host-to-device rate: timing events around each call's copies,
+    // folded into an exponentially weighted mean once they have completed.
+    struct Timed {
+        hipEvent_t a, b;
+        double bytes;
+    };
+    std::deque<Timed> timed;
+    std::vector<hipEvent_t> spare_timing_ev;
+    double bw_gbs = 0.0;
+    long long bw_samples = 0;
+    hipEvent_t timing_event() {
+        if (!spare_timing_ev.empty()) {
+            hipEvent_t e = spare_timing_ev.back();
+            spare_timing_ev.pop_back();
+            return e;
+        }
+        hipEvent_t e = nullptr;
+        if (hipEventCreate(&e) != hipSuccess) return nullptr;
+        return e;
+    }
+    void retire_timing() {
+        while (!timed.empty() && hipEventQuery(timed.front().b) == hipSuccess) {
+            const Timed t = timed.front();
+            timed.pop_front();
+            float ms = 0.0f;
+            if (hipEventElapsedTime(&ms, t.a, t.b) == hipSuccess && ms > 0.0f) {
+                const double r = t.bytes / (ms * 1e-3) / 1e9;
+                bw_gbs = bw_samples ? 0.75 * bw_gbs + 0.25 * r : r;
+                ++bw_samples;
+            }
+            spare_timing_ev.push_back(t.a);
+            spare_timing_ev.push_back(t.b);
+        }
+    }
 
     void unlink(int s) {
         if (prev[s] >= 0) next[prev[s]] = next[s]; else head = next[s];
@@ -299,10 +341,25 @@ extern "C" int expert_cache_prefetch(moe_cache *c, int layer, const int32_t *ids
     // flight), the rest of the call is not, so a failure at the first copy
     // leaves the cache, its table and its counters as they were.
     size_t issued = 0;
-    if (!miss.empty() && g_delay_us.load() > 0) {
-        rc = check_hip(hipLaunchHostFunc(c->copy_stream, sleep_host_fn,
-                                         (void *)(uintptr_t)g_delay_us.load()));
-        if (rc) return rc;
+    c->retire_timing();
+    hipEvent_t t_a = nullptr, t_b = nullptr;
+    if (!miss.empty()) {
+        t_a = c->timing_event();
+        t_b = c->timing_event();
+        if (t_a && t_b && hipEventRecord(t_a, c->copy_stream) != hipSuccess) {
+            c->spare_timing_ev.push_back(t_a);
+            c->spare_timing_ev.push_back(t_b);
+            t_a = t_b = nullptr;
+        }
+        // test knobs: a fixed hold, or a hold that makes the link look slower
+        long long hold_us = g_delay_us.load();
+        const int thr = g_throttle_mbs.load();
+        if (thr > 0) hold_us += (long long)((double)miss.size() * c->expert_bytes / thr);
+        if (hold_us > 0) {
+            rc = check_hip(hipLaunchHostFunc(c->copy_stream, sleep_host_fn,
+                                             (void *)(uintptr_t)hold_us));
+            if (rc) return rc;
+        }
     }
     // A victim's readers are covered by the entry event of generation
     // last_gen + 1; the copy stream waits for it before the copy. A wait
@@ -386,6 +443,14 @@ extern "C" int expert_cache_prefetch(moe_cache *c, int layer, const int32_t *ids
     }
     flush();
     if (!rc) rc = rc_table;
+    if (t_a && t_b) {
+        if (issued > 0 && hipEventRecord(t_b, c->copy_stream) == hipSuccess) {
+            c->timed.push_back({t_a, t_b, (double)issued * (double)c->expert_bytes});
+        } else {
+            c->spare_timing_ev.push_back(t_a);
+            c->spare_timing_ev.push_back(t_b);
+        }
+    }
     if (issued > 0 || !rc) {
         // the compute stream waits for whatever was enqueued on the copy stream
         const int rc2 = check_hip(hipEventRecord(c->ready, c->copy_stream));
@@ -558,6 +623,9 @@ extern "C" int expert_cache_destroy(moe_cache *c) {
     int rc = check_hip(hipStreamSynchronize(c->copy_stream));
     for (hipEvent_t e : c->entry_ev) (void)hipEventSynchronize(e), (void)hipEventDestroy(e);
     for (hipEvent_t e : c->spare_ev) (void)hipEventDestroy(e);
+    for (auto &t : c->timed) (void)hipEventSynchronize(t.b), (void)hipEventDestroy(t.a),
+                                   (void)hipEventDestroy(t.b);
+    for (hipEvent_t e : c->spare_timing_ev) (void)hipEventDestroy(e);
     if (c->ready) (void)hipEventDestroy(c->ready);
     if (c->d_table) {
         const int rc2 = check_hip(hipFree(c->d_table));
@@ -565,4 +633,74 @@ extern "C" int expert_cache_destroy(moe_cache *c) {
     }
     delete c;
     return rc;
+}
+
+extern "C" int expert_cache_bandwidth(moe_cache *c, double *gbs, long long *samples) {
+    if (!c) return MOE_EINVAL;
+    c->retire_timing();
+    if (gbs) *gbs = c->bw_gbs;
+    if (samples) *samples = c->bw_samples;
+    return MOE_OK;
+}
+
+// Bandwidth-adaptive placement (the pages' q* policy: the system keeps
+// measuring the bandwidth it actually gets and decides per expert whether the
+// GPU or the host CPU computes it; winzheng.com page, "FreeToken's Three-Layer
+// Mechanism"; aimodeling.com/en page, "Three Engineering Cores"). A resident
+// expert always stays on the GPU. A missing one costs expert_bytes / rate on
+// the link, or host_s_per_expert + rows x host_s_per_row on the host (decoding
+// its weights, then its rows), plus host_s_fixed once for using the host at
+// all (reading the inputs back, sending the rows), and the two sides work at
+// the same time; so misses move to the host, fewest rows first, while the
+// host's summed time stays within the copy time still left to the link.
+extern "C" int expert_cache_prefetch_qstar(moe_cache *c, int layer, const int32_t *ids,
+                                           const int32_t *rows, int n, double host_s_fixed,
+                                           double host_s_per_expert, double host_s_per_row,
+                                           double link_gbs, void *compute_stream,
+                                           const moe_expert_w **table_out, uint8_t *host_mask,
+                                           int *n_host) {
+    if (!c || layer < 0 || layer >= c->L || !ids || !rows || n < 0 || !host_mask ||
+        host_s_fixed < 0.0 || host_s_per_row < 0.0 || host_s_per_expert < 0.0)
+        return MOE_EINVAL;
+    const int E = c->E;
+    std::vector<long long> want_rows(E, 0);
+    std::vector<char> wanted(E, 0);
+    for (int i = 0; i < n; ++i) {
+        if (ids[i] < 0 || ids[i] >= E || rows[i] < 0) return MOE_EINVAL;
+        want_rows[ids[i]] += rows[i];
+        wanted[ids[i]] = 1;
+    }
+    c->retire_timing();
+    const double gbs = link_gbs > 0.0 ? link_gbs : c->bw_gbs;
+    const long base_key = (long)layer * E;
+    std::vector<int> host;
+    if (gbs > 0.0) {
+        std::vector<int> miss;
+        for (int e = 0; e < E; ++e)
+            if (wanted[e] && c->slot_of[base_key + e] < 0) miss.push_back(e);
+        std::stable_sort(miss.begin(), miss.end(),
+                         [&](int a, int b) { return want_rows[a] < want_rows[b]; });
+        // moving one more miss leaves (misses - moved - 1) copies to the link
+        const double t_copy = (double)c->expert_bytes / (gbs * 1e9);
+        double host_t = host_s_fixed;     // paid once if any expert goes to the host
+        for (int e : miss) {
+            const double h = host_t + host_s_per_expert + (double)want_rows[e] * host_s_per_row;
+            if (h > t_copy * (double)(miss.size() - host.size() - 1)) break;
+            host_t = h;
+            host.push_back(e);
+        }
+    }
+    std::vector<int32_t> dev_ids(1, 0);    // (never empty: a NULL list means every expert)
+    dev_ids.clear();
+    std::vector<char> on_host(E, 0);
+    for (int e : host) on_host[e] = 1;
+    for (int e = 0; e < E; ++e)
+        if (wanted[e] && !on_host[e]) dev_ids.push_back(e);
+    const int32_t none = 0;
+    const int rc = expert_cache_prefetch(c, layer, dev_ids.empty() ? &none : dev_ids.data(),
+                                         (int)dev_ids.size(), compute_stream, table_out);
+    if (rc) return rc;
+    for (int e = 0; e < E; ++e) host_mask[e] = (uint8_t)on_host[e];
+    if (n_host) *n_host = (int)host.size();
+    return MOE_OK;
 }

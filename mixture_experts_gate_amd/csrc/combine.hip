@@ -88,9 +88,31 @@ static void launch_combine(dim3 grid, hipStream_t s, const void *y, const float 
 #undef MOE_CB
 }
 
+// dst row idx[r] = src row r, rows of row_bytes bytes (a multiple of 16): one
+// workgroup per row.
+__global__ __launch_bounds__(256) void scatter_rows_kernel(const u32x4 *__restrict__ src,
+                                                           const int32_t *__restrict__ idx,
+                                                           size_t row16, u32x4 *__restrict__ dst) {
+    const int r = blockIdx.x;
+    const size_t to = (size_t)idx[r];
+    for (size_t i = threadIdx.x; i < row16; i += blockDim.x)
+        dst[to * row16 + i] = src[(size_t)r * row16 + i];
+}
+
 }  // namespace moe
 
 using namespace moe;
+
+extern "C" int moe_scatter_rows(const void *src, const int32_t *idx, int n, size_t row_bytes,
+                                void *dst, void *stream) {
+    if (n < 0 || row_bytes == 0 || row_bytes % 16) return MOE_EINVAL;
+    if (n == 0) return MOE_OK;
+    if (!src || !idx || !dst) return MOE_EINVAL;
+    MOE_LAUNCH(K_SCATTER, scatter_rows_kernel, dim3((unsigned)n), dim3(256), 0,
+               (hipStream_t)stream, reinterpret_cast<const u32x4 *>(src), idx, row_bytes / 16,
+               reinterpret_cast<u32x4 *>(dst));
+    return check_launch();
+}
 
 extern "C" int moe_combine(const void *y, int y_is_fp32, const float *topk_w, const void *y_shared,
                            int T, int k, int H, uint16_t *out_bf16, void *stream) {

@@ -45,6 +45,8 @@ int cache_set_fault(int n);
 int cache_get_fault();
 int cache_set_delay(int us);
 int cache_get_delay();
+int cache_set_throttle(int mbs);
+int cache_get_throttle();
 // Weights of the decode kernels' tile split for stage 1 or 2 (MOE_OPT_DEC_SPLIT).
 void dec_split_weights(int stage, float *w_slot, float *w_pos);
 
@@ -52,7 +54,7 @@ void dec_split_weights(int stage, float *w_slot, float *w_pos);
 enum KernelId {
     K_ROUTE = 0, K_PERM_SMALL, K_PERM_RANK, K_PERM_SCAN, K_PERM_SCATTER, K_PERM_EMPTY,
     K_DEC_GATE_UP, K_DEC_DOWN, K_PRE_GATE_UP, K_PRE_DOWN, K_COMBINE, K_CACHE_TABLE, K_PACK, K_ROUTE_PERMUTE, K_PRE_SPLIT,
-    K_CACHE_MOVE, K_MICRO_READ, K_MICRO_MFMA, K_COUNT
+    K_CACHE_MOVE, K_MICRO_READ, K_MICRO_MFMA, K_SCATTER, K_COUNT
 };
 
 bool timing_enabled();

@@ -121,10 +121,11 @@ class MoeLayer:
         _lib.moe_permute(self.topk_ids, T, self.k, self.E, self.offsets, self.sorted_pair,
                          self.pair_row, self.ws_perm, self.ws_perm_bytes, stream)
 
-    def ffn(self, T, x, table, stream=None):
-        _lib.moe_expert_ffn(x, self.sorted_pair, self.offsets, table, self.fmt, T, self.k, self.H,
-                            self.I, self.E, self.y, self.y_fp32, self.ws_ffn, self.ws_ffn_bytes,
-                            stream)
+    def ffn(self, T, x, table, stream=None, perm=None):
+        """perm: (sorted_pair, offsets) to use instead of the layer's own."""
+        sp, off = perm if perm is not None else (self.sorted_pair, self.offsets)
+        _lib.moe_expert_ffn(x, sp, off, table, self.fmt, T, self.k, self.H, self.I, self.E, self.y,
+                            self.y_fp32, self.ws_ffn, self.ws_ffn_bytes, stream)
 
     def combine(self, T, with_shared=False, stream=None, y_shared=None):
         """y_shared: the shared expert's rows (from ffn_with_shared); with_shared
@@ -161,7 +162,7 @@ class MoeLayer:
         self.combine(T, stream=stream, y_shared=ysh)
         return self.out[:T]
 
-    def ffn_with_shared(self, T, x, table, shared_table, stream=None, fuse=True):
+    def ffn_with_shared(self, T, x, table, shared_table, stream=None, fuse=True, perm=None):
         """Routed and shared expert FFN; returns the shared expert's output rows
         [T][H] for the combine. With fuse, where the weight-streaming kernels
         run, the shared expert is one more expert of the routed launches (its
@@ -170,8 +171,9 @@ class MoeLayer:
         if not self.shared:
             raise ValueError("layer was built without shared-expert buffers")
         n = T * self.k
+        sp, off = perm if perm is not None else (self.sorted_pair, self.offsets)
         if fuse:
-            rc = _lib.moe_expert_ffn_shared(x, self.sorted_pair, self.offsets, table, shared_table,
+            rc = _lib.moe_expert_ffn_shared(x, sp, off, table, shared_table,
                                             self.fmt, T, self.k, self.H, self.I, self.E, self.y,
                                             self.y_fp32, self.ws_ffn, self.ws_ffn_bytes, stream,
                                             check=False)
@@ -188,9 +190,97 @@ class MoeLayer:
         self._side.wait_event(self._fork)
         self.shared_ffn(T, x, shared_table, self._side)
         self._join.record(self._side)
-        self.ffn(T, x, table, stream)
+        self.ffn(T, x, table, stream, perm=perm)
         main.wait_event(self._join)
         return self.y_sh[:T]
+
+    def forward_cached_qstar(self, T, x, cache, layer, logits=None, wg=None, shared_table=None,
+                             host_s_fixed=0.0, host_s_per_expert=0.0, host_s_per_row=0.0,
+                             link_gbs=0.0, threads=0, stream=None):
+        """One layer through an expert cache with the bandwidth-adaptive choice
+        of the side that computes each missing expert: route and permute on the
+        device and read the permutation back; request the experts (a miss goes
+        to the host while the host's time stays within the copy time it saves,
+        expert_cache_prefetch_qstar); the device FFN over the permutation
+        without the host experts (moe_permute_split); the host experts' rows on
+        the host CPU from their pinned blobs (moe_cpu_expert_ffn) while the
+        device works, copied into y (moe_scatter_rows); then the combine.
+        Returns (out[:T], host_mask). Requires bf16 y and MXFP4 experts."""
+        if self.y_fp32 or self.fmt != _lib.MOE_W_MXFP4:
+            raise ValueError("the host expert path needs bf16 y and MXFP4 experts")
+        main = stream if stream is not None else torch.cuda.current_stream()
+        self.route_permute(T, x=x, wg=wg, logits=logits, stream=main, write_logits=logits is None)
+        n = T * self.k
+        # read back (one synchronisation) before the request below makes the
+        # stream wait for copies
+        if not hasattr(self, "_rb_off"):
+            self._rb_off = torch.empty(self.E + 1, dtype=torch.int32, pin_memory=True)
+            self._rb_sp = torch.empty(max(self.T_max * self.k, 1), dtype=torch.int32,
+                                      pin_memory=True)
+            self._rb_x = torch.empty((self.T_max, self.H), dtype=torch.int16, pin_memory=True)
+        with torch.cuda.stream(main):
+            self._rb_off.copy_(self.offsets, non_blocking=True)
+            self._rb_sp[:n].copy_(self.sorted_pair[:n], non_blocking=True)
+            self._rb_x[:T].copy_(x[:T].view(torch.int16), non_blocking=True)
+        main.synchronize()
+        off = self._rb_off.numpy().copy()
+        sp = self._rb_sp[:n].numpy().copy()
+        x_host = self._rb_x[:T].numpy().view(np.uint16).copy()
+        cnt = np.diff(off)
+        ids = np.nonzero(cnt)[0].astype(np.int32)
+        tab, mask = _lib.expert_cache_prefetch_qstar(cache.handle, layer, ids, cnt[ids],
+                                                     host_s_fixed, host_s_per_expert,
+                                                     host_s_per_row, self.E, link_gbs, main)
+        d_off, d_sp, h_pairs = _lib.moe_permute_split(off, sp, mask)
+        perm = None
+        if len(h_pairs):
+            if not hasattr(self, "_q_off"):
+                nn = max(self.T_max * self.k, 1)
+                dev = self.y.device
+                self._q_off = torch.empty(self.E + 1, dtype=torch.int32, device=dev)
+                self._q_sp = torch.empty(nn, dtype=torch.int32, device=dev)
+                self._q_idx = torch.empty(nn, dtype=torch.int32, device=dev)
+                self._q_rows = torch.empty((nn, self.H), dtype=torch.bfloat16, device=dev)
+                self._q_host = torch.empty((nn, self.H), dtype=torch.int16, pin_memory=True)
+                # pinned staging of [offsets | sorted pairs | host pairs]
+                self._q_stage = torch.empty(self.E + 1 + 2 * nn, dtype=torch.int32,
+                                            pin_memory=True)
+            # (the read-backs above waited for this layer's earlier copies, so
+            # the pinned buffers are free to refill)
+            st = self._q_stage.numpy()
+            E1, nd, nh = self.E + 1, len(d_sp), len(h_pairs)
+            st[:E1] = d_off
+            st[E1:E1 + nd] = d_sp
+            st[E1 + nd:E1 + nd + nh] = h_pairs
+            with torch.cuda.stream(main):
+                self._q_off.copy_(self._q_stage[:E1], non_blocking=True)
+                if nd:
+                    self._q_sp[:nd].copy_(self._q_stage[E1:E1 + nd], non_blocking=True)
+                self._q_idx[:nh].copy_(self._q_stage[E1 + nd:E1 + nd + nh], non_blocking=True)
+            perm = (self._q_sp, self._q_off)
+        if shared_table is not None:
+            ysh = self.ffn_with_shared(T, x, tab, shared_table, main, perm=perm)
+        else:
+            ysh = None
+            self.ffn(T, x, tab, main, perm=perm)
+        if len(h_pairs):
+            # the host experts, while the device runs its share
+            hy = self._q_host[:len(h_pairs)].numpy().view(np.uint16)
+            row = 0
+            for e in np.nonzero(mask)[0]:
+                pairs = sp[off[e]:off[e + 1]]
+                xr = np.ascontiguousarray(x_host[pairs // self.k])
+                yr = np.empty_like(xr)
+                _lib.moe_cpu_expert_ffn(self.fmt, *cache.store.blob_ptrs(cache.key_source(layer, e)),
+                                        self.H, self.I, xr, yr, threads)
+                hy[row:row + len(pairs)] = yr
+                row += len(pairs)
+            with torch.cuda.stream(main):
+                self._q_rows[:len(h_pairs)].view(torch.int16).copy_(self._q_host[:len(h_pairs)],
+                                                                    non_blocking=True)
+            _lib.moe_scatter_rows(self._q_rows, self._q_idx, len(h_pairs), self.H * 2, self.y, main)
+        self.combine(T, stream=main, y_shared=ysh)
+        return self.out[:T], mask
 
     def prepare_shared(self, T):
         """Write the shared expert's offsets {0, T} (outside any timed or captured region)."""
@@ -234,6 +324,11 @@ class HostExperts:
     def address(self, stored: int) -> int:
         return self.host.data_ptr() + stored * self.layout.nbytes
 
+    def blob_ptrs(self, stored: int):
+        """Host addresses (w13, s13, w2, s2) of a stored blob."""
+        b, lay = int(self.address(int(stored))), self.layout
+        return b + lay.w13, b + lay.s13, b + lay.w2, b + lay.s2
+
     def sources(self, n_layers: int, n_experts: int):
         """Host address of each key's blob, [n_layers * n_experts]."""
         out = []
@@ -260,6 +355,7 @@ class ExpertCache:
         self.slot_bytes = slot
         self.copy_stream = copy_stream if copy_stream is not None else torch.cuda.Stream(device)
         self.store = store
+        self.n_experts = n_experts
         self.srcs = store.sources(n_layers, n_experts)
         self.handle = _lib.expert_cache_reserve(self.pool, self.pool.numel(), lay.nbytes, n_layers,
                                                 n_experts, self.srcs, lay,
@@ -267,6 +363,15 @@ class ExpertCache:
 
     def prefetch(self, layer, ids=None, compute_stream=None):
         return _lib.expert_cache_prefetch(self.handle, layer, ids, compute_stream)
+
+    def key_source(self, layer, expert):
+        """Index of the stored blob behind key (layer, expert)."""
+        E = self.n_experts
+        return layer * E + expert if self.store.alias is None else self.store.alias(layer, expert)
+
+    def bandwidth(self):
+        """(GB/s, samples): the host-to-device rate the cache's copies achieved."""
+        return _lib.expert_cache_bandwidth(self.handle)
 
     def evict(self, layer, ids=None):
         return _lib.expert_cache_evict(self.handle, layer, ids)

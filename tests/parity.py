@@ -48,3 +48,26 @@ def to_dev(a: np.ndarray, dev="cuda"):
 
 def bf16_dev_to_f64(t) -> np.ndarray:
     return t.float().cpu().numpy().astype(np.float64)
+
+
+def kernel_layout_mxfp4(blobs, lay):
+    """Interchange MXFP4 blobs [n][nbytes] -> the kernel layout the library's
+    header states (16-row x 128-column blocks, lane l = row l % 16, columns
+    32 (l / 16) .. + 31), re-derived here with numpy for the host-side tests."""
+    def tiled(codes, scales, R, K):
+        nslab = K // 128
+        c = codes.reshape(R // 16, 16, nslab, 4, 16)           # rb, row, s, cb, byte
+        oc = c.transpose(0, 2, 3, 1, 4).reshape(-1)            # rb, s, lane=(cb,row), byte
+        sc = scales.reshape(R // 16, 16, nslab, 4).transpose(0, 2, 3, 1).reshape(-1)
+        return oc, sc
+
+    blobs = np.atleast_2d(blobs)
+    out = np.empty_like(blobs)
+    H, I = lay.H, lay.I
+    for e in range(blobs.shape[0]):
+        b = blobs[e]
+        c13, s13 = tiled(b[lay.w13:lay.s13], b[lay.s13:lay.w2], 2 * I, H)
+        c2, s2 = tiled(b[lay.w2:lay.s2], b[lay.s2:lay.nbytes], H, I)
+        out[e, lay.w13:lay.s13], out[e, lay.s13:lay.w2] = c13, s13
+        out[e, lay.w2:lay.s2], out[e, lay.s2:lay.nbytes] = c2, s2
+    return out

@@ -530,3 +530,82 @@ def test_thrash_at_one_layer_capacity_is_bitwise(env):
         c.close()
     for l, y in outs:
         assert torch.equal(y.cpu(), want[l]), l
+
+
+# ------------------------------------------------- bandwidth-adaptive choice --
+
+def test_bandwidth_is_measured(env):
+    """The cache's rate comes from events around its copies: positive after a
+    completed copy, and close to the forced rate when the link is throttled."""
+    torch, lib = env["torch"], env["lib"]
+    c = _cache(env, 2 * E)
+    try:
+        assert c.bandwidth() == (0.0, 0)
+        c.prefetch(0, None)
+        torch.cuda.synchronize()
+        g, n = c.bandwidth()
+        assert n == 1 and g > 0.2, (g, n)
+    finally:
+        c.close()
+    c = _cache(env, 2 * E)
+    lib.moe_set_option(lib.MOE_OPT_CACHE_THROTTLE_MBS, 200)
+    try:
+        c.prefetch(1, None)
+        torch.cuda.synchronize()
+        g, n = c.bandwidth()
+        assert n == 1 and 0.05 < g < 0.21, g          # 1 / (1/0.2 + 1/link) GB/s
+    finally:
+        lib.moe_set_option(lib.MOE_OPT_CACHE_THROTTLE_MBS, 0)
+        c.close()
+
+
+@pytest.mark.parametrize("mode", ["host", "device", "mixed"])
+def test_qstar_layer_matches_oracle(env, orc, mode):
+    """A layer through the cache with the bandwidth-adaptive choice. "host":
+    free host time, every miss is computed on the host CPU; "device": costly
+    host time, every miss is copied; "mixed": host time close to the copy time,
+    some of each. Routing and the layer output against the oracle; the host
+    experts' rows against the oracle's rows; with no host expert, the output
+    equals the resident layer's bit for bit."""
+    torch = env["torch"]
+    from mixture_experts_gate_amd.layer import MoeLayer, expert_table
+    from parity import assert_close, bf16_dev_to_f64
+    lay = env["lay"]
+    T, l = 12, 2
+    rng = np.random.default_rng(7)
+    x_bits = synth.f32_to_bf16_bits(rng.standard_normal((T, H)).astype(np.float32))
+    lg = rng.random((T, E), dtype=np.float32)
+    x = torch.from_numpy(x_bits.view(np.int16)).cuda().view(torch.bfloat16)
+    lgd = torch.from_numpy(lg).cuda()
+    costs = {"host": (0.0, 0.0, 1.0), "device": (1.0, 1.0, 1e6), "mixed": (90e-6, 0.0, 1.0)}[mode]
+    c = _cache(env, 2 * E)
+    Lq = MoeLayer(H, E, K, I, "mxfp4", T)
+    try:
+        out, mask = Lq.forward_cached_qstar(T, x, c, l, logits=lgd, host_s_per_expert=costs[0],
+                                            host_s_per_row=costs[1], link_gbs=costs[2], threads=4)
+        torch.cuda.synchronize()
+        used = np.unique(Lq.topk_ids[:T].cpu().numpy())
+        nh = int(mask.sum())
+        if mode == "host":
+            assert nh == len(used)
+        elif mode == "device":
+            assert nh == 0
+        else:
+            assert 0 < nh < len(used), nh
+        for e in range(E):
+            assert (c.slot_of(l, e) >= 0) == (e in used and not mask[e]), e
+        ref = orc.moe_layer(x_bits, lay, env["blobs"][l], K, logits=lg)
+        assert np.array_equal(Lq.topk_ids[:T].cpu().numpy(), ref["ids"])
+        assert_close(bf16_dev_to_f64(out), ref["out_f64"], f"q* layer output ({mode})")
+        y = Lq.y[:T * K].float().cpu().numpy().astype(np.float64)
+        pairs = np.nonzero(mask[ref["ids"].ravel()])[0]
+        if len(pairs):
+            assert_close(y[pairs], ref["y"][pairs], f"host expert rows ({mode})")
+        if nh == 0:
+            res = expert_table(env["resident"][l].data_ptr(), E, lay)
+            Lr = MoeLayer(H, E, K, I, "mxfp4", T)
+            out_r = Lr.forward(T, x, res, logits=lgd)
+            torch.cuda.synchronize()
+            assert torch.equal(out, out_r)
+    finally:
+        c.close()
