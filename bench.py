@@ -198,11 +198,15 @@ def time_graphs(torch, wl, steps, warmup):
 
 
 def kernel_timing(torch, wl, steps):
+    """Average dispatch time of each kernel over `steps` eager steps, each step
+    run on an idle device (synchronised after it), so that no dispatch's window
+    also covers queued work from another step."""
     from mixture_experts_gate_amd import _lib
+    torch.cuda.synchronize()
     _lib.moe_set_option(_lib.MOE_OPT_TIMING, 1)
     for i in range(steps):
         wl.step(i)
-    torch.cuda.synchronize()
+        torch.cuda.synchronize()
     rep = _lib.timing_report()
     _lib.moe_set_option(_lib.MOE_OPT_TIMING, 0)
     return {k: {"launches": n, "avg_us": 1000.0 * ms / n} for k, (n, ms) in rep.items()}
@@ -918,19 +922,11 @@ def main():
     only = set(args.only.split(",")) if args.only else None
     want = lambda name: only is None or name in only
 
-    micro_res = None
-    if not args.no_micro and not args.profile:
-        log("reference measurements: read stream, matrix cores")
-        micro_res = micro(torch, dev)
     c2 = synth.CONFIGS[2]
     sweep = {}
     log(f"headline: decode layer T={args.T}, {args.steps} steps, {args.warmup} warm-up")
     wl, head = run_workload(torch, c2, args.T, args.steps, args.warmup, dev)
     dom, roof = roofline(head, args.T)
-    if roof.get("achieved") and micro_res:
-        peak = read_peak_for(micro_res, roof["algorithmic_bytes_per_launch"])
-        roof["measured_read_stream_GBs"] = peak
-        roof["frac_of_measured_read_stream"] = roof["achieved"] / peak
     log(f"T={args.T}: {head['tokens_per_s']:.0f} tok/s, {head['ms_per_step']*1000:.1f} us/step, "
         f"layer HBM {head['layer_hbm_frac']*100:.1f}%")
     if not args.no_sweep and want("decode"):
@@ -1016,6 +1012,14 @@ def main():
         if want("qstar"):
             sweep["stack43_qstar"] = run_qstar(torch, st, store, 32 * 10**9)
         del st, store
+    micro_res = None
+    if not args.no_micro and not args.profile:
+        log("reference measurements: read stream, matrix cores")
+        micro_res = micro(torch, dev)
+        if roof.get("achieved"):
+            peak = read_peak_for(micro_res, roof["algorithmic_bytes_per_launch"])
+            roof["measured_read_stream_GBs"] = peak
+            roof["frac_of_measured_read_stream"] = roof["achieved"] / peak
     cpu = cpu_all = None
     if not args.no_cpu:
         log("CPU oracle baseline ...")

@@ -198,23 +198,21 @@ int moe_expert_ffn(const uint16_t *x_bf16, const int32_t *sorted_pair, const int
 
 /*
  * moe_expert_ffn_shared -- moe_expert_ffn for the routed experts together with
- * the always-on shared expert, in the same launches: the shared expert enters
- * as more experts of the launch, its T tokens in blocks of 16 when no routed
- * expert has more than 16 rows (every block reads the shared weights; blocks
- * run close together, so the repeats mostly hit the caches), else as one.
+ * the always-on shared expert, in the same launches (a separate shared-expert
+ * launch does not overlap a routed one that fills the device):
  *   y[p] for p < T*k as moe_expert_ffn; y[T*k + t] = W2_s (silu(W1_s x_t) *
  *   (W3_s x_t)) with the shared expert's weights `shared` (device pointer to
  *   one moe_expert_w, same format and sizes as the routed experts).
+ * Weight-streaming kernels: the shared expert enters as more experts of the
+ * launch, its T tokens in blocks of 16 when no routed expert has more than 16
+ * rows (every block reads the shared weights; blocks run close together, so
+ * the repeats mostly hit the caches), else as one. Tiled kernels: it is
+ * expert E of the token-tile map, its rows the tokens in order.
  * y: [T*k + T][H], bf16 (y_is_fp32 = 0) or fp32; moe_combine takes rows T*k ..
- * as its y_shared. Numerics as moe_expert_ffn's weight-streaming kernels.
+ * as its y_shared. Numerics as moe_expert_ffn's (on the path it chooses).
  * ws: device workspace of at least the ffn size from moe_workspace_size(T,
  * k + 1, H, I, E) (the activation holds the shared expert's rows too).
- * Runs where moe_expert_ffn would choose the weight-streaming kernels (small
- * batches, where a separate shared-expert launch leaves compute units idle
- * behind the routed one). Where it would choose the tiled kernels (or
- * MOE_OPT_FFN_PATH forces them) it returns MOE_EUNSUPPORTED before any device
- * work; the caller then makes the shared expert its own moe_expert_ffn call.
- * Other errors as moe_expert_ffn (shared == NULL is MOE_EINVAL).
+ * Errors as moe_expert_ffn (shared == NULL is MOE_EINVAL).
  */
 int moe_expert_ffn_shared(const uint16_t *x_bf16, const int32_t *sorted_pair,
                           const int32_t *offsets, const moe_expert_w *experts,
@@ -304,9 +302,14 @@ int moe_workspace_size(int T, int k, int H, int I, int E, size_t *permute_bytes,
  *   MOE_OPT_CACHE_THROTTLE_MBS: test knob: every prefetch that copies also
  *                     holds its copy stream for (bytes it copies) / (value
  *                     MB/s) before the copies, so the link looks slower (rate
- *                     1 / (1/value + 1/link)); 0 = off. */
+ *                     1 / (1/value + 1/link)); 0 = off.
+ *   MOE_OPT_PRE_GROUP: consecutive weight tiles one workgroup of the tiled
+ *                     kernels runs with its copy ring kept going (fewer
+ *                     workgroup prologues): gate/up count in the low byte,
+ *                     down count in the next (1..16 each; rounded down to a
+ *                     divisor of the tiles per expert); -1 restores the default. */
 enum { MOE_OPT_FFN_PATH = 1, MOE_OPT_TIMING = 2, MOE_OPT_DEC_SPLIT = 3, MOE_OPT_CACHE_FAULT = 4,
-       MOE_OPT_CACHE_DELAY_US = 5, MOE_OPT_CACHE_THROTTLE_MBS = 6 };
+       MOE_OPT_CACHE_DELAY_US = 5, MOE_OPT_CACHE_THROTTLE_MBS = 6, MOE_OPT_PRE_GROUP = 7 };
 int moe_set_option(int option, int value);
 int moe_get_option(int option);
 

@@ -21,6 +21,7 @@ MOE_OPT_DEC_SPLIT = 3
 MOE_OPT_CACHE_FAULT = 4
 MOE_OPT_CACHE_DELAY_US = 5
 MOE_OPT_CACHE_THROTTLE_MBS = 6
+MOE_OPT_PRE_GROUP = 7
 
 # every symbol include/moe.h declares
 EXPORTS = [

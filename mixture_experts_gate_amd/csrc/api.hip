@@ -16,6 +16,15 @@ int ffn_path_option() { return g_ffn_path.load(); }
 
 // Decode tile-split weights, one byte each in units of 1/256: stage 1 slot,
 // stage 1 position, stage 2 slot, stage 2 position (low byte first).
+// tiled kernels: weight tiles per workgroup, stage 1 in the low byte, stage 2 next
+constexpr int kPreGroupDefault = 1 | (2 << 8);
+static std::atomic<int> g_pre_group{kPreGroupDefault};
+int pre_group(int stage) {
+    const int v = g_pre_group.load(std::memory_order_relaxed);
+    const int g = stage == 1 ? (v & 0xFF) : ((v >> 8) & 0xFF);
+    return g < 1 ? 1 : g;
+}
+
 // measured on the decode layer at T = 8..64: 64/256, 38/256, 38/256, 23/256
 constexpr int kDecSplitDefault = 64 | (38 << 8) | (38 << 16) | (23 << 24);
 static std::atomic<int> g_dec_split{kDecSplitDefault};
@@ -96,8 +105,8 @@ int ffn_decode_shared(const uint16_t *x, const int32_t *sorted_pair, const int32
                       int k, int H, int I, int E, void *y, int y_is_fp32, uint16_t *act,
                       hipStream_t s);
 int ffn_prefill(const uint16_t *x, const int32_t *sorted_pair, const int32_t *offsets,
-                const moe_expert_w *experts, int fmt, int T, int k, int H, int I, int E, void *y,
-                int y_is_fp32, void *ws, hipStream_t s);
+                const moe_expert_w *experts, const moe_expert_w *shared, int fmt, int T, int k,
+                int H, int I, int E, void *y, int y_is_fp32, void *ws, hipStream_t s);
 bool ffn_prefill_supported(int fmt, int H, int I);
 size_t prefill_ws_bytes(long n_pairs, long T, int H, int I, int E);
 
@@ -147,6 +156,14 @@ extern "C" int moe_set_option(int option, int value) {
         g_ffn_path.store(value);
         return MOE_OK;
     }
+    if (option == MOE_OPT_PRE_GROUP) {
+        if (value == -1) value = kPreGroupDefault;
+        if (value < 0 || (value & 0xFF) < 1 || (value & 0xFF) > 16 || ((value >> 8) & 0xFF) < 1 ||
+            ((value >> 8) & 0xFF) > 16 || (value >> 16))
+            return MOE_EINVAL;
+        g_pre_group.store(value);
+        return MOE_OK;
+    }
     if (option == MOE_OPT_CACHE_FAULT) return cache_set_fault(value);
     if (option == MOE_OPT_CACHE_DELAY_US) return cache_set_delay(value);
     if (option == MOE_OPT_CACHE_THROTTLE_MBS) return cache_set_throttle(value);
@@ -175,6 +192,7 @@ extern "C" int moe_get_option(int option) {
     if (option == MOE_OPT_FFN_PATH) return g_ffn_path.load();
     if (option == MOE_OPT_TIMING) return g_timing.load() ? 1 : 0;
     if (option == MOE_OPT_DEC_SPLIT) return g_dec_split.load();
+    if (option == MOE_OPT_PRE_GROUP) return g_pre_group.load();
     if (option == MOE_OPT_CACHE_FAULT) return cache_get_fault();
     if (option == MOE_OPT_CACHE_DELAY_US) return cache_get_delay();
     if (option == MOE_OPT_CACHE_THROTTLE_MBS) return cache_get_throttle();
@@ -225,8 +243,8 @@ int expert_ffn_call(const uint16_t *x_bf16, const int32_t *sorted_pair, const in
     uint16_t *act = reinterpret_cast<uint16_t *>(ws);
     hipStream_t s = (hipStream_t)stream;
     if (use_prefill(n, E, fmt, H, I))
-        return ffn_prefill(x_bf16, sorted_pair, offsets, experts, fmt, T, k, H, I, E, y, y_is_fp32,
-                           ws, s);
+        return ffn_prefill(x_bf16, sorted_pair, offsets, experts, nullptr, fmt, T, k, H, I, E, y,
+                           y_is_fp32, ws, s);
     return ffn_decode(x_bf16, sorted_pair, offsets, experts, fmt, T, k, H, I, E, y, y_is_fp32,
                       act, s);
 }
@@ -256,8 +274,10 @@ extern "C" int moe_expert_ffn_shared(const uint16_t *x_bf16, const int32_t *sort
     if ((long)T * (k + 1) > 0x7FFFFFFFL) return MOE_EINVAL;
     // the activation holds the routed rows and then the shared expert's T rows
     if (ws_bytes < ffn_ws_bytes((long)T * (k + 1), T, H, I, E)) return MOE_EINVAL;
-    // the tiled kernels take the shared expert as its own call
-    if (use_prefill(n, E, fmt, H, I)) return MOE_EUNSUPPORTED;
+    // the shared expert is one more expert of the launches on either path
+    if (use_prefill(n, E, fmt, H, I))
+        return ffn_prefill(x_bf16, sorted_pair, offsets, experts, shared, fmt, T, k, H, I, E, y,
+                           y_is_fp32, ws, (hipStream_t)stream);
     return ffn_decode_shared(x_bf16, sorted_pair, offsets, experts, shared, fmt, T, k, H, I, E,
                              y, y_is_fp32, reinterpret_cast<uint16_t *>(ws),
                              (hipStream_t)stream);

@@ -47,6 +47,8 @@ int cache_set_delay(int us);
 int cache_get_delay();
 int cache_set_throttle(int mbs);
 int cache_get_throttle();
+// Consecutive weight tiles per workgroup of the tiled kernels (MOE_OPT_PRE_GROUP).
+int pre_group(int stage);
 // Weights of the decode kernels' tile split for stage 1 or 2 (MOE_OPT_DEC_SPLIT).
 void dec_split_weights(int stage, float *w_slot, float *w_pos);
 

@@ -98,15 +98,18 @@ __device__ __forceinline__ void split_quad(const float (&v)[4], float inv, uint3
 // scale bytes [rows][K/32]. One thread per 32-element block.
 // Token-tile map of the tiled kernels: map[0] = M, the number of 64-token
 // tiles over all experts; map[1 + m] = e | (mt << 16) for the m-th tile in
-// expert order (tile mt of expert e). One 256-thread workgroup.
-__device__ void build_tile_map(const int32_t *__restrict__ offsets, int E,
+// expert order (tile mt of expert e). The always-on shared expert, when the
+// launch carries it, is expert E with sh_rows rows (the tokens in order).
+// One 256-thread workgroup.
+__device__ void build_tile_map(const int32_t *__restrict__ offsets, int E, int sh_rows,
                                int32_t *__restrict__ map) {
     __shared__ int wsum[4];
     const int t = threadIdx.x, lane = lane_id(), w = t / kWave;
     int run = 0;   // tiles of the experts before this chunk
-    for (int e0 = 0; e0 < E; e0 += 256) {
+    for (int e0 = 0; e0 <= E; e0 += 256) {
         const int e = e0 + t;
-        const int tiles = e < E ? (offsets[e + 1] - offsets[e] + kPreTok - 1) / kPreTok : 0;
+        const int rows = e < E ? offsets[e + 1] - offsets[e] : e == E ? sh_rows : 0;
+        const int tiles = (rows + kPreTok - 1) / kPreTok;
         int incl = tiles;
 #pragma unroll
         for (int d = 1; d < kWave; d <<= 1) {
@@ -135,9 +138,10 @@ __global__ __launch_bounds__(256) void split_rows_kernel(const uint16_t *__restr
                                                          uint8_t *__restrict__ lo,
                                                          uint8_t *__restrict__ sc,
                                                          const int32_t *__restrict__ offsets,
-                                                         int E, int32_t *__restrict__ map) {
+                                                         int E, int sh_rows,
+                                                         int32_t *__restrict__ map) {
     if (blockIdx.x == gridDim.x - 1) {
-        build_tile_map(offsets, E, map);
+        build_tile_map(offsets, E, sh_rows, map);
         return;
     }
     const long b = (long)blockIdx.x * 256 + threadIdx.x;
@@ -186,7 +190,8 @@ struct PreArgs {
     void *out;                        // stage 2: y
     uint8_t *ohi, *olo, *osc;         // stage 1: activation hi/lo rows [n][I], scales [n][I/32]
     const int32_t *tile_map;          // token-tile map (build_tile_map)
-    int k, K, H, I, E;
+    const moe_expert_w *shared;       // the shared expert (expert index E), or NULL
+    int k, K, H, I, E, T;
     int ntiles_w;                     // weight tiles per expert
     int nt_group;                     // consecutive weight tiles per workgroup (divides ntiles_w)
 };
@@ -540,10 +545,12 @@ __global__ __launch_bounds__(kPreThreads) void ffn_pre_kernel(PreArgs A) {
     const int e = md & 0xFFFF, mt = md >> 16;
 
     const MOE_CONST int32_t *offs = as_scalar(A.offsets);
-    const int row0 = offs[e];
-    const int n_e = offs[e + 1] - row0;
+    // the shared expert (index E): rows T*k .. T*k + T - 1, token r = row r
+    const bool sh = e == A.E;
+    const int row0 = sh ? A.T * A.k : offs[e];
+    const int n_e = sh ? A.T : offs[e + 1] - row0;
     const int tok0 = mt * kPreTok;
-    const MOE_CONST moe_expert_w *W = as_scalar(A.experts) + e;
+    const MOE_CONST moe_expert_w *W = sh ? as_scalar(A.shared) : as_scalar(A.experts) + e;
     const uint8_t *wcodes = reinterpret_cast<const uint8_t *>(STAGE == 1 ? W->w13 : W->w2);
     const uint8_t *wscales = reinterpret_cast<const uint8_t *>(STAGE == 1 ? W->s13 : W->s2);
     const int nslab = A.K / 128;
@@ -554,7 +561,7 @@ __global__ __launch_bounds__(kPreThreads) void ffn_pre_kernel(PreArgs A) {
 #pragma unroll
         for (int tb = 0; tb < 2; ++tb) {
             const int r = tok0 + 32 * wm + 16 * tb + (lane & 15);
-            prow_tb[tb] = r < n_e ? A.sorted_pair[row0 + r] : 0;
+            prow_tb[tb] = r >= n_e ? 0 : sh ? row0 + r : A.sorted_pair[row0 + r];
         }
     }
 
@@ -562,7 +569,8 @@ __global__ __launch_bounds__(kPreThreads) void ffn_pre_kernel(PreArgs A) {
     {
         auto token_row = [&](int r) -> long {   // operand row of tile row r
             r = r < n_e ? r : n_e - 1;             // rows past the expert's end repeat its last row
-            return STAGE == 1 ? (long)(A.sorted_pair[row0 + r] / A.k) : (long)(row0 + r);
+            if (STAGE == 1) return sh ? (long)r : (long)(A.sorted_pair[row0 + r] / A.k);
+            return (long)(row0 + r);
         };
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
@@ -635,8 +643,10 @@ static size_t al256(size_t b) { return (b + 255) & ~(size_t)255; }
 
 // Workspace of the tiled path: the activation's two terms and scales
 // [n_pairs][I] and the token rows' [T][H].
+// (map[0] and at most n_pairs / 64 + E + 1 tiles: one partial tile per expert,
+// the shared expert included)
 static size_t tile_map_bytes(long n_pairs, int E) {
-    return al256(((size_t)n_pairs / kPreTok + E + 1) * sizeof(int32_t));
+    return al256(((size_t)n_pairs / kPreTok + E + 3) * sizeof(int32_t));
 }
 
 size_t prefill_ws_bytes(long n_pairs, long T, int H, int I, int E) {
@@ -644,20 +654,17 @@ size_t prefill_ws_bytes(long n_pairs, long T, int H, int I, int E) {
            2 * al256((size_t)T * H) + al256((size_t)T * H / 32) + tile_map_bytes(n_pairs, E);
 }
 
-#ifndef MOE_PRE_GROUP1
-#define MOE_PRE_GROUP1 1
-#endif
-#ifndef MOE_PRE_GROUP2
-#define MOE_PRE_GROUP2 2
-#endif
 template <int STAGE, bool YF32, int FMT>
 static int launch_pre(hipStream_t s, PreArgs A, long n_pairs) {
+    // n_pairs: rows over all experts of the launch (the shared expert's included)
     // weight tiles per workgroup: stage 2's short contraction (I / 128 slabs
-    // per tile) runs two tiles per workgroup so the copy ring spans more slabs
-    const int want = STAGE == 1 ? MOE_PRE_GROUP1 : MOE_PRE_GROUP2;
-    A.nt_group = A.ntiles_w % want == 0 ? want : 1;
-    // upper bound on token tiles: sum_e ceil(count_e / 64) <= n_pairs / 64 + E
-    const long mt_max = n_pairs / kPreTok + A.E;
+    // per tile) runs several tiles per workgroup so the copy ring spans more
+    // slabs (MOE_OPT_PRE_GROUP)
+    int want = pre_group(STAGE);
+    while (want > 1 && A.ntiles_w % want) --want;
+    A.nt_group = want;
+    // upper bound on token tiles: sum_e ceil(count_e / 64) <= n_pairs / 64 + E (+ 1 shared)
+    const long mt_max = n_pairs / kPreTok + A.E + 1;
     const long tiles_max = mt_max * (A.ntiles_w / A.nt_group);
     const long grid = ((tiles_max + 7) / 8) * 8;
     if (grid > 0x7FFFFFFFL) return MOE_EUNSUPPORTED;
@@ -667,10 +674,11 @@ static int launch_pre(hipStream_t s, PreArgs A, long n_pairs) {
 }
 
 int ffn_prefill(const uint16_t *x, const int32_t *sorted_pair, const int32_t *offsets,
-                const moe_expert_w *experts, int fmt, int T, int k, int H, int I, int E, void *y,
-                int y_is_fp32, void *ws, hipStream_t s) {
+                const moe_expert_w *experts, const moe_expert_w *shared, int fmt, int T, int k,
+                int H, int I, int E, void *y, int y_is_fp32, void *ws, hipStream_t s) {
     if (!ffn_prefill_supported(fmt, H, I)) return MOE_EUNSUPPORTED;
-    const long n = (long)T * k;
+    // activation rows: the routed pairs, then the shared expert's T rows
+    const long n = (long)T * k + (shared ? T : 0);
     uint8_t *p = reinterpret_cast<uint8_t *>(ws);
     uint8_t *ahi = p;
     uint8_t *alo = ahi + al256((size_t)n * I);
@@ -684,14 +692,14 @@ int ffn_prefill(const uint16_t *x, const int32_t *sorted_pair, const int32_t *of
     const long grid = (nblk + 255) / 256 + 1;   // + the tile-map workgroup
     if (grid > 0x7FFFFFFFL) return MOE_EUNSUPPORTED;
     MOE_LAUNCH(K_PRE_SPLIT, split_rows_kernel, dim3((unsigned)grid), dim3(256), 0, s, x, nblk,
-                                 xhi, xlo, xsc, offsets, E, map);
+                                 xhi, xlo, xsc, offsets, E, shared ? T : 0, map);
     int rc = check_launch();
     if (rc) return rc;
 
     PreArgs a1{xhi, xlo, xsc, sorted_pair, offsets, experts, nullptr, ahi, alo, asc, map,
-               k, H, H, I, E, I / 128, 1};
+               shared, k, H, H, I, E, T, I / 128, 1};
     PreArgs a2{ahi, alo, asc, sorted_pair, offsets, experts, y, nullptr, nullptr, nullptr, map,
-               k, I, H, I, E, H / 256, 1};
+               shared, k, I, H, I, E, T, H / 256, 1};
     if (fmt == MOE_W_FP8) {
         rc = launch_pre<1, false, MOE_W_FP8>(s, a1, n);
         if (rc) return rc;

@@ -678,29 +678,30 @@ def test_decode_multipass_one_hot_expert(lib, orc, T, k, shared):
     _check_layer_full(orc, w, T, x, L, out, logits=lg)
 
 
-def test_ffn_shared_tiled_path_unsupported(lib, orc):
-    """Where the tiled kernels would run, moe_expert_ffn_shared declines before
-    any device work and the layer runs the shared expert as its own call."""
-    _announce("ffn+shared: tiled path forced -> EUNSUPPORTED, layer falls back")
-    H, I, E, k, T = 512, 256, 16, 4, 24
+@pytest.mark.parametrize("T,kind", [(24, "uniform"), (300, "skew")])
+def test_ffn_shared_in_tiled_launch(lib, orc, T, kind):
+    """The tiled kernels (forced) with the shared expert as expert E of the
+    token-tile map: every routed and every shared row against the oracle, the
+    layer output too, and the same layer with the shared expert as its own
+    call on a side stream."""
+    _announce(f"ffn+shared one tiled launch: T={T} ({kind})")
+    H, I, E, k = 512, 256, 16, 4
     cfg = synth.LayerConfig("shared_tiled", H, E, k, I, "mxfp4", 1, "uniform", (T,),
                             "gauss_mxfp4", seed=32)
     w = Workload(cfg)
     x = synth.activations(cfg, T, step=1)
-    lg = synth.router_logits(cfg, T, step=1)
-    from mixture_experts_gate_amd.layer import MoeLayer
-    M = MoeLayer(H, E, k, I, "mxfp4", T, shared=True, device=DEV)
-    M.route_permute(T, logits=to_dev(lg))
+    lg = synth.router_logits(cfg, T, step=1) if kind == "uniform" else _perm_case(T, E, k, kind)
     lib.moe_set_option(lib.MOE_OPT_FFN_PATH, 2)
     try:
-        rc = lib.moe_expert_ffn_shared(to_dev_bf16(x), M.sorted_pair, M.offsets, w.dev.table,
-                                       w.dev_shared.table, M.fmt, T, k, H, I, E, M.y, False,
-                                       M.ws_ffn, M.ws_ffn_bytes, check=False)
-        assert rc == lib.MOE_EUNSUPPORTED
         L, out = run_layer(w, T, x, logits=lg)
+        L2, out2 = run_layer(w, T, x, logits=lg, fuse_shared=False)
     finally:
         lib.moe_set_option(lib.MOE_OPT_FFN_PATH, 0)
-    _check_layer_full(orc, w, T, x, L, out, logits=lg)
+    ref = _check_layer_full(orc, w, T, x, L, out, logits=lg)
+    ysh_ref = orc.ffn_rows(x, w.shared[None], w.lay, np.arange(T, dtype=np.int32),
+                           np.zeros(T, np.int32))
+    assert_close(L.y[T * k:T * k + T].float().cpu().numpy(), ysh_ref, f"shared rows (T={T})")
+    assert_close(bf16_dev_to_f64(out2), ref["out_f64"], "layer output, separate shared call")
 
 
 @pytest.mark.parametrize("fmt", ["nvfp4", "fp8"])
