@@ -114,11 +114,14 @@ def measured_traffic(kernel, T):
 
 class Workload:
     """One routed MoE layer of config ``cfg`` at T tokens, inputs resident in
-    HBM: ``replicas`` copies of the expert weights and as many input batches,
-    rotated step by step (plus the shared expert when the config has one)."""
+    HBM: ``replicas`` copies of the expert weights and ``batches`` input
+    batches (default: as many as replicas, 64 at T <= 8 so that a cycle of
+    steps touches several times the 256 MB last-level cache even when each
+    step touches few experts), step i using replica i mod R and batch i mod B
+    (plus the shared expert when the config has one)."""
 
     def __init__(self, torch, cfg, T, dev, replicas=REPLICAS, pool=None, dexp=None,
-                 shared=None):
+                 shared=None, batches=None):
         from mixture_experts_gate_amd import synth
         from mixture_experts_gate_amd.layer import DeviceExperts, MoeLayer
         self.cfg = c = cfg
@@ -133,25 +136,28 @@ class Workload:
             self.sh = shared if shared is not None else DeviceExperts(
                 synth.shared_expert(c)[None, :], self.lay, copies=self.R, device=dev)
         to16 = lambda a: torch.from_numpy(a.view("int16")).to(dev)
-        self.x_host = [synth.activations(c, T, step=r) for r in range(self.R)]
-        self.lg_host = [synth.router_logits(c, T, step=r) for r in range(self.R)]
+        self.B = batches if batches is not None else (64 if T <= 8 else self.R)
+        self.x_host = [synth.activations(c, T, step=r) for r in range(self.B)]
+        self.lg_host = [synth.router_logits(c, T, step=r) for r in range(self.B)]
         self.x = [to16(a) for a in self.x_host]
         self.lg = [torch.from_numpy(a).to(dev) for a in self.lg_host]
         self.layer = MoeLayer(c.H, c.E, c.k, c.I, c.fmt, T, shared=self.has_shared, device=dev)
+        self.fuse_shared = True
         if self.has_shared:
             self.layer.prepare_shared(T)
 
     def step(self, i):
-        r = i % self.R
-        self.layer.forward(self.T, self.x[r], self.dexp.tables[r], logits=self.lg[r],
-                           shared_table=self.sh.tables[r] if self.has_shared else None)
+        r, b = i % self.R, i % self.B
+        self.layer.forward(self.T, self.x[b], self.dexp.tables[r], logits=self.lg[b],
+                           shared_table=self.sh.tables[r] if self.has_shared else None,
+                           fuse_shared=self.fuse_shared)
 
     def unique_experts(self, torch):
         """Distinct experts the GPU router picks per step (average over the input
         batches), read back from its top-k ids."""
         import numpy as np
         us = []
-        for r in range(self.R):
+        for r in range(self.B):
             self.layer.route(self.T, logits=self.lg[r], write_logits=False)
             torch.cuda.synchronize()
             us.append(len(np.unique(self.layer.topk_ids[:self.T].cpu().numpy())))
@@ -980,17 +986,28 @@ def main():
         for T, steps in ((1, 100), (64, 100), (4096, 8)):
             if T not in c4_T:
                 continue
-            w, r = run_workload(torch, c4, T, steps, 3, dev, replicas=2,
+            # decode sizes rotate 8 weight replicas (27 GB) so that a hot
+            # expert's bytes come back from HBM, not from the last-level cache
+            w, r = run_workload(torch, c4, T, steps, 3, dev, replicas=8 if T <= 64 else 2,
                                 pool=None if w4 is None else w4.pool,
                                 dexp=None if w4 is None else w4.dexp,
                                 shared=None if w4 is None else w4.sh,
                                 kernel_steps=min(steps, 16))
             w4 = w4 or w
+            if T <= 64:
+                # the same steps with the shared expert as its own call on a
+                # side stream, for the gain of running it in the routed launches
+                w.fuse_shared = False
+                ms, _ = time_graphs(torch, w, steps, 3)
+                w.fuse_shared = True
+                r["unfused_shared_ms_per_step"] = ms / steps
             if T == 4096:
                 r["mfma_frac_bf16_peak"] = r["layer_tflops"] / BF16_PEAK_TFLOPS
             sweep[f"cfg4_T{T}"] = r
             log(f"config 4 T={T}: {r['tokens_per_s']:.0f} tok/s, {r['ms_per_step']*1000:.1f} us/step, "
-                f"layer HBM {r['layer_hbm_frac']*100:.1f}%, {r['layer_tflops']:.1f} TFLOP/s")
+                f"layer HBM {r['layer_hbm_frac']*100:.1f}%, {r['layer_tflops']:.1f} TFLOP/s"
+                + (f", shared expert as its own call {r['unfused_shared_ms_per_step']*1000:.1f} us/step"
+                   if "unfused_shared_ms_per_step" in r else ""))
         del w4
         torch.cuda.empty_cache()
     if not args.no_sweep and not args.no_stack and (want("stack") or want("stream") or
