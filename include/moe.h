@@ -251,6 +251,32 @@ int moe_combine(const void *y, int y_is_fp32, const float *topk_w, const void *y
                 int k, int H, uint16_t *out_bf16, void *stream);
 
 /*
+ * moe_expert_ffn_combine -- the expert FFN followed by the weighted combine:
+ *   moe_expert_ffn (shared == NULL) or moe_expert_ffn_shared into y_bf16,
+ *   then out_bf16[t] = moe_combine of those rows (the shared expert's rows
+ *   T*k .. T*k + T - 1 as y_shared), both with bf16 y.
+ * The combine is the second half of the layer's output step (the pages'
+ * routed experts are mixed by the router's weights; winzheng.com page, "Why
+ * Now of All Times"). At a handful of rows (T*k plus the shared expert's T
+ * at most 15, block-scaled weights, the weight-streaming kernels)
+ * the down projection and the combine run as one launch: each workgroup
+ * computes 16 output columns of every routed row and sums each token's rows
+ * for those columns. out is moe_combine's expression on the bf16 y this call
+ * writes (fp32, j ascending), and y is within the tolerance of moe_expert_ffn
+ * (the down projection's K order differs, so y need not equal
+ * moe_expert_ffn's bit for bit). Otherwise the call is exactly the two calls.
+ * y_bf16: [T*k][H], or [T*k + T][H] with the shared expert; out_bf16 [T][H];
+ * topk_w [T][k] (moe_route's weights). ws: the ffn workspace of
+ * moe_workspace_size(T, k, ...), or (T, k + 1, ...) with the shared expert.
+ * Errors as moe_expert_ffn; topk_w, y_bf16 and out_bf16 must not be NULL.
+ */
+int moe_expert_ffn_combine(const uint16_t *x_bf16, const int32_t *sorted_pair,
+                           const int32_t *offsets, const moe_expert_w *experts,
+                           const moe_expert_w *shared, int fmt, int T, int k, int H, int I, int E,
+                           const float *topk_w, uint16_t *y_bf16, uint16_t *out_bf16, void *ws,
+                           size_t ws_bytes, void *stream);
+
+/*
  * moe_pack_mxfp4 -- convert n expert blobs from the interchange MXFP4 layout
  * to the kernel layout (see the top of this file). src and dst are device
  * buffers of n blobs spaced src_stride / dst_stride bytes apart; within a blob

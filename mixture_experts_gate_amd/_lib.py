@@ -26,7 +26,7 @@ MOE_OPT_PRE_GROUP = 7
 # every symbol include/moe.h declares
 EXPORTS = [
     "moe_strerror", "moe_last_hip_error", "moe_route", "moe_permute", "moe_expert_ffn",
-    "moe_expert_ffn_shared", "moe_expert_ffn_noalloc",
+    "moe_expert_ffn_shared", "moe_expert_ffn_noalloc", "moe_expert_ffn_combine",
     "moe_combine", "moe_workspace_size", "moe_set_option", "moe_get_option", "moe_kernel_name",
     "moe_timing_query", "moe_pack_mxfp4", "moe_pack_weights", "moe_route_permute",
     "expert_cache_reserve", "expert_cache_prefetch", "expert_cache_evict", "expert_cache_stats",
@@ -71,6 +71,7 @@ def load(path: str | None = None):
         "moe_expert_ffn": (I, [P, P, P, P, I, I, I, I, I, I, P, I, P, Z, P]),
         "moe_expert_ffn_shared": (I, [P, P, P, P, P, I, I, I, I, I, I, P, I, P, Z, P]),
         "moe_expert_ffn_noalloc": (I, [P, P, P, P, I, I, I, I, I, I, P, I, P]),
+        "moe_expert_ffn_combine": (I, [P, P, P, P, P, I, I, I, I, I, I, P, P, P, P, Z, P]),
         "moe_combine": (I, [P, I, P, P, I, I, I, P, P]),
         "moe_workspace_size": (I, [I, I, I, I, I, C.POINTER(Z), C.POINTER(Z)]),
         "moe_set_option": (I, [I, I]),
@@ -172,6 +173,19 @@ def moe_expert_ffn_shared(x_bf16, sorted_pair, offsets, experts, shared, fmt, T,
     if not check and rc == MOE_EUNSUPPORTED:
         return rc
     return _check("moe_expert_ffn_shared", rc)
+
+
+def moe_expert_ffn_combine(x_bf16, sorted_pair, offsets, experts, shared, fmt, T, k, H, I, E,
+                           topk_w, y, out, ws, ws_bytes, stream=None, check=True):
+    """Expert FFN (with the shared expert when `shared` is given) and the
+    weighted combine into `out`; y (bf16) holds the expert rows. check=False
+    returns MOE_EUNSUPPORTED instead of raising."""
+    rc = load().moe_expert_ffn_combine(
+        _ptr(x_bf16), _ptr(sorted_pair), _ptr(offsets), _ptr(experts), _ptr(shared), fmt, T, k, H,
+        I, E, _ptr(topk_w), _ptr(y), _ptr(out), _ptr(ws), ws_bytes, _stream(stream))
+    if not check and rc == MOE_EUNSUPPORTED:
+        return rc
+    return _check("moe_expert_ffn_combine", rc)
 
 
 FFN_NOALLOC_MAX_WS = 64 << 20

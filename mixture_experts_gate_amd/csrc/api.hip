@@ -104,6 +104,14 @@ int ffn_decode_shared(const uint16_t *x, const int32_t *sorted_pair, const int32
                       const moe_expert_w *experts, const moe_expert_w *shared, int fmt, int T,
                       int k, int H, int I, int E, void *y, int y_is_fp32, uint16_t *act,
                       hipStream_t s);
+int ffn_decode_comb(const uint16_t *x, const int32_t *sorted_pair, const int32_t *offsets,
+                    const moe_expert_w *experts, int fmt, const float *topk_w, int T, int k,
+                    int H, int I, int E, uint16_t *y, uint16_t *out, uint16_t *act, hipStream_t s);
+int ffn_decode_comb_shared(const uint16_t *x, const int32_t *sorted_pair,
+                           const int32_t *offsets, const moe_expert_w *experts,
+                           const moe_expert_w *shared, int fmt, const float *topk_w, int T,
+                           int k, int H, int I, int E, uint16_t *y, uint16_t *out, uint16_t *act,
+                           hipStream_t s);
 int ffn_prefill(const uint16_t *x, const int32_t *sorted_pair, const int32_t *offsets,
                 const moe_expert_w *experts, const moe_expert_w *shared, int fmt, int T, int k,
                 int H, int I, int E, void *y, int y_is_fp32, void *ws, hipStream_t s);
@@ -281,4 +289,43 @@ extern "C" int moe_expert_ffn_shared(const uint16_t *x_bf16, const int32_t *sort
     return ffn_decode_shared(x_bf16, sorted_pair, offsets, experts, shared, fmt, T, k, H, I, E,
                              y, y_is_fp32, reinterpret_cast<uint16_t *>(ws),
                              (hipStream_t)stream);
+}
+
+extern "C" int moe_expert_ffn_combine(const uint16_t *x_bf16, const int32_t *sorted_pair,
+                                      const int32_t *offsets, const moe_expert_w *experts,
+                                      const moe_expert_w *shared, int fmt, int T, int k, int H,
+                                      int I, int E, const float *topk_w, uint16_t *y_bf16,
+                                      uint16_t *out_bf16, void *ws, size_t ws_bytes,
+                                      void *stream) {
+    if (T < 0 || k < 1 || E < 1 || E > 512 || H < 32 || I < 32 || H % 32 || I % 32)
+        return MOE_EINVAL;
+    if (fmt != MOE_W_MXFP4 && fmt != MOE_W_BF16 && fmt != MOE_W_NVFP4 && fmt != MOE_W_FP8)
+        return MOE_EINVAL;
+    if (fmt != MOE_W_BF16 && (H % 128 || I % 128)) return MOE_EINVAL;
+    if (T == 0) return MOE_OK;
+    if (!x_bf16 || !sorted_pair || !offsets || !experts || !topk_w || !y_bf16 || !out_bf16 || !ws)
+        return MOE_EINVAL;
+    const long n = (long)T * k;
+    const long rows = n + (shared ? T : 0);
+    if (rows > 0x7FFFFFFFL) return MOE_EINVAL;
+    if (ws_bytes < ffn_ws_bytes(rows, T, H, I, E)) return MOE_EINVAL;
+    hipStream_t s = (hipStream_t)stream;
+    if (!use_prefill(n, E, fmt, H, I)) {
+        uint16_t *act = reinterpret_cast<uint16_t *>(ws);
+        const int rc = shared ? ffn_decode_comb_shared(x_bf16, sorted_pair, offsets, experts,
+                                                       shared, fmt, topk_w, T, k, H, I, E,
+                                                       y_bf16, out_bf16, act, s)
+                              : ffn_decode_comb(x_bf16, sorted_pair, offsets, experts, fmt,
+                                                topk_w, T, k, H, I, E, y_bf16, out_bf16, act, s);
+        if (rc != MOE_EUNSUPPORTED) return rc;
+    }
+    // the two calls
+    const int rc = shared ? moe_expert_ffn_shared(x_bf16, sorted_pair, offsets, experts, shared,
+                                                  fmt, T, k, H, I, E, y_bf16, 0, ws, ws_bytes,
+                                                  stream)
+                          : expert_ffn_call(x_bf16, sorted_pair, offsets, experts, fmt, T, k, H,
+                                            I, E, y_bf16, 0, ws, ws_bytes, stream);
+    if (rc) return rc;
+    return moe_combine(y_bf16, 0, topk_w, shared ? y_bf16 + (size_t)n * H : nullptr, T, k, H,
+                       out_bf16, stream);
 }

@@ -117,6 +117,10 @@ __device__ __forceinline__ uint32_t load_u8(const void *p) {
     return *(const MOE_GLOBAL uint8_t *)(p);
 }
 
+__device__ __forceinline__ uint32_t load_u32(const void *p) {
+    return *(const MOE_GLOBAL uint32_t *)(p);
+}
+
 // Raw buffer loads through a resource with a byte range: an offset at or past
 // the range returns zeros without a memory access. A load that is issued on
 // every path and switched off by its offset keeps the count of loads in
@@ -145,6 +149,25 @@ __device__ __forceinline__ uint32_t buf_load_u8(buf_rsrc r, uint32_t off) {
 template <typename T>
 __device__ __forceinline__ const MOE_CONST T *as_scalar(const T *p) {
     return (const MOE_CONST T *)(p);
+}
+
+#define MOE_LDS __attribute__((address_space(3)))
+
+// Direct global -> LDS copies: lane l's 16 (4) bytes land at dst + 16 l (4 l);
+// dst is wavefront-uniform.
+__device__ __forceinline__ void lds_dma16(const void *src, void *dst) {
+    __builtin_amdgcn_global_load_lds((const MOE_GLOBAL void *)src, (MOE_LDS void *)dst, 16, 0, 0);
+}
+__device__ __forceinline__ void lds_dma4(const void *src, void *dst) {
+    __builtin_amdgcn_global_load_lds((const MOE_GLOBAL void *)src, (MOE_LDS void *)dst, 4, 0, 0);
+}
+
+// Waits until at most n of this wavefront's vector-memory operations are
+// outstanding (n < 64). gfx9 s_waitcnt fields: vmcnt[3:0] | expcnt[6:4] |
+// lgkmcnt[11:8] | vmcnt_hi[15:14].
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) {

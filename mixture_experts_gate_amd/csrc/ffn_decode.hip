@@ -761,6 +761,294 @@ static int ffn_decode_fmt(const uint16_t *x, const int32_t *sorted_pair, const i
     return launch_stage<FMT, 2, false, SH>((I + 127) / 128, s, a2, S, slots);
 }
 
+// ---------------------------------------- small batches: down + combine --
+//
+// At a few tokens the down projection moves a few MB and every launch's
+// start-up costs microseconds, so the combine rides in the down launch.
+// Workgroup c computes output columns 16c .. 16c+15 for the rows of every
+// active expert (the expert's 16-row block c of W2 over K = I), keeps those
+// columns of all the layer's rows in LDS, and then writes
+//   out[t][16c + i] = bf16( sum_{j<k} w[t][j] y[t*k+j][16c+i]  (+ y_sh[t][16c+i]) ),
+// j ascending in fp32 from the bf16 y it also stores: the combine's
+// arithmetic on the same y. The activation rows are copied into LDS once per
+// workgroup, directly in the matrix-core operand order: 1 KB block
+// (g, s, j) holds at byte 16 (m + 16 c) the elements s*128 + 32c + 8j .. +7
+// of row 16g + m, so an expert's operand is one 16-byte read per lane and
+// MFMA, conflict-free whatever its first row. The four wavefronts take the
+// active experts in turn, each with the weights of D experts in registers
+// (D - 1 in flight while one is multiplied); two wavefronts per SIMD, so one
+// multiplies while the other waits for its weights.
+constexpr int kDcMaxT = 16;             // one token pass per expert
+// activation rows (T*k routed + T shared): with 16 rows or more (two tokens
+// of the 128-expert decode layer, 128 workgroups) the separate down and
+// combine launches were as fast or faster in graphs (one workgroup per 16
+// output columns then streams several experts' blocks in turn)
+constexpr int kDcMaxRows = 15;
+constexpr size_t kDcMaxActLds = 128 * 1024;
+constexpr int kDcWaves = 8;             // wavefronts per workgroup (two per SIMD)
+
+template <int FMT>
+constexpr int wfrag_regs() { return FMT == MOE_W_FP8 ? 8 : 5; }
+// experts whose weights are held at once: about 160 registers of weights
+template <int FMT, int NS>
+constexpr int dc_depth() {
+    return 160 / (NS * wfrag_regs<FMT>()) > 4 ? 4 : 160 / (NS * wfrag_regs<FMT>());
+}
+
+struct DcArgs {
+    const float *topk_w;   // [T][k]
+    uint16_t *out;         // [T][H] bf16
+    int T, nrows;          // tokens; activation rows (T*k, + T with the shared expert)
+};
+
+// An expert of the down + combine launch: rows and W2 resources.
+template <int FMT>
+struct DcExpert : TensorScale<tensor_scaled(FMT)> {
+    int row0, n_e;
+    buf_rsrc wr, sr;
+};
+
+// Lane q (q < n) of a wavefront describes its q-th expert (active expert
+// wv + kDcWaves q): loaded by vector loads once, before the expert loop, and handed
+// to the loop by lane reads, so that no expert waits for a load of its
+// description (scalar loads there would also hold up the LDS waits).
+struct DcMeta {
+    int row0, n_e;
+    uint64_t w, s;
+    float g;
+};
+
+__device__ __forceinline__ uint64_t ld_global_u64(const void *p) {
+    return *(const MOE_GLOBAL uint64_t *)(p);
+}
+
+__device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int l) {
+    return (uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, l) |
+           ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), l) << 32);
+}
+
+template <int FMT, bool SH>
+__device__ __forceinline__ DcMeta dc_meta(const DecArgs &A, const ShArgs &S, const ActiveSet &act,
+                                          int a, bool valid) {
+    DcMeta d{0, 0, 0, 0, 1.0f};
+    if (!valid) return d;
+    const int e = act.template nth<SH>(a, A.E);
+    const bool sh = SH && e == A.E;      // the shared expert: one block of all T (<= 16) tokens
+    d.row0 = sh ? S.T * A.k : (int)load_u32(A.offsets + e);
+    d.n_e = sh ? S.T : (int)load_u32(A.offsets + e + 1) - d.row0;
+    const moe_expert_w *W = sh ? S.shared : A.experts + e;
+    d.w = ld_global_u64(&W->w2);
+    d.s = ld_global_u64(&W->s2);
+    if constexpr (tensor_scaled(FMT)) {
+        // the matrix's fp32 scale: after the block scales (NVFP4), or first (FP8)
+        const size_t at = FMT == MOE_W_NVFP4 ? (size_t)A.H * A.K / 16 : 0;
+        d.g = __uint_as_float(load_u32(reinterpret_cast<const uint8_t *>(d.s) + at));
+    }
+    return d;
+}
+
+template <int FMT>
+__device__ __forceinline__ void dc_state(const DecArgs &A, const DcMeta &M, int q,
+                                         DcExpert<FMT> &st) {
+    st.row0 = __builtin_amdgcn_readlane(M.row0, q);
+    st.n_e = __builtin_amdgcn_readlane(M.n_e, q);
+    const void *w = reinterpret_cast<const void *>(readlane_u64(M.w, q));
+    const void *sc = reinterpret_cast<const void *>(readlane_u64(M.s, q));
+    const uint32_t elems = (uint32_t)A.H * (uint32_t)A.K;
+    st.wr = make_rsrc(w, FMT == MOE_W_FP8 ? elems : elems / 2);
+    st.sr = make_rsrc(sc, FMT == MOE_W_NVFP4 ? elems / 16 : elems / 32);
+    if constexpr (tensor_scaled(FMT))
+        st.g = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(M.g), q));
+}
+
+template <int FMT, int NS>
+__device__ __forceinline__ void dc_load(const DcExpert<FMT> &st, int rb, int lane,
+                                        WFrag<FMT> (&f)[NS], bool on) {
+#pragma unroll
+    for (int s = 0; s < NS; ++s) f[s].load_block(st.wr, st.sr, (uint32_t)(rb * NS + s), lane, on);
+}
+
+// One expert's 16 output columns for its rows (at most 16): the product, the
+// bf16 y row pieces to global memory and their values to the LDS rows yl.
+template <int FMT, int NS>
+__device__ __forceinline__ void dc_expert(const DecArgs &A, const DcExpert<FMT> &st,
+                                          WFrag<FMT> (&f)[NS], const uint8_t *actL, float *yl,
+                                          const int *spl, int rb, int m, int c, int nrows) {
+    int r = st.row0 + m;               // operand row (columns m >= n_e are not used)
+    r = r < nrows ? r : nrows - 1;
+    const uint8_t *bp = actL + (size_t)(r >> 4) * NS * 4096 + 16 * ((r & 15) + 16 * c);
+    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int s = 0; s < NS; ++s) f[s].pin();
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const u32x4 b = *reinterpret_cast<const u32x4 *>(bp + (s * 4 + j) * 1024);
+            if constexpr (f16_path(FMT))
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(f[s].get(j), __builtin_bit_cast(f16x8, b),
+                                                            acc, 0, 0, 0);
+            else
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f[s].get(j), as_bf16x8(b), acc, 0, 0,
+                                                             0);
+        }
+    if constexpr (tensor_scaled(FMT)) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[i] *= st.g;
+    }
+    if (m < st.n_e) {
+        const int p = spl[st.row0 + m];
+        uint2 pk;
+        pk.x = pack_bf16x2(acc[0], acc[1]);
+        pk.y = pack_bf16x2(acc[2], acc[3]);
+        *reinterpret_cast<uint2 *>(reinterpret_cast<uint16_t *>(A.out) + (size_t)p * A.H +
+                                   16 * rb + 4 * c) = pk;
+        const f32x4 v = {bf16_bits_to_f32(pk.x & 0xFFFFu), bf16_bits_to_f32(pk.x >> 16),
+                         bf16_bits_to_f32(pk.y & 0xFFFFu), bf16_bits_to_f32(pk.y >> 16)};
+        *reinterpret_cast<f32x4 *>(yl + p * 16 + 4 * c) = v;
+    }
+}
+
+template <int FMT, int NS, bool SH>
+__global__ __launch_bounds__(kWave *kDcWaves) void ffn_dc_kernel(DecArgs A, ShArgs S, DcArgs C) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t dc_lds[];
+    constexpr int D = dc_depth<FMT, NS>();
+    static_assert(D >= 2, "down+combine needs two weight buffers");
+    const int lane = lane_id();
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int m = lane & 15, c = lane >> 4;
+    const int rb = blockIdx.x;
+    const int nrows = C.nrows, ngroups = (nrows + 15) / 16, nk = C.T * A.k;
+    uint8_t *actL = dc_lds;
+    float *yl = reinterpret_cast<float *>(dc_lds + (size_t)ngroups * NS * 4096);
+    int *spl = reinterpret_cast<int *>(yl + nrows * 16);
+    float *wl = reinterpret_cast<float *>(spl + nrows);
+
+    ActiveSet act;
+    act.template init<SH>(A.offsets, A.E, S);
+    // this wavefront's experts: active experts wv, wv + kDcWaves, ...
+    const int nmine = act.count > wv ? (act.count - wv + kDcWaves - 1) / kDcWaves : 0;
+    const DcMeta meta = dc_meta<FMT, SH>(A, S, act, wv + kDcWaves * lane, lane < nmine);
+    DcExpert<FMT> es[D];
+    WFrag<FMT> wr[D][NS];
+    if (nmine > 0) {
+#pragma unroll
+        for (int d = 0; d < D - 1; ++d) {
+            dc_state<FMT>(A, meta, d < nmine ? d : nmine - 1, es[d]);
+            dc_load<FMT, NS>(es[d], rb, lane, wr[d], d < nmine);
+        }
+    }
+    // the activation rows into LDS (rows past the end repeat the last one)
+    const uint16_t *actg = A.src;
+    const int ndma = ngroups * NS * 4;
+    for (int d = wv; d < ndma; d += kDcWaves) {
+        const int g = d / (NS * 4), s = (d >> 2) % NS, j = d & 3;
+        int row = 16 * g + m;
+        row = row < nrows ? row : nrows - 1;
+        lds_dma16(actg + (size_t)row * A.K + s * 128 + 32 * c + 8 * j, actL + (size_t)d * 1024);
+    }
+    // each row's pair (the shared expert's rows are their own) and the weights
+    const int tid = threadIdx.x;
+    if (tid < nrows) spl[tid] = tid < nk ? A.sorted_pair[tid] : tid;
+    if (tid < nk) wl[tid] = C.topk_w[tid];
+    wait_vm<0>();
+    __syncthreads();
+
+    if (nmine > 0) {
+        for (int i = 0; i < nmine; i += D) {
+#pragma unroll
+            for (int d = 0; d < D; ++d) {
+                if (i + d < nmine) {
+                    // prefetch the expert D - 1 ahead into the buffer freed last
+                    const int fd = (d + D - 1) % D, qn = i + d + D - 1;
+                    const bool pf = qn < nmine;
+                    if (pf) dc_state<FMT>(A, meta, qn, es[fd]);
+                    else es[fd] = es[d];
+                    dc_load<FMT, NS>(es[fd], rb, lane, wr[fd], pf);
+                    dc_expert<FMT, NS>(A, es[d], wr[d], actL, yl, spl, rb, m, c, nrows);
+                }
+            }
+        }
+    }
+    __syncthreads();
+    const int t = tid >> 4, col = tid & 15;
+    if (t < C.T) {
+        float acc = 0.0f;
+        for (int j = 0; j < A.k; ++j) acc += wl[t * A.k + j] * yl[(t * A.k + j) * 16 + col];
+        if (SH) acc += yl[(nk + t) * 16 + col];
+        C.out[(size_t)t * A.H + 16 * rb + col] = (uint16_t)f32_to_bf16_bits(acc);
+    }
+}
+
+static size_t dc_lds_bytes(int nrows, int ns, int nk) {
+    return (size_t)((nrows + 15) / 16) * ns * 4096 + (size_t)nrows * 16 * 4 + (size_t)nrows * 4 +
+           (size_t)nk * 4;
+}
+
+template <int FMT, int NS, bool SH>
+static int launch_dc(hipStream_t s, const DecArgs &A, const ShArgs &S, const DcArgs &C) {
+    const size_t lds = dc_lds_bytes(C.nrows, NS, C.T * A.k);
+    static bool attr = false;
+    if (!attr) {
+        if (int rc = check_hip(hipFuncSetAttribute(
+                reinterpret_cast<const void *>(&ffn_dc_kernel<FMT, NS, SH>),
+                hipFuncAttributeMaxDynamicSharedMemorySize, (int)(kDcMaxActLds + 8192))))
+            return rc;
+        attr = true;
+    }
+    MOE_LAUNCH(K_DEC_DOWN, (ffn_dc_kernel<FMT, NS, SH>), dim3((unsigned)(A.H / 16)),
+               dim3(kWave * kDcWaves), lds,
+               s, A, S, C);
+    return check_launch();
+}
+
+// Whether the down + combine launch takes this batch (host check, no device work).
+static bool dc_eligible(int fmt, int T, int k, bool sh, int H, int I) {
+    if (fmt != MOE_W_MXFP4 && fmt != MOE_W_NVFP4 && fmt != MOE_W_FP8) return false;
+    const int nrows = T * k + (sh ? T : 0), ns = I / 128;
+    if (T < 1 || T > kDcMaxT || nrows > kDcMaxRows || H % 16 || I % 128) return false;
+    if (ns != 2 && ns != 4 && ns != 6 && ns != 8 && ns != 12 && ns != 16) return false;
+    if (fmt == MOE_W_FP8 && ns > 8) return false;    // two buffers of 16 slabs exceed the registers
+    return (size_t)((nrows + 15) / 16) * ns * 4096 <= kDcMaxActLds;
+}
+
+template <int FMT, bool SH>
+static int ffn_decode_comb_fmt(const uint16_t *x, const int32_t *sorted_pair,
+                               const int32_t *offsets, const moe_expert_w *experts,
+                               const moe_expert_w *shared, const float *topk_w, int T, int k,
+                               int H, int I, int E, uint16_t *y, uint16_t *out, uint16_t *act,
+                               hipStream_t s) {
+    const long n_pairs = (long)T * k;
+    const long slots = (n_pairs < E ? n_pairs : E) + (SH ? (T + kPass - 1) / kPass : 0);
+    const ShArgs S{shared, T, T * k};
+    DecArgs a1{x, sorted_pair, offsets, experts, act, k, H, H, I, E, 0, 1, 0.0f, 0.0f};
+    int rc = launch_stage<FMT, 1, false, SH>((H + 127) / 128, s, a1, S, slots);
+    if (rc) return rc;
+    const DecArgs a2{act, sorted_pair, offsets, experts, y, k, I, H, I, E, 0, 1, 0.0f, 0.0f};
+    const DcArgs C{topk_w, out, T, T * k + (SH ? T : 0)};
+    switch (I / 128) {
+        case 2: return launch_dc<FMT, 2, SH>(s, a2, S, C);
+        case 4: return launch_dc<FMT, 4, SH>(s, a2, S, C);
+        case 6: return launch_dc<FMT, 6, SH>(s, a2, S, C);
+        case 8: return launch_dc<FMT, 8, SH>(s, a2, S, C);
+        default: break;
+    }
+    if constexpr (FMT != MOE_W_FP8) {
+        if (I / 128 == 12) return launch_dc<FMT, 12, SH>(s, a2, S, C);
+        if (I / 128 == 16) return launch_dc<FMT, 16, SH>(s, a2, S, C);
+    }
+    return MOE_EUNSUPPORTED;
+}
+
+#define MOE_DC_FMT(F, SH)                                                                      \
+    return ffn_decode_comb_fmt<F, SH>(x, sorted_pair, offsets, experts, shared, topk_w, T, k, H, \
+                                      I, E, y, out, act, s)
+#define MOE_DC_DISPATCH(SH)                                                                    \
+    if (!dc_eligible(fmt, T, k, SH, H, I)) return MOE_EUNSUPPORTED;                             \
+    if (fmt == MOE_W_MXFP4) MOE_DC_FMT(MOE_W_MXFP4, SH);                                       \
+    if (fmt == MOE_W_NVFP4) MOE_DC_FMT(MOE_W_NVFP4, SH);                                       \
+    MOE_DC_FMT(MOE_W_FP8, SH)
+
 #define MOE_DEC_FMT(F, SH)                                                                     \
     return ffn_decode_fmt<F, SH>(x, sorted_pair, offsets, experts, shared, T, k, H, I, E, y,   \
                                  y_is_fp32, act, s)
@@ -780,6 +1068,14 @@ int ffn_decode(const uint16_t *x, const int32_t *sorted_pair, const int32_t *off
     const moe_expert_w *shared = nullptr;
     MOE_DEC_DISPATCH(false);
 }
+// Gate/up, then down + combine in one launch; MOE_EUNSUPPORTED (before any
+// device work) when the batch does not fit that launch.
+int ffn_decode_comb(const uint16_t *x, const int32_t *sorted_pair, const int32_t *offsets,
+                    const moe_expert_w *experts, int fmt, const float *topk_w, int T, int k,
+                    int H, int I, int E, uint16_t *y, uint16_t *out, uint16_t *act, hipStream_t s) {
+    const moe_expert_w *shared = nullptr;
+    MOE_DC_DISPATCH(false);
+}
 #else
 int ffn_decode_shared(const uint16_t *x, const int32_t *sorted_pair, const int32_t *offsets,
                       const moe_expert_w *experts, const moe_expert_w *shared, int fmt, int T,
@@ -787,8 +1083,17 @@ int ffn_decode_shared(const uint16_t *x, const int32_t *sorted_pair, const int32
                       hipStream_t s) {
     MOE_DEC_DISPATCH(true);
 }
+int ffn_decode_comb_shared(const uint16_t *x, const int32_t *sorted_pair,
+                           const int32_t *offsets, const moe_expert_w *experts,
+                           const moe_expert_w *shared, int fmt, const float *topk_w, int T,
+                           int k, int H, int I, int E, uint16_t *y, uint16_t *out, uint16_t *act,
+                           hipStream_t s) {
+    MOE_DC_DISPATCH(true);
+}
 #endif
 #undef MOE_DEC_DISPATCH
 #undef MOE_DEC_FMT
+#undef MOE_DC_DISPATCH
+#undef MOE_DC_FMT
 
 }  // namespace moe

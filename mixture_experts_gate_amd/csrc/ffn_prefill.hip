@@ -218,25 +218,6 @@ constexpr int kPreStages = 2;     // computing s, landing s+1
 
 __device__ __forceinline__ int tok_swz(int r) { return (r >> 1) & 7; }
 
-#define MOE_LDS __attribute__((address_space(3)))
-
-// Direct global -> LDS copies: lane l's 16 (4) bytes land at dst + 16 l (4 l);
-// dst is wavefront-uniform.
-__device__ __forceinline__ void lds_dma16(const void *src, void *dst) {
-    __builtin_amdgcn_global_load_lds((const MOE_GLOBAL void *)src, (MOE_LDS void *)dst, 16, 0, 0);
-}
-__device__ __forceinline__ void lds_dma4(const void *src, void *dst) {
-    __builtin_amdgcn_global_load_lds((const MOE_GLOBAL void *)src, (MOE_LDS void *)dst, 4, 0, 0);
-}
-
-// Waits until at most n of this wavefront's vector-memory operations are
-// outstanding (n < 64). gfx9 s_waitcnt fields: vmcnt[3:0] | expcnt[6:4] |
-// lgkmcnt[11:8] | vmcnt_hi[15:14].
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
-}
-
 // Per-lane copy sources of one tile (slab 0; slab s adds s * 128 bytes to a
 // token row, s * 4 to a scale row, s * 1024 / s * 64 to a weight block).
 struct PreSrc {

@@ -137,13 +137,15 @@ class MoeLayer:
 
     # whole layer -----------------------------------------------------------
     def forward(self, T, x, table, logits=None, wg=None, shared_table=None, renormalize=True,
-                stream=None, write_logits=False, fused_routing=True, fuse_shared=True):
+                stream=None, write_logits=False, fused_routing=True, fuse_shared=True,
+                fuse_combine=True):
         """route -> permute -> expert FFN (+ shared expert) -> combine; returns out[:T].
         fused_routing: route and permute with the one-call entry (one kernel for
         small batches) instead of the two separate calls.
         fuse_shared: run the shared expert in the routed FFN's launches
-        (moe_expert_ffn_shared) where the weight-streaming kernels run; else,
-        and where the tiled kernels run, it is its own call on a side stream."""
+        (moe_expert_ffn_shared); else it is its own call on a side stream.
+        fuse_combine: the FFN and the combine through moe_expert_ffn_combine
+        (one down + combine launch at a handful of tokens; bf16 y only)."""
         if T > self.T_max:
             raise ValueError("T exceeds the buffers' T_max")
         wl = write_logits or logits is None
@@ -154,6 +156,13 @@ class MoeLayer:
             self.route(T, x=x, wg=wg, logits=logits, renormalize=renormalize, stream=stream,
                        write_logits=wl)
             self.permute(T, stream)
+        if fuse_combine and not self.y_fp32 and (shared_table is None or fuse_shared):
+            rc = _lib.moe_expert_ffn_combine(
+                x, self.sorted_pair, self.offsets, table, shared_table, self.fmt, T, self.k,
+                self.H, self.I, self.E, self.topk_w, self.y, self.out, self.ws_ffn,
+                self.ws_ffn_bytes, stream, check=False)
+            if rc != _lib.MOE_EUNSUPPORTED:
+                return self.out[:T]
         if shared_table is None:
             self.ffn(T, x, table, stream)
             self.combine(T, stream=stream)

@@ -69,7 +69,7 @@ def workload(c, E=None):
 
 
 def run_layer(w: Workload, T, x, logits=None, wg=None, y_fp32=False, renormalize=True,
-              fused=True, fuse_shared=True):
+              fused=True, fuse_shared=True, fuse_combine=True):
     from mixture_experts_gate_amd.layer import MoeLayer
     cfg = w.cfg
     L = MoeLayer(cfg.H, w.E, cfg.k, cfg.I, cfg.fmt, T, shared=bool(cfg.n_shared), y_fp32=y_fp32,
@@ -80,7 +80,7 @@ def run_layer(w: Workload, T, x, logits=None, wg=None, y_fp32=False, renormalize
                     wg=None if wg is None else to_dev_bf16(wg),
                     shared_table=w.dev_shared.table if w.dev_shared else None,
                     renormalize=renormalize, write_logits=True, fused_routing=fused,
-                    fuse_shared=fuse_shared)
+                    fuse_shared=fuse_shared, fuse_combine=fuse_combine)
     torch.cuda.synchronize()
     return L, out
 
@@ -356,7 +356,7 @@ def test_layer_prefill_cfg3(lib, orc):
     _check_layer_sampled(orc, w, T, x, lg, L, out)
 
 
-@pytest.mark.parametrize("T", [1, 64])
+@pytest.mark.parametrize("T", [1, 2, 64])
 def test_layer_large_sparse_cfg4(lib, orc, T):
     """Config 4 (Zipf routing, shared expert) at decode sizes, every token
     against the oracle: at T=64 the hottest experts take several 16-row token
@@ -622,6 +622,55 @@ def test_layer_nvfp4_fp8_weights(lib, orc, fmt, H, I, E, k, T, kind):
     lg = synth.router_logits(cfg, T, step=2) if kind == "uniform" else _perm_case(T, E, k, kind)
     L, out = run_layer(w, T, x, logits=lg)
     _check_layer_full(orc, w, T, x, L, out, logits=lg)
+
+
+_FC_CASES = [
+    # (fmt, H, I, E, k, shared, T, logits kind)
+    ("mxfp4", 2048, 768, 128, 8, False, 1, "uniform"),   # the decode layer at one token
+    ("mxfp4", 1024, 2048, 32, 6, True, 2, "uniform"),    # 16-slab contraction, 14 rows
+    ("mxfp4", 2048, 768, 128, 4, False, 3, "skew"),      # one expert in every token's first slot
+    ("mxfp4", 512, 256, 16, 1, False, 1, "uniform"),     # one active expert, seven idle wavefronts
+    ("mxfp4", 512, 256, 16, 2, True, 5, "skew"),         # 15 rows, the shared expert's 5
+    ("nvfp4", 1024, 512, 16, 4, True, 3, "uniform"),
+    ("fp8", 1024, 1024, 16, 4, False, 3, "skew"),        # 8 slabs
+    ("fp8", 2048, 768, 128, 8, False, 1, "uniform"),
+    ("mxfp4", 2048, 768, 128, 8, False, 2, "uniform"),   # 16 rows: the two calls
+    ("mxfp4", 512, 256, 16, 1, False, 17, "uniform"),    # more than 16 tokens: the two calls
+]
+
+
+@pytest.mark.parametrize("fmt,H,I,E,k,shared,T,kind", _FC_CASES,
+                         ids=[f"{c[0]}-H{c[1]}-I{c[2]}-E{c[3]}-k{c[4]}{'-sh' if c[5] else ''}"
+                              f"-T{c[6]}-{c[7]}" for c in _FC_CASES])
+def test_ffn_combine(lib, orc, fmt, H, I, E, k, shared, T, kind):
+    """moe_expert_ffn_combine (the layer's default FFN + combine): y rows, the
+    shared expert's rows and the layer output against the oracle; the output
+    against the same layer through moe_expert_ffn + moe_combine (within the
+    tolerance; equal bit for bit where the batch takes the two calls); a
+    repeat call equal bit for bit."""
+    _announce(f"ffn+combine: {fmt} H={H} I={I} E={E} k={k} shared={shared} T={T} {kind}")
+    cfg = synth.LayerConfig(f"fc_{fmt}", H, E, k, I, fmt, 1 if shared else 0, "uniform", (T,),
+                            "gauss_" + fmt, seed=37)
+    w = Workload(cfg)
+    x = synth.activations(cfg, T, step=6)
+    lg = synth.router_logits(cfg, T, step=6) if kind == "uniform" else _perm_case(T, E, k, kind)
+    L, out = run_layer(w, T, x, logits=lg)
+    _check_layer_full(orc, w, T, x, L, out, logits=lg)
+    out_a = out.clone()
+    if shared:
+        ysh_ref = orc.ffn_rows(x, w.shared[None], w.lay, np.arange(T, dtype=np.int32),
+                               np.zeros(T, np.int32))
+        assert_close(L.y[T * k:T * k + T].float().cpu().numpy(), ysh_ref, "shared expert rows")
+    L2, out2 = run_layer(w, T, x, logits=lg, fuse_combine=False)
+    o1, o2 = bf16_dev_to_f64(out_a), bf16_dev_to_f64(out2)
+    two_calls = T > 16 or T * k + (T if shared else 0) > 15
+    if two_calls:
+        assert np.array_equal(o1, o2), "the two-call fallback differs from the two calls"
+    else:
+        assert_close(o1, o2, "fused against the two calls")
+    L3, out3 = run_layer(w, T, x, logits=lg)
+    assert torch.equal(out3, out_a), "repeat call differs"
+    assert torch.equal(L3.y[:T * k], L.y[:T * k])
 
 
 _SHARED_CASES = [("mxfp4", 1, "uniform", False), ("mxfp4", 7, "uniform", False),

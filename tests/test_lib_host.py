@@ -120,6 +120,26 @@ def test_ffn_shared_argument_errors(lib):
                                    0, None) == lib.MOE_OK
 
 
+def test_ffn_combine_argument_errors(lib):
+    """moe_expert_ffn_combine: missing router weights or outputs, a workspace
+    sized without the shared expert's rows and a bad format are refused
+    before device work; T == 0 succeeds."""
+    L = lib.load()
+    dummy = 0x1000  # never dereferenced: validation fails first
+    T, k, H, I, E = 4, 4, 256, 128, 16
+    _, fb_k = lib.moe_workspace_size(T, k, H, I, E)
+    _, fb_k1 = lib.moe_workspace_size(T, k + 1, H, I, E)
+    args = lambda shared, fmt, tw, y, out, wsb: (dummy, dummy, dummy, dummy, shared, fmt, T, k, H,
+                                                 I, E, tw, y, out, dummy, wsb, None)
+    assert L.moe_expert_ffn_combine(*args(None, 1, None, dummy, dummy, fb_k)) == lib.MOE_EINVAL
+    assert L.moe_expert_ffn_combine(*args(None, 1, dummy, None, dummy, fb_k)) == lib.MOE_EINVAL
+    assert L.moe_expert_ffn_combine(*args(None, 1, dummy, dummy, None, fb_k)) == lib.MOE_EINVAL
+    assert L.moe_expert_ffn_combine(*args(dummy, 1, dummy, dummy, dummy, fb_k)) == lib.MOE_EINVAL
+    assert L.moe_expert_ffn_combine(*args(None, 9, dummy, dummy, dummy, fb_k1)) == lib.MOE_EINVAL
+    assert L.moe_expert_ffn_combine(None, None, None, None, None, 1, 0, k, H, I, E, None, None,
+                                    None, None, 0, None) == lib.MOE_OK
+
+
 def test_cache_reserve_argument_errors(lib):
     L = lib.load()
     h = C.c_void_p(0)
