@@ -38,6 +38,8 @@
 // on XCD b % 8), so an expert's tiles share one XCD's L2.
 #include <math.h>
 
+#include <type_traits>
+
 #include "common.hpp"
 
 namespace moe {
@@ -315,8 +317,11 @@ __device__ __forceinline__ void pre_read(const PreStage<FMT> &st, PreFrag<FMT> &
     }
 }
 
-template <int FMT>
-__device__ __forceinline__ void pre_math(const PreFrag<FMT> &f, f32x4 (&acc)[8][2]) {
+// nvb: this wavefront's token blocks that hold rows of the expert (2, 1 or
+// 0; wavefront-uniform): a block wholly past the expert's last row (in the
+// expert's last, partial tile) issues no matrix instructions.
+template <int FMT, int NTB>
+__device__ __forceinline__ void pre_math_tb(const PreFrag<FMT> &f, f32x4 (&acc)[8][2]) {
 #pragma unroll
     for (int term = 0; term < 2; ++term)
 #pragma unroll
@@ -331,7 +336,7 @@ __device__ __forceinline__ void pre_math(const PreFrag<FMT> &f, f32x4 (&acc)[8][
                 a = __builtin_shufflevector(w4, w4, 0, 1, 2, 3, -1, -1, -1, -1);
             }
 #pragma unroll
-            for (int tb = 0; tb < 2; ++tb) {
+            for (int tb = 0; tb < NTB; ++tb) {
                 const int tsc = (int)f.ts[tb] - (term ? kLoShift : 0);
                 // A: E2M1 (format 4) with its E8M0 block scale, or E4M3 (format
                 // 0) with unit scale 127; B: E4M3 (format 0)
@@ -374,7 +379,11 @@ __device__ __forceinline__ void bare_barrier() {
 // `first` runs once, after the first slab's barrier and copies: the previous
 // tile's deferred output stores go there, so that the wait at the top of the
 // first slab does not also wait for them to complete.
-template <int STAGE, int FMT, class First>
+// NVB: this wavefront's token blocks that hold rows of the expert (2, 1 or
+// 0): a block wholly past the expert's last row (in the expert's last,
+// partial tile) issues no matrix instructions. A template argument, chosen
+// once per workgroup, so that the slab loop has no branch around them.
+template <int STAGE, int FMT, int NVB, class First>
 __device__ __forceinline__ void pre_mainloop(PreStage<FMT> (&lds)[kPreStages], f32x4 (&acc)[8][2],
                                              int n, int g0, int wv, int wm, int wn, int lane,
                                              const PreSrc &src, size_t woff, size_t woff_next,
@@ -389,7 +398,7 @@ __device__ __forceinline__ void pre_mainloop(PreStage<FMT> (&lds)[kPreStages], f
         else if (has_next) pre_issue<FMT>(lds[st ^ 1], 0, wv, src, woff_next);
         if (j == 0) first();
         pre_read<STAGE, FMT>(lds[st], F, wm, wn, lane, tp);
-        pre_math<FMT>(F, acc);
+        pre_math_tb<FMT, NVB>(F, acc);
     }
 }
 
@@ -531,6 +540,9 @@ __global__ __launch_bounds__(kPreThreads) void ffn_pre_kernel(PreArgs A) {
     const int row0 = sh ? A.T * A.k : offs[e];
     const int n_e = sh ? A.T : offs[e + 1] - row0;
     const int tok0 = mt * kPreTok;
+    // token blocks of this wavefront (rows tok0 + 32 wm + 16 tb ..) with rows of the expert
+    const int left = n_e - tok0 - 32 * wm;
+    const int nvb = left <= 0 ? 0 : left <= 16 ? 1 : 2;
     const MOE_CONST moe_expert_w *W = sh ? as_scalar(A.shared) : as_scalar(A.experts) + e;
     const uint8_t *wcodes = reinterpret_cast<const uint8_t *>(STAGE == 1 ? W->w13 : W->w2);
     const uint8_t *wscales = reinterpret_cast<const uint8_t *>(STAGE == 1 ? W->s13 : W->s2);
@@ -587,29 +599,37 @@ __global__ __launch_bounds__(kPreThreads) void ffn_pre_kernel(PreArgs A) {
     constexpr bool kDefer = STAGE == 2 && !YF32;
     PreOut pend;
     bool pending = false;
-    for (int t = 0; t < A.nt_group; ++t) {
-        pre_mainloop<STAGE, FMT>(lds, acc, nslab, t * nslab, wv, wm, wn, lane, src, t * wstep,
-                            (t + 1) * wstep, t + 1 < A.nt_group, [&]() {
-                                if (kDefer && pending)
-                                    pre_store_y(A, pend, tok0, n_e, wm, wn, lane, prow_tb);
-                            });
-        if (FMT == MOE_W_FP8) {
+    // the tile group's loop, compiled for 2, 1 and 0 token blocks with rows
+    // (a branch inside the slab loop instead made the kernels 1.6x slower)
+    auto tiles = [&](auto nvb_c) {
+        constexpr int NVB = decltype(nvb_c)::value;
+        for (int t = 0; t < A.nt_group; ++t) {
+            pre_mainloop<STAGE, FMT, NVB>(
+                lds, acc, nslab, t * nslab, wv, wm, wn, lane, src, t * wstep, (t + 1) * wstep,
+                t + 1 < A.nt_group, [&]() {
+                    if (kDefer && pending) pre_store_y(A, pend, tok0, n_e, wm, wn, lane, prow_tb);
+                });
+            if (FMT == MOE_W_FP8) {
+#pragma unroll
+                for (int b = 0; b < 8; ++b)
+#pragma unroll
+                    for (int tb = 0; tb < 2; ++tb) acc[b][tb] *= gsc;
+            }
+            if (kDefer) {
+                pre_pack_y(acc, nt + t, pend);
+                pending = true;
+            } else {
+                pre_epilogue<STAGE, YF32>(A, acc, nt + t, tok0, row0, n_e, wm, wn, lane, prow_tb);
+            }
 #pragma unroll
             for (int b = 0; b < 8; ++b)
 #pragma unroll
-                for (int tb = 0; tb < 2; ++tb) acc[b][tb] *= gsc;
+                for (int tb = 0; tb < 2; ++tb) acc[b][tb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
         }
-        if (kDefer) {
-            pre_pack_y(acc, nt + t, pend);
-            pending = true;
-        } else {
-            pre_epilogue<STAGE, YF32>(A, acc, nt + t, tok0, row0, n_e, wm, wn, lane, prow_tb);
-        }
-#pragma unroll
-        for (int b = 0; b < 8; ++b)
-#pragma unroll
-            for (int tb = 0; tb < 2; ++tb) acc[b][tb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-    }
+    };
+    if (nvb == 2) tiles(std::integral_constant<int, 2>());
+    else if (nvb == 1) tiles(std::integral_constant<int, 1>());
+    else tiles(std::integral_constant<int, 0>());
     if (kDefer && pending) pre_store_y(A, pend, tok0, n_e, wm, wn, lane, prow_tb);
 }
 
