@@ -440,8 +440,7 @@ def run_stack_cached(torch, st, runs, pool_bytes, resize_T=1, resize_steps=32, s
                 ly.route_permute(T, logits=lg[i - s0][l], write_logits=False)
                 ids = ly.topk_ids[:T].cpu().numpy().ravel()
                 tab = cache.prefetch(l, ids)
-                ysh = ly.ffn_with_shared(T, x, tab, stabs[l])
-                ly.combine(T, y_shared=ysh)
+                ly.ffn_combine(T, x, tab, stabs[l])
                 x = ly.out[:T]
 
         for i in range(s0, first):

@@ -193,78 +193,109 @@ __device__ __forceinline__ const uint8_t *srow(const uint8_t *base, long r, int 
 }
 
 // The shared expert of a launch that carries one, as active experts with
-// index E after the routed ones. When no routed expert has more than 16 rows,
-// its T token rows are cut into blocks of one token pass (16 rows), each one
-// more active expert: so the launch keeps its contiguous tile order (one
-// expert over T > 16 rows would switch it to the strided order), and the
-// blocks read the same weights close together in time (mostly from cache).
-// When some routed expert needs several passes anyway, it stays one expert
-// over all T rows. Token t's activation and output row is base + t, base =
-// T*k. A second kernel argument, so that launches without it keep the
-// argument layout (and scalar registers) they had.
+// index E after the routed ones: its T token rows in blocks of one token pass
+// (16 rows), each one more active entry, so the blocks read the same weights
+// close together in time (mostly from cache). Token t's activation and output
+// row is base + t, base = T*k. A second kernel argument, so that launches
+// without it keep the argument layout (and scalar registers) they had.
 struct ShArgs {
     const moe_expert_w *shared;
     int T, base;
 };
 
-// Experts that received at least one pair, as a bitmask (E <= 512), computed
-// by the whole wavefront from one round of loads; lookups afterwards are
-// scalar. With a shared expert it is one more active expert, the last, with
-// expert index E and all T tokens as its rows.
+// Inclusive prefix sum over the wavefront: within rows of 16 lanes by DPP
+// row shifts (lanes before a row's start read 0), then the totals of the
+// rows before this lane's, by lane reads.
+__device__ __forceinline__ int wave_incl_scan(int v) {
+    v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, false);   // row_shr:1
+    v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, false);   // row_shr:2
+    v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, false);   // row_shr:4
+    v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, false);   // row_shr:8
+    const int t0 = __builtin_amdgcn_readlane(v, 15);
+    const int t1 = __builtin_amdgcn_readlane(v, 31);
+    const int t2 = __builtin_amdgcn_readlane(v, 47);
+    const int r = lane_id() >> 4;
+    return v + (r >= 1 ? t0 : 0) + (r >= 2 ? t1 : 0) + (r >= 3 ? t2 : 0);
+}
+
+// Active experts in blocks of one token pass: an expert that received r > 0
+// pairs takes ceil(r / 16) consecutive active entries, each with at most 16
+// rows, so every tile has one token pass and the launch keeps its contiguous
+// tile order whatever the popularity skew (a hot expert's blocks sit side by
+// side and read the same weights close together in time). For group i of 64
+// experts, lane l holds the inclusive count of blocks of experts 64i ..
+// 64i + l (a wavefront scan, from one round of loads); a lookup is a ballot
+// and a lane read. With a shared expert its ceil(T/16) blocks come last, with
+// expert index E. Requires E <= 512.
 struct ActiveSet {
-    uint64_t w[8];
-    int count;               // active experts, the shared one included
-    int routed;              // active routed experts
+    int gtot[8];             // blocks of expert group i (wavefront-uniform)
+    int incl[8];             // lane l: blocks of experts 64i .. 64i + l
+    int count;               // blocks, the shared expert's included
+    int routed;              // blocks of routed experts
     const moe_expert_w *sh_w;  // shared expert's weights and tokens (SH launches)
     int sh_T;
-    bool multi_pass;         // some routed expert has more rows than one token pass
     template <bool SH>
     __device__ __forceinline__ void init(const int32_t *__restrict__ offsets, int E,
                                          const ShArgs &S) {
-        count = 0;
-        int cnt[8];
+        const int lane = lane_id();
+        // all loads first (experts past E read offsets[E] twice: no rows),
+        // so that one wait covers them; groups wholly past E are skipped
+        int o0[8], o1[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            const int e = i * kWave + lane_id();
-            cnt[i] = e < E ? offsets[e + 1] - offsets[e] : 0;
+            o0[i] = o1[i] = 0;
+            if (i * kWave < E) {
+                const int e = min(i * kWave + lane, E);
+                o0[i] = offsets[e];
+                o1[i] = offsets[min(e + 1, E)];
+            }
         }
-        uint64_t many = 0;
+        count = 0;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            w[i] = __ballot(cnt[i] > 0);
-            many |= __ballot(cnt[i] > kPass);
-            count += __popcll(w[i]);
+            incl[i] = 0;
+            gtot[i] = 0;
+            if (i * kWave < E) {
+                incl[i] = wave_incl_scan((o1[i] - o0[i] + kPass - 1) / kPass);
+                gtot[i] = __builtin_amdgcn_readlane(incl[i], kWave - 1);
+            }
+            count += gtot[i];
         }
         routed = count;
-        multi_pass = many != 0;
-        // the shared expert: blocks of 16 tokens, or one block over all T when
-        // the launch has several passes anyway (shared_block)
         if constexpr (SH) {
-            count += multi_pass ? 1 : (S.T + kPass - 1) / kPass;
+            count += (S.T + kPass - 1) / kPass;
             sh_w = S.shared;
             sh_T = S.T;
         }
     }
-    // index of the a-th (0-based) active expert; a < count
-    // (a shared-expert block: E)
+    // expert of the a-th block (a < count; a shared-expert block: E) and the
+    // block's index j within that expert
     template <bool SH>
-    __device__ __forceinline__ int nth(int a, int E) const {
+    __device__ __forceinline__ int nth(int a, int E, int &j) const {
         if constexpr (SH) {
-            if (a >= routed) return E;
+            if (a >= routed) {
+                j = a - routed;
+                return E;
+            }
         }
-        int base = 0;
+        // the group holding block a, found with constant indices only (a
+        // dynamically indexed array would live in scratch memory, and its
+        // load's wait would also drain the weight prefetch in flight)
+        int g = 0, ai = a, inc = incl[0], before = 0;
+        bool found = false;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            const int c = __popcll(w[i]);
-            if (a < c) {
-                uint64_t m = w[i];
-                for (int r = 0; r < a; ++r) m &= m - 1;
-                return i * kWave + __ffsll((long long)m) - 1;
-            }
-            a -= c;
-            base += c;
+            const bool here = !found && a - before < gtot[i];
+            g = here ? i : g;
+            ai = here ? a - before : ai;
+            inc = here ? incl[i] : inc;
+            found = found || here;
+            before += gtot[i];
         }
-        return -1;
+        const uint64_t m = __ballot(inc > ai);
+        const int l = __ffsll((long long)m) - 1;
+        j = ai - (l ? __builtin_amdgcn_readlane(inc, l - 1) : 0);
+        return g * kWave + l;
     }
 };
 
@@ -330,13 +361,12 @@ template <int STAGE, int FMT, bool SH>
 __device__ __forceinline__ void expert_state(const DecArgs &A, const ShArgs &S,
                                              const ActiveSet &act, int a, ExpertState<FMT> &st) {
     st.a = a;
-    st.e = act.template nth<SH>(a, A.E);
+    int j;                                    // block of the expert
+    st.e = act.template nth<SH>(a, A.E, j);
     const MOE_CONST int32_t *off = as_scalar(A.offsets);
     const bool sh = SH && st.e == A.E;        // a block of the shared expert's tokens
-    const int bs = act.multi_pass ? act.sh_T : kPass;   // (its rows per block)
-    const int j = a - act.routed;             // (which block)
-    st.row0 = sh ? act.sh_T * A.k + j * bs : off[st.e];
-    st.n_e = sh ? min(bs, act.sh_T - j * bs) : off[st.e + 1] - st.row0;
+    st.row0 = (sh ? act.sh_T * A.k : off[st.e]) + j * kPass;
+    st.n_e = min(kPass, (sh ? act.sh_T * (A.k + 1) : off[st.e + 1]) - st.row0);
     const MOE_CONST moe_expert_w *W = sh ? as_scalar(act.sh_w) : as_scalar(A.experts) + st.e;
     st.w = reinterpret_cast<const uint8_t *>(STAGE == 1 ? W->w13 : W->w2);
     st.s = reinterpret_cast<const uint8_t *>(STAGE == 1 ? W->s13 : W->s2);
@@ -573,25 +603,15 @@ __device__ __forceinline__ void ffn_dec_body(const DecArgs &A, const ShArgs &S,
 
     ActiveSet act;
     act.template init<SH>(A.offsets, A.E, S);
-    // Tiles are active-expert-major. Workgroups take contiguous ranges, which
-    // keep an expert's token operand in registers across its tiles, unless some
-    // expert has more rows than one token pass: then workgroup b takes tiles b,
-    // b + g, b + 2g, .. (g workgroups), so the tiles of the few experts with
-    // many rows (skewed popularity) spread over many workgroups instead of
-    // stretching the ones that hold them.
+    // Tiles are block-major (a block: up to 16 rows of one expert). Workgroups
+    // take contiguous ranges, which keep a block's token operand in registers
+    // across its tiles; every tile costs one token pass, so equal ranges are
+    // balanced.
     const int total = act.count * A.nrt;
-    int t0, n, ts;
-    if (act.multi_pass) {
-        t0 = blockIdx.x;
-        ts = gridDim.x;
-        n = t0 < total ? (total - t0 + ts - 1) / ts : 0;
-    } else {
-        t0 = split_start(blockIdx.x, gridDim.x, total, A);
-        n = split_start(blockIdx.x + 1, gridDim.x, total, A) - t0;
-        ts = 1;
-    }
+    const int t0 = split_start(blockIdx.x, gridDim.x, total, A);
+    const int n = split_start(blockIdx.x + 1, gridDim.x, total, A) - t0;
     if (n <= 0) return;
-    const int sa = ts / A.nrt, srt = ts % A.nrt;
+    const int sa = 0, srt = 1;
 
     // D register buffers used in turn: tile i computes from one while the
     // weights of tiles i+1 .. i+D-1 are in flight into the others (no copies
@@ -750,8 +770,10 @@ static int ffn_decode_fmt(const uint16_t *x, const int32_t *sorted_pair, const i
                           int H, int I, int E, void *y, int y_is_fp32, uint16_t *act,
                           hipStream_t s) {
     const long n_pairs = (long)T * k;
-    // a shared expert adds one active expert per 16 tokens
-    const long slots = (n_pairs < E ? n_pairs : E) + (SH ? (T + kPass - 1) / kPass : 0);
+    // active blocks: at most one per expert with pairs plus one per 16 pairs,
+    // and one per 16 tokens of a shared expert
+    const long slots = (n_pairs < E ? n_pairs : E) + n_pairs / kPass +
+                       (SH ? (T + kPass - 1) / kPass : 0);
     const ShArgs S{shared, T, T * k};
     DecArgs a1{x, sorted_pair, offsets, experts, act, k, H, H, I, E, 0, 1, 0.0f, 0.0f};
     int rc = launch_stage<FMT, 1, false, SH>((H + 127) / 128, s, a1, S, slots);
@@ -827,15 +849,27 @@ __device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int l) {
            ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), l) << 32);
 }
 
+// Lane q < n of wavefront wv describes active block wv + kDcWaves q. The
+// lookups run with a wavefront-uniform block index (nth is a cross-lane
+// search), one per q; the loads then run per lane.
 template <int FMT, bool SH>
 __device__ __forceinline__ DcMeta dc_meta(const DecArgs &A, const ShArgs &S, const ActiveSet &act,
-                                          int a, bool valid) {
+                                          int wv, int n) {
     DcMeta d{0, 0, 0, 0, 1.0f};
-    if (!valid) return d;
-    const int e = act.template nth<SH>(a, A.E);
-    const bool sh = SH && e == A.E;      // the shared expert: one block of all T (<= 16) tokens
-    d.row0 = sh ? S.T * A.k : (int)load_u32(A.offsets + e);
-    d.n_e = sh ? S.T : (int)load_u32(A.offsets + e + 1) - d.row0;
+    const int lane = lane_id();
+    int e = 0, j = 0;
+    for (int q = 0; q < n; ++q) {
+        int jq;
+        const int eq = act.template nth<SH>(wv + kDcWaves * q, A.E, jq);
+        if (lane == q) {
+            e = eq;
+            j = jq;
+        }
+    }
+    if (lane >= n) return d;
+    const bool sh = SH && e == A.E;      // a block of the shared expert's tokens
+    d.row0 = (sh ? S.T * A.k : (int)load_u32(A.offsets + e)) + j * kPass;
+    d.n_e = min(kPass, (sh ? S.T * (A.k + 1) : (int)load_u32(A.offsets + e + 1)) - d.row0);
     const moe_expert_w *W = sh ? S.shared : A.experts + e;
     d.w = ld_global_u64(&W->w2);
     d.s = ld_global_u64(&W->s2);
@@ -928,7 +962,7 @@ __global__ __launch_bounds__(kWave *kDcWaves) void ffn_dc_kernel(DecArgs A, ShAr
     act.template init<SH>(A.offsets, A.E, S);
     // this wavefront's experts: active experts wv, wv + kDcWaves, ...
     const int nmine = act.count > wv ? (act.count - wv + kDcWaves - 1) / kDcWaves : 0;
-    const DcMeta meta = dc_meta<FMT, SH>(A, S, act, wv + kDcWaves * lane, lane < nmine);
+    const DcMeta meta = dc_meta<FMT, SH>(A, S, act, wv, nmine);
     DcExpert<FMT> es[D];
     WFrag<FMT> wr[D][NS];
     if (nmine > 0) {
@@ -1019,7 +1053,8 @@ static int ffn_decode_comb_fmt(const uint16_t *x, const int32_t *sorted_pair,
                                int H, int I, int E, uint16_t *y, uint16_t *out, uint16_t *act,
                                hipStream_t s) {
     const long n_pairs = (long)T * k;
-    const long slots = (n_pairs < E ? n_pairs : E) + (SH ? (T + kPass - 1) / kPass : 0);
+    const long slots = (n_pairs < E ? n_pairs : E) + n_pairs / kPass +
+                       (SH ? (T + kPass - 1) / kPass : 0);
     const ShArgs S{shared, T, T * k};
     DecArgs a1{x, sorted_pair, offsets, experts, act, k, H, H, I, E, 0, 1, 0.0f, 0.0f};
     int rc = launch_stage<FMT, 1, false, SH>((H + 127) / 128, s, a1, S, slots);

@@ -157,11 +157,7 @@ class MoeLayer:
                        write_logits=wl)
             self.permute(T, stream)
         if fuse_combine and not self.y_fp32 and (shared_table is None or fuse_shared):
-            rc = _lib.moe_expert_ffn_combine(
-                x, self.sorted_pair, self.offsets, table, shared_table, self.fmt, T, self.k,
-                self.H, self.I, self.E, self.topk_w, self.y, self.out, self.ws_ffn,
-                self.ws_ffn_bytes, stream, check=False)
-            if rc != _lib.MOE_EUNSUPPORTED:
+            if self.ffn_combine(T, x, table, shared_table, stream) is not None:
                 return self.out[:T]
         if shared_table is None:
             self.ffn(T, x, table, stream)
@@ -170,6 +166,16 @@ class MoeLayer:
         ysh = self.ffn_with_shared(T, x, table, shared_table, stream, fuse=fuse_shared)
         self.combine(T, stream=stream, y_shared=ysh)
         return self.out[:T]
+
+    def ffn_combine(self, T, x, table, shared_table=None, stream=None):
+        """The expert FFN (with the shared expert when shared_table is given)
+        and the combine through moe_expert_ffn_combine (bf16 y); returns
+        out[:T], or None when the call declines (MOE_EUNSUPPORTED)."""
+        rc = _lib.moe_expert_ffn_combine(
+            x, self.sorted_pair, self.offsets, table, shared_table, self.fmt, T, self.k, self.H,
+            self.I, self.E, self.topk_w, self.y, self.out, self.ws_ffn, self.ws_ffn_bytes, stream,
+            check=False)
+        return None if rc == _lib.MOE_EUNSUPPORTED else self.out[:T]
 
     def ffn_with_shared(self, T, x, table, shared_table, stream=None, fuse=True, perm=None):
         """Routed and shared expert FFN; returns the shared expert's output rows

@@ -359,8 +359,8 @@ def test_layer_prefill_cfg3(lib, orc):
 @pytest.mark.parametrize("T", [1, 2, 64])
 def test_layer_large_sparse_cfg4(lib, orc, T):
     """Config 4 (Zipf routing, shared expert) at decode sizes, every token
-    against the oracle: at T=64 the hottest experts take several 16-row token
-    passes, and checking all tokens covers every row of every pass."""
+    against the oracle: at T=64 the hottest experts' rows span several 16-row
+    blocks, and checking all tokens covers every row of every block."""
     _announce(f"layer: config 4 (shared expert, Zipf), T={T}, all tokens")
     w = workload(4)
     x = synth.activations(w.cfg, T)
@@ -368,7 +368,7 @@ def test_layer_large_sparse_cfg4(lib, orc, T):
     L, out = run_layer(w, T, x, logits=lg)
     ids, _, _ = orc.topk(lg, w.cfg.k)
     if T == 64:
-        assert np.bincount(ids.ravel(), minlength=w.E).max() > 16   # multi-pass experts
+        assert np.bincount(ids.ravel(), minlength=w.E).max() > 16   # experts over one block
     _check_layer_sampled(orc, w, T, x, lg, L, out, n_sample=T)
 
 
@@ -708,10 +708,10 @@ def test_ffn_shared_in_routed_launch(lib, orc, fmt, T, kind, y_fp32):
 @pytest.mark.parametrize("T,k,shared", [(200, 1, False), (200, 1, True), (45, 2, True)])
 def test_decode_multipass_one_hot_expert(lib, orc, T, k, shared):
     """Weight-streaming kernels with every token's first choice on one expert
-    (up to 13 token passes per tile): the strided tile order taken when an
-    expert needs several passes must still cover every row exactly once, and
-    the token operand must be reloaded for the next tile after a later pass."""
-    _announce(f"decode multi-pass: T={T} k={k} one hot expert, shared={shared}")
+    (up to 13 blocks of 16 rows): the expert's blocks, each its own entry of
+    the active set, must cover every row exactly once, and every block must
+    load its own token operand."""
+    _announce(f"decode, one hot expert over many blocks: T={T} k={k} shared={shared}")
     H, I, E = 256, 128, 16
     cfg = synth.LayerConfig("one_hot", H, E, k, I, "mxfp4", int(shared), "uniform", (T,),
                             "gauss_mxfp4", seed=33)

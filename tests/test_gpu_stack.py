@@ -131,8 +131,7 @@ def test_stack_decode_through_cache(stack, orc, T, steps, n_tok):
                 lyc.route_permute(T, logits=lgd, write_logits=False)
                 ids_d = lyc.topk_ids[:T].cpu().numpy()
                 tab = cache.prefetch(l, ids_d.ravel())
-                ysh = lyc.ffn_with_shared(T, x, tab, st["sh_tabs"][l])
-                lyc.combine(T, y_shared=ysh)
+                assert lyc.ffn_combine(T, x, tab, st["sh_tabs"][l]) is not None
                 out_r = lyr.forward(T, x, st["res_tabs"][l], logits=lgd,
                                     shared_table=st["sh_tabs"][l])
                 torch.cuda.synchronize()
