@@ -727,6 +727,37 @@ def test_decode_multipass_one_hot_expert(lib, orc, T, k, shared):
     _check_layer_full(orc, w, T, x, L, out, logits=lg)
 
 
+@pytest.mark.parametrize("E,k,T,kind,shared", [
+    (512, 8, 64, "uniform", False),   # every group of 64 experts in the active set
+    (500, 6, 40, "skew", True),       # a partial last group; one hot expert over 3 blocks
+    (65, 4, 33, "uniform", False),    # the second group holds one expert
+    (1, 1, 40, "uniform", True),      # a single expert: 3 blocks, plus the shared expert's 3
+])
+def test_decode_block_set_shapes(lib, orc, E, k, T, kind, shared):
+    """Weight-streaming kernels (forced) on expert counts that exercise the
+    block set's groups of 64 experts: all eight groups, a partial last
+    group, a single expert split into several blocks; every token against
+    the oracle."""
+    _announce(f"decode block set: E={E} k={k} T={T} {kind} shared={shared}")
+    H, I = 256, 128
+    cfg = synth.LayerConfig("blocks", H, E, k, I, "mxfp4", int(shared), "uniform", (T,),
+                            "gauss_mxfp4", seed=41)
+    w = Workload(cfg)
+    x = synth.activations(cfg, T, step=3)
+    lg = synth.router_logits(cfg, T, step=3) if kind == "uniform" or E < 8 else \
+        _perm_case(T, E, k, kind)
+    lib.moe_set_option(lib.MOE_OPT_FFN_PATH, 1)
+    try:
+        L, out = run_layer(w, T, x, logits=lg)
+    finally:
+        lib.moe_set_option(lib.MOE_OPT_FFN_PATH, 0)
+    _check_layer_full(orc, w, T, x, L, out, logits=lg)
+    if shared:
+        ysh_ref = orc.ffn_rows(x, w.shared[None], w.lay, np.arange(T, dtype=np.int32),
+                               np.zeros(T, np.int32))
+        assert_close(L.y[T * k:T * k + T].float().cpu().numpy(), ysh_ref, "shared expert rows")
+
+
 @pytest.mark.parametrize("T,kind", [(24, "uniform"), (300, "skew")])
 def test_ffn_shared_in_tiled_launch(lib, orc, T, kind):
     """The tiled kernels (forced) with the shared expert as expert E of the
