@@ -15,17 +15,18 @@
 // feed 4 MFMAs, and the token operand is loaded with the same K mapping, so
 // the K order inside an MFMA is a consistent permutation on both sides.
 //
-// Work decomposition (both stages): a tile is two 16-row blocks of one
-// touched expert over the full contraction length K; the KS wavefronts of a
-// workgroup split K, and their partial sums meet in LDS (fixed order). Each
-// workgroup owns a contiguous range of the U * tiles_per_expert tiles (U =
+// Work decomposition (both stages): a tile is NB 16-row blocks of one
+// touched expert's matrix over the full contraction length K, for one block
+// of at most 16 of the expert's rows; the KS wavefronts of a workgroup split
+// K, and their partial sums meet in LDS (fixed order). Each workgroup owns a
+// contiguous range of the U * tiles_per_expert tiles (U = row blocks of the
 // experts with pairs, counted on the device), so the grid is fixed and no
 // host round trip is needed. While a tile is being multiplied, the next
 // tile's weights are already in flight; the token operand stays in registers
-// while consecutive tiles belong to the same expert.
+// while consecutive tiles belong to the same row block.
 //   stage 1: blocks = 16 gate rows and the matching 16 up rows of W13 (K = H);
 //            epilogue a = silu(g) * u -> act[sorted row][I] (bf16).
-//   stage 2: blocks = 32 consecutive rows of W2 (K = I);
+//   stage 2: blocks = 32 or 64 consecutive rows of W2 (K = I);
 //            epilogue -> y[pair][H] (bf16 or fp32).
 #include <math.h>
 
