@@ -645,6 +645,34 @@ def micro(torch, dev):
                 f"{nbytes/(us*1e-6)/1e9:.0f} GB/s")
         del bufs
     torch.cuda.empty_cache()
+    # per-launch floor: back-to-back dependent launches replayed from a graph,
+    # each one workgroup reading 64 KB (one round trip to memory), and the
+    # same with 256 workgroups reading 16 MB (start-up of a full-chip launch)
+    floor = []
+    for nbytes, grid in ((65536, 1), (16 << 20, 256)):
+        small = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        small.fill_(1)
+        n = 32
+        _lib.moe_micro_read(small, nbytes, grid, sink)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(n):
+                _lib.moe_micro_read(small, nbytes, grid, sink)
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(10):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        us = 1000.0 * e0.elapsed_time(e1) / (10 * n)
+        floor.append({"bytes": nbytes, "grid": grid, "us_per_launch": us})
+        log(f"launch floor: {grid} workgroup(s) reading {nbytes/1e6:.2f} MB, {us:.2f} us per launch "
+            f"in a graph")
+        del g, small
+    out["launch_floor"] = floor
     for kind, label in ((0, "bf16_32x32x16"), (1, "scaled_fp4xfp8_16x16x128")):
         grid, iters = 4 * ncu, 2000
         flops = _lib.moe_micro_mfma(kind, grid, iters, sink)
