@@ -20,6 +20,8 @@
 
 #include <vector>
 
+#include <immintrin.h>
+
 #ifdef _OPENMP
 #include <omp.h>
 #endif
@@ -69,22 +71,100 @@ inline void decode_block(const uint8_t *codes, const uint8_t *scales, long rb, i
     }
 }
 
+// The same with AVX2: each code becomes twice its E2M1 value as an int8
+// through a 16-entry byte table (exact integers -12..12), widened to fp32 and
+// multiplied by half the block scale (exact, so the values equal the table
+// decode's bit for bit).
+__attribute__((target("avx2"))) void decode_block_avx2(const uint8_t *codes,
+                                                       const uint8_t *scales, long rb, int s,
+                                                       int nslab, float (*w)[128]) {
+    const size_t blk = (size_t)rb * nslab + s;
+    const uint8_t *c = codes + blk * 1024;
+    const uint8_t *sc = scales + blk * 64;
+    const __m128i lut = _mm_setr_epi8(0, 1, 2, 3, 4, 6, 8, 12, 0, -1, -2, -3, -4, -6, -8, -12);
+    const __m128i m4 = _mm_set1_epi8(0x0F);
+    for (int l = 0; l < 64; ++l) {
+        const __m256 f = _mm256_set1_ps(0.5f * e8m0(sc[l]));
+        const __m128i q = _mm_loadu_si128(reinterpret_cast<const __m128i *>(c + 16 * l));
+        const __m128i lo = _mm_shuffle_epi8(lut, _mm_and_si128(q, m4));
+        const __m128i hi = _mm_shuffle_epi8(lut, _mm_and_si128(_mm_srli_epi16(q, 4), m4));
+        const __m128i v0 = _mm_unpacklo_epi8(lo, hi);   // elements 0..15 (even = low nibble)
+        const __m128i v1 = _mm_unpackhi_epi8(lo, hi);   // elements 16..31
+        float *dst = &w[l & 15][32 * (l >> 4)];
+        _mm256_storeu_ps(dst, _mm256_mul_ps(_mm256_cvtepi32_ps(_mm256_cvtepi8_epi32(v0)), f));
+        _mm256_storeu_ps(dst + 8, _mm256_mul_ps(
+            _mm256_cvtepi32_ps(_mm256_cvtepi8_epi32(_mm_srli_si128(v0, 8))), f));
+        _mm256_storeu_ps(dst + 16,
+                         _mm256_mul_ps(_mm256_cvtepi32_ps(_mm256_cvtepi8_epi32(v1)), f));
+        _mm256_storeu_ps(dst + 24, _mm256_mul_ps(
+            _mm256_cvtepi32_ps(_mm256_cvtepi8_epi32(_mm_srli_si128(v1, 8))), f));
+    }
+}
+
+const bool kHostAvx2 = __builtin_cpu_supports("avx2") && __builtin_cpu_supports("fma");
+
+// moe_cpu_block_rows with AVX2 + FMA: per token row, the 16 output rows'
+// sums are kept as 8-lane partial vectors across all slabs (one horizontal
+// sum per output at the end), each slab's block decoded once for all rows.
+__attribute__((target("avx2,fma"))) void block_rows_avx2(const uint8_t *codes,
+                                                         const uint8_t *scales, long rb, int K,
+                                                         const float *in, int n, float *out,
+                                                         int out_stride) {
+    const int nslab = K / 128;
+    alignas(32) float w[16][128];
+    // 8-lane partial sums [n][16][8] (unaligned loads and stores: a vector of
+    // __m256 would not keep the type's 32-byte alignment)
+    std::vector<float> acc((size_t)n * 16 * 8, 0.0f);
+    for (int s = 0; s < nslab; ++s) {
+        decode_block_avx2(codes, scales, rb, s, nslab, w);
+        for (int r = 0; r < n; ++r) {
+            const float *x = in + (size_t)r * K + 128 * s;
+            float *a = acc.data() + (size_t)r * 128;
+            for (int h = 0; h < 2; ++h) {
+                __m256 t[8];
+                for (int i = 0; i < 8; ++i) t[i] = _mm256_loadu_ps(a + 8 * (8 * h + i));
+                for (int k = 0; k < 128; k += 8) {
+                    const __m256 xv = _mm256_loadu_ps(x + k);
+                    for (int i = 0; i < 8; ++i)
+                        t[i] = _mm256_fmadd_ps(_mm256_load_ps(&w[8 * h + i][k]), xv, t[i]);
+                }
+                for (int i = 0; i < 8; ++i) _mm256_storeu_ps(a + 8 * (8 * h + i), t[i]);
+            }
+        }
+    }
+    for (int r = 0; r < n; ++r)
+        for (int i = 0; i < 16; ++i) {
+            const __m256 v = _mm256_loadu_ps(acc.data() + ((size_t)r * 16 + i) * 8);
+            const __m128 q = _mm_add_ps(_mm256_castps256_ps128(v), _mm256_extractf128_ps(v, 1));
+            const __m128 d = _mm_add_ps(q, _mm_movehl_ps(q, q));
+            const __m128 e = _mm_add_ss(d, _mm_shuffle_ps(d, d, 1));
+            out[(size_t)r * out_stride + 16 * rb + i] = _mm_cvtss_f32(e);
+        }
+}
+
 }  // namespace
 
 // out[r][16 rb + i] = sum_k in[r][k] * W[16 rb + i][k] for the 16 rows of row
-// block rb, every row r < n (in: fp32 rows of length K). Built for AVX2 + FMA
-// hosts and for any x86-64 host; the loader picks the one the host runs.
-__attribute__((target_clones("arch=haswell", "default")))
+// block rb, every row r < n (in: fp32 rows of length K). On hosts with AVX2
+// and FMA (checked once at load) the vector kernel above runs; elsewhere this
+// portable loop (the fp32 sums then add in another order).
 void moe_cpu_block_rows(const uint8_t *codes, const uint8_t *scales, long rb, int K,
                        const float *in, int n, float *out, int out_stride) {
+    if (kHostAvx2) {
+        block_rows_avx2(codes, scales, rb, K, in, n, out, out_stride);
+        return;
+    }
     const int nslab = K / 128;
     float w[16][128];
-    std::vector<float> acc((size_t)n * 16, 0.0f);
+    float acc_small[16 * 16];
+    std::vector<float> acc_big(n > 16 ? (size_t)n * 16 : 0);
+    float *acc = n > 16 ? acc_big.data() : acc_small;
+    for (int i = 0; i < n * 16; ++i) acc[i] = 0.0f;
     for (int s = 0; s < nslab; ++s) {
         decode_block(codes, scales, rb, s, nslab, w);
         for (int r = 0; r < n; ++r) {
             const float *x = in + (size_t)r * K + 128 * s;
-            float *a = &acc[(size_t)r * 16];
+            float *a = acc + (size_t)r * 16;
             for (int i = 0; i < 16; ++i) {
                 float sum = 0.0f;
 #pragma omp simd reduction(+ : sum)
