@@ -692,22 +692,35 @@ def read_peak_for(micro_res, nbytes):
     return max(r["GBs"] for r in rs if r["bytes"] == size)
 
 
-def calibrate_host_expert(lay, blob_ptrs, H, I, threads=0):
+def calibrate_host_expert(torch, dev, store, keys, H, I, threads=0):
     """Host expert kernel cost: seconds per expert (its weights decoded) and per
-    token row, from timing one expert at 1 and 8 rows."""
+    token row, from timing calls at 1 and 8 rows over distinct experts' pinned
+    blobs in turn (so the weights come from host memory, not the host's
+    caches) while host-to-device copies stream on a side stream, as the
+    cache's copies do while the host computes its experts."""
     import numpy as np
     from mixture_experts_gate_amd import _lib
     rng = np.random.default_rng(0)
+    # copy traffic for the timing window: 512 MB pinned -> device, repeated
+    src = torch.empty(512 << 20, dtype=torch.uint8, pin_memory=True)
+    dst = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    side = torch.cuda.Stream(device=dev)
+    with torch.cuda.stream(side):
+        for _ in range(48):            # about 0.4 s at the native link
+            dst.copy_(src, non_blocking=True)
     t = {}
     for n in (1, 8):
         x = (rng.standard_normal((n, H)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
         y = np.empty_like(x)
-        _lib.moe_cpu_expert_ffn(_lib.MOE_W_MXFP4, *blob_ptrs, H, I, x, y, threads)
+        _lib.moe_cpu_expert_ffn(_lib.MOE_W_MXFP4, *store.blob_ptrs(keys[0]), H, I, x, y, threads)
         reps, t0 = 0, time.perf_counter()
-        while time.perf_counter() - t0 < 0.5:
-            _lib.moe_cpu_expert_ffn(_lib.MOE_W_MXFP4, *blob_ptrs, H, I, x, y, threads)
+        while time.perf_counter() - t0 < 0.15:
+            _lib.moe_cpu_expert_ffn(_lib.MOE_W_MXFP4, *store.blob_ptrs(keys[reps % len(keys)]), H, I,
+                                    x, y, threads)
             reps += 1
         t[n] = (time.perf_counter() - t0) / reps
+    side.synchronize()
+    del src, dst
     per_row = max((t[8] - t[1]) / 7.0, 0.0)
     return t[1] - per_row, per_row
 
@@ -754,7 +767,7 @@ def run_qstar(torch, st, store, pool_bytes, T=1, warmup=8, steps=24, links=(None
     c, lay, dev = st.cfg, st.lay, st.dev
     spacked = [pack_to_device(b[None, :], lay, dev) for b in st.shared_blobs]
     stabs = [expert_table(spacked[l % st.D].data_ptr(), 1, lay, device=dev) for l in range(st.L)]
-    a, b = calibrate_host_expert(lay, store.blob_ptrs(0), c.H, c.I)
+    a, b = calibrate_host_expert(torch, dev, store, list(range(0, 64 * 7, 7)), c.H, c.I)
     f = calibrate_host_fixed(torch, dev, c.H)
     native = h2d_peak(torch, dev)
     crossover = lay.nbytes / (a + b) / 1e9
@@ -784,7 +797,8 @@ def run_qstar(torch, st, store, pool_bytes, T=1, warmup=8, steps=24, links=(None
                                                               shared_table=stabs[l],
                                                               host_s_fixed=f,
                                                               host_s_per_expert=a,
-                                                              host_s_per_row=b)
+                                                              host_s_per_row=b,
+                                                              live_host=True)
                             host_experts[0] += int(mask.sum())
                         else:
                             ly.route_permute(T, logits=lg[i][l], write_logits=False)
@@ -807,9 +821,11 @@ def run_qstar(torch, st, store, pool_bytes, T=1, warmup=8, steps=24, links=(None
                 el = time.perf_counter() - t0
                 h1, m1, b1 = cache.stats()
                 gbs, _ = cache.bandwidth()
+                live = cache.host_s_per_expert_live
                 cache.close()
                 r = {"link": "native" if link is None else f"{link:g} GB/s (emulated)",
                      "mode": mode, "T": T, "steps": steps, "tokens_per_s": T * steps / el,
+                     "host_s_per_expert_live": live,
                      "ms_per_step": 1000.0 * el / steps, "measured_link_GBs": gbs,
                      "copied_per_step": (m1 - m0) / steps,
                      "host_experts_per_step": host_experts[0] / steps,
@@ -818,7 +834,8 @@ def run_qstar(torch, st, store, pool_bytes, T=1, warmup=8, steps=24, links=(None
                 log(f"q* leg, link {r['link']}, {mode}: {r['tokens_per_s']:.1f} tok/s, "
                     f"{r['ms_per_step']:.1f} ms/step, copied {r['copied_per_step']:.1f} and "
                     f"host {r['host_experts_per_step']:.1f} experts per step, measured link "
-                    f"{gbs:.1f} GB/s")
+                    f"{gbs:.1f} GB/s" + (f", host {live*1e3:.2f} ms per expert measured live"
+                                         if live else ""))
         finally:
             _lib.moe_set_option(_lib.MOE_OPT_CACHE_THROTTLE_MBS, 0)
     return out

@@ -6,6 +6,8 @@ PyTorch only provides device memory and the stream; every step of the layer
 """
 from __future__ import annotations
 
+import time
+
 import numpy as np
 import torch
 
@@ -211,7 +213,7 @@ class MoeLayer:
 
     def forward_cached_qstar(self, T, x, cache, layer, logits=None, wg=None, shared_table=None,
                              host_s_fixed=0.0, host_s_per_expert=0.0, host_s_per_row=0.0,
-                             link_gbs=0.0, threads=0, stream=None):
+                             link_gbs=0.0, threads=0, stream=None, live_host=False):
         """One layer through an expert cache with the bandwidth-adaptive choice
         of the side that computes each missing expert: route and permute on the
         device and read the permutation back; request the experts (a miss goes
@@ -220,6 +222,10 @@ class MoeLayer:
         without the host experts (moe_permute_split); the host experts' rows on
         the host CPU from their pinned blobs (moe_cpu_expert_ffn) while the
         device works, copied into y (moe_scatter_rows); then the combine.
+        With live_host, the host's cost per expert is the one its expert calls
+        have actually taken in earlier layers through this cache (an
+        exponentially weighted mean, weight 1/4 for the newest layer, seeded
+        by host_s_per_expert), as the link's rate is the one its copies took.
         Returns (out[:T], host_mask). Requires bf16 y and MXFP4 experts."""
         if self.y_fp32 or self.fmt != _lib.MOE_W_MXFP4:
             raise ValueError("the host expert path needs bf16 y and MXFP4 experts")
@@ -243,6 +249,8 @@ class MoeLayer:
         x_host = self._rb_x[:T].numpy().view(np.uint16).copy()
         cnt = np.diff(off)
         ids = np.nonzero(cnt)[0].astype(np.int32)
+        if live_host and cache.host_s_per_expert_live is not None:
+            host_s_per_expert = cache.host_s_per_expert_live
         tab, mask = _lib.expert_cache_prefetch_qstar(cache.handle, layer, ids, cnt[ids],
                                                      host_s_fixed, host_s_per_expert,
                                                      host_s_per_row, self.E, link_gbs, main)
@@ -282,6 +290,7 @@ class MoeLayer:
             # the host experts, while the device runs its share
             hy = self._q_host[:len(h_pairs)].numpy().view(np.uint16)
             row = 0
+            t_host = time.perf_counter()
             for e in np.nonzero(mask)[0]:
                 pairs = sp[off[e]:off[e + 1]]
                 xr = np.ascontiguousarray(x_host[pairs // self.k])
@@ -290,6 +299,12 @@ class MoeLayer:
                                         self.H, self.I, xr, yr, threads)
                 hy[row:row + len(pairs)] = yr
                 row += len(pairs)
+            if live_host:
+                # this layer's host cost per expert, its rows' share taken out
+                n_he = int(mask.sum())
+                per = max(time.perf_counter() - t_host - row * host_s_per_row, 0.0) / n_he
+                prev = cache.host_s_per_expert_live
+                cache.host_s_per_expert_live = per if prev is None else 0.75 * prev + 0.25 * per
             with torch.cuda.stream(main):
                 self._q_rows[:len(h_pairs)].view(torch.int16).copy_(self._q_host[:len(h_pairs)],
                                                                     non_blocking=True)
@@ -375,6 +390,8 @@ class ExpertCache:
         self.handle = _lib.expert_cache_reserve(self.pool, self.pool.numel(), lay.nbytes, n_layers,
                                                 n_experts, self.srcs, lay,
                                                 self.copy_stream.cuda_stream)
+        # host cost per expert measured by the q* path (forward_cached_qstar)
+        self.host_s_per_expert_live = None
 
     def prefetch(self, layer, ids=None, compute_stream=None):
         return _lib.expert_cache_prefetch(self.handle, layer, ids, compute_stream)

@@ -609,3 +609,37 @@ def test_qstar_layer_matches_oracle(env, orc, mode):
             assert torch.equal(out, out_r)
     finally:
         c.close()
+
+
+def test_qstar_live_host_cost(env, orc):
+    """q* with the host's cost per expert measured live: after a layer whose
+    misses ran on the host (a zero seed), the cache holds a positive
+    per-expert time, the next layer's choice uses it in place of the seed, and
+    both layers' outputs match the oracle."""
+    torch = env["torch"]
+    from mixture_experts_gate_amd.layer import MoeLayer
+    from parity import assert_close, bf16_dev_to_f64
+    lay = env["lay"]
+    T = 12
+    rng = np.random.default_rng(9)
+    c = _cache(env, 2 * E)
+    Lq = MoeLayer(H, E, K, I, "mxfp4", T)
+    try:
+        assert c.host_s_per_expert_live is None
+        for l in (1, 3):
+            x_bits = synth.f32_to_bf16_bits(rng.standard_normal((T, H)).astype(np.float32))
+            lg = rng.random((T, E), dtype=np.float32)
+            x = torch.from_numpy(x_bits.view(np.int16)).cuda().view(torch.bfloat16)
+            out, mask = Lq.forward_cached_qstar(T, x, c, l, logits=torch.from_numpy(lg).cuda(),
+                                                host_s_per_expert=0.0, host_s_per_row=0.0,
+                                                link_gbs=1.0, threads=4, live_host=True)
+            torch.cuda.synchronize()
+            if l == 1:
+                assert mask.sum() > 0        # free host time: every miss on the host
+            live = c.host_s_per_expert_live
+            assert live is not None and 0.0 < live < 1.0, live
+            ref = orc.moe_layer(x_bits, lay, env["blobs"][l], K, logits=lg)
+            assert np.array_equal(Lq.topk_ids[:T].cpu().numpy(), ref["ids"])
+            assert_close(bf16_dev_to_f64(out), ref["out_f64"], f"q* live layer {l}")
+    finally:
+        c.close()
