@@ -520,15 +520,15 @@ def test_layer_deterministic(lib, c, T):
         assert torch.equal(u, v)
 
 
-@pytest.mark.parametrize("fuse_shared", [True, False])
-def test_layer_graph_replays(lib, fuse_shared):
-    """Graph replays of the layer (config 4, T=64, its shared expert in the
-    routed launches or as its own call on a side stream) repeat the eager
-    result exactly, with eager calls on the same buffers between the replays."""
-    _announce(f"graph replays of config 4 T=64 against the eager result (fused={fuse_shared})")
+@pytest.mark.parametrize("T,fuse_shared", [(64, True), (64, False), (1, True), (2, True)])
+def test_layer_graph_replays(lib, T, fuse_shared):
+    """Graph replays of the layer (config 4, its shared expert in the routed
+    launches or as its own call on a side stream; at T=1 and 2 the down
+    projection and the combine in one launch) repeat the eager result
+    exactly, with eager calls on the same buffers between the replays."""
+    _announce(f"graph replays of config 4 T={T} against the eager result (fused={fuse_shared})")
     from mixture_experts_gate_amd.layer import MoeLayer
     w = workload(4)
-    T = 64
     x = to_dev_bf16(synth.activations(w.cfg, T, step=6))
     lg = to_dev(synth.router_logits(w.cfg, T, step=6))
     L = MoeLayer(w.cfg.H, w.E, w.cfg.k, w.cfg.I, w.cfg.fmt, T, shared=True, device=DEV)
