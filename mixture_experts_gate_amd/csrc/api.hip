@@ -236,8 +236,8 @@ namespace moe {
 int expert_ffn_call(const uint16_t *x_bf16, const int32_t *sorted_pair, const int32_t *offsets,
                     const moe_expert_w *experts, int fmt, int T, int k, int H, int I, int E,
                     void *y, int y_is_fp32, void *ws, size_t ws_bytes, void *stream) {
-    // E <= 512: the weight-streaming kernels keep the set of active experts
-    // as a 512-bit mask
+    // E <= 512: the weight-streaming kernels scan the active experts in
+    // eight groups of 64
     if (T < 0 || k < 1 || E < 1 || E > 512 || H < 32 || I < 32 || H % 32 || I % 32)
         return MOE_EINVAL;
     if (fmt != MOE_W_MXFP4 && fmt != MOE_W_BF16 && fmt != MOE_W_NVFP4 && fmt != MOE_W_FP8)
