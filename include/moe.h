@@ -277,6 +277,31 @@ int moe_expert_ffn_combine(const uint16_t *x_bf16, const int32_t *sorted_pair,
                            size_t ws_bytes, void *stream);
 
 /*
+ * moe_permute_ffn_combine -- moe_permute followed by moe_expert_ffn_combine
+ * (the router's ids in; the permutation, y and the layer output out), with
+ * the same results as the two calls: offsets, sorted_pair and pair_row
+ * bitwise, y and out as moe_expert_ffn_combine gives them.
+ *
+ * The routed experts are found from the ids (winzheng.com page, "Why Now of
+ * All Times": a few of the layer's experts per token), so the grouping by
+ * expert can happen where the experts' weights are first needed. For MXFP4
+ * weights with E <= 256, 16 to 512 pairs and more than 15 activation rows on
+ * the weight-streaming kernels, the gate/up launch derives the permutation
+ * itself (every wavefront counts and ranks the ids in LDS) and writes it out
+ * for the down projection and the combine, so no permutation launch runs.
+ * Otherwise the two calls run; the permutation's workspace, where it needs
+ * one, is ws. T = 0 writes offsets only (all zero).
+ * ws / ws_bytes as for moe_expert_ffn_combine. Errors as moe_expert_ffn_combine;
+ * topk_ids, sorted_pair and pair_row must not be NULL for T > 0.
+ */
+int moe_permute_ffn_combine(const uint16_t *x_bf16, const int32_t *topk_ids,
+                            const float *topk_w, const moe_expert_w *experts,
+                            const moe_expert_w *shared, int fmt, int T, int k, int H, int I,
+                            int E, int32_t *offsets, int32_t *sorted_pair, int32_t *pair_row,
+                            uint16_t *y_bf16, uint16_t *out_bf16, void *ws, size_t ws_bytes,
+                            void *stream);
+
+/*
  * moe_pack_mxfp4 -- convert n expert blobs from the interchange MXFP4 layout
  * to the kernel layout (see the top of this file). src and dst are device
  * buffers of n blobs spaced src_stride / dst_stride bytes apart; within a blob

@@ -32,7 +32,7 @@ EXPORTS = [
     "expert_cache_reserve", "expert_cache_prefetch", "expert_cache_evict", "expert_cache_stats",
     "expert_cache_slots", "expert_cache_slot_of", "expert_cache_destroy", "expert_cache_resize",
     "moe_micro_read", "moe_micro_mfma", "expert_cache_bandwidth", "expert_cache_prefetch_qstar",
-    "moe_permute_split", "moe_cpu_expert_ffn", "moe_scatter_rows",
+    "moe_permute_split", "moe_cpu_expert_ffn", "moe_scatter_rows", "moe_permute_ffn_combine",
 ]
 
 
@@ -72,6 +72,8 @@ def load(path: str | None = None):
         "moe_expert_ffn_shared": (I, [P, P, P, P, P, I, I, I, I, I, I, P, I, P, Z, P]),
         "moe_expert_ffn_noalloc": (I, [P, P, P, P, I, I, I, I, I, I, P, I, P]),
         "moe_expert_ffn_combine": (I, [P, P, P, P, P, I, I, I, I, I, I, P, P, P, P, Z, P]),
+        "moe_permute_ffn_combine": (I, [P, P, P, P, P, I, I, I, I, I, I, P, P, P, P, P, P, Z,
+                                        P]),
         "moe_combine": (I, [P, I, P, P, I, I, I, P, P]),
         "moe_workspace_size": (I, [I, I, I, I, I, C.POINTER(Z), C.POINTER(Z)]),
         "moe_set_option": (I, [I, I]),
@@ -186,6 +188,16 @@ def moe_expert_ffn_combine(x_bf16, sorted_pair, offsets, experts, shared, fmt, T
     if not check and rc == MOE_EUNSUPPORTED:
         return rc
     return _check("moe_expert_ffn_combine", rc)
+
+
+def moe_permute_ffn_combine(x_bf16, topk_ids, topk_w, experts, shared, fmt, T, k, H, I, E,
+                            offsets, sorted_pair, pair_row, y, out, ws, ws_bytes, stream=None):
+    """The permutation of the router's ids, the expert FFN (with the shared
+    expert when `shared` is given) and the weighted combine into `out`."""
+    _check("moe_permute_ffn_combine", load().moe_permute_ffn_combine(
+        _ptr(x_bf16), _ptr(topk_ids), _ptr(topk_w), _ptr(experts), _ptr(shared), fmt, T, k, H, I,
+        E, _ptr(offsets), _ptr(sorted_pair), _ptr(pair_row), _ptr(y), _ptr(out), _ptr(ws),
+        ws_bytes, _stream(stream)))
 
 
 FFN_NOALLOC_MAX_WS = 64 << 20

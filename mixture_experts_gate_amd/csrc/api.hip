@@ -112,6 +112,13 @@ int ffn_decode_comb_shared(const uint16_t *x, const int32_t *sorted_pair,
                            const moe_expert_w *shared, int fmt, const float *topk_w, int T,
                            int k, int H, int I, int E, uint16_t *y, uint16_t *out, uint16_t *act,
                            hipStream_t s);
+int ffn_decode_ids(const uint16_t *x, const int32_t *ids, const moe_expert_w *experts, int fmt,
+                   int T, int k, int H, int I, int E, void *y, int y_is_fp32, int32_t *offsets,
+                   int32_t *sorted_pair, int32_t *pair_row, uint16_t *act, hipStream_t s);
+int ffn_decode_ids_shared(const uint16_t *x, const int32_t *ids, const moe_expert_w *experts,
+                          const moe_expert_w *shared, int fmt, int T, int k, int H, int I, int E,
+                          void *y, int y_is_fp32, int32_t *offsets, int32_t *sorted_pair,
+                          int32_t *pair_row, uint16_t *act, hipStream_t s);
 int ffn_prefill(const uint16_t *x, const int32_t *sorted_pair, const int32_t *offsets,
                 const moe_expert_w *experts, const moe_expert_w *shared, int fmt, int T, int k,
                 int H, int I, int E, void *y, int y_is_fp32, void *ws, hipStream_t s);
@@ -328,4 +335,47 @@ extern "C" int moe_expert_ffn_combine(const uint16_t *x_bf16, const int32_t *sor
     if (rc) return rc;
     return moe_combine(y_bf16, 0, topk_w, shared ? y_bf16 + (size_t)n * H : nullptr, T, k, H,
                        out_bf16, stream);
+}
+
+extern "C" int moe_permute_ffn_combine(const uint16_t *x_bf16, const int32_t *topk_ids,
+                                       const float *topk_w, const moe_expert_w *experts,
+                                       const moe_expert_w *shared, int fmt, int T, int k, int H,
+                                       int I, int E, int32_t *offsets, int32_t *sorted_pair,
+                                       int32_t *pair_row, uint16_t *y_bf16, uint16_t *out_bf16,
+                                       void *ws, size_t ws_bytes, void *stream) {
+    if (T < 0 || k < 1 || E < 1 || E > 512 || H < 32 || I < 32 || H % 32 || I % 32)
+        return MOE_EINVAL;
+    if (fmt != MOE_W_MXFP4 && fmt != MOE_W_BF16 && fmt != MOE_W_NVFP4 && fmt != MOE_W_FP8)
+        return MOE_EINVAL;
+    if (fmt != MOE_W_BF16 && (H % 128 || I % 128)) return MOE_EINVAL;
+    if (!offsets) return MOE_EINVAL;
+    if (T > 0 && (!x_bf16 || !topk_ids || !topk_w || !experts || !sorted_pair || !pair_row ||
+                  !y_bf16 || !out_bf16 || !ws))
+        return MOE_EINVAL;
+    const long n = (long)T * k;
+    const long rows = n + (shared ? T : 0);
+    if (rows > 0x7FFFFFFFL) return MOE_EINVAL;
+    if (T > 0 && ws_bytes < ffn_ws_bytes(rows, T, H, I, E)) return MOE_EINVAL;
+    hipStream_t s = (hipStream_t)stream;
+    // the permutation inside the gate/up launch: more than 15 rows (fewer
+    // take the down + combine launch), weight-streaming kernels
+    if (rows > 15 && !use_prefill(n, E, fmt, H, I)) {
+        uint16_t *act = reinterpret_cast<uint16_t *>(ws);
+        int rc = shared ? ffn_decode_ids_shared(x_bf16, topk_ids, experts, shared, fmt, T, k, H,
+                                                I, E, y_bf16, 0, offsets, sorted_pair, pair_row,
+                                                act, s)
+                        : ffn_decode_ids(x_bf16, topk_ids, experts, fmt, T, k, H, I, E, y_bf16,
+                                         0, offsets, sorted_pair, pair_row, act, s);
+        if (rc != MOE_EUNSUPPORTED) {
+            if (rc) return rc;
+            return moe_combine(y_bf16, 0, topk_w, shared ? y_bf16 + (size_t)n * H : nullptr, T,
+                               k, H, out_bf16, stream);
+        }
+    }
+    // the two calls (the permutation's workspace, when it needs one, is the
+    // FFN's: the stream runs the permutation before the FFN uses it)
+    int rc = moe_permute(topk_ids, T, k, E, offsets, sorted_pair, pair_row, ws, ws_bytes, stream);
+    if (rc) return rc;
+    return moe_expert_ffn_combine(x_bf16, sorted_pair, offsets, experts, shared, fmt, T, k, H, I,
+                                  E, topk_w, y_bf16, out_bf16, ws, ws_bytes, stream);
 }

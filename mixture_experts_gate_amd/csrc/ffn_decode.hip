@@ -228,6 +228,58 @@ __device__ __forceinline__ int wave_incl_scan(int v) {
 // 64i + l (a wavefront scan, from one round of loads); a lookup is a ballot
 // and a lane read. With a shared expert its ceil(T/16) blocks come last, with
 // expert index E. Requires E <= 512.
+// A gate/up launch may also take the routing ids instead of the permutation
+// and derive what it needs itself (moe_permute_ffn_combine), so that no
+// permutation launch runs before it: every wavefront of a tile workgroup
+// counts the ids per expert in its own LDS region (no barrier: one
+// wavefront's LDS operations run in order) for the offsets, and finds a
+// block's pairs, the occurrences j*16 .. j*16+15 of its expert in pair
+// order, with one ballot per 64-pair chunk. One more workgroup (index 0,
+// dispatched first) ranks all pairs, the stable counting sort of
+// moe_permute, and writes the permutation out for the down projection and
+// the combine. Per wavefront: offsets [E + 1], running bases [E], sorted
+// pairs [n] (used by workgroup 0 only).
+constexpr int kIdsMaxPairs = 512;       // pairs (T * k) of such a launch
+constexpr size_t kLdsPerCu = 160 * 1024;
+constexpr int kIdsMaxE = 256;           // experts: ids fit 8 bits
+constexpr int kIdsChunks = kIdsMaxPairs / kWave;
+__host__ __device__ constexpr int ids_wave_ints(int E, int n) { return (2 * E + 1 + n + 3) & ~3; }
+
+// Rank of this lane's value e among the lanes before it with the same e
+// (lanes with !valid take no part), by one ballot per bit of e (a
+// multisplit); *same = lanes with this lane's e.
+template <int NBITS>
+__device__ __forceinline__ int wave_rank_bits(bool valid, int e, int *same) {
+    uint64_t m = __ballot(valid);
+#pragma unroll
+    for (int b = 0; b < NBITS; ++b) {
+        const bool bit = valid && ((e >> b) & 1);
+        const uint64_t bb = __ballot(bit);
+        m &= bit ? bb : ~bb;
+    }
+    *same = __popcll(m);
+    return __popcll(m & lanemask_lt());
+}
+
+// Position of the k-th (0-based) set bit of b (k < popcount(b)).
+__device__ __forceinline__ int nth_bit(uint64_t b, int k) {
+    const uint32_t lo = (uint32_t)b;
+    const int plo = __popc(lo);
+    const bool hi = k >= plo;
+    uint32_t w = hi ? (uint32_t)(b >> 32) : lo;
+    int pos = hi ? 32 : 0;
+    k = hi ? k - plo : k;
+#pragma unroll
+    for (int sh = 16; sh >= 1; sh >>= 1) {
+        const int pl = __popc(w & ((1u << sh) - 1u));
+        const bool up = k >= pl;
+        k = up ? k - pl : k;
+        w = up ? w >> sh : w;
+        pos += up ? sh : 0;
+    }
+    return pos;
+}
+
 struct ActiveSet {
     int gtot[8];             // blocks of expert group i (wavefront-uniform)
     int incl[8];             // lane l: blocks of experts 64i .. 64i + l
@@ -235,6 +287,108 @@ struct ActiveSet {
     int routed;              // blocks of routed experts
     const moe_expert_w *sh_w;  // shared expert's weights and tokens (SH launches)
     int sh_T;
+    // launches from the routing ids: this wavefront's permutation in LDS
+    int *loff;               // [E + 1] offsets, then [E] running bases
+    int *lsrt;               // [n] sorted pair indices
+    int idv[kIdsChunks];     // lane l: id of pair 64c + l (-1: none, or outside [0, E))
+
+    // From the routing ids (n <= kIdsMaxPairs pairs, E <= kIdsMaxE): the
+    // counts and offsets; the ranks follow in rank_ids. wl: ids_wave_ints(E, n)
+    // ints of LDS for this wavefront alone.
+    template <bool SH>
+    __device__ __forceinline__ void init_ids(const int32_t *__restrict__ ids, int n, int E,
+                                             const ShArgs &S, int *wl, int *ids_wg) {
+        const int lane = lane_id();
+        loff = wl;
+        int *cnt = wl + E + 1;
+        lsrt = wl + 2 * E + 1;
+        for (int e = lane; e < E; e += kWave) cnt[e] = 0;
+        // the workgroup's wavefronts load the chunks in turn (lanes past n
+        // read the last id again and drop it) into the workgroup's copy
+        // (ids_wg, kIdsMaxPairs ints), and each then reads all of them
+        const int wv = threadIdx.x / kWave, nw = blockDim.x / kWave;
+        for (int c = wv; c < kIdsChunks; c += nw) {
+            if (c * kWave < n) {
+                const int p = c * kWave + lane;
+                const int v = ids[min(p, n - 1)];
+                ids_wg[p] = p < n && v >= 0 && v < E ? v : -1;
+            }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int c = 0; c < kIdsChunks; ++c) idv[c] = c * kWave < n ? ids_wg[c * kWave + lane] : -1;
+#pragma unroll
+        for (int c = 0; c < kIdsChunks; ++c)
+            if (idv[c] >= 0) atomicAdd(&cnt[idv[c]], 1);
+        // per group of 64 experts: offsets (exclusive scan of the counts) and
+        // blocks (as init)
+        count = 0;
+        int base = 0;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            incl[i] = 0;
+            gtot[i] = 0;
+            if (i * kWave < E) {
+                const int e = i * kWave + lane;
+                const int ce = e < E ? cnt[e] : 0;
+                const int ic = wave_incl_scan(ce);
+                if (e < E) {
+                    loff[e] = base + ic - ce;
+                    cnt[e] = base + ic - ce;
+                }
+                base += __builtin_amdgcn_readlane(ic, kWave - 1);
+                incl[i] = wave_incl_scan((ce + kPass - 1) / kPass);
+                gtot[i] = __builtin_amdgcn_readlane(incl[i], kWave - 1);
+            }
+            count += gtot[i];
+        }
+        if (lane == 0) loff[E] = base;
+        routed = count;
+        if constexpr (SH) {
+            count += (S.T + kPass - 1) / kPass;
+            sh_w = S.shared;
+            sh_T = S.T;
+        }
+    }
+    // Pair index of occurrence q (in pair order) of expert e (q past e's
+    // pairs: 0), by one ballot per chunk, the chunk holding q chosen by
+    // selects against the chunks' running counts, and one bit search. No
+    // branches: a branch here, inside the tile loop, made the compiler's
+    // waits before the products also wait for part of the weight prefetch.
+    __device__ __forceinline__ int pair_of(int e, int q) const {
+        uint64_t bm = 0;
+        int before = 0, base = 0, cc = 0;
+#pragma unroll
+        for (int c = 0; c < kIdsChunks; ++c) {
+            const uint64_t b = __ballot(idv[c] == e);
+            const bool ge = q >= before;        // chunk c starts at or before q
+            bm = ge ? b : bm;
+            base = ge ? before : base;
+            cc = ge ? c : cc;
+            before += __popcll(b);
+        }
+        const bool ok = q < before;
+        return ok ? cc * kWave + nth_bit(bm, ok ? q - base : 0) : 0;
+    }
+    // Stable ranks: pair p of expert e goes to lsrt[offsets[e] + (pairs of e
+    // before p)], chunk by chunk in pair order.
+    __device__ __forceinline__ void rank_ids(int n, int E) {
+        const int lane = lane_id();
+        int *cnt = loff + E + 1;
+#pragma unroll
+        for (int c = 0; c < kIdsChunks; ++c) {
+            if (c * kWave < n) {
+                const bool valid = idv[c] >= 0;
+                int same;
+                const int r = wave_rank_bits<8>(valid, idv[c], &same);
+                if (valid) {
+                    const int b = cnt[idv[c]];
+                    lsrt[b + r] = c * kWave + lane;
+                    if (r == 0) cnt[idv[c]] = b + same;
+                }
+            }
+        }
+    }
     template <bool SH>
     __device__ __forceinline__ void init(const int32_t *__restrict__ offsets, int E,
                                          const ShArgs &S) {
@@ -300,6 +454,15 @@ struct ActiveSet {
     }
 };
 
+// Routing ids of a gate/up launch that derives the permutation (init_ids);
+// the permutation's offsets and sorted pairs go to DecArgs' offsets and
+// sorted_pair, which are outputs then.
+struct IdsArgs {
+    const int32_t *ids;             // [n] expert ids of the pairs (topk_ids)
+    int32_t *pair_row;              // [n] output: sorted position of each pair
+    int n;
+};
+
 struct DecArgs {
     const uint16_t *src;            // B-operand rows: x [T][H] (stage 1) or act [T*k][I] (stage 2)
     const int32_t *sorted_pair;
@@ -358,16 +521,26 @@ struct ExpertState : TensorScale<tensor_scaled(FMT)> {
 // SH: the launch carries the shared expert (compiled out otherwise). Only its
 // weights and token count stay in registers (the gate/up kernels run at the
 // scalar-register limit); block size and row base are derived where used.
-template <int STAGE, int FMT, bool SH>
+template <int STAGE, int FMT, bool SH, bool IDS = false>
 __device__ __forceinline__ void expert_state(const DecArgs &A, const ShArgs &S,
                                              const ActiveSet &act, int a, ExpertState<FMT> &st) {
     st.a = a;
     int j;                                    // block of the expert
     st.e = act.template nth<SH>(a, A.E, j);
-    const MOE_CONST int32_t *off = as_scalar(A.offsets);
     const bool sh = SH && st.e == A.E;        // a block of the shared expert's tokens
-    st.row0 = (sh ? act.sh_T * A.k : off[st.e]) + j * kPass;
-    st.n_e = min(kPass, (sh ? act.sh_T * (A.k + 1) : off[st.e + 1]) - st.row0);
+    int o_lo, o_hi;                           // offsets[e], offsets[e + 1]
+    if constexpr (IDS) {
+        // from this wavefront's LDS copy (uniform address; e == E reads
+        // past the offsets, unused)
+        o_lo = __builtin_amdgcn_readfirstlane(act.loff[st.e]);
+        o_hi = __builtin_amdgcn_readfirstlane(act.loff[st.e + 1]);
+    } else {
+        const MOE_CONST int32_t *off = as_scalar(A.offsets);
+        o_lo = off[st.e];
+        o_hi = off[st.e + 1];
+    }
+    st.row0 = (sh ? act.sh_T * A.k : o_lo) + j * kPass;
+    st.n_e = min(kPass, (sh ? act.sh_T * (A.k + 1) : o_hi) - st.row0);
     const MOE_CONST moe_expert_w *W = sh ? as_scalar(act.sh_w) : as_scalar(A.experts) + st.e;
     st.w = reinterpret_cast<const uint8_t *>(STAGE == 1 ? W->w13 : W->w2);
     st.s = reinterpret_cast<const uint8_t *>(STAGE == 1 ? W->s13 : W->s2);
@@ -425,17 +598,23 @@ __device__ __forceinline__ void load_tile(const DecArgs &A, const ExpertState<FM
 
 // Token operand of pass p (rows p*16 .. p*16+15 of the expert), K slabs of
 // this wavefront; for stage 2 also the pair index each row's output goes to.
-template <int STAGE, int SPW, bool SH, class ES>
+template <int STAGE, int SPW, bool SH, bool IDS, class ES>
 __device__ __forceinline__ void load_tokens(const DecArgs &A, const ShArgs &S, const ES &st,
                                             int p, int wv, int m, int c, u32x4 (&xr)[SPW][4],
-                                            int &pidx) {
+                                            int &pidx, const ActiveSet &act) {
     const int nblk = A.K / 32;
     const int r = p * kPass + m;
     const bool has = r < st.n_e;
     const uint16_t *row;
     // shared-expert block: row r is token row0 - base + r; its output row is row0 + r
     const bool sh = SH && st.e == A.E;
-    if (STAGE == 1) {
+    if (STAGE == 1 && IDS) {
+        // lane m's pair: occurrence (row - offsets[e]) of the expert among the
+        // ids (rows past the block give pair 0, not loaded)
+        const int q = st.row0 - __builtin_amdgcn_readfirstlane(act.loff[st.e]) + r;
+        const int pair = act.pair_of(st.e, q);
+        row = A.src + (size_t)(sh ? st.row0 - S.T * A.k + r : pair / A.k) * A.K;
+    } else if (STAGE == 1) {
         // the pass's 16 pair indices by scalar loads; lane m takes the m-th.
         // (A shared-expert block reads the first entries instead, in bounds
         // since p * 16 + i < n_e <= T <= T*k, and takes its token: a select,
@@ -462,7 +641,8 @@ __device__ __forceinline__ void load_tokens(const DecArgs &A, const ShArgs &S, c
 
 // One tile: token operand if the expert changed, prefetch of the next tile's
 // weights into `wn`, multiply from `wc`, K-split reduction, epilogue.
-template <int FMT, int STAGE, int SPW, int KS, int NB, bool YF32, bool FULL, int D, bool SH>
+template <int FMT, int STAGE, int SPW, int KS, int NB, bool YF32, bool FULL, int D, bool SH,
+          bool IDS>
 __device__ __forceinline__ void dec_step(const DecArgs &A, const ShArgs &S, const ActiveSet &act,
                                          float (&red)[2][KS > 1 ? KS - 1 : 1][NB][4][kWave],
                                          WFrag<FMT> (&wc)[SPW][NB], WFrag<FMT> (&wn)[SPW][NB],
@@ -475,7 +655,7 @@ __device__ __forceinline__ void dec_step(const DecArgs &A, const ShArgs &S, cons
         // prefetch, so that waiting for it does not wait for the prefetched weights).
         // x_key: the active expert whose first pass the registers hold, or -1
         if (x_key != cur.a) {
-            load_tokens<STAGE, SPW, SH>(A, S, cur, 0, wv, m, c, xr, pidx);
+            load_tokens<STAGE, SPW, SH, IDS>(A, S, cur, 0, wv, m, c, xr, pidx, act);
             x_key = cur.a;
             x_raw = true;
         }
@@ -483,12 +663,12 @@ __device__ __forceinline__ void dec_step(const DecArgs &A, const ShArgs &S, cons
         // `prev` holds the state of the tile before it. Issued, switched off,
         // also past the end (see buf_rsrc).
         const int an = pf ? pn.a : prev.a;
-        if (an != prev.a) expert_state<STAGE, FMT, SH>(A, S, act, an, nxt);
+        if (an != prev.a) expert_state<STAGE, FMT, SH, IDS>(A, S, act, an, nxt);
         else nxt = prev;
         load_tile<FMT, STAGE, SPW, NB, FULL>(A, nxt, pf ? pn.rt : 0, wv, lane, wn, pf);
         for (int p = 0; p * kPass < cur.n_e; ++p) {
             if (p > 0) {   // more than 16 tokens: next 16 of this expert
-                load_tokens<STAGE, SPW, SH>(A, S, cur, p, wv, m, c, xr, pidx);
+                load_tokens<STAGE, SPW, SH, IDS>(A, S, cur, p, wv, m, c, xr, pidx, act);
                 x_key = -1;     // a later pass: the next tile reloads its first
                 x_raw = true;
             }
@@ -595,22 +775,53 @@ __device__ __forceinline__ void dec_step(const DecArgs &A, const ShArgs &S, cons
         }
 }
 
-template <int FMT, int STAGE, int SPW, int KS, int NB, bool YF32, bool FULL, bool SH>
-__device__ __forceinline__ void ffn_dec_body(const DecArgs &A, const ShArgs &S,
-                                             float (&red)[2][KS > 1 ? KS - 1 : 1][NB][4][kWave]) {
+// Workgroup 0 of a launch from the routing ids writes the permutation out
+// (offsets, sorted pairs and each pair's sorted position, as moe_permute).
+__device__ __forceinline__ void write_perm(const DecArgs &A, const IdsArgs &I,
+                                           const ActiveSet &act) {
+    const int lane = lane_id();
+    int32_t *offsets = const_cast<int32_t *>(A.offsets);
+    int32_t *sorted = const_cast<int32_t *>(A.sorted_pair);
+    for (int e = lane; e <= A.E; e += kWave) offsets[e] = act.loff[e];
+    const int nv = act.loff[A.E];
+    for (int q = lane; q < nv; q += kWave) {
+        const int pair = act.lsrt[q];
+        sorted[q] = pair;
+        I.pair_row[pair] = q;
+    }
+}
+
+template <int FMT, int STAGE, int SPW, int KS, int NB, bool YF32, bool FULL, bool SH, bool IDS>
+__device__ __forceinline__ void ffn_dec_body(const DecArgs &A, const ShArgs &S, const IdsArgs &I,
+                                             float (&red)[2][KS > 1 ? KS - 1 : 1][NB][4][kWave],
+                                             int *ids_lds) {
     const int lane = lane_id();
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);   // wavefront-uniform
     const int m = lane & 15, c = lane >> 4;
 
     ActiveSet act;
-    act.template init<SH>(A.offsets, A.E, S);
+    if constexpr (IDS) {
+        act.template init_ids<SH>(I.ids, I.n, A.E, S, ids_lds + wv * ids_wave_ints(A.E, I.n),
+                                  ids_lds + KS * ids_wave_ints(A.E, I.n));
+        if (blockIdx.x == 0) {
+            // the permutation workgroup: one wavefront ranks and writes
+            if (wv == 0) {
+                act.rank_ids(I.n, A.E);
+                write_perm(A, I, act);
+            }
+            return;
+        }
+    } else {
+        act.template init<SH>(A.offsets, A.E, S);
+    }
     // Tiles are block-major (a block: up to 16 rows of one expert). Workgroups
     // take contiguous ranges, which keep a block's token operand in registers
     // across its tiles; every tile costs one token pass, so equal ranges are
-    // balanced.
+    // balanced. (Launches from the ids: tile workgroups 1 .. grid - 1.)
+    const int wb = IDS ? blockIdx.x - 1 : blockIdx.x, wg = IDS ? gridDim.x - 1 : gridDim.x;
     const int total = act.count * A.nrt;
-    const int t0 = split_start(blockIdx.x, gridDim.x, total, A);
-    const int n = split_start(blockIdx.x + 1, gridDim.x, total, A) - t0;
+    const int t0 = split_start(wb, wg, total, A);
+    const int n = split_start(wb + 1, wg, total, A) - t0;
     if (n <= 0) return;
     const int sa = 0, srt = 1;
 
@@ -623,24 +834,24 @@ __device__ __forceinline__ void ffn_dec_body(const DecArgs &A, const ShArgs &S,
     TilePos pos[D];
     WFrag<FMT> wr[D][SPW][NB];
     pos[0] = TilePos{t0 / A.nrt, t0 % A.nrt};
-    expert_state<STAGE, FMT, SH>(A, S, act, pos[0].a, es[0]);
+    expert_state<STAGE, FMT, SH, IDS>(A, S, act, pos[0].a, es[0]);
 #pragma unroll
     for (int d = 1; d < D - 1; ++d) {
         pos[d] = d < n ? advance(pos[d - 1], sa, srt, A.nrt) : pos[d - 1];
         if (pos[d].a == es[d - 1].a) es[d] = es[d - 1];
-        else expert_state<STAGE, FMT, SH>(A, S, act, pos[d].a, es[d]);
+        else expert_state<STAGE, FMT, SH, IDS>(A, S, act, pos[d].a, es[d]);
     }
-    // the first tile's token operand is requested before any weights, so that
-    // resolving its row indices does not wait behind the weight prefetch
     u32x4 xr[SPW][4];
     int pidx = 0;
-    load_tokens<STAGE, SPW, SH>(A, S, es[0], 0, wv, m, c, xr, pidx);
-    int x_key = es[0].a;
-    bool x_raw = true;      // tokens just loaded (not yet in the product type)
-    int buf = 0;
+    // the first tile's token operand is requested before any weights, so
+    // that resolving its row indices does not wait behind the weight prefetch
+    load_tokens<STAGE, SPW, SH, IDS>(A, S, es[0], 0, wv, m, c, xr, pidx, act);
 #pragma unroll
     for (int d = 0; d < D - 1; ++d)
         load_tile<FMT, STAGE, SPW, NB, FULL>(A, es[d], pos[d].rt, wv, lane, wr[d], d < n);
+    int x_key = es[0].a;
+    bool x_raw = true;      // tokens just loaded (not yet in the product type)
+    int buf = 0;
 
     for (int i = 0; i < n; i += D) {
 #pragma unroll
@@ -649,7 +860,7 @@ __device__ __forceinline__ void ffn_dec_body(const DecArgs &A, const ShArgs &S,
                 const int fd = (d + D - 1) % D, pd = (d + D - 2) % D;
                 const bool pf = i + d + D - 1 < n;
                 pos[fd] = pf ? advance(pos[pd], sa, srt, A.nrt) : pos[pd];
-                dec_step<FMT, STAGE, SPW, KS, NB, YF32, FULL, D, SH>(
+                dec_step<FMT, STAGE, SPW, KS, NB, YF32, FULL, D, SH, IDS>(
                     A, S, act, red, wr[d], wr[fd], xr, es[d], es[pd], es[fd], pidx, x_key, x_raw, buf,
                     pos[d].rt, pos[fd], pf, lane, wv, m, c);
             }
@@ -660,14 +871,27 @@ __device__ __forceinline__ void ffn_dec_body(const DecArgs &A, const ShArgs &S,
 template <int FMT, int STAGE, int SPW, int KS, int NB, bool YF32, bool FULL>
 __global__ __launch_bounds__(kWave *KS) void ffn_dec_kernel(DecArgs A) {
     __shared__ float red[2][KS > 1 ? KS - 1 : 1][NB][4][kWave];
-    ffn_dec_body<FMT, STAGE, SPW, KS, NB, YF32, FULL, false>(A, ShArgs{nullptr, 0}, red);
+    ffn_dec_body<FMT, STAGE, SPW, KS, NB, YF32, FULL, false, false>(A, ShArgs{nullptr, 0},
+                                                                    IdsArgs{nullptr, nullptr, 0},
+                                                                    red, nullptr);
 }
 
 // the same with the shared expert as one more expert of the launch
 template <int FMT, int STAGE, int SPW, int KS, int NB, bool YF32, bool FULL>
 __global__ __launch_bounds__(kWave *KS) void ffn_dec_kernel_sh(DecArgs A, ShArgs S) {
     __shared__ float red[2][KS > 1 ? KS - 1 : 1][NB][4][kWave];
-    ffn_dec_body<FMT, STAGE, SPW, KS, NB, YF32, FULL, true>(A, S, red);
+    ffn_dec_body<FMT, STAGE, SPW, KS, NB, YF32, FULL, true, false>(
+        A, S, IdsArgs{nullptr, nullptr, 0}, red, nullptr);
+}
+
+// gate/up from the routing ids (the permutation derived in the launch; with
+// or without the shared expert). Dynamic LDS: KS x ids_wave_ints(E, n) ints
+// (one region per wavefront), then kIdsMaxPairs ints (the workgroup's ids).
+template <int FMT, int SPW, int KS, int NB, bool FULL, bool SH>
+__global__ __launch_bounds__(kWave *KS) void ffn_dec_kernel_ids(DecArgs A, ShArgs S, IdsArgs I) {
+    __shared__ float red[2][KS > 1 ? KS - 1 : 1][NB][4][kWave];
+    extern __shared__ __attribute__((aligned(16))) int dec_ids_lds[];
+    ffn_dec_body<FMT, 1, SPW, KS, NB, false, FULL, SH, true>(A, S, I, red, dec_ids_lds);
 }
 
 // ------------------------------------------------------------- launchers --
@@ -763,6 +987,93 @@ static int launch_stage(int slabs, hipStream_t s, const DecArgs &A, const ShArgs
     if (slabs <= 32) MOE_ST(4, 8, false);
 #undef MOE_ST
     return MOE_EUNSUPPORTED;
+}
+
+// Gate/up from the routing ids: launch_dec's grid and split, with the
+// permutation's LDS (KS regions) bounding the workgroups per compute unit.
+template <int FMT, int SPW, int KS, int NB, bool FULL, bool SH>
+static int launch_dec_ids(hipStream_t s, DecArgs A, const ShArgs &S, const IdsArgs &I,
+                          long slots) {
+    static unsigned full = 0;
+    if (!full) {
+        const unsigned res = resident_grid(ffn_dec_kernel_ids<FMT, SPW, KS, NB, FULL, SH>,
+                                           kWave * KS);
+        full = MOE_DEC_WG_PER_CU ? MOE_DEC_WG_PER_CU * num_cus() : res;
+    }
+    const size_t lds = ((size_t)KS * ids_wave_ints(A.E, I.n) + kIdsMaxPairs) * sizeof(int);
+    const size_t red = (size_t)2 * (KS > 1 ? KS - 1 : 1) * NB * 4 * kWave * sizeof(float);
+    const unsigned by_lds = (unsigned)(kLdsPerCu / (red + lds)) * (unsigned)num_cus();
+    const unsigned fullc = full < by_lds ? full : by_lds;
+    A.nrt = A.I / (8 * NB);
+    A.slot_size = num_cus();
+    dec_split_weights(1, &A.w_slot, &A.w_pos);
+    {   // keep every workgroup's weight at 1/4 or more
+        const int last_slot = (int)((fullc + A.slot_size - 1) / A.slot_size) - 1;
+        if (last_slot > 0 && A.w_slot * last_slot + A.w_pos > 0.75f)
+            A.w_slot = (0.75f - A.w_pos) / last_slot;
+    }
+    const long max_tiles = slots * A.nrt;
+    // tile workgroups, plus workgroup 0, which writes the permutation: all
+    // resident at once (a tile workgroup that waited for the permutation
+    // workgroup's slot would start microseconds late and end the launch late)
+    const unsigned tiles_max = fullc > 1 ? fullc - 1 : 1;
+    const unsigned grid = (unsigned)(max_tiles < (long)tiles_max ? max_tiles : (long)tiles_max);
+    MOE_LAUNCH(K_DEC_GATE_UP, (ffn_dec_kernel_ids<FMT, SPW, KS, NB, FULL, SH>), dim3(grid + 1),
+               dim3(kWave * KS), lds, s, A, S, I);
+    return check_launch();
+}
+
+// Stage 1 shapes as launch_stage.
+template <int FMT, bool SH>
+static int launch_stage_ids(int slabs, hipStream_t s, const DecArgs &A, const ShArgs &S,
+                            const IdsArgs &I, long slots) {
+#define MOE_STI(SPW_, KS_, FULL_) return launch_dec_ids<FMT, SPW_, KS_, 2, FULL_, SH>(s, A, S, I, slots)
+    switch (slabs) {
+        case 1: MOE_STI(1, 1, true);
+        case 2: MOE_STI(1, 2, true);
+        case 3: MOE_STI(1, 3, true);
+        case 4: MOE_STI(1, 4, true);
+        case 6: MOE_STI(2, 3, true);
+        case 8: MOE_STI(2, 4, true);
+        case 12: MOE_STI(3, 4, true);
+        case 16:
+            if (slots * (A.I / 16) < 2L * num_cus()) MOE_STI(2, 8, true);
+            MOE_STI(4, 4, true);
+        case 24: MOE_STI(3, 8, true);
+        case 32: MOE_STI(4, 8, true);
+        default: break;
+    }
+    if (slabs <= 16) MOE_STI(4, 4, false);
+    if (slabs <= 32) MOE_STI(4, 8, false);
+#undef MOE_STI
+    return MOE_EUNSUPPORTED;
+}
+
+// Whether the gate/up launch can derive the permutation from the ids (host
+// check, no device work).
+static bool ffn_ids_supported(int fmt, int T, int k, int E) {
+    const long n = (long)T * k;
+    return fmt == MOE_W_MXFP4 && E <= kIdsMaxE && n >= 1 && n <= kIdsMaxPairs;
+}
+
+// The permutation (from the ids, in the gate/up launch) and the expert FFN:
+// offsets, sorted_pair and pair_row are written as moe_permute writes them.
+template <int FMT, bool SH>
+static int ffn_decode_ids_fmt(const uint16_t *x, const int32_t *ids, const moe_expert_w *experts,
+                              const moe_expert_w *shared, int T, int k, int H, int I, int E,
+                              void *y, int y_is_fp32, int32_t *offsets, int32_t *sorted_pair,
+                              int32_t *pair_row, uint16_t *act, hipStream_t s) {
+    const long n_pairs = (long)T * k;
+    const long slots = (n_pairs < E ? n_pairs : E) + n_pairs / kPass +
+                       (SH ? (T + kPass - 1) / kPass : 0);
+    const ShArgs S{shared, T, T * k};
+    const IdsArgs ia{ids, pair_row, (int)n_pairs};
+    DecArgs a1{x, sorted_pair, offsets, experts, act, k, H, H, I, E, 0, 1, 0.0f, 0.0f};
+    int rc = launch_stage_ids<FMT, SH>((H + 127) / 128, s, a1, S, ia, slots);
+    if (rc) return rc;
+    DecArgs a2{act, sorted_pair, offsets, experts, y, k, I, H, I, E, 0, 1, 0.0f, 0.0f};
+    if (y_is_fp32) return launch_stage<FMT, 2, true, SH>((I + 127) / 128, s, a2, S, slots);
+    return launch_stage<FMT, 2, false, SH>((I + 127) / 128, s, a2, S, slots);
 }
 
 template <int FMT, bool SH>
@@ -1098,6 +1409,14 @@ static int ffn_decode_comb_fmt(const uint16_t *x, const int32_t *sorted_pair,
 // unit of their own (ffn_decode_shared.hip), so that the two sets compile in
 // parallel and the routed-only kernels carry none of that path.
 #ifndef MOE_DEC_SHARED_UNIT
+int ffn_decode_ids(const uint16_t *x, const int32_t *ids, const moe_expert_w *experts, int fmt,
+                   int T, int k, int H, int I, int E, void *y, int y_is_fp32, int32_t *offsets,
+                   int32_t *sorted_pair, int32_t *pair_row, uint16_t *act, hipStream_t s) {
+    if (!ffn_ids_supported(fmt, T, k, E)) return MOE_EUNSUPPORTED;
+    return ffn_decode_ids_fmt<MOE_W_MXFP4, false>(x, ids, experts, nullptr, T, k, H, I, E, y,
+                                                  y_is_fp32, offsets, sorted_pair, pair_row, act,
+                                                  s);
+}
 int ffn_decode(const uint16_t *x, const int32_t *sorted_pair, const int32_t *offsets,
                const moe_expert_w *experts, int fmt, int T, int k, int H, int I, int E, void *y,
                int y_is_fp32, uint16_t *act, hipStream_t s) {
@@ -1113,6 +1432,15 @@ int ffn_decode_comb(const uint16_t *x, const int32_t *sorted_pair, const int32_t
     MOE_DC_DISPATCH(false);
 }
 #else
+int ffn_decode_ids_shared(const uint16_t *x, const int32_t *ids, const moe_expert_w *experts,
+                          const moe_expert_w *shared, int fmt, int T, int k, int H, int I, int E,
+                          void *y, int y_is_fp32, int32_t *offsets, int32_t *sorted_pair,
+                          int32_t *pair_row, uint16_t *act, hipStream_t s) {
+    if (!ffn_ids_supported(fmt, T, k, E)) return MOE_EUNSUPPORTED;
+    return ffn_decode_ids_fmt<MOE_W_MXFP4, true>(x, ids, experts, shared, T, k, H, I, E, y,
+                                                 y_is_fp32, offsets, sorted_pair, pair_row, act,
+                                                 s);
+}
 int ffn_decode_shared(const uint16_t *x, const int32_t *sorted_pair, const int32_t *offsets,
                       const moe_expert_w *experts, const moe_expert_w *shared, int fmt, int T,
                       int k, int H, int I, int E, void *y, int y_is_fp32, uint16_t *act,

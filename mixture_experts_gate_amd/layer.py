@@ -14,6 +14,10 @@ import torch
 from . import _lib
 from .synth import blob_layout
 
+# moe_route_permute runs the router and the permutation as one launch up to
+# these batch sizes (logits given: 8 tokens; gate computed in the kernel: 16)
+_ROUTE_PERMUTE_ONE_LAUNCH = {True: 8, False: 16}
+
 FMT = {"bf16": _lib.MOE_W_BF16, "mxfp4": _lib.MOE_W_MXFP4, "nvfp4": _lib.MOE_W_NVFP4,
        "fp8": _lib.MOE_W_FP8}
 
@@ -143,7 +147,9 @@ class MoeLayer:
                 fuse_combine=True):
         """route -> permute -> expert FFN (+ shared expert) -> combine; returns out[:T].
         fused_routing: route and permute with the one-call entry (one kernel for
-        small batches) instead of the two separate calls.
+        small batches) instead of the two separate calls; above those batches
+        (with fuse_combine, bf16 y) the router, then moe_permute_ffn_combine,
+        whose gate/up launch derives the permutation itself where it can.
         fuse_shared: run the shared expert in the routed FFN's launches
         (moe_expert_ffn_shared); else it is its own call on a side stream.
         fuse_combine: the FFN and the combine through moe_expert_ffn_combine
@@ -151,6 +157,18 @@ class MoeLayer:
         if T > self.T_max:
             raise ValueError("T exceeds the buffers' T_max")
         wl = write_logits or logits is None
+        if (fused_routing and fuse_combine and not self.y_fp32
+                and (shared_table is None or fuse_shared)
+                and T > _ROUTE_PERMUTE_ONE_LAUNCH[logits is not None]):
+            # above the batches moe_route_permute runs as one launch: the
+            # router, then the permutation inside the gate/up launch
+            self.route(T, x=x, wg=wg, logits=logits, renormalize=renormalize, stream=stream,
+                       write_logits=wl)
+            _lib.moe_permute_ffn_combine(
+                x, self.topk_ids, self.topk_w, table, shared_table, self.fmt, T, self.k, self.H,
+                self.I, self.E, self.offsets, self.sorted_pair, self.pair_row, self.y, self.out,
+                self.ws_ffn, self.ws_ffn_bytes, stream)
+            return self.out[:T]
         if fused_routing:
             self.route_permute(T, x=x, wg=wg, logits=logits, renormalize=renormalize,
                                stream=stream, write_logits=wl)

@@ -854,3 +854,102 @@ def test_fp8_weights_tiled_path(lib, orc, H, I, E, k, T, kind, path):
         off, sp, _ = orc.permute(ids, E)
         rows = _tile_rows(off, 2, 24, 64, np.random.default_rng(T))
         _check_rows(orc, w, x, L, rows, off, sp)
+
+
+# (H, I, E, k, shared, T, ids kind)
+_PFC_CASES = [
+    (2048, 768, 128, 8, False, 64, "uniform"),   # the decode layer at its headline batch
+    (2048, 768, 128, 8, False, 9, "uniform"),    # 72 pairs
+    (1024, 512, 128, 8, False, 2, "uniform"),    # 16 pairs: the smallest in-launch batch
+    (1024, 512, 65, 4, False, 33, "hot"),        # a 33-row expert (three blocks); E % 64 != 0
+    (1024, 512, 256, 6, True, 40, "zipf"),       # shared expert: 240 pairs + 40 shared rows
+    (512, 256, 16, 8, False, 64, "hot"),         # 512 pairs, a 64-row expert (four blocks)
+    (512, 256, 16, 4, False, 20, "invalid"),     # ids outside [0, E) are skipped
+    (512, 256, 16, 4, True, 100, "uniform"),     # 400 pairs + 100 shared rows
+    (512, 256, 1, 1, False, 16, "uniform"),      # one expert
+    (512, 256, 16, 8, False, 65, "uniform"),     # 520 pairs: above the in-launch limit
+    (512, 256, 300, 2, False, 20, "uniform"),    # E above the in-launch limit
+]
+
+
+def _pfc_ids(T, E, k, kind, seed):
+    """Router-like ids [T][k] (distinct experts per token unless E < k)."""
+    rng = np.random.default_rng(seed)
+    if kind == "zipf":
+        p = 1.0 / np.arange(1, E + 1) ** 1.1
+        p = p[rng.permutation(E)]
+        ids = np.stack([rng.choice(E, k, replace=False, p=p / p.sum()) for _ in range(T)])
+    else:
+        ids = np.stack([rng.permutation(E)[:k] if E >= k else rng.integers(0, E, k)
+                        for _ in range(T)])
+    if kind == "hot":
+        for t in range(T):
+            row = [e for e in ids[t] if e != 3][:k - 1]
+            ids[t] = [3] + row if len(row) == k - 1 else ids[t]
+    if kind == "invalid":
+        m = rng.random((T, k)) < 0.15
+        ids[m] = np.where(rng.random(m.sum()) < 0.5, -1, E)
+    return ids.astype(np.int32)
+
+
+@pytest.mark.parametrize("H,I,E,k,shared,T,kind", _PFC_CASES,
+                         ids=[f"H{c[0]}-I{c[1]}-E{c[2]}-k{c[3]}{'-sh' if c[4] else ''}-T{c[5]}-{c[6]}"
+                              for c in _PFC_CASES])
+def test_permute_ffn_combine(lib, orc, H, I, E, k, shared, T, kind):
+    """moe_permute_ffn_combine against moe_permute + moe_expert_ffn_combine on
+    the same ids: offsets, sorted pairs, pair rows, y and the layer output bit
+    for bit (the in-launch permutation is the same stable counting sort, and
+    the FFN tiles compute the same sums); the permutation also against the
+    oracle's; and whether the permutation launch ran (it must not where the
+    gate/up launch derives the permutation)."""
+    _announce(f"permute+ffn+combine: H={H} I={I} E={E} k={k} shared={shared} T={T} {kind}")
+    cfg = synth.LayerConfig("pfc", H, E, k, I, "mxfp4", 1 if shared else 0, "uniform", (T,),
+                            "gauss_mxfp4", seed=43)
+    w = Workload(cfg)
+    x = to_dev_bf16(synth.activations(cfg, T, step=2))
+    ids_np = _pfc_ids(T, E, k, kind, seed=T * 7 + E)
+    ids = torch.from_numpy(ids_np).to(DEV)
+    wts = torch.from_numpy(np.random.default_rng(T).random((T, k), dtype=np.float32)).to(DEV)
+    n = T * k
+    rows = n + (T if shared else 0)
+    _, fb = lib.moe_workspace_size(T, k + 1 if shared else k, H, I, E)
+    sh_table = w.dev_shared.table if shared else None
+
+    def bufs():
+        return dict(off=torch.full((E + 1,), -5, dtype=torch.int32, device=DEV),
+                    sp=torch.full((n,), -5, dtype=torch.int32, device=DEV),
+                    pr=torch.full((n,), -5, dtype=torch.int32, device=DEV),
+                    y=torch.zeros((rows, H), dtype=torch.bfloat16, device=DEV),
+                    out=torch.zeros((T, H), dtype=torch.bfloat16, device=DEV),
+                    ws=torch.empty(fb, dtype=torch.uint8, device=DEV))
+
+    a = bufs()
+    torch.cuda.synchronize()
+    lib.moe_set_option(lib.MOE_OPT_TIMING, 1)
+    lib.moe_permute_ffn_combine(x, ids, wts, w.dev.table, sh_table, lib.MOE_W_MXFP4, T, k, H, I,
+                                E, a["off"], a["sp"], a["pr"], a["y"], a["out"], a["ws"], fb)
+    torch.cuda.synchronize()
+    launched = lib.timing_report()
+    lib.moe_set_option(lib.MOE_OPT_TIMING, 0)
+    b = bufs()
+    lib.moe_permute(ids, T, k, E, b["off"], b["sp"], b["pr"], b["ws"], fb)
+    lib.moe_expert_ffn_combine(x, b["sp"], b["off"], w.dev.table, sh_table, lib.MOE_W_MXFP4, T, k,
+                               H, I, E, wts, b["y"], b["out"], b["ws"], fb)
+    torch.cuda.synchronize()
+    for name in ("off", "sp", "pr", "y", "out"):
+        assert torch.equal(a[name], b[name]), f"{name} differs from the two calls"
+    in_launch = n <= 512 and E <= 256 and rows > 15
+    perm_kernels = [kn for kn in launched if kn.startswith("permute")]
+    if in_launch:
+        assert not perm_kernels, f"permutation launched: {launched}"
+    else:
+        assert perm_kernels, f"no permutation launch: {launched}"
+    if kind != "invalid":
+        off_r, sp_r, pr_r = orc.permute(ids_np, E)
+        assert np.array_equal(a["off"].cpu().numpy(), off_r)
+        assert np.array_equal(a["sp"].cpu().numpy(), sp_r)
+        assert np.array_equal(a["pr"].cpu().numpy(), pr_r)
+    else:
+        valid = (ids_np >= 0) & (ids_np < E)
+        assert int(a["off"][E]) == int(valid.sum())
+        assert (a["pr"].cpu().numpy().reshape(T, k)[~valid] == -5).all(), "skipped pairs written"

@@ -140,6 +140,30 @@ def test_ffn_combine_argument_errors(lib):
                                     None, None, 0, None) == lib.MOE_OK
 
 
+def test_permute_ffn_combine_argument_errors(lib):
+    """moe_permute_ffn_combine: missing offsets, ids, permutation outputs or
+    router weights, a workspace sized without the shared expert's rows, too
+    many experts and a bad format are refused before device work."""
+    L = lib.load()
+    dummy = 0x1000  # never dereferenced: validation fails first
+    T, k, H, I, E = 8, 4, 256, 128, 16
+    _, fb_k = lib.moe_workspace_size(T, k, H, I, E)
+    _, fb_k1 = lib.moe_workspace_size(T, k + 1, H, I, E)
+
+    def call(ids=dummy, tw=dummy, shared=None, fmt=1, E_=E, off=dummy, sp=dummy, pr=dummy,
+             wsb=fb_k):
+        return L.moe_permute_ffn_combine(dummy, ids, tw, dummy, shared, fmt, T, k, H, I, E_, off,
+                                         sp, pr, dummy, dummy, dummy, wsb, None)
+    assert call(off=None) == lib.MOE_EINVAL
+    assert call(ids=None) == lib.MOE_EINVAL
+    assert call(tw=None) == lib.MOE_EINVAL
+    assert call(sp=None) == lib.MOE_EINVAL
+    assert call(pr=None) == lib.MOE_EINVAL
+    assert call(shared=dummy) == lib.MOE_EINVAL          # workspace without the shared rows
+    assert call(fmt=9, wsb=fb_k1) == lib.MOE_EINVAL
+    assert call(E_=513, wsb=1 << 30) == lib.MOE_EINVAL
+
+
 def test_cache_reserve_argument_errors(lib):
     L = lib.load()
     h = C.c_void_p(0)
