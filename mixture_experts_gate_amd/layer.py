@@ -17,6 +17,9 @@ from .synth import blob_layout
 # moe_route_permute runs the router and the permutation as one launch up to
 # these batch sizes (logits given: 8 tokens; gate computed in the kernel: 16)
 _ROUTE_PERMUTE_ONE_LAUNCH = {True: 8, False: 16}
+# moe_permute_ffn_combine derives the permutation in its gate/up launch up to
+# this many pairs (more make it the two calls, which the layer then makes)
+_PERMUTE_IN_FFN_MAX_PAIRS = 512
 
 FMT = {"bf16": _lib.MOE_W_BF16, "mxfp4": _lib.MOE_W_MXFP4, "nvfp4": _lib.MOE_W_NVFP4,
        "fp8": _lib.MOE_W_FP8}
@@ -159,7 +162,8 @@ class MoeLayer:
         wl = write_logits or logits is None
         if (fused_routing and fuse_combine and not self.y_fp32
                 and (shared_table is None or fuse_shared)
-                and T > _ROUTE_PERMUTE_ONE_LAUNCH[logits is not None]):
+                and _ROUTE_PERMUTE_ONE_LAUNCH[logits is not None] < T
+                and T * self.k <= _PERMUTE_IN_FFN_MAX_PAIRS):
             # above the batches moe_route_permute runs as one launch: the
             # router, then the permutation inside the gate/up launch
             self.route(T, x=x, wg=wg, logits=logits, renormalize=renormalize, stream=stream,
