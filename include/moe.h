@@ -285,12 +285,13 @@ int moe_expert_ffn_combine(const uint16_t *x_bf16, const int32_t *sorted_pair,
  * The routed experts are found from the ids (winzheng.com page, "Why Now of
  * All Times": a few of the layer's experts per token), so the grouping by
  * expert can happen where the experts' weights are first needed. For MXFP4
- * weights with E <= 256, 16 to 512 pairs and more than 15 activation rows on
- * the weight-streaming kernels, the gate/up launch derives the permutation
- * itself (every wavefront counts and ranks the ids in LDS) and writes it out
- * for the down projection and the combine, so no permutation launch runs.
- * Otherwise the two calls run; the permutation's workspace, where it needs
- * one, is ws. T = 0 writes offsets only (all zero).
+ * weights with E <= 256 and up to 512 pairs on the weight-streaming kernels,
+ * the gate/up launch derives the expert offsets and each block's pairs from
+ * the ids itself (in LDS), one of its workgroups writes the permutation out
+ * for the down projection (with the combine in the same launch at up to 15
+ * activation rows, as in moe_expert_ffn_combine) and the combine, so no
+ * permutation launch runs. Otherwise the two calls run; the permutation's
+ * workspace, where it needs one, is ws. T = 0 writes offsets only (all zero).
  * ws / ws_bytes as for moe_expert_ffn_combine. Errors as moe_expert_ffn_combine;
  * topk_ids, sorted_pair and pair_row must not be NULL for T > 0.
  */

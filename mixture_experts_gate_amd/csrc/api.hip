@@ -119,6 +119,16 @@ int ffn_decode_ids_shared(const uint16_t *x, const int32_t *ids, const moe_exper
                           const moe_expert_w *shared, int fmt, int T, int k, int H, int I, int E,
                           void *y, int y_is_fp32, int32_t *offsets, int32_t *sorted_pair,
                           int32_t *pair_row, uint16_t *act, hipStream_t s);
+int ffn_decode_ids_comb(const uint16_t *x, const int32_t *ids, const moe_expert_w *experts,
+                        int fmt, const float *topk_w, int T, int k, int H, int I, int E,
+                        uint16_t *y, uint16_t *out, int32_t *offsets, int32_t *sorted_pair,
+                        int32_t *pair_row, uint16_t *act, hipStream_t s);
+int ffn_decode_ids_comb_shared(const uint16_t *x, const int32_t *ids,
+                               const moe_expert_w *experts, const moe_expert_w *shared, int fmt,
+                               const float *topk_w, int T, int k, int H, int I, int E,
+                               uint16_t *y, uint16_t *out, int32_t *offsets,
+                               int32_t *sorted_pair, int32_t *pair_row, uint16_t *act,
+                               hipStream_t s);
 int ffn_prefill(const uint16_t *x, const int32_t *sorted_pair, const int32_t *offsets,
                 const moe_expert_w *experts, const moe_expert_w *shared, int fmt, int T, int k,
                 int H, int I, int E, void *y, int y_is_fp32, void *ws, hipStream_t s);
@@ -357,15 +367,22 @@ extern "C" int moe_permute_ffn_combine(const uint16_t *x_bf16, const int32_t *to
     if (rows > 0x7FFFFFFFL) return MOE_EINVAL;
     if (T > 0 && ws_bytes < ffn_ws_bytes(rows, T, H, I, E)) return MOE_EINVAL;
     hipStream_t s = (hipStream_t)stream;
-    // the permutation inside the gate/up launch: more than 15 rows (fewer
-    // take the down + combine launch), weight-streaming kernels
-    if (rows > 15 && !use_prefill(n, E, fmt, H, I)) {
+    // the permutation inside the gate/up launch (weight-streaming kernels):
+    // then the down projection and the combine in one launch (at most 15
+    // rows), or the down launch and the combine
+    if (T > 0 && !use_prefill(n, E, fmt, H, I)) {
         uint16_t *act = reinterpret_cast<uint16_t *>(ws);
-        int rc = shared ? ffn_decode_ids_shared(x_bf16, topk_ids, experts, shared, fmt, T, k, H,
-                                                I, E, y_bf16, 0, offsets, sorted_pair, pair_row,
-                                                act, s)
-                        : ffn_decode_ids(x_bf16, topk_ids, experts, fmt, T, k, H, I, E, y_bf16,
-                                         0, offsets, sorted_pair, pair_row, act, s);
+        int rc = shared ? ffn_decode_ids_comb_shared(x_bf16, topk_ids, experts, shared, fmt,
+                                                     topk_w, T, k, H, I, E, y_bf16, out_bf16,
+                                                     offsets, sorted_pair, pair_row, act, s)
+                        : ffn_decode_ids_comb(x_bf16, topk_ids, experts, fmt, topk_w, T, k, H, I,
+                                              E, y_bf16, out_bf16, offsets, sorted_pair,
+                                              pair_row, act, s);
+        if (rc != MOE_EUNSUPPORTED) return rc;
+        rc = shared ? ffn_decode_ids_shared(x_bf16, topk_ids, experts, shared, fmt, T, k, H, I,
+                                            E, y_bf16, 0, offsets, sorted_pair, pair_row, act, s)
+                    : ffn_decode_ids(x_bf16, topk_ids, experts, fmt, T, k, H, I, E, y_bf16, 0,
+                                     offsets, sorted_pair, pair_row, act, s);
         if (rc != MOE_EUNSUPPORTED) {
             if (rc) return rc;
             return moe_combine(y_bf16, 0, topk_w, shared ? y_bf16 + (size_t)n * H : nullptr, T,

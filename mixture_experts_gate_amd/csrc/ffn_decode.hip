@@ -1387,6 +1387,39 @@ static int ffn_decode_comb_fmt(const uint16_t *x, const int32_t *sorted_pair,
     return MOE_EUNSUPPORTED;
 }
 
+// From the routing ids, with the down projection and the combine in one
+// launch (the permutation written by the gate/up launch's workgroup 0, read
+// by the down + combine launch); MOE_EUNSUPPORTED (before any device work)
+// when the batch does not fit that launch.
+template <int FMT, bool SH>
+static int ffn_decode_ids_comb_fmt(const uint16_t *x, const int32_t *ids,
+                                   const moe_expert_w *experts, const moe_expert_w *shared,
+                                   const float *topk_w, int T, int k, int H, int I, int E,
+                                   uint16_t *y, uint16_t *out, int32_t *offsets,
+                                   int32_t *sorted_pair, int32_t *pair_row, uint16_t *act,
+                                   hipStream_t s) {
+    if (!dc_eligible(FMT, T, k, SH, H, I)) return MOE_EUNSUPPORTED;
+    const long n_pairs = (long)T * k;
+    const long slots = (n_pairs < E ? n_pairs : E) + n_pairs / kPass +
+                       (SH ? (T + kPass - 1) / kPass : 0);
+    const ShArgs S{shared, T, T * k};
+    const IdsArgs ia{ids, pair_row, (int)n_pairs};
+    DecArgs a1{x, sorted_pair, offsets, experts, act, k, H, H, I, E, 0, 1, 0.0f, 0.0f};
+    int rc = launch_stage_ids<FMT, SH>((H + 127) / 128, s, a1, S, ia, slots);
+    if (rc) return rc;
+    const DecArgs a2{act, sorted_pair, offsets, experts, y, k, I, H, I, E, 0, 1, 0.0f, 0.0f};
+    const DcArgs C{topk_w, out, T, T * k + (SH ? T : 0)};
+    switch (I / 128) {   // the slab counts dc_eligible admits
+        case 2: return launch_dc<FMT, 2, SH>(s, a2, S, C);
+        case 4: return launch_dc<FMT, 4, SH>(s, a2, S, C);
+        case 6: return launch_dc<FMT, 6, SH>(s, a2, S, C);
+        case 8: return launch_dc<FMT, 8, SH>(s, a2, S, C);
+        case 12: return launch_dc<FMT, 12, SH>(s, a2, S, C);
+        case 16: return launch_dc<FMT, 16, SH>(s, a2, S, C);
+        default: return MOE_EUNSUPPORTED;
+    }
+}
+
 #define MOE_DC_FMT(F, SH)                                                                      \
     return ffn_decode_comb_fmt<F, SH>(x, sorted_pair, offsets, experts, shared, topk_w, T, k, H, \
                                       I, E, y, out, act, s)
@@ -1409,6 +1442,15 @@ static int ffn_decode_comb_fmt(const uint16_t *x, const int32_t *sorted_pair,
 // unit of their own (ffn_decode_shared.hip), so that the two sets compile in
 // parallel and the routed-only kernels carry none of that path.
 #ifndef MOE_DEC_SHARED_UNIT
+int ffn_decode_ids_comb(const uint16_t *x, const int32_t *ids, const moe_expert_w *experts,
+                        int fmt, const float *topk_w, int T, int k, int H, int I, int E,
+                        uint16_t *y, uint16_t *out, int32_t *offsets, int32_t *sorted_pair,
+                        int32_t *pair_row, uint16_t *act, hipStream_t s) {
+    if (!ffn_ids_supported(fmt, T, k, E)) return MOE_EUNSUPPORTED;
+    return ffn_decode_ids_comb_fmt<MOE_W_MXFP4, false>(x, ids, experts, nullptr, topk_w, T, k, H,
+                                                       I, E, y, out, offsets, sorted_pair,
+                                                       pair_row, act, s);
+}
 int ffn_decode_ids(const uint16_t *x, const int32_t *ids, const moe_expert_w *experts, int fmt,
                    int T, int k, int H, int I, int E, void *y, int y_is_fp32, int32_t *offsets,
                    int32_t *sorted_pair, int32_t *pair_row, uint16_t *act, hipStream_t s) {
@@ -1432,6 +1474,17 @@ int ffn_decode_comb(const uint16_t *x, const int32_t *sorted_pair, const int32_t
     MOE_DC_DISPATCH(false);
 }
 #else
+int ffn_decode_ids_comb_shared(const uint16_t *x, const int32_t *ids,
+                               const moe_expert_w *experts, const moe_expert_w *shared, int fmt,
+                               const float *topk_w, int T, int k, int H, int I, int E,
+                               uint16_t *y, uint16_t *out, int32_t *offsets,
+                               int32_t *sorted_pair, int32_t *pair_row, uint16_t *act,
+                               hipStream_t s) {
+    if (!ffn_ids_supported(fmt, T, k, E)) return MOE_EUNSUPPORTED;
+    return ffn_decode_ids_comb_fmt<MOE_W_MXFP4, true>(x, ids, experts, shared, topk_w, T, k, H,
+                                                      I, E, y, out, offsets, sorted_pair,
+                                                      pair_row, act, s);
+}
 int ffn_decode_ids_shared(const uint16_t *x, const int32_t *ids, const moe_expert_w *experts,
                           const moe_expert_w *shared, int fmt, int T, int k, int H, int I, int E,
                           void *y, int y_is_fp32, int32_t *offsets, int32_t *sorted_pair,

@@ -14,12 +14,14 @@ import torch
 from . import _lib
 from .synth import blob_layout
 
-# moe_route_permute runs the router and the permutation as one launch up to
-# these batch sizes (logits given: 8 tokens; gate computed in the kernel: 16)
-_ROUTE_PERMUTE_ONE_LAUNCH = {True: 8, False: 16}
-# moe_permute_ffn_combine derives the permutation in its gate/up launch up to
-# this many pairs (more make it the two calls, which the layer then makes)
-_PERMUTE_IN_FFN_MAX_PAIRS = 512
+# moe_permute_ffn_combine derives the permutation in its gate/up launch from
+# 8 up to 512 pairs (more make it the two calls, which the layer then makes).
+# Below 8 pairs (config 4 at one token: 6 pairs over 256 experts, 33.2
+# against 32.8 us per step) the one-launch router + permutation of
+# moe_route_permute costs less; from 8 pairs the router alone and the
+# permutation in the gate/up launch win (config 2, T=1..8: 0.7 to 1.0 us,
+# T=9..64: 3.2 to 3.8 us per step).
+_PERMUTE_IN_FFN_PAIRS = (8, 512)
 
 FMT = {"bf16": _lib.MOE_W_BF16, "mxfp4": _lib.MOE_W_MXFP4, "nvfp4": _lib.MOE_W_NVFP4,
        "fp8": _lib.MOE_W_FP8}
@@ -150,9 +152,9 @@ class MoeLayer:
                 fuse_combine=True):
         """route -> permute -> expert FFN (+ shared expert) -> combine; returns out[:T].
         fused_routing: route and permute with the one-call entry (one kernel for
-        small batches) instead of the two separate calls; above those batches
+        small batches) instead of the two separate calls; from 8 to 512 pairs
         (with fuse_combine, bf16 y) the router, then moe_permute_ffn_combine,
-        whose gate/up launch derives the permutation itself where it can.
+        whose gate/up launch derives the permutation itself.
         fuse_shared: run the shared expert in the routed FFN's launches
         (moe_expert_ffn_shared); else it is its own call on a side stream.
         fuse_combine: the FFN and the combine through moe_expert_ffn_combine
@@ -162,10 +164,8 @@ class MoeLayer:
         wl = write_logits or logits is None
         if (fused_routing and fuse_combine and not self.y_fp32
                 and (shared_table is None or fuse_shared)
-                and _ROUTE_PERMUTE_ONE_LAUNCH[logits is not None] < T
-                and T * self.k <= _PERMUTE_IN_FFN_MAX_PAIRS):
-            # above the batches moe_route_permute runs as one launch: the
-            # router, then the permutation inside the gate/up launch
+                and _PERMUTE_IN_FFN_PAIRS[0] <= T * self.k <= _PERMUTE_IN_FFN_PAIRS[1]):
+            # the router, then the permutation inside the gate/up launch
             self.route(T, x=x, wg=wg, logits=logits, renormalize=renormalize, stream=stream,
                        write_logits=wl)
             _lib.moe_permute_ffn_combine(

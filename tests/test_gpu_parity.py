@@ -869,6 +869,10 @@ _PFC_CASES = [
     (512, 256, 1, 1, False, 16, "uniform"),      # one expert
     (512, 256, 16, 8, False, 65, "uniform"),     # 520 pairs: above the in-launch limit
     (512, 256, 300, 2, False, 20, "uniform"),    # E above the in-launch limit
+    (2048, 768, 128, 8, False, 1, "uniform"),    # 8 rows: down + combine in one launch
+    (1024, 2048, 32, 6, True, 2, "uniform"),     # 14 rows with the shared expert's, 16 slabs
+    (512, 256, 16, 1, False, 1, "uniform"),      # one row
+    (512, 256, 16, 2, True, 5, "hot"),           # 15 rows, a hot expert
 ]
 
 
@@ -938,7 +942,7 @@ def test_permute_ffn_combine(lib, orc, H, I, E, k, shared, T, kind):
     torch.cuda.synchronize()
     for name in ("off", "sp", "pr", "y", "out"):
         assert torch.equal(a[name], b[name]), f"{name} differs from the two calls"
-    in_launch = n <= 512 and E <= 256 and rows > 15
+    in_launch = n <= 512 and E <= 256
     perm_kernels = [kn for kn in launched if kn.startswith("permute")]
     if in_launch:
         assert not perm_kernels, f"permutation launched: {launched}"
