@@ -302,6 +302,52 @@ int moe_permute_ffn_combine(const uint16_t *x_bf16, const int32_t *topk_ids,
                             uint16_t *y_bf16, uint16_t *out_bf16, void *ws, size_t ws_bytes,
                             void *stream);
 
+/* Bytes of the barrier buffer moe_layer_fused takes. */
+#define MOE_LAYER_SYNC_BYTES 8192
+
+/*
+ * moe_layer_fused -- the whole layer from given router logits in one launch,
+ * for a handful of tokens: moe_route (logits given, no logits written), then
+ * moe_permute_ffn_combine, with the same results: topk_ids, topk_w, offsets,
+ * sorted_pair and pair_row bitwise, y and out as moe_expert_ffn_combine gives
+ * them at these sizes.
+ *
+ * Batch-1 decoding is the pages' use case (winzheng.com page, "Why Now of All
+ * Times": per token and layer a few routed experts out of hundreds); there
+ * the layer's weight bytes take microseconds to stream while a chain of
+ * dependent launches costs several microseconds per launch. Every workgroup
+ * routes the tokens and derives the permutation itself, the gate/up tiles
+ * are spread over all compute units, and the down projection + combine
+ * workgroups request their weights before waiting at a grid barrier for the
+ * activation rows.
+ *
+ * Taken for MXFP4 weights, 1 <= T <= 8, T*k (+ T with the shared expert) <=
+ * 15 rows, E <= 256, H in {1024, 2048, 4096} and I/128 in {4, 6, 16} (H/16
+ * workgroups must fit one per compute unit); otherwise MOE_EUNSUPPORTED
+ * before any device work (use moe_route + moe_permute_ffn_combine).
+ *   logits [T][E] fp32; renormalize as moe_route; topk_ids/topk_w [T][k] out;
+ *   offsets [E+1], sorted_pair and pair_row [T*k] out; y_bf16, out_bf16, ws
+ *   and ws_bytes as moe_permute_ffn_combine.
+ *   sync: MOE_LAYER_SYNC_BYTES of device memory (8-byte aligned) holding the
+ *     launch's barrier counters. Zero it before the first call that uses it
+ *     (e.g. one hipMemset); the calls keep it consistent from then on (its
+ *     counters only grow). One of its words becomes nonzero if a barrier
+ *     wait ran out (about a second), in which case that call's outputs are
+ *     not valid; this happens only if the launch's workgroups cannot all be
+ *     resident at once. Calls on one sync buffer must not overlap in time
+ *     (one stream, or ordered streams); calls that may run side by side need
+ *     their own sync buffers and workspaces, and two such launches on one
+ *     device may each hold compute units the other waits for: run them on one
+ *     stream.
+ * Errors: MOE_EINVAL for NULL pointers, sizes out of range or a workspace too
+ * small; MOE_EHIP if the launch fails.
+ */
+int moe_layer_fused(const uint16_t *x_bf16, const float *logits, const moe_expert_w *experts,
+                    const moe_expert_w *shared, int fmt, int T, int k, int H, int I, int E,
+                    int renormalize, int32_t *topk_ids, float *topk_w, int32_t *offsets,
+                    int32_t *sorted_pair, int32_t *pair_row, uint16_t *y_bf16,
+                    uint16_t *out_bf16, void *ws, size_t ws_bytes, void *sync, void *stream);
+
 /*
  * moe_pack_mxfp4 -- convert n expert blobs from the interchange MXFP4 layout
  * to the kernel layout (see the top of this file). src and dst are device

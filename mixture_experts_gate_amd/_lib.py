@@ -33,6 +33,7 @@ EXPORTS = [
     "expert_cache_slots", "expert_cache_slot_of", "expert_cache_destroy", "expert_cache_resize",
     "moe_micro_read", "moe_micro_mfma", "expert_cache_bandwidth", "expert_cache_prefetch_qstar",
     "moe_permute_split", "moe_cpu_expert_ffn", "moe_scatter_rows", "moe_permute_ffn_combine",
+    "moe_layer_fused",
 ]
 
 
@@ -74,6 +75,8 @@ def load(path: str | None = None):
         "moe_expert_ffn_combine": (I, [P, P, P, P, P, I, I, I, I, I, I, P, P, P, P, Z, P]),
         "moe_permute_ffn_combine": (I, [P, P, P, P, P, I, I, I, I, I, I, P, P, P, P, P, P, Z,
                                         P]),
+        "moe_layer_fused": (I, [P, P, P, P, I, I, I, I, I, I, I, P, P, P, P, P, P, P, P, Z, P,
+                                P]),
         "moe_combine": (I, [P, I, P, P, I, I, I, P, P]),
         "moe_workspace_size": (I, [I, I, I, I, I, C.POINTER(Z), C.POINTER(Z)]),
         "moe_set_option": (I, [I, I]),
@@ -199,6 +202,23 @@ def moe_permute_ffn_combine(x_bf16, topk_ids, topk_w, experts, shared, fmt, T, k
         E, _ptr(offsets), _ptr(sorted_pair), _ptr(pair_row), _ptr(y), _ptr(out), _ptr(ws),
         ws_bytes, _stream(stream)))
 
+
+def moe_layer_fused(x_bf16, logits, experts, shared, fmt, T, k, H, I, E, renormalize, topk_ids,
+                    topk_w, offsets, sorted_pair, pair_row, y, out, ws, ws_bytes, sync,
+                    stream=None, check=True):
+    """The whole layer from given logits in one launch (a handful of tokens);
+    sync: LAYER_SYNC_BYTES of zero-initialised device memory (the calls keep
+    it consistent). check=False returns MOE_EUNSUPPORTED instead of raising."""
+    rc = load().moe_layer_fused(
+        _ptr(x_bf16), _ptr(logits), _ptr(experts), _ptr(shared), fmt, T, k, H, I, E,
+        int(bool(renormalize)), _ptr(topk_ids), _ptr(topk_w), _ptr(offsets), _ptr(sorted_pair),
+        _ptr(pair_row), _ptr(y), _ptr(out), _ptr(ws), ws_bytes, _ptr(sync), _stream(stream))
+    if not check and rc == MOE_EUNSUPPORTED:
+        return rc
+    return _check("moe_layer_fused", rc)
+
+
+LAYER_SYNC_BYTES = 8192      # MOE_LAYER_SYNC_BYTES
 
 FFN_NOALLOC_MAX_WS = 64 << 20
 

@@ -14,7 +14,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libmoe.so")
 OBJDIR = os.path.join(PKG, "_build")
 
-SOURCES = ["api.hip", "route.hip", "permute.hip", "ffn_decode.hip", "ffn_decode_shared.hip",
+SOURCES = ["api.hip", "route.hip", "permute.hip", "ffn_decode.hip", "ffn_decode_shared.hip", "ffn_small.hip",
            "ffn_prefill.hip", "pack.hip", "noalloc.hip", "micro.hip",
            "combine.hip", "cache.hip"]
 

@@ -54,7 +54,7 @@ static const char *const g_kernel_names[K_COUNT] = {
     "route", "permute_small", "permute_rank", "permute_scan", "permute_scatter", "permute_empty",
     "ffn_decode_gate_up", "ffn_decode_down", "ffn_prefill_gate_up", "ffn_prefill_down",
     "combine", "cache_table", "pack_mxfp4", "route_permute", "ffn_prefill_split",
-    "cache_move", "micro_read", "micro_mfma", "scatter_rows"};
+    "cache_move", "micro_read", "micro_mfma", "scatter_rows", "layer_fused"};
 
 static hipEvent_t pool_event() {
     if (!g_evpool.empty()) {
@@ -133,6 +133,11 @@ int ffn_prefill(const uint16_t *x, const int32_t *sorted_pair, const int32_t *of
                 const moe_expert_w *experts, const moe_expert_w *shared, int fmt, int T, int k,
                 int H, int I, int E, void *y, int y_is_fp32, void *ws, hipStream_t s);
 bool ffn_prefill_supported(int fmt, int H, int I);
+int ffn_small_layer(const uint16_t *x, const float *logits, const moe_expert_w *experts,
+                    const moe_expert_w *shared, int fmt, int T, int k, int H, int I, int E,
+                    int renorm, int32_t *topk_ids, float *topk_w, int32_t *offsets,
+                    int32_t *sorted_pair, int32_t *pair_row, uint16_t *y, uint16_t *out,
+                    uint16_t *act, uint64_t *sync, hipStream_t s);
 size_t prefill_ws_bytes(long n_pairs, long T, int H, int I, int E);
 
 static size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
@@ -345,6 +350,29 @@ extern "C" int moe_expert_ffn_combine(const uint16_t *x_bf16, const int32_t *sor
     if (rc) return rc;
     return moe_combine(y_bf16, 0, topk_w, shared ? y_bf16 + (size_t)n * H : nullptr, T, k, H,
                        out_bf16, stream);
+}
+
+extern "C" int moe_layer_fused(const uint16_t *x_bf16, const float *logits,
+                               const moe_expert_w *experts, const moe_expert_w *shared, int fmt,
+                               int T, int k, int H, int I, int E, int renormalize,
+                               int32_t *topk_ids, float *topk_w, int32_t *offsets,
+                               int32_t *sorted_pair, int32_t *pair_row, uint16_t *y_bf16,
+                               uint16_t *out_bf16, void *ws, size_t ws_bytes, void *sync,
+                               void *stream) {
+    if (T < 1 || k < 1 || E < 1 || k > E || H < 128 || I < 128 || H % 128 || I % 128)
+        return MOE_EINVAL;
+    if (fmt != MOE_W_MXFP4 && fmt != MOE_W_BF16 && fmt != MOE_W_NVFP4 && fmt != MOE_W_FP8)
+        return MOE_EINVAL;
+    if (!x_bf16 || !logits || !experts || !topk_ids || !topk_w || !offsets || !sorted_pair ||
+        !pair_row || !y_bf16 || !out_bf16 || !ws || !sync || (uintptr_t)sync % 8)
+        return MOE_EINVAL;
+    const long rows = (long)T * k + (shared ? T : 0);
+    if (rows > 0x7FFFFFFFL) return MOE_EINVAL;
+    if (ws_bytes < ffn_ws_bytes(rows, T, H, I, E)) return MOE_EINVAL;
+    return ffn_small_layer(x_bf16, logits, experts, shared, fmt, T, k, H, I, E, renormalize,
+                           topk_ids, topk_w, offsets, sorted_pair, pair_row, y_bf16, out_bf16,
+                           reinterpret_cast<uint16_t *>(ws), reinterpret_cast<uint64_t *>(sync),
+                           (hipStream_t)stream);
 }
 
 extern "C" int moe_permute_ffn_combine(const uint16_t *x_bf16, const int32_t *topk_ids,

@@ -642,7 +642,7 @@ __device__ __forceinline__ void load_tokens(const DecArgs &A, const ShArgs &S, c
 // One tile: token operand if the expert changed, prefetch of the next tile's
 // weights into `wn`, multiply from `wc`, K-split reduction, epilogue.
 template <int FMT, int STAGE, int SPW, int KS, int NB, bool YF32, bool FULL, int D, bool SH,
-          bool IDS>
+          bool IDS, bool COH = false>
 __device__ __forceinline__ void dec_step(const DecArgs &A, const ShArgs &S, const ActiveSet &act,
                                          float (&red)[2][KS > 1 ? KS - 1 : 1][NB][4][kWave],
                                          WFrag<FMT> (&wc)[SPW][NB], WFrag<FMT> (&wn)[SPW][NB],
@@ -752,7 +752,16 @@ __device__ __forceinline__ void dec_step(const DecArgs &A, const ShArgs &S, cons
                                          silu_mul(acc[b][1], acc[b + H2][1]));
                             pk.y = pack2(silu_mul(acc[b][2], acc[b + H2][2]),
                                          silu_mul(acc[b][3], acc[b + H2][3]));
-                            *reinterpret_cast<uint2 *>(actp + (rt * H2 + b) * 16 + 4 * c) = pk;
+                            uint16_t *ap = actp + (rt * H2 + b) * 16 + 4 * c;
+                            if constexpr (COH) {
+                                // written through to the device's coherence point
+                                // (read in the same launch by other workgroups)
+                                __hip_atomic_store(reinterpret_cast<uint64_t *>(ap),
+                                                   (uint64_t)pk.x | ((uint64_t)pk.y << 32),
+                                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                            } else {
+                                *reinterpret_cast<uint2 *>(ap) = pk;
+                            }
                         }
                     } else {
                         const size_t prow = (size_t)pidx * A.H;
@@ -791,14 +800,17 @@ __device__ __forceinline__ void write_perm(const DecArgs &A, const IdsArgs &I,
     }
 }
 
+template <int FMT, int STAGE, int SPW, int KS, int NB, bool YF32, bool FULL, bool SH, bool IDS,
+          bool COH = false, int DEPTH = 0>
+__device__ __forceinline__ void dec_tiles(const DecArgs &A, const ShArgs &S, const ActiveSet &act,
+                                          float (&red)[2][KS > 1 ? KS - 1 : 1][NB][4][kWave],
+                                          int t0, int n);
+
 template <int FMT, int STAGE, int SPW, int KS, int NB, bool YF32, bool FULL, bool SH, bool IDS>
 __device__ __forceinline__ void ffn_dec_body(const DecArgs &A, const ShArgs &S, const IdsArgs &I,
                                              float (&red)[2][KS > 1 ? KS - 1 : 1][NB][4][kWave],
                                              int *ids_lds) {
-    const int lane = lane_id();
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);   // wavefront-uniform
-    const int m = lane & 15, c = lane >> 4;
-
     ActiveSet act;
     if constexpr (IDS) {
         act.template init_ids<SH>(I.ids, I.n, A.E, S, ids_lds + wv * ids_wave_ints(A.E, I.n),
@@ -823,13 +835,28 @@ __device__ __forceinline__ void ffn_dec_body(const DecArgs &A, const ShArgs &S, 
     const int t0 = split_start(wb, wg, total, A);
     const int n = split_start(wb + 1, wg, total, A) - t0;
     if (n <= 0) return;
+    dec_tiles<FMT, STAGE, SPW, KS, NB, YF32, FULL, SH, IDS>(A, S, act, red, t0, n);
+}
+
+// Tiles t0 .. t0 + n - 1 (n > 0) of a launch, by every wavefront of the
+// workgroup (the K-split reduction has workgroup barriers). COH: stage-1
+// activation stores written through to the coherence point. DEPTH: weight
+// tiles held in registers (0: the default of the stage).
+template <int FMT, int STAGE, int SPW, int KS, int NB, bool YF32, bool FULL, bool SH, bool IDS,
+          bool COH, int DEPTH>
+__device__ __forceinline__ void dec_tiles(const DecArgs &A, const ShArgs &S, const ActiveSet &act,
+                                          float (&red)[2][KS > 1 ? KS - 1 : 1][NB][4][kWave],
+                                          int t0, int n) {
+    const int lane = lane_id();
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);   // wavefront-uniform
+    const int m = lane & 15, c = lane >> 4;
     const int sa = 0, srt = 1;
 
     // D register buffers used in turn: tile i computes from one while the
     // weights of tiles i+1 .. i+D-1 are in flight into the others (no copies
     // between them, so nothing waits for a prefetch before it is needed).
     // Slots past the end repeat the last tile's position and load nothing.
-    constexpr int D = STAGE == 2 ? kDepth2 : kDepth;
+    constexpr int D = DEPTH ? DEPTH : STAGE == 2 ? kDepth2 : kDepth;
     ExpertState<FMT> es[D];
     TilePos pos[D];
     WFrag<FMT> wr[D][SPW][NB];
@@ -860,7 +887,7 @@ __device__ __forceinline__ void ffn_dec_body(const DecArgs &A, const ShArgs &S, 
                 const int fd = (d + D - 1) % D, pd = (d + D - 2) % D;
                 const bool pf = i + d + D - 1 < n;
                 pos[fd] = pf ? advance(pos[pd], sa, srt, A.nrt) : pos[pd];
-                dec_step<FMT, STAGE, SPW, KS, NB, YF32, FULL, D, SH, IDS>(
+                dec_step<FMT, STAGE, SPW, KS, NB, YF32, FULL, D, SH, IDS, COH>(
                     A, S, act, red, wr[d], wr[fd], xr, es[d], es[pd], es[fd], pidx, x_key, x_raw, buf,
                     pos[d].rt, pos[fd], pf, lane, wv, m, c);
             }
@@ -1441,7 +1468,9 @@ static int ffn_decode_ids_comb_fmt(const uint16_t *x, const int32_t *ids,
 // The kernels with the shared-expert path are instantiated in a translation
 // unit of their own (ffn_decode_shared.hip), so that the two sets compile in
 // parallel and the routed-only kernels carry none of that path.
-#ifndef MOE_DEC_SHARED_UNIT
+#if defined(MOE_DEC_SMALL_UNIT)
+// (the single-launch kernels of ffn_small.hip follow this file there)
+#elif !defined(MOE_DEC_SHARED_UNIT)
 int ffn_decode_ids_comb(const uint16_t *x, const int32_t *ids, const moe_expert_w *experts,
                         int fmt, const float *topk_w, int T, int k, int H, int I, int E,
                         uint16_t *y, uint16_t *out, int32_t *offsets, int32_t *sorted_pair,

@@ -22,6 +22,9 @@ from .synth import blob_layout
 # permutation in the gate/up launch win (config 2, T=1..8: 0.7 to 1.0 us,
 # T=9..64: 3.2 to 3.8 us per step).
 _PERMUTE_IN_FFN_PAIRS = (8, 512)
+# activation rows (T*k, + T with the shared expert) up to which forward()
+# tries the one-launch layer (moe_layer_fused) when the logits are given
+_ONE_LAUNCH_ROWS = 15
 
 FMT = {"bf16": _lib.MOE_W_BF16, "mxfp4": _lib.MOE_W_MXFP4, "nvfp4": _lib.MOE_W_NVFP4,
        "fp8": _lib.MOE_W_FP8}
@@ -112,6 +115,8 @@ class MoeLayer:
             self.ws_sh_bytes = fbs
             self.ws_sh = torch.empty(fbs, dtype=torch.uint8, device=dev)
             self.y_sh = torch.empty((T_max, H), dtype=ydt, device=dev)
+        # barrier counters of the one-launch layer (zero before its first call)
+        self.sync = torch.zeros(_lib.LAYER_SYNC_BYTES // 8, dtype=torch.int64, device=dev)
         self._sh_T = -1
         self._side = None       # stream of the shared expert (default priority)
 
@@ -162,6 +167,16 @@ class MoeLayer:
         if T > self.T_max:
             raise ValueError("T exceeds the buffers' T_max")
         wl = write_logits or logits is None
+        if (fused_routing and fuse_combine and fuse_shared and not wl and not self.y_fp32
+                and T * (self.k + (shared_table is not None)) <= _ONE_LAUNCH_ROWS):
+            # router, permutation, expert FFN and combine in one launch
+            rc = _lib.moe_layer_fused(
+                x, logits, table, shared_table, self.fmt, T, self.k, self.H, self.I, self.E,
+                renormalize, self.topk_ids, self.topk_w, self.offsets, self.sorted_pair,
+                self.pair_row, self.y, self.out, self.ws_ffn, self.ws_ffn_bytes, self.sync,
+                stream, check=False)
+            if rc != _lib.MOE_EUNSUPPORTED:
+                return self.out[:T]
         if (fused_routing and fuse_combine and not self.y_fp32
                 and (shared_table is None or fuse_shared)
                 and _PERMUTE_IN_FFN_PAIRS[0] <= T * self.k <= _PERMUTE_IN_FFN_PAIRS[1]):

@@ -164,6 +164,37 @@ def test_permute_ffn_combine_argument_errors(lib):
     assert call(E_=513, wsb=1 << 30) == lib.MOE_EINVAL
 
 
+def test_layer_fused_argument_errors(lib):
+    """moe_layer_fused: missing logits, outputs or sync buffer, a misaligned
+    sync buffer, a workspace too small or T = 0 are refused (MOE_EINVAL), and
+    batches outside the one-launch sizes are declined (MOE_EUNSUPPORTED), both
+    before any device work."""
+    L = lib.load()
+    dummy = 0x1000  # never dereferenced: validation fails first
+    T, k, H, I, E = 1, 8, 2048, 768, 128
+    _, fb = lib.moe_workspace_size(T, k, H, I, E)
+
+    def call(T_=T, k_=k, H_=H, I_=I, E_=E, fmt=1, lg=dummy, out=dummy, sync=dummy, wsb=fb,
+             shared=None):
+        return L.moe_layer_fused(dummy, lg, dummy, shared, fmt, T_, k_, H_, I_, E_, 1, dummy,
+                                 dummy, dummy, dummy, dummy, dummy, out, dummy, wsb, sync, None)
+    assert call(lg=None) == lib.MOE_EINVAL
+    assert call(out=None) == lib.MOE_EINVAL
+    assert call(sync=None) == lib.MOE_EINVAL
+    assert call(sync=dummy + 4) == lib.MOE_EINVAL            # not 8-byte aligned
+    assert call(wsb=fb - 1) == lib.MOE_EINVAL
+    assert call(T_=0) == lib.MOE_EINVAL
+    assert call(k_=200) == lib.MOE_EINVAL                    # k > E
+    big = 1 << 30
+    assert call(T_=2, wsb=big) == lib.MOE_EUNSUPPORTED       # 16 rows
+    assert call(T_=9, k_=1, wsb=big) == lib.MOE_EUNSUPPORTED  # more tokens than wavefronts
+    assert call(E_=300, wsb=big) == lib.MOE_EUNSUPPORTED     # ids past 8 bits
+    assert call(fmt=0, wsb=big) == lib.MOE_EUNSUPPORTED      # bf16 weights
+    assert call(H_=1536, wsb=big) == lib.MOE_EUNSUPPORTED    # 12 slabs of gate/up
+    assert call(I_=1024, wsb=big) == lib.MOE_EUNSUPPORTED    # 8 slabs of down
+    assert call(shared=dummy, k_=7, T_=2, wsb=big) == lib.MOE_EUNSUPPORTED  # 16 rows
+
+
 def test_cache_reserve_argument_errors(lib):
     L = lib.load()
     h = C.c_void_p(0)
