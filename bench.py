@@ -69,7 +69,7 @@ def parse():
                     help="skip the read-stream / matrix-core reference measurements")
     ap.add_argument("--stack-steps", type=int, default=1024,
                     help="timed steps of the cached 43-layer stack at T=1")
-    ap.add_argument("--cfg4-T", default="1,64,4096",
+    ap.add_argument("--cfg4-T", default="1,2,64,4096",
                     help="comma list of the large sparse layer's batch sizes to run")
     return ap.parse_args()
 
@@ -1027,7 +1027,7 @@ def main():
         log("config 4: generating 256 experts + shared ...")
         w4 = None
         c4_T = {int(v) for v in args.cfg4_T.split(",") if v}
-        for T, steps in ((1, 100), (64, 100), (4096, 8)):
+        for T, steps in ((1, 100), (2, 100), (64, 100), (4096, 8)):
             if T not in c4_T:
                 continue
             # decode sizes rotate 8 weight replicas (27 GB) so that a hot
