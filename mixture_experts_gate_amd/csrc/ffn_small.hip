@@ -176,12 +176,18 @@ __device__ __forceinline__ int init_small(ActiveSet &act, const int32_t *rid, in
     const int lane = lane_id();
     act.loff = wl;
     act.lsrt = wl + 2 * E + 1;
+    // every pair's id in registers (LDS broadcast reads; -1 past n), so that
+    // the comparisons below stay in the vector unit: a lane read per pair
+    // (vector -> scalar -> vector) made this part several times slower
+    int idq[kFsMaxRows];
+#pragma unroll
+    for (int q = 0; q < kFsMaxRows; ++q) idq[q] = q < n ? rid[q] : -1;
     const int idp = lane < n ? rid[lane] : -1;
     int less = 0, same = 0, sbefore = 0;
-#pragma unroll 1
-    for (int q = 0; q < n; ++q) {
-        const int iq = __builtin_amdgcn_readlane(idp, q);
-        less += iq < idp ? 1 : 0;
+#pragma unroll
+    for (int q = 0; q < kFsMaxRows; ++q) {
+        const int iq = idq[q];
+        less += (iq >= 0 && iq < idp) ? 1 : 0;
         same += iq == idp ? 1 : 0;
         sbefore += (iq == idp && q < lane) ? 1 : 0;
     }
@@ -201,8 +207,8 @@ __device__ __forceinline__ int init_small(ActiveSet &act, const int32_t *rid, in
         if (i * kWave < E) {
             const int e = i * kWave + lane;
             bool on = false;
-#pragma unroll 1
-            for (int q = 0; q < n; ++q) on = on || __builtin_amdgcn_readlane(idp, q) == e;
+#pragma unroll
+            for (int q = 0; q < kFsMaxRows; ++q) on = on || idq[q] == e;
             const uint64_t mb = __ballot(on);
             act.incl[i] = __popcll(mb & (lanemask_lt() | (1ull << lane)));
             act.gtot[i] = __popcll(mb);

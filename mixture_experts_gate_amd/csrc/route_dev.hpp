@@ -61,14 +61,32 @@ __device__ __forceinline__ uint64_t readlane64(uint64_t v, int l) {
 // DPP controls: quad_perm [1,0,3,2], quad_perm [2,3,0,1], row_ror:4, row_ror:8
 constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppRor4 = 0x124, kDppRor8 = 0x128;
 
-// Maximum of a 64-bit key over the wavefront (wavefront-uniform result).
+// DPP move of a 64-bit value restricted to the rows in ROWS (other rows get 0,
+// which ranks last).
+template <int CTRL, int ROWS>
+__device__ __forceinline__ uint64_t dpp64_rows(uint64_t v) {
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)v, CTRL, ROWS, 0xF, false);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(v >> 32), CTRL, ROWS, 0xF, false);
+    return (uint64_t)lo | ((uint64_t)hi << 32);
+}
+
+// DPP controls: row_bcast:15 (lane 15 of each row into the next row),
+// row_bcast:31 (lane 31 into rows 2 and 3)
+constexpr int kDppBcast15 = 0x142, kDppBcast31 = 0x143;
+
+// Maximum of a 64-bit key over the wavefront (wavefront-uniform result). The
+// whole reduction stays in the vector unit (the row maxima meet in lane 63 by
+// row broadcasts) and one lane read hands the result out: lane reads of each
+// row's maximum followed by scalar comparisons cost a round trip between the
+// vector and scalar units per step.
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t k) {
     k = max_u64(k, dpp64<kDppXor1>(k));
     k = max_u64(k, dpp64<kDppXor2>(k));
     k = max_u64(k, dpp64<kDppRor4>(k));
     k = max_u64(k, dpp64<kDppRor8>(k));
-    return max_u64(max_u64(readlane64(k, 0), readlane64(k, 16)),
-                   max_u64(readlane64(k, 32), readlane64(k, 48)));
+    k = max_u64(k, dpp64_rows<kDppBcast15, 0xA>(k));
+    k = max_u64(k, dpp64_rows<kDppBcast31, 0xC>(k));
+    return readlane64(k, kWave - 1);
 }
 
 // Sum over the wavefront in a fixed order (wavefront-uniform result).
