@@ -290,3 +290,40 @@ def test_layer_forward_takes_the_fused_launch(lib, orc):
     ref = orc.moe_layer(x_np, L.lay, L.pool, c.k, logits=lg_np, shared_blob=L.shared)
     assert np.array_equal(M.topk_ids[:1].cpu().numpy(), ref["ids"])
     assert_close(bf16_dev_to_f64(out), ref["out_f64"], "forward out T=1")
+
+
+@pytest.mark.parametrize("name,H,E,k,I,shared,T", [
+    ("decode", 2048, 128, 8, 768, False, 1),
+    ("large_sparse", 4096, 256, 6, 2048, True, 2),
+])
+def test_fused_layer_tied_logits(lib, orc, name, H, E, k, I, shared, T):
+    """Logits with many exact ties (a few distinct values, signed zeros), so
+    that the choice at the k boundary is decided by the lower expert index:
+    ids and the permutation bit for bit against the oracle, out within the
+    tolerance."""
+    weights = "marginal_mxfp4" if name == "large_sparse" else "gauss_mxfp4"
+    L = layer(name, H, E, k, I, shared, weights=weights)
+    c = L.cfg
+    rng = np.random.default_rng(99)
+    lg_np = rng.choice(np.array([-1.0, -0.0, 0.0, 0.5, 0.5, 1.0], np.float32), size=(T, E))
+    x_np = synth.activations(c, T, step=7)
+    a = bufs(lib, c, T)
+    assert fused(lib, L, T, to_dev_bf16(x_np), to_dev(lg_np), a) == 0
+    torch.cuda.synchronize()
+    check_vs_oracle(orc, L, T, x_np, lg_np, a)
+
+
+def test_fused_layer_deterministic(lib):
+    """The same call twice on fresh buffers: every output bit for bit."""
+    L = layer("large_sparse", 4096, 256, 6, 2048, True, weights="marginal_mxfp4")
+    c = L.cfg
+    x = to_dev_bf16(synth.activations(c, 2, step=8))
+    lg = to_dev(synth.router_logits(c, 2, step=8))
+    runs = []
+    for _ in range(2):
+        b = bufs(lib, c, 2)
+        assert fused(lib, L, 2, x, lg, b) == 0
+        runs.append(b)
+    torch.cuda.synchronize()
+    for key in ("ids", "w", "off", "sp", "pr", "y", "out"):
+        assert torch.equal(runs[0][key], runs[1][key]), f"{key} differs between runs"
