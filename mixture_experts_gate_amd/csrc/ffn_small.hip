@@ -313,9 +313,11 @@ __global__ __launch_bounds__(kWave *kFsWaves) void ffn_small_kernel(DecArgs A1, 
     const DcMeta meta = fs_meta<FMT, SH>(A2, S, act, wv, nmine);
     DcExpert<FMT> es[D];
     WFrag<FMT> wr[D][NS2];
+    // the weights of this wavefront's first D experts (every one it has at
+    // these sizes) are requested before the wait, so they arrive during it
     if (nmine > 0) {
 #pragma unroll
-        for (int dd = 0; dd < D - 1; ++dd) {
+        for (int dd = 0; dd < D; ++dd) {
             dc_state<FMT>(A2, meta, dd < nmine ? dd : nmine - 1, es[dd]);
             dc_load<FMT, NS2>(es[dd], rb, lane, wr[dd], dd < nmine);
         }
@@ -342,12 +344,13 @@ __global__ __launch_bounds__(kWave *kFsWaves) void ffn_small_kernel(DecArgs A1, 
 #pragma unroll
             for (int dd = 0; dd < D; ++dd) {
                 if (i + dd < nmine) {
-                    const int fd = (dd + D - 1) % D, qn = i + dd + D - 1;
-                    const bool pf = qn < nmine;
-                    if (pf) dc_state<FMT>(A2, meta, qn, es[fd]);
-                    else es[fd] = es[dd];
-                    dc_load<FMT, NS2>(es[fd], rb, lane, wr[fd], pf);
                     dc_expert<FMT, NS2>(A2, es[dd], wr[dd], actL, yl, spl, rb, m, c, nrows);
+                    // the buffer just used takes the expert D further on
+                    const int qn = i + dd + D;
+                    if (qn < nmine) {
+                        dc_state<FMT>(A2, meta, qn, es[dd]);
+                        dc_load<FMT, NS2>(es[dd], rb, lane, wr[dd], true);
+                    }
                 }
             }
         }
