@@ -97,7 +97,7 @@ __device__ __forceinline__ void split_quad(const float (&v)[4], float inv, uint3
 }
 
 // Row split of bf16 rows [rows][K] into hi [rows][K], lo [rows][K] and hi
-// scale bytes [rows][K/32]. One thread per 32-element block.
+// scale bytes [rows][K/32]. Four threads per 32-element block.
 // Token-tile map of the tiled kernels: map[0] = M, the number of 64-token
 // tiles over all experts; map[1 + m] = e | (mt << 16) for the m-th tile in
 // expert order (tile mt of expert e). The always-on shared expert, when the
@@ -146,40 +146,37 @@ __global__ __launch_bounds__(256) void split_rows_kernel(const uint16_t *__restr
         build_tile_map(offsets, E, sh_rows, map);
         return;
     }
-    const long b = (long)blockIdx.x * 256 + threadIdx.x;
-    if (b >= nblk) return;
-    u32x4 q[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) q[j] = load_nt16(src + b * 32 + 8 * j);
+    // four threads per 32-element block, eight elements each, so that loads
+    // and stores are contiguous across the wavefront; the block maximum meets
+    // over the four lanes of a DPP quad (a block's threads are one quad)
+    const long g = (long)blockIdx.x * 256 + threadIdx.x;
+    const long b = g >> 2;
+    const int qd = (int)(g & 3);
+    const bool ok = b < nblk;
+    const u32x4 v = ok ? load_nt16(src + b * 32 + 8 * qd) : u32x4{0, 0, 0, 0};
     float amax = 0.0f;
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int c = 0; c < 4; ++c)
-            amax = fmaxf(amax, fmaxf(fabsf(bf16_bits_to_f32(q[j][c] & 0xFFFFu)),
-                                     fabsf(bf16_bits_to_f32(q[j][c] >> 16))));
+    for (int c = 0; c < 4; ++c)
+        amax = fmaxf(amax, fmaxf(fabsf(bf16_bits_to_f32(v[c] & 0xFFFFu)),
+                                 fabsf(bf16_bits_to_f32(v[c] >> 16))));
+    // quad_perm [1,0,3,2], then [2,3,0,1]
+    amax = fmaxf(amax, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(amax), 0xB1,
+                                                                  0xF, 0xF, false)));
+    amax = fmaxf(amax, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(amax), 0x4E,
+                                                                  0xF, 0xF, false)));
     const int sb = split_scale_byte(amax);
     const float inv = split_inv_scale(sb);
-    u32x4 oh[2], ol[2];
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int c = 0; c < 4; c += 2) {
-            const float v[4] = {bf16_bits_to_f32(q[j][c] & 0xFFFFu), bf16_bits_to_f32(q[j][c] >> 16),
-                                bf16_bits_to_f32(q[j][c + 1] & 0xFFFFu),
-                                bf16_bits_to_f32(q[j][c + 1] >> 16)};
-            uint32_t h, l;
-            split_quad(v, inv, h, l);
-            oh[j >> 1][2 * (j & 1) + (c >> 1)] = h;
-            ol[j >> 1][2 * (j & 1) + (c >> 1)] = l;
-        }
-    u32x4 *ph = reinterpret_cast<u32x4 *>(hi + b * 32);
-    u32x4 *pl = reinterpret_cast<u32x4 *>(lo + b * 32);
-    ph[0] = oh[0];
-    ph[1] = oh[1];
-    pl[0] = ol[0];
-    pl[1] = ol[1];
-    sc[b] = (uint8_t)sb;
+    const float v0[4] = {bf16_bits_to_f32(v[0] & 0xFFFFu), bf16_bits_to_f32(v[0] >> 16),
+                         bf16_bits_to_f32(v[1] & 0xFFFFu), bf16_bits_to_f32(v[1] >> 16)};
+    const float v1[4] = {bf16_bits_to_f32(v[2] & 0xFFFFu), bf16_bits_to_f32(v[2] >> 16),
+                         bf16_bits_to_f32(v[3] & 0xFFFFu), bf16_bits_to_f32(v[3] >> 16)};
+    uint2 oh, ol;
+    split_quad(v0, inv, oh.x, ol.x);
+    split_quad(v1, inv, oh.y, ol.y);
+    if (!ok) return;
+    *reinterpret_cast<uint2 *>(hi + b * 32 + 8 * qd) = oh;
+    *reinterpret_cast<uint2 *>(lo + b * 32 + 8 * qd) = ol;
+    if (qd == 0) sc[b] = (uint8_t)sb;
 }
 
 // ------------------------------------------------------------ GEMM tiles --
@@ -690,7 +687,7 @@ int ffn_prefill(const uint16_t *x, const int32_t *sorted_pair, const int32_t *of
     int32_t *map = reinterpret_cast<int32_t *>(xsc + al256((size_t)T * H / 32));
 
     const long nblk = (long)T * H / 32;
-    const long grid = (nblk + 255) / 256 + 1;   // + the tile-map workgroup
+    const long grid = (nblk * 4 + 255) / 256 + 1;   // four threads per block, + the tile-map workgroup
     if (grid > 0x7FFFFFFFL) return MOE_EUNSUPPORTED;
     MOE_LAUNCH(K_PRE_SPLIT, split_rows_kernel, dim3((unsigned)grid), dim3(256), 0, s, x, nblk,
                                  xhi, xlo, xsc, offsets, E, shared ? T : 0, map);

@@ -376,7 +376,8 @@ static int launch_small(hipStream_t s, const DecArgs &A1, const DecArgs &A2, con
     auto kern = ffn_small_kernel<SPW1, NS2, SH>;
     const size_t lds = fs_lds_bytes(A1.E, F.T * A1.k, F.nrows, NS2);
     static bool attr = false;
-    static int per_cu = 0;
+    static size_t occ_lds = 0;      // LDS size of the last occupancy query, and its answer
+    static int occ_per_cu = 0;
     if (!attr) {
         if (int rc = check_hip(hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                                    hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -386,10 +387,15 @@ static int launch_small(hipStream_t s, const DecArgs &A1, const DecArgs &A2, con
     }
     if (lds > 96 * 1024) return MOE_EUNSUPPORTED;
     // every workgroup resident at once, or no launch
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, kWave * kFsWaves, lds) !=
-            hipSuccess ||
-        per_cu < 1)
-        return MOE_EUNSUPPORTED;
+    if (lds != occ_lds) {
+        int per_cu = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, kWave * kFsWaves, lds) !=
+            hipSuccess)
+            per_cu = 0;
+        occ_lds = lds;
+        occ_per_cu = per_cu;
+    }
+    if (occ_per_cu < 1) return MOE_EUNSUPPORTED;
     const int G = num_cus();
     if (F.nd2 > G || G % kFsGroups) return MOE_EUNSUPPORTED;
     MOE_LAUNCH(K_DEC_SMALL, kern, dim3((unsigned)G), dim3(kWave * kFsWaves), lds, s, A1, A2, S, F);
