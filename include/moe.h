@@ -322,19 +322,21 @@ int moe_permute_ffn_combine(const uint16_t *x_bf16, const int32_t *topk_ids,
  * activation rows.
  *
  * Taken for MXFP4 weights, 1 <= T <= 8, T*k (+ T with the shared expert) <=
- * 15 rows, E <= 256, H in {1024, 2048, 4096} and I/128 in {4, 6, 16} (H/16
- * workgroups must fit one per compute unit); otherwise MOE_EUNSUPPORTED
- * before any device work (use moe_route + moe_permute_ffn_combine).
+ * 31 rows, E <= 256 and (H, I) one of (1024, 512), (2048, 512), (2048, 768),
+ * (4096, 768), (4096, 2048), on a device whose compute units hold one
+ * workgroup each for all H/16 down-projection workgroups (a multiple of 16
+ * compute units, at least H/16); otherwise MOE_EUNSUPPORTED before any
+ * device work (use moe_route + moe_permute_ffn_combine).
  *   logits [T][E] fp32; renormalize as moe_route; topk_ids/topk_w [T][k] out;
  *   offsets [E+1], sorted_pair and pair_row [T*k] out; y_bf16, out_bf16, ws
  *   and ws_bytes as moe_permute_ffn_combine.
  *   sync: MOE_LAYER_SYNC_BYTES of device memory (8-byte aligned) holding the
  *     launch's barrier counters. Zero it before the first call that uses it
  *     (e.g. one hipMemset); the calls keep it consistent from then on (its
- *     counters only grow). One of its words becomes nonzero if a barrier
- *     wait ran out (about a second), in which case that call's outputs are
- *     not valid; this happens only if the launch's workgroups cannot all be
- *     resident at once. Calls on one sync buffer must not overlap in time
+ *     counters only grow). The 64-bit word at byte offset 4224 becomes
+ *     nonzero if a barrier wait ran out (about a second), in which case that
+ *     call's outputs are not valid; this happens only if the launch's
+ *     workgroups cannot all be resident at once. Calls on one sync buffer must not overlap in time
  *     (one stream, or ordered streams); calls that may run side by side need
  *     their own sync buffers and workspaces, and two such launches on one
  *     device may each hold compute units the other waits for: run them on one

@@ -34,7 +34,7 @@
 namespace moe {
 
 constexpr int kFsWaves = kDcWaves;      // 8 wavefronts per workgroup
-constexpr int kFsMaxRows = kDcMaxRows;  // activation rows (T*k, + T shared)
+constexpr int kFsMaxRows = 31;          // activation rows (T*k, + T shared)
 constexpr int kFsVpl = 4;               // logits per lane: E <= 256
 constexpr unsigned kFsSpinLimit = 1u << 21;
 
@@ -231,18 +231,26 @@ __device__ __forceinline__ void lds_dma16_coherent(const void *src, void *dst) {
                                      16 /* sc1 */);
 }
 
-// Dynamic LDS: per-wavefront permutation regions, the workgroup's ids, the
-// routed ids and weights, then the down + combine part (activation rows in
-// operand order, y columns, pair of each row, router weights).
-__host__ __device__ constexpr size_t fs_ids_bytes(int E, int n) {
-    return ((size_t)kFsWaves * ids_wave_ints(E, n) + 2 * kFsMaxRows + 2) * 4;
+// LDS (all dynamic): a head that lives through the launch (routed ids and
+// weights, each row's pair, the router weight of each pair; 32 entries each),
+// then one region used twice: by the gate/up part (the K-split partial sums,
+// then the wavefronts' permutation regions) and, once those are dead (after
+// the grid barrier), by the down + combine part (the activation rows in
+// operand order, 4 KB per 16 rows and 128 columns, then the y columns).
+constexpr size_t kFsHead = 4 * 32 * 4;
+constexpr size_t kFsRed = (size_t)2 * (kFsWaves - 1) * 2 * 4 * kWave * 4;
+__host__ __device__ constexpr size_t fs_phase1_bytes(int E, int n) {
+    return kFsRed + (size_t)kFsWaves * ids_wave_ints(E, n) * 4;
 }
+__host__ __device__ constexpr size_t fs_phase3_bytes(int nrows, int ns2) {
+    return (size_t)((nrows + 15) / 16) * ns2 * 4096 + (size_t)nrows * 16 * 4;
+}
+constexpr size_t kFsMaxLds = 160 * 1024;
 
 template <int SPW1, int NS2, bool SH>
 __global__ __launch_bounds__(kWave *kFsWaves) void ffn_small_kernel(DecArgs A1, DecArgs A2,
                                                                     ShArgs S, FsArgs F) {
     constexpr int FMT = MOE_W_MXFP4;
-    __shared__ float red[2][kFsWaves - 1][2][4][kWave];
     extern __shared__ __attribute__((aligned(16))) uint8_t fs_lds[];
     const int lane = lane_id();
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -252,10 +260,13 @@ __global__ __launch_bounds__(kWave *kFsWaves) void ffn_small_kernel(DecArgs A1, 
     const int G = gridDim.x;
 
     const int wints = ids_wave_ints(E, n);
-    int *ids_lds = reinterpret_cast<int *>(fs_lds);
-    int32_t *rid = ids_lds + kFsWaves * wints;      // [n] routed ids
-    float *rw = reinterpret_cast<float *>(rid + kFsMaxRows + 1);   // [n] weights
-    uint8_t *dc = fs_lds + fs_ids_bytes(E, n);
+    int32_t *rid = reinterpret_cast<int32_t *>(fs_lds);        // [n] routed ids
+    float *rw = reinterpret_cast<float *>(rid + 32);           // [n] weights
+    int *spl = reinterpret_cast<int *>(rw + 32);               // [nrows] pair of each row
+    float *wl = reinterpret_cast<float *>(spl + 32);           // [n] router weight of each pair
+    uint8_t *reg = fs_lds + kFsHead;                           // the shared region
+    auto &red = *reinterpret_cast<float (*)[2][kFsWaves - 1][2][4][kWave]>(reg);
+    int *ids_lds = reinterpret_cast<int *>(reg + kFsRed);
 
     // 1. routing: wavefront t routes token t
     if (wv < F.T) {
@@ -304,10 +315,9 @@ __global__ __launch_bounds__(kWave *kFsWaves) void ffn_small_kernel(DecArgs A1, 
     static_assert(D >= 2, "down+combine needs two weight buffers");
     const int rb = blockIdx.x;
     const int nrows = F.nrows, ngroups = (nrows + 15) / 16;
-    uint8_t *actL = dc;
-    float *yl = reinterpret_cast<float *>(dc + (size_t)ngroups * NS2 * 4096);
-    int *spl = reinterpret_cast<int *>(yl + nrows * 16);
-    float *wl = reinterpret_cast<float *>(spl + nrows);
+    // (written only after the barrier, when the gate/up part's LDS is dead)
+    uint8_t *actL = reg;
+    float *yl = reinterpret_cast<float *>(reg + (size_t)ngroups * NS2 * 4096);
 
     const int nmine = act.count > wv ? (act.count - wv + kFsWaves - 1) / kFsWaves : 0;
     const DcMeta meta = fs_meta<FMT, SH>(A2, S, act, wv, nmine);
@@ -366,8 +376,8 @@ __global__ __launch_bounds__(kWave *kFsWaves) void ffn_small_kernel(DecArgs A1, 
 }
 
 static size_t fs_lds_bytes(int E, int n, int nrows, int ns2) {
-    return fs_ids_bytes(E, n) + (size_t)((nrows + 15) / 16) * ns2 * 4096 +
-           (size_t)nrows * 16 * 4 + (size_t)nrows * 4 + (size_t)n * 4;
+    const size_t p1 = fs_phase1_bytes(E, n), p3 = fs_phase3_bytes(nrows, ns2);
+    return kFsHead + (p1 > p3 ? p1 : p3);
 }
 
 template <int SPW1, int NS2, bool SH>
@@ -381,11 +391,11 @@ static int launch_small(hipStream_t s, const DecArgs &A1, const DecArgs &A2, con
     if (!attr) {
         if (int rc = check_hip(hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                                    hipFuncAttributeMaxDynamicSharedMemorySize,
-                                                   96 * 1024)))
+                                                   (int)kFsMaxLds)))
             return rc;
         attr = true;
     }
-    if (lds > 96 * 1024) return MOE_EUNSUPPORTED;
+    if (lds > kFsMaxLds) return MOE_EUNSUPPORTED;
     // every workgroup resident at once, or no launch
     if (lds != occ_lds) {
         int per_cu = 0;

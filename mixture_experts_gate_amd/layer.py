@@ -24,7 +24,7 @@ from .synth import blob_layout
 _PERMUTE_IN_FFN_PAIRS = (8, 512)
 # activation rows (T*k, + T with the shared expert) up to which forward()
 # tries the one-launch layer (moe_layer_fused) when the logits are given
-_ONE_LAUNCH_ROWS = 15
+_ONE_LAUNCH_ROWS = 31
 
 FMT = {"bf16": _lib.MOE_W_BF16, "mxfp4": _lib.MOE_W_MXFP4, "nvfp4": _lib.MOE_W_NVFP4,
        "fp8": _lib.MOE_W_FP8}

@@ -145,6 +145,12 @@ _CASES = [
     ("small", 1024, 64, 4, 512, True, 3),
     ("mid", 2048, 96, 3, 512, True, 2),
     ("wide", 4096, 200, 2, 768, False, 7),
+    # 16 to 31 activation rows: two 16-row groups in the down part
+    ("decode", 2048, 128, 8, 768, False, 2),
+    ("decode", 2048, 128, 8, 768, False, 3),
+    ("large_sparse", 4096, 256, 6, 2048, True, 3),
+    ("large_sparse", 4096, 256, 6, 2048, True, 4),
+    ("small", 1024, 64, 4, 512, True, 6),
 ]
 
 
@@ -170,12 +176,16 @@ def test_fused_layer_vs_chain_and_oracle(lib, orc, name, H, E, k, I, shared, T):
         torch.cuda.synchronize()
         for key in ("ids", "w", "off", "sp", "pr"):
             assert torch.equal(a[key], b[key]), f"{key} differs from the launch chain"
-        if H // 128 in (16, 32):
-            # the chain's gate/up tiles also split K over 8 wavefronts here
+        rows = T * k + (T if shared else 0)
+        if H // 128 in (16, 32) and rows <= 15:
+            # the chain's gate/up tiles also split K over 8 wavefronts here,
+            # and its down projection + combine is the same launch code
             for key in ("y", "out"):
                 assert torch.equal(a[key], b[key]), f"{key} differs from the launch chain"
         else:
-            # 8 slabs: the chain splits K over 4 wavefronts (another fp32 order)
+            # 8 slabs: the chain splits K over 4 wavefronts; from 16 rows its
+            # down projection is the tiled weight-streaming launch (other fp32
+            # orders)
             assert_close(bf16_dev_to_f64(a["out"]), bf16_dev_to_f64(b["out"]), "out vs chain")
         check_vs_oracle(orc, L, T, x_np, lg_np, a)
 
@@ -261,7 +271,7 @@ def test_fused_layer_declines_outside_its_sizes(lib):
     every output untouched."""
     L = layer("decode", 2048, 128, 8, 768, False)
     c = L.cfg
-    T = 2                                   # 16 rows: more than one token pass
+    T = 4                                   # 32 rows: more than the down part's two row groups
     b = bufs(lib, c, T)
     x = to_dev_bf16(synth.activations(c, T))
     lg = to_dev(synth.router_logits(c, T))

@@ -186,13 +186,13 @@ def test_layer_fused_argument_errors(lib):
     assert call(T_=0) == lib.MOE_EINVAL
     assert call(k_=200) == lib.MOE_EINVAL                    # k > E
     big = 1 << 30
-    assert call(T_=2, wsb=big) == lib.MOE_EUNSUPPORTED       # 16 rows
+    assert call(T_=4, wsb=big) == lib.MOE_EUNSUPPORTED       # 32 rows
     assert call(T_=9, k_=1, wsb=big) == lib.MOE_EUNSUPPORTED  # more tokens than wavefronts
     assert call(E_=300, wsb=big) == lib.MOE_EUNSUPPORTED     # ids past 8 bits
     assert call(fmt=0, wsb=big) == lib.MOE_EUNSUPPORTED      # bf16 weights
     assert call(H_=1536, wsb=big) == lib.MOE_EUNSUPPORTED    # 12 slabs of gate/up
     assert call(I_=1024, wsb=big) == lib.MOE_EUNSUPPORTED    # 8 slabs of down
-    assert call(shared=dummy, k_=7, T_=2, wsb=big) == lib.MOE_EUNSUPPORTED  # 16 rows
+    assert call(shared=dummy, k_=7, T_=4, wsb=big) == lib.MOE_EUNSUPPORTED  # 32 rows
 
 
 def test_cache_reserve_argument_errors(lib):
