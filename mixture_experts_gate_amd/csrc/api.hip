@@ -25,8 +25,11 @@ int pre_group(int stage) {
     return g < 1 ? 1 : g;
 }
 
-// measured on the decode layer at T = 8..64: 64/256, 38/256, 38/256, 23/256
-constexpr int kDecSplitDefault = 64 | (38 << 8) | (38 << 16) | (23 << 24);
+// measured on the decode layer at T = 8..64 and the large sparse layer at
+// T = 64 (graph-replayed steps): stage 1 96/256 by slot and none by position
+// within a slot (68.3 against 69.9 us per T=64 step with 64/256 and 38/256),
+// stage 2 38/256 and 23/256
+constexpr int kDecSplitDefault = 96 | (0 << 8) | (38 << 16) | (23 << 24);
 static std::atomic<int> g_dec_split{kDecSplitDefault};
 void dec_split_weights(int stage, float *w_slot, float *w_pos) {
     const unsigned v = (unsigned)g_dec_split.load(std::memory_order_relaxed);
