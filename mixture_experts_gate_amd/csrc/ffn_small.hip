@@ -2,7 +2,7 @@
 // top-k from given logits), permutation, gate/up + SwiGLU, down projection
 // and weighted combine.
 //
-// At batch 1 or 2 (the single-user decoding the pages are built around:
+// At one to four tokens (the single-user decoding the pages are built around:
 // winzheng.com page, "Why Now of All Times", a few routed experts per token
 // and layer) the layer moves a few tens of MB, and a chain of launches costs
 // more than the bytes: every dependent launch adds its start-up, and each
@@ -10,7 +10,7 @@
 // one persistent launch does it all:
 //   1. every workgroup routes the T tokens itself (one wavefront per token,
 //      the router kernel's device code, so ids and weights are the router's
-//      bit for bit) and derives the permutation of the at most 15 pairs in
+//      bit for bit) and derives the permutation of the at most 31 pairs in
 //      registers; workgroup 0 writes ids, weights and the permutation out;
 //   2. gate/up tiles (16 gate + 16 up rows over K = H, K split over the 8
 //      wavefronts, the weight-streaming kernel's tile code), split over all
@@ -21,8 +21,9 @@
 //      projection and the combine then run as in the down + combine launch
 //      (the activation rows staged in LDS in operand order, y and out
 //      written; out is the combine's expression on the bf16 y).
-// All workgroups must be resident at once: the grid is at most one workgroup
-// per compute unit and the launch is refused unless the occupancy allows it.
+// All workgroups must be resident at once: the grid is one workgroup per
+// compute unit and the launch is refused unless the occupancy allows at least
+// that many.
 // The barrier's counters live in a caller buffer (zero before the first
 // call; the counters only grow, so no call has to return them to zero); the
 // wait is bounded (a flag reports a wait that ran out, and the call's
@@ -162,9 +163,9 @@ __device__ __forceinline__ void fs_wait(uint64_t *sync, int b, uint64_t want) {
 }
 
 
-// ---- the permutation of at most 15 pairs, in registers -------------------
+// ---- the permutation of at most 31 pairs, in registers -------------------
 //
-// The state init_ids + rank_ids build, for n <= 15 valid pairs (lane p holds
+// The state init_ids + rank_ids build, for n <= 31 valid pairs (lane p holds
 // pair p) and T <= 8 tokens, so every expert has at most 8 rows (one block):
 // offsets of the active experts, each pair's stable rank (pairs of lower
 // experts, then earlier pairs of its own), the active-expert blocks per group
