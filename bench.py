@@ -255,6 +255,8 @@ def algorithmic_bytes(wl, U):
         "ffn_prefill_down": U * w2 + n * I * 2 + n * H * 2 + s2,
         "combine": n * H * 2 + n * 4 + T * H * 2 + (T * H * 2 if c.n_shared else 0),
         "layer": U * lay.nbytes + 2 * T * H * 2 + T * E * 4 + n * 8 + sh,
+        # the one-launch layer moves the whole layer's bytes
+        "layer_fused": U * lay.nbytes + 2 * T * H * 2 + T * E * 4 + n * 8 + sh,
     }
 
 
