@@ -801,7 +801,7 @@ __device__ __forceinline__ void write_perm(const DecArgs &A, const IdsArgs &I,
 }
 
 template <int FMT, int STAGE, int SPW, int KS, int NB, bool YF32, bool FULL, bool SH, bool IDS,
-          bool COH = false, int DEPTH = 0>
+          bool COH = false>
 __device__ __forceinline__ void dec_tiles(const DecArgs &A, const ShArgs &S, const ActiveSet &act,
                                           float (&red)[2][KS > 1 ? KS - 1 : 1][NB][4][kWave],
                                           int t0, int n);
@@ -840,10 +840,9 @@ __device__ __forceinline__ void ffn_dec_body(const DecArgs &A, const ShArgs &S, 
 
 // Tiles t0 .. t0 + n - 1 (n > 0) of a launch, by every wavefront of the
 // workgroup (the K-split reduction has workgroup barriers). COH: stage-1
-// activation stores written through to the coherence point. DEPTH: weight
-// tiles held in registers (0: the default of the stage).
+// activation stores written through to the coherence point.
 template <int FMT, int STAGE, int SPW, int KS, int NB, bool YF32, bool FULL, bool SH, bool IDS,
-          bool COH, int DEPTH>
+          bool COH>
 __device__ __forceinline__ void dec_tiles(const DecArgs &A, const ShArgs &S, const ActiveSet &act,
                                           float (&red)[2][KS > 1 ? KS - 1 : 1][NB][4][kWave],
                                           int t0, int n) {
@@ -856,7 +855,7 @@ __device__ __forceinline__ void dec_tiles(const DecArgs &A, const ShArgs &S, con
     // weights of tiles i+1 .. i+D-1 are in flight into the others (no copies
     // between them, so nothing waits for a prefetch before it is needed).
     // Slots past the end repeat the last tile's position and load nothing.
-    constexpr int D = DEPTH ? DEPTH : STAGE == 2 ? kDepth2 : kDepth;
+    constexpr int D = STAGE == 2 ? kDepth2 : kDepth;
     ExpertState<FMT> es[D];
     TilePos pos[D];
     WFrag<FMT> wr[D][SPW][NB];

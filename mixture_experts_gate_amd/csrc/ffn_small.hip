@@ -28,6 +28,8 @@
 // call; the counters only grow, so no call has to return them to zero); the
 // wait is bounded (a flag reports a wait that ran out, and the call's
 // results are then not valid).
+#include <atomic>
+
 #define MOE_DEC_SMALL_UNIT 1
 #include "ffn_decode.hip"
 #include "route_dev.hpp"
@@ -119,8 +121,7 @@ __device__ __forceinline__ DcMeta fs_meta(const DecArgs &A, const ShArgs &S, con
 // the release words are polled and the rows read back with device-coherent
 // loads (measured faster than one acquire per workgroup followed by cached
 // reads, and than cache write-backs at the arrivals). Order between a
-// wavefront's own accesses
-// comes from waiting for their completion (s_waitcnt, or the value an atomic
+// wavefront's own accesses comes from waiting for their completion (s_waitcnt, or the value an atomic
 // returns) before the next is issued.
 //
 // Arrival of workgroup b (one lane, after its activation stores completed);
@@ -387,8 +388,10 @@ static int launch_small(hipStream_t s, const DecArgs &A1, const DecArgs &A2, con
     auto kern = ffn_small_kernel<SPW1, NS2, SH>;
     const size_t lds = fs_lds_bytes(A1.E, F.T * A1.k, F.nrows, NS2);
     static bool attr = false;
-    static size_t occ_lds = 0;      // LDS size of the last occupancy query, and its answer
-    static int occ_per_cu = 0;
+    // LDS size of the last occupancy query (high half) and its answer (low
+    // half), in one word so that calls from several host threads read a
+    // consistent pair
+    static std::atomic<uint64_t> occ{0};
     if (!attr) {
         if (int rc = check_hip(hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                                    hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -398,15 +401,16 @@ static int launch_small(hipStream_t s, const DecArgs &A1, const DecArgs &A2, con
     }
     if (lds > kFsMaxLds) return MOE_EUNSUPPORTED;
     // every workgroup resident at once, or no launch
-    if (lds != occ_lds) {
+    uint64_t o = occ.load(std::memory_order_relaxed);
+    if ((o >> 32) != lds) {
         int per_cu = 0;
         if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, kWave * kFsWaves, lds) !=
-            hipSuccess)
+            hipSuccess || per_cu < 0)
             per_cu = 0;
-        occ_lds = lds;
-        occ_per_cu = per_cu;
+        o = ((uint64_t)lds << 32) | (uint32_t)per_cu;
+        occ.store(o, std::memory_order_relaxed);
     }
-    if (occ_per_cu < 1) return MOE_EUNSUPPORTED;
+    if ((uint32_t)o < 1) return MOE_EUNSUPPORTED;
     const int G = num_cus();
     if (F.nd2 > G || G % kFsGroups) return MOE_EUNSUPPORTED;
     MOE_LAUNCH(K_DEC_SMALL, kern, dim3((unsigned)G), dim3(kWave * kFsWaves), lds, s, A1, A2, S, F);
