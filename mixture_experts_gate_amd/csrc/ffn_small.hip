@@ -172,7 +172,7 @@ __device__ __forceinline__ void fs_wait(uint64_t *sync, int b, uint64_t want) {
 // experts, then earlier pairs of its own), the active-expert blocks per group
 // of 64 and the sorted pairs in this wavefront's LDS region (loff: [E + 1],
 // the offsets of the active experts and of the expert after each; lsrt: [n]).
-template <bool SH>
+template <bool SH, int MAXN>
 __device__ __forceinline__ int init_small(ActiveSet &act, const int32_t *rid, int n, int E,
                                           const ShArgs &S, int *wl) {
     const int lane = lane_id();
@@ -180,14 +180,15 @@ __device__ __forceinline__ int init_small(ActiveSet &act, const int32_t *rid, in
     act.lsrt = wl + 2 * E + 1;
     // every pair's id in registers (LDS broadcast reads; -1 past n), so that
     // the comparisons below stay in the vector unit: a lane read per pair
-    // (vector -> scalar -> vector) made this part several times slower
-    int idq[kFsMaxRows];
+    // (vector -> scalar -> vector) made this part several times slower.
+    // MAXN >= n: the unrolled length of the loops
+    int idq[MAXN];
 #pragma unroll
-    for (int q = 0; q < kFsMaxRows; ++q) idq[q] = q < n ? rid[q] : -1;
+    for (int q = 0; q < MAXN; ++q) idq[q] = q < n ? rid[q] : -1;
     const int idp = lane < n ? rid[lane] : -1;
     int less = 0, same = 0, sbefore = 0;
 #pragma unroll
-    for (int q = 0; q < kFsMaxRows; ++q) {
+    for (int q = 0; q < MAXN; ++q) {
         const int iq = idq[q];
         less += (iq >= 0 && iq < idp) ? 1 : 0;
         same += iq == idp ? 1 : 0;
@@ -210,7 +211,7 @@ __device__ __forceinline__ int init_small(ActiveSet &act, const int32_t *rid, in
             const int e = i * kWave + lane;
             bool on = false;
 #pragma unroll
-            for (int q = 0; q < kFsMaxRows; ++q) on = on || idq[q] == e;
+            for (int q = 0; q < MAXN; ++q) on = on || idq[q] == e;
             const uint64_t mb = __ballot(on);
             act.incl[i] = __popcll(mb & (lanemask_lt() | (1ull << lane)));
             act.gtot[i] = __popcll(mb);
@@ -279,7 +280,11 @@ __global__ __launch_bounds__(kWave *kFsWaves) void ffn_small_kernel(DecArgs A1, 
     }
     __syncthreads();
     ActiveSet act;
-    const int rank = init_small<SH>(act, rid, n, E, S, ids_lds + wv * wints);
+    // (shorter forms for up to 8 and 16 pairs: one or two tokens at k <= 8)
+    int *const wl_ = ids_lds + wv * wints;
+    const int rank = n <= 8    ? init_small<SH, 8>(act, rid, n, E, S, wl_)
+                     : n <= 16 ? init_small<SH, 16>(act, rid, n, E, S, wl_)
+                               : init_small<SH, kFsMaxRows>(act, rid, n, E, S, wl_);
     if (blockIdx.x == 0 && wv == 0) {
         // the router's and the permutation's outputs
         if (lane < n) {
