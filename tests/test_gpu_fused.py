@@ -151,6 +151,13 @@ _CASES = [
     ("large_sparse", 4096, 256, 6, 2048, True, 3),
     ("large_sparse", 4096, 256, 6, 2048, True, 4),
     ("small", 1024, 64, 4, 512, True, 6),
+    # the permutation's unrolled forms (up to 8, 16 and 31 routed pairs) at
+    # their edges: 8 pairs + a shared row, 9, 17, 20 + 2 shared rows, 31
+    ("small", 1024, 64, 8, 512, True, 1),
+    ("small", 1024, 64, 3, 512, False, 3),
+    ("mid", 2048, 96, 17, 512, False, 1),
+    ("mid", 2048, 96, 10, 512, True, 2),
+    ("small", 1024, 64, 31, 512, False, 1),
 ]
 
 
